@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked Gated DeltaNet prefill on one MI355X.
+
+One step = the whole prefill (chunk table when packed, the fused L2-norm /
+gate-prep / WY kernel, the fused state-scan / output kernel) over one batch
+of seeded synthetic inputs already resident in device memory.  Default
+workload: one 4096-token prompt, 16 heads, d_k = d_v = 128, chunk 64, bf16.
+
+Prints ONE JSON line (rank 0) with the tokens/s, a roofline object for the
+dominant kernel (HIP events around its launches on the stream it runs on)
+and the float64 oracle's throughput on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/sec at T=4096,H=16,d=128 bf16; % of MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published
+F32_MFMA_PEAK_TFLOPS = 157.3
+KERNEL_SOURCES = ["gated_deltanet_02_amd/csrc/gdn_kernels.hip",
+                  "gated_deltanet_02_amd/csrc/gdn_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w) -> int:
+    """Bytes the prefill must move: read q, k, v, g, beta; write out; read
+    the initial state when given; write the final state (fp32)."""
+    es = w.q.element_size()
+    T, hk, dk = w.q.shape
+    hv, dv = w.v.shape[1], w.v.shape[2]
+    per_token = 2 * hk * dk * es + 2 * hv * dv * es + 2 * hv * 4
+    states = w.n_seqs * hv * dk * dv * 4 * (2 if w.init_state is not None else 1)
+    return T * per_token + states
+
+
+def algorithmic_flops(w) -> int:
+    """Triangle-aware flops per value-head token of the chunked form:
+    (C-1)dk (K^K^T) + (C+1)dk (Q^K^T) + C^2/3 (inverse) + (C+1)(dk+dv) (W, U~)
+    + 6 dk dv (W H, K~^T U, Q^ H) + (C+1) dv (P U)."""
+    C = w.chunk
+    T, hk, dk = w.q.shape
+    hv, dv = w.v.shape[1], w.v.shape[2]
+    per = (C - 1) * dk + (C + 1) * dk + C * C / 3 + (C + 1) * (dk + dv) + 6 * dk * dv + (C + 1) * dv
+    return int(T * hv * per)
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if the record
+    matches the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(workload, {}).get(kernel)
+    if not ent or ent.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The float64 oracle as it stands, on the host cores: repeat the whole
+    workload until about ``budget_s`` seconds have passed."""
+    from oracle import oracle
+    oracle.load()
+    cores = len(os.sched_getaffinity(0))
+    units = w.n_seqs * w.v.shape[1]
+    threads = max(1, min(cores, units))
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.reference_workload(w, threads=threads)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 200:
+            break
+    return {"value": runs * w.t_total / el, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the full workload ({w.t_total} tokens x {w.v.shape[1]} heads) "
+                      f"run {runs} times, {el:.1f} s wall, float64 token recurrence, "
+                      f"one thread per (sequence, head) of {units}, {cores} host cores visible"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prompt_4k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_02_amd as G
+    from gated_deltanet_02_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 5 copies of {n} bytes")
+        return
+
+    w = W.make_workload(args.workload)
+    log(f"workload {args.workload}: T={w.t_total} N={w.n_seqs} dims={w.dims} chunk={w.chunk}")
+    d = W.to_device(w, dev)
+    cu = d["cu_seqlens"] if w.n_seqs > 1 else None
+    opts = G.options(chunk=w.chunk)
+    full = G.PreparedPrefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, d["init_state"],
+                             d["out"], d["final_state"], opts=opts)
+    pre = full.with_stages(G.STAGE_TABLE | G.STAGE_WY)
+    scan = full.with_stages(G.STAGE_SCAN)
+
+    for _ in range(args.warmup):
+        pre()
+        scan()
+    torch.cuda.synchronize()
+    assert torch.isfinite(d["out"].float()).all()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        pre()
+        ev[i][1].record()
+        scan()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / K
+    t_pre = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    t_scan = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    t_gpu = sum(e[0].elapsed_time(e[2]) for e in ev) / K
+    kernels = {"gdn_wy_kernel(+table)": t_pre, "gdn_scan_kernel": t_scan}
+    dom = max(kernels, key=kernels.get)
+    t_dom = kernels[dom]
+    nbytes = algorithmic_bytes(w)
+    nflops = algorithmic_flops(w)
+    achieved = nbytes / (t_dom * 1e-3) / 1e9
+    traffic = load_traffic(args.workload, dom)
+    bf16 = w.q.dtype == torch.bfloat16
+    mfma_peak = BF16_MFMA_PEAK_TFLOPS if bf16 else F32_MFMA_PEAK_TFLOPS
+    result = {
+        "metric": METRIC,
+        "value": w.t_total / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded; q, k unit rows, v ~ N(0,1), g ~ U(g_low,0), beta = sigmoid)",
+        "config": {"workload": args.workload, "T": w.t_total, "n_seqs": w.n_seqs,
+                   "hk": int(w.q.shape[1]), "hv": int(w.v.shape[1]),
+                   "dk": int(w.q.shape[2]), "dv": int(w.v.shape[2]), "chunk": w.chunk,
+                   "seed": 0, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_ms": t_dom},
+        "path_roofline": {"hbm_GBs": nbytes / (ms_step * 1e-3) / 1e9,
+                          "hbm_frac": nbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "mfma_TFLOPs": nflops / (ms_step * 1e-3) / 1e12,
+                          "mfma_frac": nflops / (ms_step * 1e-3) / 1e12 / mfma_peak,
+                          "algorithmic_flops": nflops},
+        "kernel_ms": {k: round(v, 5) for k, v in kernels.items()},
+        "gpu_event_ms_per_step": t_gpu,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on the host cores ...")
+        result["cpu_baseline"] = cpu_baseline(w)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,249 @@
+"""ctypes binding of libgdn.so (the C ABI in include/gdn.h).
+
+Argument marshalling only: torch tensors become ``gdn_tensor`` descriptors
+and the current HIP stream is passed through.  Every step of the prefill runs
+in the library's gfx950 kernels; there is no fallback.  The library is found
+at $GDN_LIB or next to this file (built by ``gated_deltanet_02_amd.build``);
+if it is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+GDN_OK = 0
+STATUS_NAMES = {0: "GDN_OK", -1: "GDN_ERR_NULL_ARG", -2: "GDN_ERR_DTYPE",
+                -3: "GDN_ERR_SHAPE", -4: "GDN_ERR_LAYOUT",
+                -5: "GDN_ERR_UNSUPPORTED", -6: "GDN_ERR_WORKSPACE",
+                -7: "GDN_ERR_HIP"}
+STAGE_TABLE, STAGE_WY, STAGE_SCAN, STAGE_ALL = 1, 2, 4, 7
+EXPORTED = ("gdn_abi_version", "gdn_default_options", "gdn_prefill",
+            "gdn_prefill_ex", "gdn_workspace_size", "gdn_get_workspace_layout",
+            "gdn_status_string", "gdn_last_error")
+
+_DTYPES = {torch.bfloat16: 1, torch.float32: 2, torch.int32: 3}
+
+
+class GdnTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("ndim", ctypes.c_int32), ("shape", ctypes.c_int64 * 4),
+                ("stride", ctypes.c_int64 * 4)]
+
+
+class GdnOptions(ctypes.Structure):
+    _fields_ = [("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("l2_eps", ctypes.c_float), ("stages", ctypes.c_uint32)]
+
+
+class GdnWorkspaceLayout(ctypes.Structure):
+    _fields_ = [("total_bytes", ctypes.c_size_t), ("max_chunks", ctypes.c_int64)] + [
+        (n, ctypes.c_size_t) for n in ("chunk_table", "chunk_offsets", "seq_starts",
+                                       "decay", "w", "qp", "kt", "ut", "oloc")]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    env = os.environ.get("GDN_LIB")
+    if env:
+        return env
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"libgdn.so not found at {path}; build it with "
+                "`python -m gated_deltanet_02_amd.build`")
+        L = ctypes.CDLL(path)
+        P = ctypes.POINTER
+        T = P(GdnTensor)
+        L.gdn_abi_version.restype = ctypes.c_int
+        L.gdn_default_options.argtypes = [P(GdnOptions)]
+        L.gdn_default_options.restype = None
+        L.gdn_prefill.argtypes = [T] * 9 + [ctypes.c_void_p]
+        L.gdn_prefill.restype = ctypes.c_int
+        L.gdn_prefill_ex.argtypes = [T] * 9 + [P(GdnOptions), ctypes.c_void_p,
+                                               ctypes.c_size_t, ctypes.c_void_p]
+        L.gdn_prefill_ex.restype = ctypes.c_int
+        L.gdn_workspace_size.argtypes = [T, T, T, T, P(GdnOptions), P(ctypes.c_size_t)]
+        L.gdn_workspace_size.restype = ctypes.c_int
+        L.gdn_get_workspace_layout.argtypes = [T, T, T, T, P(GdnOptions), P(GdnWorkspaceLayout)]
+        L.gdn_get_workspace_layout.restype = ctypes.c_int
+        L.gdn_status_string.argtypes = [ctypes.c_int]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def describe(t: Optional[torch.Tensor]):
+    """A gdn_tensor descriptor for a torch tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if t.dim() > 4:
+        raise ValueError("at most 4 dimensions")
+    d = GdnTensor()
+    d.data = t.data_ptr() if t.numel() > 0 else 0
+    d.dtype = _DTYPES.get(t.dtype, 0)
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _ref(d):
+    return ctypes.byref(d) if d is not None else None
+
+
+def options(chunk: int = 0, scale: float = 1.0, l2_eps: float = 1e-6,
+            stages: int = STAGE_ALL) -> GdnOptions:
+    o = GdnOptions()
+    o.chunk, o.scale, o.l2_eps, o.stages = chunk, scale, l2_eps, stages
+    return o
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        raise GdnError(status, lib().gdn_last_error().decode())
+
+
+def _stream_handle(stream, ref: torch.Tensor) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(ref.device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def gdn_abi_version() -> int:
+    return lib().gdn_abi_version()
+
+
+def gdn_status_string(status: int) -> str:
+    return lib().gdn_status_string(status).decode()
+
+
+def gdn_last_error() -> str:
+    return lib().gdn_last_error().decode()
+
+
+def gdn_default_options() -> GdnOptions:
+    o = GdnOptions()
+    lib().gdn_default_options(ctypes.byref(o))
+    return o
+
+
+def _descs(q, k, v, g, beta, cu_seqlens, init_state, out, final_state):
+    ts = (q, k, v, g, beta, cu_seqlens, init_state, out, final_state)
+    for name, t in zip(("q", "k", "v", "g", "beta", "cu_seqlens", "init_state",
+                        "out", "final_state"), ts):
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    return [describe(x) for x in ts]
+
+
+def gdn_prefill(q, k, v, g, beta, cu_seqlens=None, init_state=None, out=None,
+                final_state=None, stream=None):
+    """Whole prefill with default options; the library allocates its
+    workspace stream-ordered.  ``out`` is allocated like ``v`` if None;
+    ``final_state`` is written only when given.  Returns (out, final_state)."""
+    if out is None:
+        out = torch.empty_like(v)
+    ds = _descs(q, k, v, g, beta, cu_seqlens, init_state, out, final_state)
+    _check(lib().gdn_prefill(*[_ref(d) for d in ds], _stream_handle(stream, v)))
+    return out, final_state
+
+
+def gdn_workspace_size(q, k, v, cu_seqlens=None, opts: Optional[GdnOptions] = None) -> int:
+    n = ctypes.c_size_t(0)
+    ds = [describe(x) for x in (q, k, v, cu_seqlens)]
+    _check(lib().gdn_workspace_size(*[_ref(d) for d in ds],
+                                    ctypes.byref(opts) if opts else None, ctypes.byref(n)))
+    return n.value
+
+
+def gdn_get_workspace_layout(q, k, v, cu_seqlens=None,
+                             opts: Optional[GdnOptions] = None) -> GdnWorkspaceLayout:
+    lay = GdnWorkspaceLayout()
+    ds = [describe(x) for x in (q, k, v, cu_seqlens)]
+    _check(lib().gdn_get_workspace_layout(*[_ref(d) for d in ds],
+                                          ctypes.byref(opts) if opts else None,
+                                          ctypes.byref(lay)))
+    return lay
+
+
+def alloc_workspace(q, k, v, cu_seqlens=None, opts=None) -> torch.Tensor:
+    """A device byte tensor large enough for gdn_prefill_ex (torch's caching
+    allocator returns 256-byte aligned blocks)."""
+    n = gdn_workspace_size(q, k, v, cu_seqlens, opts)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+
+
+def gdn_prefill_ex(q, k, v, g, beta, cu_seqlens=None, init_state=None,
+                   out=None, final_state=None, opts: Optional[GdnOptions] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """Prefill with options and a caller-owned workspace (allocated here with
+    torch if None).  Returns (out, final_state)."""
+    if out is None:
+        out = torch.empty_like(v)
+    if workspace is None:
+        workspace = alloc_workspace(q, k, v, cu_seqlens, opts)
+    if workspace.device.type != "cuda":
+        raise ValueError("workspace must be a GPU tensor")
+    ds = _descs(q, k, v, g, beta, cu_seqlens, init_state, out, final_state)
+    _check(lib().gdn_prefill_ex(*[_ref(d) for d in ds],
+                                ctypes.byref(opts) if opts else None,
+                                workspace.data_ptr(), workspace.numel(),
+                                _stream_handle(stream, v)))
+    return out, final_state
+
+
+class PreparedPrefill:
+    """gdn_prefill_ex with its descriptors built once, for tight loops
+    (benchmarks, repeated calls on fixed buffers).  Calling it enqueues the
+    selected stages on the given stream (default: current) and raises on a
+    non-zero status.  The tensors must stay alive as long as this object."""
+
+    def __init__(self, q, k, v, g, beta, cu_seqlens=None, init_state=None,
+                 out=None, final_state=None, opts: Optional[GdnOptions] = None,
+                 workspace: Optional[torch.Tensor] = None):
+        if out is None:
+            out = torch.empty_like(v)
+        if workspace is None:
+            workspace = alloc_workspace(q, k, v, cu_seqlens, opts)
+        self.tensors = (q, k, v, g, beta, cu_seqlens, init_state, out, final_state, workspace)
+        self.out, self.final_state, self.workspace = out, final_state, workspace
+        self._d = _descs(q, k, v, g, beta, cu_seqlens, init_state, out, final_state)
+        self._refs = [_ref(d) for d in self._d]
+        self._opts = opts if opts is not None else gdn_default_options()
+        self._fn = lib().gdn_prefill_ex
+        self._ws = (workspace.data_ptr(), workspace.numel())
+        self._dev = v.device
+
+    def with_stages(self, stages: int) -> "PreparedPrefill":
+        o = GdnOptions.from_buffer_copy(self._opts)
+        o.stages = stages
+        p = object.__new__(PreparedPrefill)
+        p.__dict__.update(self.__dict__)
+        p._opts = o
+        return p
+
+    def __call__(self, stream=None):
+        s = torch.cuda.current_stream(self._dev).cuda_stream if stream is None else stream
+        rc = self._fn(*self._refs, ctypes.byref(self._opts), self._ws[0], self._ws[1], s)
+        if rc != GDN_OK:
+            _check(rc)

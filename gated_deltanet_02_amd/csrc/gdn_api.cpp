@@ -1,0 +1,455 @@
+// C ABI of the chunked Gated DeltaNet prefill (declared in include/gdn.h).
+//
+// Host side only: argument validation (no HIP call and no device read before
+// it passes), workspace layout, and the launch sequence on the caller's
+// stream.  Invalid input is rejected before any work is enqueued, as the
+// serving pages require of oversize prompts ("Open-Jev-27B-v1.1 native text
+// worker", section "Prepare the checkpoint").
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+#include "gdn_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// A token-major view: [T, H, D] (or [B, Tb, H, D] flattened to T = B * Tb).
+struct View {
+  int64_t T = 0, H = 0, D = 0;
+  int64_t st = 0, sh = 0;  // token and head strides (elements)
+  int64_t B = 1;           // leading batch of a 4-D view
+};
+
+// 3-D/4-D per-head vectors (q, k, v, out).
+int parse_vec_tensor(const gdn_tensor* t, const char* name, View* v) {
+  if (t->ndim == 3) {
+    v->B = 1;
+    v->T = t->shape[0];
+    v->H = t->shape[1];
+    v->D = t->shape[2];
+    v->st = t->stride[0];
+    v->sh = t->stride[1];
+  } else if (t->ndim == 4) {
+    v->B = t->shape[0];
+    v->T = t->shape[0] * t->shape[1];
+    v->H = t->shape[2];
+    v->D = t->shape[3];
+    v->st = t->stride[1];
+    v->sh = t->stride[2];
+  } else {
+    return fail(GDN_ERR_SHAPE, "%s: expected 3 or 4 dimensions, got %d", name, t->ndim);
+  }
+  int64_t numel = 1;
+  for (int i = 0; i < t->ndim; ++i) {
+    if (t->shape[i] < 0) return fail(GDN_ERR_SHAPE, "%s: negative size", name);
+    numel *= t->shape[i];
+  }
+  if (numel == 0) return GDN_OK;  // strides of an empty tensor carry no layout
+  for (int i = 0; i < t->ndim; ++i)
+    if (t->stride[i] < 0) return fail(GDN_ERR_LAYOUT, "%s: negative stride", name);
+  if (t->stride[t->ndim - 1] != 1) return fail(GDN_ERR_LAYOUT, "%s: last dimension must have unit stride", name);
+  if (t->ndim == 4 && t->shape[0] > 1 && t->stride[0] != t->shape[1] * t->stride[1])
+    return fail(GDN_ERR_LAYOUT, "%s: batch stride must equal seq_len * token stride", name);
+  return GDN_OK;
+}
+
+// 2-D/3-D per-head scalars (g, beta).
+int parse_scalar_tensor(const gdn_tensor* t, const char* name, View* v) {
+  if (t->ndim == 2) {
+    v->B = 1;
+    v->T = t->shape[0];
+    v->H = t->shape[1];
+    v->st = t->stride[0];
+    v->sh = t->stride[1];
+  } else if (t->ndim == 3) {
+    v->B = t->shape[0];
+    v->T = t->shape[0] * t->shape[1];
+    v->H = t->shape[2];
+    v->st = t->stride[1];
+    v->sh = t->stride[2];
+  } else {
+    return fail(GDN_ERR_SHAPE, "%s: expected 2 or 3 dimensions, got %d", name, t->ndim);
+  }
+  int64_t numel = 1;
+  for (int i = 0; i < t->ndim; ++i) {
+    if (t->shape[i] < 0) return fail(GDN_ERR_SHAPE, "%s: negative size", name);
+    numel *= t->shape[i];
+  }
+  if (numel == 0) return GDN_OK;
+  for (int i = 0; i < t->ndim; ++i)
+    if (t->stride[i] < 0) return fail(GDN_ERR_LAYOUT, "%s: negative stride", name);
+  if (t->ndim == 3 && t->shape[0] > 1 && t->stride[0] != t->shape[1] * t->stride[1])
+    return fail(GDN_ERR_LAYOUT, "%s: batch stride must equal seq_len * token stride", name);
+  return GDN_OK;
+}
+
+bool supported_head_dim(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+struct Problem {
+  bool bf16 = true;
+  int chunk = 64;
+  int dk = 0, dv = 0, hk = 0, hv = 0;
+  int64_t T = 0;
+  int n_seq = 1;
+  bool packed = false;
+  int seq_len = 0, chunks_per_seq = 0;
+  int64_t max_chunks = 0;
+  View q, k, v, o, g, b;
+  float scale = 1.f, eps = 1e-6f;
+  uint32_t stages = GDN_STAGE_ALL;
+};
+
+struct Layout {
+  size_t table = 0, chunk_off = 0, seq_start = 0, decay = 0;
+  size_t w = 0, qp = 0, kt = 0, ut = 0, oloc = 0, total = 0;
+};
+
+Layout make_layout(const Problem& P) {
+  Layout L;
+  const size_t es = P.bf16 ? 2 : 4;
+  const size_t blocks = (size_t)P.max_chunks * P.hv;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.table = take(P.packed ? (size_t)P.max_chunks * 16 : 0);
+  L.chunk_off = take(P.packed ? (size_t)(P.n_seq + 1) * 4 : 0);
+  L.seq_start = take(P.packed ? (size_t)(P.n_seq + 1) * 4 : 0);
+  L.decay = take(blocks * 4);
+  L.w = take(blocks * P.chunk * P.dk * es);
+  L.qp = take(blocks * P.chunk * P.dk * es);
+  L.kt = take(blocks * P.chunk * P.dk * es);
+  L.ut = take(blocks * P.chunk * P.dv * es);
+  L.oloc = take(blocks * P.chunk * P.dv * es);
+  L.total = off;
+  return L;
+}
+
+int resolve_options(const gdn_options* opts, bool bf16, Problem* P) {
+  gdn_options o;
+  gdn_default_options(&o);
+  if (opts) o = *opts;
+  int chunk = o.chunk;
+  if (chunk == 0) chunk = bf16 ? 64 : 32;
+  if (chunk != 16 && chunk != 32 && chunk != 64)
+    return fail(GDN_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64 (got %d)", chunk);
+  if (!(o.l2_eps >= 0.f)) return fail(GDN_ERR_SHAPE, "l2_eps must be >= 0");
+  if ((o.stages & ~GDN_STAGE_ALL) != 0) return fail(GDN_ERR_SHAPE, "unknown stage bits 0x%x", o.stages);
+  P->chunk = chunk;
+  P->scale = o.scale;
+  P->eps = o.l2_eps;
+  P->stages = o.stages;
+  return GDN_OK;
+}
+
+// Shape/dtype/layout checks shared by every entry point.  When `full` is
+// false only the tensors that determine the workspace are examined.
+int validate(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
+             const gdn_tensor* g, const gdn_tensor* beta, const gdn_tensor* cu,
+             const gdn_tensor* init, const gdn_tensor* out,
+             const gdn_tensor* fin, const gdn_options* opts, bool full,
+             Problem* P) {
+  if (!q || !k || !v) return fail(GDN_ERR_NULL_ARG, "q, k and v are required");
+  if (full && (!g || !beta || !out)) return fail(GDN_ERR_NULL_ARG, "g, beta and out are required");
+  if (q->dtype != GDN_DTYPE_BF16 && q->dtype != GDN_DTYPE_F32)
+    return fail(GDN_ERR_DTYPE, "q must be bf16 or f32");
+  if (k->dtype != q->dtype || v->dtype != q->dtype || (full && out->dtype != q->dtype))
+    return fail(GDN_ERR_DTYPE, "q, k, v and out must share one dtype");
+  P->bf16 = q->dtype == GDN_DTYPE_BF16;
+  int rc;
+  if ((rc = resolve_options(opts, P->bf16, P))) return rc;
+  if ((rc = parse_vec_tensor(q, "q", &P->q))) return rc;
+  if ((rc = parse_vec_tensor(k, "k", &P->k))) return rc;
+  if ((rc = parse_vec_tensor(v, "v", &P->v))) return rc;
+  if (q->ndim != k->ndim || q->ndim != v->ndim) return fail(GDN_ERR_SHAPE, "q, k and v must have the same rank");
+  if (P->q.T != P->k.T || P->q.H != P->k.H || P->q.D != P->k.D || P->q.B != P->k.B)
+    return fail(GDN_ERR_SHAPE, "q and k shapes differ");
+  if (P->v.T != P->q.T || P->v.B != P->q.B) return fail(GDN_ERR_SHAPE, "v token count differs from q");
+  if (!supported_head_dim(P->q.D) || !supported_head_dim(P->v.D))
+    return fail(GDN_ERR_UNSUPPORTED, "d_k and d_v must be 16, 32, 64 or 128 (got %lld, %lld)",
+                (long long)P->q.D, (long long)P->v.D);
+  if (P->q.H < 1 || P->v.H < 1 || P->v.H % P->q.H)
+    return fail(GDN_ERR_SHAPE, "value heads (%lld) must be a positive multiple of key heads (%lld)",
+                (long long)P->v.H, (long long)P->q.H);
+  if (P->q.H > 65535) return fail(GDN_ERR_UNSUPPORTED, "at most 65535 key heads");
+  if (P->q.T >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "T must be < 2^31");
+  P->dk = (int)P->q.D;
+  P->dv = (int)P->v.D;
+  P->hk = (int)P->q.H;
+  P->hv = (int)P->v.H;
+  P->T = P->q.T;
+  if (!gdn::kernels_available(P->bf16, P->chunk, P->dk))
+    return fail(GDN_ERR_UNSUPPORTED, "no %s kernel for chunk %d with d_k %d (LDS limit)",
+                P->bf16 ? "bf16" : "f32", P->chunk, P->dk);
+
+  // Sequences.
+  if (cu) {
+    if (cu->dtype != GDN_DTYPE_I32) return fail(GDN_ERR_DTYPE, "cu_seqlens must be int32");
+    if (cu->ndim != 1 || cu->shape[0] < 2) return fail(GDN_ERR_SHAPE, "cu_seqlens must be 1-D with N+1 >= 2 entries");
+    if (cu->stride[0] != 1) return fail(GDN_ERR_LAYOUT, "cu_seqlens must be contiguous");
+    if (!cu->data) return fail(GDN_ERR_NULL_ARG, "cu_seqlens data is NULL");
+    if (P->q.B != 1) return fail(GDN_ERR_SHAPE, "with cu_seqlens the batch dimension must be 1");
+    if (cu->shape[0] - 1 >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "too many sequences");
+    P->n_seq = (int)(cu->shape[0] - 1);
+    P->packed = P->n_seq > 1;
+    P->seq_len = (int)P->T;  // used only when not packed (a single sequence)
+  } else {
+    P->n_seq = (int)P->q.B;
+    P->packed = false;
+    P->seq_len = P->n_seq > 0 ? (int)(P->T / P->n_seq) : 0;
+  }
+  if (P->n_seq < 1) return fail(GDN_ERR_SHAPE, "at least one sequence is required");
+  if (P->packed) {
+    P->max_chunks = P->T / P->chunk + P->n_seq;
+  } else {
+    P->chunks_per_seq = (P->seq_len + P->chunk - 1) / P->chunk;
+    P->max_chunks = (int64_t)P->n_seq * P->chunks_per_seq;
+  }
+  if (P->max_chunks >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "too many chunks");
+  const int64_t n_slices = P->dv / 16;
+  const int64_t scan_blocks = ((int64_t)P->n_seq * P->hv + 7) / 8 * 8 * n_slices;
+  if (scan_blocks >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "too many (sequence, head) pairs");
+  if (!full) return GDN_OK;
+
+  // The remaining tensors.
+  int gr = P->bf16 ? 8 : 4;  // elements per 16 bytes
+  if ((rc = parse_vec_tensor(out, "out", &P->o))) return rc;
+  if (P->o.T != P->T || P->o.H != P->hv || P->o.D != P->dv) return fail(GDN_ERR_SHAPE, "out must match v");
+  if (g->dtype != GDN_DTYPE_F32 || beta->dtype != GDN_DTYPE_F32) return fail(GDN_ERR_DTYPE, "g and beta must be f32");
+  if ((rc = parse_scalar_tensor(g, "g", &P->g))) return rc;
+  if ((rc = parse_scalar_tensor(beta, "beta", &P->b))) return rc;
+  if (P->g.T != P->T || P->g.H != P->hv || P->b.T != P->T || P->b.H != P->hv)
+    return fail(GDN_ERR_SHAPE, "g and beta must be [T, Hv]");
+  const struct { const gdn_tensor* t; const View* v; const char* n; } vecs[] = {
+      {q, &P->q, "q"}, {k, &P->k, "k"}, {v, &P->v, "v"}, {out, &P->o, "out"}};
+  for (const auto& x : vecs) {
+    if (P->T == 0) break;  // nothing is read or written
+    if (!x.t->data) return fail(GDN_ERR_NULL_ARG, "%s data is NULL", x.n);
+    if ((uintptr_t)x.t->data % 16) return fail(GDN_ERR_LAYOUT, "%s must be 16-byte aligned", x.n);
+    if (x.v->st % gr || x.v->sh % gr)
+      return fail(GDN_ERR_LAYOUT, "%s: token/head strides must be multiples of %d elements", x.n, gr);
+  }
+  if (P->T > 0 && (!g->data || !beta->data)) return fail(GDN_ERR_NULL_ARG, "g/beta data is NULL");
+  if (P->T > 0 && ((uintptr_t)g->data % 4 || (uintptr_t)beta->data % 4))
+    return fail(GDN_ERR_LAYOUT, "g/beta must be 4-byte aligned");
+  const gdn_tensor* states[2] = {init, fin};
+  const char* snames[2] = {"init_state", "final_state"};
+  for (int i = 0; i < 2; ++i) {
+    const gdn_tensor* s = states[i];
+    if (!s) continue;
+    if (s->dtype != GDN_DTYPE_F32) return fail(GDN_ERR_DTYPE, "%s must be f32", snames[i]);
+    if (s->ndim != 4 || s->shape[0] != P->n_seq || s->shape[1] != P->hv || s->shape[2] != P->dk ||
+        s->shape[3] != P->dv)
+      return fail(GDN_ERR_SHAPE, "%s must be [N=%d, Hv=%d, dk=%d, dv=%d]", snames[i], P->n_seq, P->hv,
+                  P->dk, P->dv);
+    if (s->stride[3] != 1 || s->stride[2] != P->dv || s->stride[1] != (int64_t)P->dk * P->dv ||
+        s->stride[0] != (int64_t)P->hv * P->dk * P->dv)
+      return fail(GDN_ERR_LAYOUT, "%s must be contiguous", snames[i]);
+    if (!s->data) return fail(GDN_ERR_NULL_ARG, "%s data is NULL", snames[i]);
+    if ((uintptr_t)s->data % 16) return fail(GDN_ERR_LAYOUT, "%s must be 16-byte aligned", snames[i]);
+  }
+  return GDN_OK;
+}
+
+int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
+        const gdn_tensor* v, const gdn_tensor* g, const gdn_tensor* beta,
+        const gdn_tensor* cu, const gdn_tensor* init, gdn_tensor* out,
+        gdn_tensor* fin, void* ws, hipStream_t s) {
+  const Layout L = make_layout(P);
+  char* base = (char*)ws;
+  gdn::ChunkMap map{};
+  map.packed = P.packed ? 1 : 0;
+  map.n_seq = P.n_seq;
+  map.seq_len = P.seq_len;
+  map.chunks_per_seq = P.chunks_per_seq;
+  map.table = (const int32_t*)(base + L.table);
+  map.chunk_off = (const int32_t*)(base + L.chunk_off);
+  map.seq_start = (const int32_t*)(base + L.seq_start);
+  gdn::Intermediates im{};
+  im.w = base + L.w;
+  im.qp = base + L.qp;
+  im.kt = base + L.kt;
+  im.ut = base + L.ut;
+  im.oloc = base + L.oloc;
+  im.decay = (float*)(base + L.decay);
+
+  hipError_t e;
+  if (P.packed && (P.stages & GDN_STAGE_TABLE)) {
+    gdn::TableParams tp{};
+    tp.cu = (const int32_t*)cu->data;
+    tp.seq_start = (int32_t*)(base + L.seq_start);
+    tp.chunk_off = (int32_t*)(base + L.chunk_off);
+    tp.table = (int32_t*)(base + L.table);
+    tp.n_seq = P.n_seq;
+    tp.t_total = (int32_t)P.T;
+    tp.chunk = P.chunk;
+    tp.max_chunks = (int32_t)P.max_chunks;
+    if ((e = gdn::launch_table(tp, s)) != hipSuccess)
+      return fail(GDN_ERR_HIP, "chunk table launch: %s", hipGetErrorString(e));
+  }
+  if ((P.stages & GDN_STAGE_WY) && P.max_chunks > 0) {
+    gdn::WyParams wp{};
+    wp.q = q->data;
+    wp.k = k->data;
+    wp.v = v->data;
+    wp.g = (const float*)g->data;
+    wp.beta = (const float*)beta->data;
+    wp.q_st = P.q.st; wp.q_sh = P.q.sh;
+    wp.k_st = P.k.st; wp.k_sh = P.k.sh;
+    wp.v_st = P.v.st; wp.v_sh = P.v.sh;
+    wp.g_st = P.g.st; wp.g_sh = P.g.sh;
+    wp.b_st = P.b.st; wp.b_sh = P.b.sh;
+    wp.hk = P.hk;
+    wp.hv = P.hv;
+    wp.dv = P.dv;
+    wp.scale = P.scale;
+    wp.eps = P.eps;
+    wp.map = map;
+    wp.im = im;
+    if ((e = gdn::launch_wy(P.bf16, P.chunk, P.dk, wp, (int)P.max_chunks, P.hk, s)) != hipSuccess)
+      return fail(GDN_ERR_HIP, "WY launch: %s", hipGetErrorString(e));
+  }
+  if (P.stages & GDN_STAGE_SCAN) {
+    gdn::ScanParams sp{};
+    sp.out = out->data;
+    sp.o_st = P.o.st;
+    sp.o_sh = P.o.sh;
+    sp.init = init ? (const float*)init->data : nullptr;
+    sp.final_state = fin ? (float*)fin->data : nullptr;
+    sp.hv = P.hv;
+    sp.dv = P.dv;
+    sp.n_slices = P.dv / 16;
+    sp.map = map;
+    sp.im = im;
+    const int64_t blocks = ((int64_t)P.n_seq * P.hv + 7) / 8 * 8 * sp.n_slices;
+    if ((e = gdn::launch_scan(P.bf16, P.chunk, P.dk, sp, (int)blocks, s)) != hipSuccess)
+      return fail(GDN_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
+  }
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+void gdn_default_options(gdn_options* opts) {
+  if (!opts) return;
+  opts->chunk = 0;  // 64 for bf16, 32 for f32
+  opts->scale = 1.0f;
+  opts->l2_eps = 1e-6f;
+  opts->stages = GDN_STAGE_ALL;
+}
+
+const char* gdn_status_string(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL_ARG: return "null argument";
+    case GDN_ERR_DTYPE: return "unsupported or mismatched dtype";
+    case GDN_ERR_SHAPE: return "inconsistent or out-of-range shape";
+    case GDN_ERR_LAYOUT: return "unsupported strides or alignment";
+    case GDN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GDN_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case GDN_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+int gdn_workspace_size(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
+                       const gdn_tensor* cu_seqlens, const gdn_options* opts, size_t* bytes) {
+  if (!bytes) return fail(GDN_ERR_NULL_ARG, "bytes is NULL");
+  Problem P;
+  const int rc = validate(q, k, v, nullptr, nullptr, cu_seqlens, nullptr, nullptr, nullptr, opts, false, &P);
+  if (rc) return rc;
+  *bytes = make_layout(P).total;
+  return GDN_OK;
+}
+
+int gdn_get_workspace_layout(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
+                             const gdn_tensor* cu_seqlens, const gdn_options* opts,
+                             gdn_workspace_layout* layout) {
+  if (!layout) return fail(GDN_ERR_NULL_ARG, "layout is NULL");
+  Problem P;
+  const int rc = validate(q, k, v, nullptr, nullptr, cu_seqlens, nullptr, nullptr, nullptr, opts, false, &P);
+  if (rc) return rc;
+  const Layout L = make_layout(P);
+  layout->total_bytes = L.total;
+  layout->max_chunks = P.max_chunks;
+  layout->chunk_table = L.table;
+  layout->chunk_offsets = L.chunk_off;
+  layout->seq_starts = L.seq_start;
+  layout->decay = L.decay;
+  layout->w = L.w;
+  layout->qp = L.qp;
+  layout->kt = L.kt;
+  layout->ut = L.ut;
+  layout->oloc = L.oloc;
+  return GDN_OK;
+}
+
+int gdn_prefill_ex(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
+                   const gdn_tensor* g, const gdn_tensor* beta, const gdn_tensor* cu_seqlens,
+                   const gdn_tensor* init_state, gdn_tensor* out, gdn_tensor* final_state,
+                   const gdn_options* opts, void* workspace, size_t workspace_bytes, void* stream) {
+  Problem P;
+  int rc = validate(q, k, v, g, beta, cu_seqlens, init_state, out, final_state, opts, true, &P);
+  if (rc) return rc;
+  const size_t need = make_layout(P).total;
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if ((uintptr_t)workspace % kAlign) return fail(GDN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  g_last_error.clear();
+  return run(P, q, k, v, g, beta, cu_seqlens, init_state, out, final_state, workspace,
+             (hipStream_t)stream);
+}
+
+int gdn_prefill(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
+                const gdn_tensor* g, const gdn_tensor* beta, const gdn_tensor* cu_seqlens,
+                const gdn_tensor* init_state, gdn_tensor* out, gdn_tensor* final_state,
+                void* stream) {
+  Problem P;
+  int rc = validate(q, k, v, g, beta, cu_seqlens, init_state, out, final_state, nullptr, true, &P);
+  if (rc) return rc;
+  const size_t need = make_layout(P).total;
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = hipMallocAsync(&ws, need, s);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "workspace allocation of %zu bytes: %s", need, hipGetErrorString(e));
+  }
+  g_last_error.clear();
+  rc = run(P, q, k, v, g, beta, cu_seqlens, init_state, out, final_state, ws, s);
+  if (ws) {
+    const hipError_t e = hipFreeAsync(ws, s);
+    if (rc == GDN_OK && e != hipSuccess) rc = fail(GDN_ERR_HIP, "workspace release: %s", hipGetErrorString(e));
+  }
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Parameter blocks shared by the host launcher and the gfx950 kernels of the
+// chunked Gated DeltaNet prefill.  Plain structs passed by value as kernel
+// arguments.
+#pragma once
+
+#include <stdint.h>
+
+namespace gdn {
+
+// How a global chunk id maps to (sequence, first token, length).
+//   uniform: n_seq sequences of seq_len tokens each, chunk ids in sequence
+//            order (covers the single-sequence case); no table is read.
+//   packed:  the chunk table built on the device from cu_seqlens.
+struct ChunkMap {
+  int32_t packed;        // 0 = uniform, 1 = packed
+  int32_t n_seq;
+  int32_t seq_len;       // uniform mode
+  int32_t chunks_per_seq;// uniform mode
+  const int32_t* table;      // packed: int32[max_chunks][4]
+  const int32_t* chunk_off;  // packed: int32[n_seq + 1]
+  const int32_t* seq_start;  // packed: sanitised cu_seqlens, int32[n_seq + 1]
+};
+
+struct TableParams {
+  const int32_t* cu;     // caller's cu_seqlens, int32[n_seq + 1]
+  int32_t* seq_start;    // out: sanitised copy
+  int32_t* chunk_off;    // out: exclusive prefix of chunk counts
+  int32_t* table;        // out: per chunk (seq, t0, n, 0)
+  int32_t n_seq;
+  int32_t t_total;
+  int32_t chunk;
+  int32_t max_chunks;
+};
+
+// Per-(chunk, value head) intermediates, all in the input element type.
+struct Intermediates {
+  void* w;       // [C][dk]
+  void* qp;      // [C][dk]
+  void* kt;      // [dk][C]
+  void* ut;      // [dv][C]
+  void* oloc;    // [C][dv]
+  float* decay;  // [chunk][Hv]
+};
+
+struct WyParams {
+  const void* q;  // [T, Hk, dk] with token stride q_st, head stride q_sh
+  const void* k;
+  const void* v;  // [T, Hv, dv]
+  const float* g;     // [T, Hv] strides g_st, g_sh
+  const float* beta;  // [T, Hv] strides b_st, b_sh
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh;
+  int64_t g_st, g_sh, b_st, b_sh;
+  int32_t hk, hv, dv;
+  float scale, eps;
+  ChunkMap map;
+  Intermediates im;
+};
+
+struct ScanParams {
+  void* out;             // [T, Hv, dv] strides o_st, o_sh
+  int64_t o_st, o_sh;
+  const float* init;     // [N, Hv, dk, dv] or null
+  float* final_state;    // [N, Hv, dk, dv] or null
+  int32_t hv, dv;
+  int32_t n_slices;      // dv / 16
+  ChunkMap map;
+  Intermediates im;
+};
+
+}  // namespace gdn

@@ -1,0 +1,738 @@
+// gfx950 (CDNA4) kernels of the chunked Gated DeltaNet prefill.
+//
+// The operation is the gated delta rule (Gated Delta Networks, Yang, Kautz,
+// Hatamizadeh, ICLR 2025, section 3), evaluated chunk by chunk in its WY
+// form (Parallelizing Linear Transformers with the Delta Rule over Sequence
+// Length, Yang et al., NeurIPS 2024, section 3).  For a chunk of n <= C
+// tokens with chunk-local cumulative gate gamma_r = g_0 + ... + g_r and
+// D_rs = exp(gamma_r - gamma_s) (s <= r):
+//
+//   A   = strictly-lower part of beta_r D_rs (k^_r . k^_s)
+//   T   = (I + A)^-1                              (forward substitution)
+//   W   = T diag(beta e^gamma) K^,   U~ = T diag(beta) V
+//   P   = scale * D o (Q^ K^T)                    (causal, diagonal included)
+//   Q'  = scale diag(e^gamma) Q^ - P W,   O_loc = P U~
+//   K~_r = e^(gamma_last - gamma_r) k^_r
+// and, carried from chunk to chunk with state H (d_k x d_v, fp32):
+//   U = U~ - W H,   O = Q' H + O_loc,   H <- e^gamma_last H + K~^T U.
+//
+// Kernels, launched in this order on the caller's stream:
+//   table_kernel  packed batches only: sanitised sequence starts, the
+//                 exclusive prefix of per-sequence chunk counts and a
+//                 (sequence, first token, length) row per chunk.
+//   wy_kernel     one workgroup per (chunk, key head), looping over the value
+//                 heads of the group: L2 norms of q and k rows, the gate
+//                 cumulative sum, K^K^T and Q^K^T (shared by the group), the
+//                 blocked triangular inverse and every per-chunk matrix above.
+//                 Fully parallel over chunks.
+//   scan_kernel   one workgroup per (sequence, value head, 16-column slice of
+//                 d_v): the only sequential part.  The state slice lives in
+//                 MFMA accumulators; each step stages the next chunk's W, Q'
+//                 and K~^T from global memory into LDS while the current one
+//                 is consumed.  The output is produced in the same step.
+//
+// bf16 inputs use bf16 MFMA operands with fp32 accumulation; the triangular
+// solve and every gate exponential are fp32.  fp32 inputs use fp32 MFMA
+// throughout.  All exponents are <= 0 when g <= 0: differences of gamma are
+// only formed for s <= r and never factored into exp(gamma_r) exp(-gamma_s).
+#include <hip/hip_runtime.h>
+
+#include "gdn_device.h"
+#include "gdn_internal.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+constexpr int kThreads = 256;
+constexpr int kLdsLimit = 160 * 1024;
+
+// ---------------------------------------------------------------------------
+// chunk bookkeeping
+
+__device__ __forceinline__ bool chunk_info(const ChunkMap& m, int c, int C,
+                                           int& seq, int& t0, int& n) {
+  if (!m.packed) {
+    if (c >= m.n_seq * m.chunks_per_seq) return false;
+    seq = c / m.chunks_per_seq;
+    const int j = c - seq * m.chunks_per_seq;
+    t0 = seq * m.seq_len + j * C;
+    n = min(C, m.seq_len - j * C);
+    return true;
+  }
+  if (c >= m.chunk_off[m.n_seq]) return false;
+  const int* row = m.table + 4 * (int64_t)c;
+  seq = row[0];
+  t0 = row[1];
+  n = row[2];
+  return true;
+}
+
+__device__ __forceinline__ void seq_range(const ChunkMap& m, int seq, int C,
+                                          int& c_begin, int& c_end, int& tok0,
+                                          int& tok_end) {
+  if (!m.packed) {
+    c_begin = seq * m.chunks_per_seq;
+    c_end = c_begin + m.chunks_per_seq;
+    tok0 = seq * m.seq_len;
+    tok_end = tok0 + m.seq_len;
+    return;
+  }
+  c_begin = m.chunk_off[seq];
+  c_end = m.chunk_off[seq + 1];
+  tok0 = m.seq_start[seq];
+  tok_end = m.seq_start[seq + 1];
+}
+
+// Single workgroup.  Sequence ends are clamped into [previous end, T] so a
+// malformed cu_seqlens can only produce wrong results, never an access
+// outside the tensors.
+__global__ __launch_bounds__(1024) void table_kernel(TableParams p) {
+  __shared__ int s_max[1024];
+  __shared__ int s_sum[1024];
+  __shared__ int s_carry_end, s_carry_chunks;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    s_carry_end = 0;
+    s_carry_chunks = 0;
+    p.seq_start[0] = 0;
+    p.chunk_off[0] = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < p.n_seq; base += 1024) {
+    const int i = base + tid;
+    int e = (i < p.n_seq) ? p.cu[i + 1] : 0;
+    e = min(max(e, 0), p.t_total);
+    s_max[tid] = e;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int y = tid >= off ? s_max[tid - off] : 0;
+      __syncthreads();
+      s_max[tid] = max(s_max[tid], y);
+      __syncthreads();
+    }
+    const int carry_end = s_carry_end;
+    const int end_i = max(s_max[tid], carry_end);
+    const int start_i = tid > 0 ? max(s_max[tid - 1], carry_end) : carry_end;
+    const int nch = (i < p.n_seq) ? (end_i - start_i + p.chunk - 1) / p.chunk : 0;
+    if (i < p.n_seq) p.seq_start[i + 1] = end_i;
+    s_sum[tid] = nch;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int y = tid >= off ? s_sum[tid - off] : 0;
+      __syncthreads();
+      s_sum[tid] += y;
+      __syncthreads();
+    }
+    const int carry_chunks = s_carry_chunks;
+    if (i < p.n_seq) p.chunk_off[i + 1] = carry_chunks + s_sum[tid];
+    __syncthreads();
+    if (tid == 1023) {
+      s_carry_chunks = carry_chunks + s_sum[1023];
+      s_carry_end = max(carry_end, s_max[1023]);
+    }
+    __syncthreads();
+  }
+  __threadfence();
+  __syncthreads();
+  const int total = min(p.chunk_off[p.n_seq], p.max_chunks);
+  for (int c = tid; c < total; c += 1024) {
+    int lo = 0, hi = p.n_seq - 1;  // largest i with chunk_off[i] <= c
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.chunk_off[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    const int j = c - p.chunk_off[lo];
+    const int t0 = p.seq_start[lo] + j * p.chunk;
+    int* row = p.table + 4 * (int64_t)c;
+    row[0] = lo;
+    row[1] = t0;
+    row[2] = min(p.chunk, p.seq_start[lo + 1] - t0);
+    row[3] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LDS helpers (whole workgroup)
+
+// dst[d][r] = src[r][d] for r < R (even), d < D (multiple of a granule).
+// Pairs of rows are packed so each LDS write carries two elements.
+template <typename TI>
+__device__ __forceinline__ void transpose_lds(const TI* src, int lds, TI* dst,
+                                              int ldd, int R, int D, int tid) {
+  constexpr int GR = Gran<TI>::n;
+  typedef TI pair_t __attribute__((ext_vector_type(2)));
+  const int npair = R / 2, ngran = D / GR;
+  for (int idx = tid; idx < npair * ngran; idx += kThreads) {
+    const int m = idx % npair, gc = idx / npair;
+    const uint4 va = ld16(src + (2 * m) * lds + gc * GR);
+    const uint4 vb = ld16(src + (2 * m + 1) * lds + gc * GR);
+    const TI* ea = (const TI*)&va;
+    const TI* eb = (const TI*)&vb;
+#pragma unroll
+    for (int j = 0; j < GR; ++j) {
+      pair_t pr;
+      pr[0] = ea[j];
+      pr[1] = eb[j];
+      *(pair_t*)(dst + (gc * GR + j) * ldd + 2 * m) = pr;
+    }
+  }
+}
+
+// out[r] = 1 / sqrt(sum_d src[r][d]^2 + eps); four lanes per row.
+template <typename TI, int D>
+__device__ __forceinline__ void row_inv_norms(const TI* src, int lds, int R,
+                                              float eps, float* out, int tid) {
+  for (int base = 0; base < R * 4; base += kThreads) {
+    const int idx = base + tid;
+    const int r = idx >> 2, part = idx & 3;
+    float s = 0.f;
+    if (r < R) {
+      const TI* row = src + r * lds + part * (D / 4);
+#pragma unroll
+      for (int d = 0; d < D / 4; ++d) {
+        const float x = to_float(row[d]);
+        s += x * x;
+      }
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    if (r < R && part == 0) out[r] = 1.0f / sqrtf(s + eps);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// WY kernel
+
+template <typename TI, int C, int DK>
+struct WyLayout {
+  static constexpr int S = sizeof(TI);
+  static constexpr int PADE = 16 / S;
+  static constexpr int DVM = 128;  // largest d_v
+  static constexpr int LK = DK + PADE;
+  static constexpr int LV = DVM + PADE;
+  static constexpr int LC = C + PADE;
+  static constexpr int LF = C + 4;
+  static constexpr int cmax(int a, int b) { return a > b ? a : b; }
+  static constexpr int sz_f = C * LF * 4;
+  static constexpr int r_kt = 0;                      // K^T [DK][LC]
+  static constexpr int r_q = r_kt + DK * LC * S;      // Q [C][LK]
+  static constexpr int r_g = r_q + C * LK * S;        // K^K^T (f32)
+  static constexpr int r_s = r_g + sz_f;              // Q^K^T (f32)
+  static constexpr int r_t = r_s + sz_f;              // T (f32)
+  static constexpr int r_kv = r_t + sz_f;             // K | V^T | W^T
+  static constexpr int sz_kv = cmax(cmax(C * LK, DVM * LC), DK * LC) * S;
+  static constexpr int r_x = r_kv + sz_kv;            // A (f32) | Tb, Tv, P
+  static constexpr int sz_x = cmax(sz_f, 3 * C * LC * S);
+  static constexpr int r_ut = r_x + sz_x;             // V | U~^T
+  static constexpr int sz_ut = cmax(C * LV, DVM * LC) * S;
+  static constexpr int r_scr = r_ut + sz_ut;          // per-wave 16x20 f32
+  static constexpr int r_vec = r_scr + 4 * 16 * 20 * 4;
+  static constexpr int total = r_vec + 6 * C * 4;
+};
+
+template <typename TI, int C, int DK>
+__global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
+  using L = WyLayout<TI, C, DK>;
+  constexpr int LK = L::LK, LV = L::LV, LC = L::LC, LF = L::LF;
+  constexpr int GR = Gran<TI>::n;
+  constexpr int NB = C / 16;    // 16-row tiles along the chunk
+  constexpr int NKT = DK / 16;  // 16-row tiles along d_k
+  __shared__ __attribute__((aligned(16))) char smem[L::total];
+  TI* sKt = (TI*)(smem + L::r_kt);
+  TI* sQ = (TI*)(smem + L::r_q);
+  float* sG = (float*)(smem + L::r_g);
+  float* sS = (float*)(smem + L::r_s);
+  float* sT = (float*)(smem + L::r_t);
+  TI* sKV = (TI*)(smem + L::r_kv);
+  float* sA = (float*)(smem + L::r_x);
+  TI* sTb = (TI*)(smem + L::r_x);
+  TI* sTv = sTb + C * LC;
+  TI* sP = sTv + C * LC;
+  TI* sUT = (TI*)(smem + L::r_ut);
+  float* sScr = (float*)(smem + L::r_scr);
+  float* sRq = (float*)(smem + L::r_vec);
+  float* sRk = sRq + C;
+  float* sGam = sRk + C;
+  float* sBeta = sGam + C;
+  float* sEg = sBeta + C;   // e^gamma_r
+  float* sKs = sEg + C;     // rk_r e^(gamma_last - gamma_r)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x, kh = blockIdx.y;
+  int seq, t0, n;
+  if (!chunk_info(p.map, c, C, seq, t0, n)) return;
+  (void)seq;
+  const TI* qg = (const TI*)p.q;
+  const TI* kg = (const TI*)p.k;
+  const TI* vg = (const TI*)p.v;
+  const int DV = p.dv;
+
+  // Q and K rows of the chunk (zero past the chunk's end).
+  constexpr int GPR = DK / GR;
+  for (int idx = tid; idx < C * GPR; idx += kThreads) {
+    const int r = idx / GPR, gc = idx % GPR;
+    uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
+    if (r < n) {
+      const int64_t t = t0 + r;
+      kv = ld16(kg + t * p.k_st + kh * p.k_sh + gc * GR);
+      qv = ld16(qg + t * p.q_st + kh * p.q_sh + gc * GR);
+    }
+    st16(sKV + r * LK + gc * GR, kv);
+    st16(sQ + r * LK + gc * GR, qv);
+  }
+  __syncthreads();
+  transpose_lds<TI>(sKV, LK, sKt, LC, C, DK, tid);
+  row_inv_norms<TI, DK>(sKV, LK, C, p.eps, sRk, tid);
+  row_inv_norms<TI, DK>(sQ, LK, C, p.eps, sRq, tid);
+  __syncthreads();
+
+  // K^K^T and Q^K^T, lower-triangular tiles only (diagonal included).
+  constexpr int NTRI = NB * (NB + 1) / 2;
+  for (int t = wave; t < 2 * NTRI; t += 4) {
+    const bool is_s = t >= NTRI;
+    const int tt = is_s ? t - NTRI : t;
+    int i = 0;
+    while ((i + 1) * (i + 2) / 2 <= tt) ++i;
+    const int j = tt - i * (i + 1) / 2;
+    f32x4 acc = zero4();
+    mma16<DK>(acc, (is_s ? sQ : sKV) + 16 * i * LK, LK, sKV + 16 * j * LK, LK, lane);
+    float* dst = is_s ? sS : sG;
+    const float* ra = is_s ? sRq : sRk;
+    const int col = 16 * j + (lane & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * i + (lane >> 4) * 4 + e;
+      dst[row * LF + col] = acc[e] * ra[row] * sRk[col];
+    }
+  }
+  __syncthreads();
+
+  const int grp = p.hv / p.hk;
+  for (int gi = 0; gi < grp; ++gi) {
+    const int h = kh * grp + gi;
+    const int64_t blk = (int64_t)c * p.hv + h;
+
+    // V rows (row-major, into the U~ region for now) and the gates.
+    const int GPRV = DV / GR;
+    for (int idx = tid; idx < C * GPRV; idx += kThreads) {
+      const int r = idx / GPRV, gc = idx % GPRV;
+      uint4 vv = make_uint4(0, 0, 0, 0);
+      if (r < n) vv = ld16(vg + (int64_t)(t0 + r) * p.v_st + h * p.v_sh + gc * GR);
+      st16(sUT + r * LV + gc * GR, vv);
+    }
+    if (wave == 0) {
+      float gv = 0.f, bv = 0.f;
+      if (lane < n) {
+        gv = p.g[(int64_t)(t0 + lane) * p.g_st + h * p.g_sh];
+        bv = p.beta[(int64_t)(t0 + lane) * p.b_st + h * p.b_sh];
+      }
+      float x = gv;  // inclusive scan over the chunk
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+      }
+      const float glast = __shfl(x, C - 1);
+      if (lane < C) {
+        sGam[lane] = x;
+        sBeta[lane] = bv;
+        sEg[lane] = expf(x);
+        sKs[lane] = sRk[lane] * expf(glast - x);
+      }
+    }
+    __syncthreads();
+    transpose_lds<TI>(sUT, LV, sKV, LC, C, DV, tid);  // V^T [dv][s]
+
+    // A_rs = beta_r exp(gamma_r - gamma_s) (k^_r . k^_s), s < r.
+    for (int idx = tid; idx < C * C; idx += kThreads) {
+      const int r = idx / C, s = idx % C;
+      float a = 0.f;
+      if (s < r) a = sBeta[r] * expf(sGam[r] - sGam[s]) * sG[r * LF + s];
+      sA[r * LF + s] = a;
+    }
+    __syncthreads();
+
+    // T = (I + A)^-1.  Diagonal 16x16 blocks by forward substitution, one
+    // lane per column; then block rows i = 1.. by
+    //   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj   (fp32 MFMA).
+    if (wave == 0) {
+      const int b = lane >> 4, col = lane & 15;
+      if (b < NB) {
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (i == col) ? 1.f : 0.f;
+        const float* Ab = sA + (16 * b) * LF + 16 * b;
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
+          float acc = x[r];
+#pragma unroll
+          for (int s = 0; s < r; ++s) acc -= Ab[r * LF + s] * x[s];
+          x[r] = acc;
+        }
+        float* Tb = sT + (16 * b) * LF + 16 * b;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Tb[i * LF + col] = x[i];
+      }
+    }
+    __syncthreads();
+    for (int bi = 1; bi < NB; ++bi) {
+      float* scr = sScr + wave * 16 * 20;
+      if (wave < bi) {
+        const int bj = wave;
+        f32x4 acc = zero4();
+        for (int bk = bj; bk < bi; ++bk)
+          mma16_f32_kn(acc, sA + (16 * bi) * LF + 16 * bk, LF, sT + (16 * bk) * LF + 16 * bj, LF, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) scr[((lane >> 4) * 4 + e) * 20 + (lane & 15)] = acc[e];
+      }
+      __syncthreads();
+      if (wave < bi) {
+        const int bj = wave;
+        f32x4 acc = zero4();
+        mma16_f32_kn(acc, sT + (16 * bi) * LF + 16 * bi, LF, scr, 20, lane);
+        float* dst = sT + (16 * bi) * LF + 16 * bj;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[((lane >> 4) * 4 + e) * LF + (lane & 15)] = -acc[e];
+      }
+      __syncthreads();
+    }
+
+    // Tb = T diag(beta e^gamma rk), Tv = T diag(beta), P = scale D o (Q^K^T).
+    for (int idx = tid; idx < C * C; idx += kThreads) {
+      const int r = idx / C, s = idx % C;
+      const float tv = (s <= r) ? sT[r * LF + s] : 0.f;
+      sTb[r * LC + s] = from_float<TI>(tv * sBeta[s] * sEg[s] * sRk[s]);
+      sTv[r * LC + s] = from_float<TI>(tv * sBeta[s]);
+      const float pv = (s <= r) ? p.scale * sS[r * LF + s] * expf(sGam[r] - sGam[s]) : 0.f;
+      sP[r * LC + s] = from_float<TI>(pv);
+    }
+    __syncthreads();
+
+    // U~ = Tv V, stored as U~^T [dv][r] (global and LDS).
+    TI* ut_g = (TI*)p.im.ut + blk * DV * C;
+    const int NVT = DV / 16;
+    for (int t = wave; t < NB * NVT; t += 4) {
+      const int i = t % NB, j = t / NB;
+      f32x4 acc = zero4();
+      mma16<C>(acc, sTv + 16 * i * LC, LC, sKV + 16 * j * LC, LC, lane);
+      const int dv = 16 * j + (lane & 15), r0 = 16 * i + (lane >> 4) * 4;
+      store4<TI>(ut_g + dv * C + r0, acc[0], acc[1], acc[2], acc[3]);
+      store4<TI>(sUT + dv * LC + r0, acc[0], acc[1], acc[2], acc[3]);
+    }
+    __syncthreads();
+
+    // W^T tiles (rows d_k, columns r): W[r][dk] = sum_s Tb[r][s] K[s][dk].
+    TI* w_g = (TI*)p.im.w + blk * C * DK;
+    for (int t = wave; t < NKT * NB; t += 4) {
+      const int i = t % NKT, j = t / NKT;
+      f32x4 acc = zero4();
+      mma16<C>(acc, sKt + 16 * i * LC, LC, sTb + 16 * j * LC, LC, lane);
+      const int r = 16 * j + (lane & 15), dk0 = 16 * i + (lane >> 4) * 4;
+      store4<TI>(w_g + r * DK + dk0, acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sKV[(dk0 + e) * LC + r] = from_float<TI>(acc[e]);
+    }
+    __syncthreads();
+
+    // Q' = scale diag(e^gamma rq) Q - P W (as Q'^T tiles) and O_loc = P U~.
+    TI* qp_g = (TI*)p.im.qp + blk * C * DK;
+    for (int t = wave; t < NKT * NB; t += 4) {
+      const int i = t % NKT, j = t / NKT;
+      f32x4 acc = zero4();
+      mma16<C>(acc, sKV + 16 * i * LC, LC, sP + 16 * j * LC, LC, lane);
+      const int r = 16 * j + (lane & 15), dk0 = 16 * i + (lane >> 4) * 4;
+      const float qs = p.scale * sEg[r] * sRq[r];
+      const f32x4 qv = load4<TI>(sQ + r * LK + dk0);
+      store4<TI>(qp_g + r * DK + dk0, qs * qv[0] - acc[0], qs * qv[1] - acc[1],
+                 qs * qv[2] - acc[2], qs * qv[3] - acc[3]);
+    }
+    TI* ol_g = (TI*)p.im.oloc + blk * C * DV;
+    for (int t = wave; t < NVT * NB; t += 4) {
+      const int i = t % NVT, j = t / NVT;
+      f32x4 acc = zero4();
+      mma16<C>(acc, sUT + 16 * i * LC, LC, sP + 16 * j * LC, LC, lane);
+      const int r = 16 * j + (lane & 15), dv0 = 16 * i + (lane >> 4) * 4;
+      store4<TI>(ol_g + r * DV + dv0, acc[0], acc[1], acc[2], acc[3]);
+    }
+    // K~^T [dk][r] = K^T[dk][r] rk_r e^(gamma_last - gamma_r).
+    TI* kt_g = (TI*)p.im.kt + blk * DK * C;
+    constexpr int GPC = C / GR;
+    for (int idx = tid; idx < DK * GPC; idx += kThreads) {
+      const int dk = idx / GPC, gc = idx % GPC;
+      uint4 kv = ld16(sKt + dk * LC + gc * GR);
+      TI* e = (TI*)&kv;
+#pragma unroll
+      for (int j = 0; j < GR; ++j) e[j] = from_float<TI>(to_float(e[j]) * sKs[gc * GR + j]);
+      st16(kt_g + dk * C + gc * GR, kv);
+    }
+    if (tid == 0) p.im.decay[blk] = sEg[C - 1];
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// state scan fused with the output
+
+template <typename TI, int C, int DK>
+struct ScanLayout {
+  static constexpr int S = sizeof(TI);
+  static constexpr int PADE = 16 / S;
+  static constexpr int LK = DK + PADE;
+  static constexpr int LC = C + PADE;
+  static constexpr int sz_w = C * LK * S;   // W or Q' [C][LK]
+  static constexpr int sz_kt = DK * LC * S; // K~^T [DK][LC]
+  static constexpr int sz_buf = 2 * sz_w + sz_kt;
+  static constexpr int r_ht = 2 * sz_buf;   // H^T slice [16][LK]
+  static constexpr int r_ut = r_ht + 16 * LK * S;  // U^T slice [16][LC]
+  static constexpr int total = r_ut + 16 * LC * S;
+};
+
+template <typename TI, int C, int DK>
+__global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
+  using L = ScanLayout<TI, C, DK>;
+  constexpr int LK = L::LK, LC = L::LC;
+  constexpr int GR = Gran<TI>::n;
+  constexpr int NB = C / 16;
+  constexpr int NKT = DK / 16;
+  constexpr int NHW = (NKT + 3) / 4;      // state tiles per wave
+  constexpr int NGW = C * DK / GR;        // granules in one W / Q' / K~^T block
+  constexpr int NG = 3 * NGW;
+  constexpr int NPT = (NG + kThreads - 1) / kThreads;
+  __shared__ __attribute__((aligned(16))) char smem[L::total];
+  TI* sHt = (TI*)(smem + L::r_ht);
+  TI* sUt = (TI*)(smem + L::r_ut);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NS = p.n_slices;
+  // XCD-aware: the slices of one (sequence, head) share blockIdx % 8 and so
+  // land on the same XCD, where they share W, Q' and K~^T through its L2.
+  const int b = blockIdx.x;
+  const int u = (b / (8 * NS)) * 8 + (b % 8);
+  const int sl = (b / 8) % NS;
+  if (u >= p.map.n_seq * p.hv) return;
+  const int seq = u / p.hv, h = u % p.hv;
+  const int DV = p.dv;
+  const int dv0 = 16 * sl;
+  int c_begin, c_end, tok0, tok_end;
+  seq_range(p.map, seq, C, c_begin, c_end, tok0, tok_end);
+
+  const int64_t sbase = ((int64_t)seq * p.hv + h) * DK * DV;
+  f32x4 hacc[NHW];
+#pragma unroll
+  for (int j = 0; j < NHW; ++j) {
+    hacc[j] = zero4();
+    const int ti = wave + 4 * j;
+    if (ti < NKT && p.init) {
+      const int dk0 = 16 * ti + (lane >> 4) * 4, dv = dv0 + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hacc[j][e] = p.init[sbase + (int64_t)(dk0 + e) * DV + dv];
+    }
+  }
+
+  const TI* wg = (const TI*)p.im.w;
+  const TI* qpg = (const TI*)p.im.qp;
+  const TI* ktg = (const TI*)p.im.kt;
+  const TI* utg = (const TI*)p.im.ut;
+  const TI* olg = (const TI*)p.im.oloc;
+  TI* outg = (TI*)p.out;
+
+  // Register staging of the next chunk's W, Q' and K~^T (granule g of the
+  // three consecutive blocks goes to thread g % 256, slot g / 256).
+  uint4 stg[NPT];
+#define GDN_SCAN_ISSUE(CC)                                                      \
+  {                                                                             \
+    const int64_t blk_ = (int64_t)(CC) * p.hv + h;                              \
+    _Pragma("unroll") for (int k = 0; k < NPT; ++k) {                           \
+      const int g = tid + k * kThreads;                                         \
+      if (g < NG) {                                                             \
+        const int a = g / NGW, gg = g - a * NGW;                                \
+        const TI* src = (a == 0 ? wg : (a == 1 ? qpg : ktg)) + blk_ * C * DK + gg * GR; \
+        stg[k] = ld16(src);                                                     \
+      }                                                                         \
+    }                                                                           \
+  }
+#define GDN_SCAN_COMMIT(BUF)                                                    \
+  {                                                                             \
+    TI* base_ = (TI*)(smem + (BUF) * L::sz_buf);                                \
+    _Pragma("unroll") for (int k = 0; k < NPT; ++k) {                           \
+      const int g = tid + k * kThreads;                                         \
+      if (g < NG) {                                                             \
+        const int a = g / NGW, gg = g - a * NGW;                                \
+        TI* dst = (a < 2)                                                       \
+            ? base_ + a * (L::sz_w / L::S) + (gg / (DK / GR)) * LK + (gg % (DK / GR)) * GR \
+            : base_ + 2 * (L::sz_w / L::S) + (gg / (C / GR)) * LC + (gg % (C / GR)) * GR;  \
+        st16(dst, stg[k]);                                                      \
+      }                                                                         \
+    }                                                                           \
+  }
+  // Per-lane U~ (U layout) and O_loc (O^T layout) pieces of this slice.
+#define GDN_SCAN_SMALL(CC, UT, OL, DEC)                                         \
+  {                                                                             \
+    const int64_t blk_ = (int64_t)(CC) * p.hv + h;                              \
+    DEC = p.im.decay[blk_];                                                     \
+    if (wave < NB) {                                                            \
+      UT = load4<TI>(utg + blk_ * DV * C + (int64_t)(dv0 + (lane & 15)) * C + 16 * wave + (lane >> 4) * 4); \
+      OL = load4<TI>(olg + blk_ * C * DV + (int64_t)(16 * wave + (lane & 15)) * DV + dv0 + (lane >> 4) * 4); \
+    }                                                                           \
+  }
+  f32x4 ut_c = zero4(), ol_c = zero4(), ut_n = zero4(), ol_n = zero4();
+  float dec_c = 1.f, dec_n = 1.f;
+
+  if (c_begin < c_end) {
+    GDN_SCAN_ISSUE(c_begin);
+    GDN_SCAN_SMALL(c_begin, ut_c, ol_c, dec_c);
+    GDN_SCAN_COMMIT(0);
+  }
+  for (int cc = c_begin; cc < c_end; ++cc) {
+    const int buf = (cc - c_begin) & 1;
+    const bool has_next = cc + 1 < c_end;
+    if (has_next) {
+      GDN_SCAN_ISSUE(cc + 1);
+      GDN_SCAN_SMALL(cc + 1, ut_n, ol_n, dec_n);
+    }
+    const TI* sW = (const TI*)(smem + buf * L::sz_buf);
+    const TI* sQp = sW + L::sz_w / L::S;
+    const TI* sKt = sW + 2 * (L::sz_w / L::S);
+    // H (as operand precision) -> sHt[dv][dk]
+#pragma unroll
+    for (int j = 0; j < NHW; ++j) {
+      const int ti = wave + 4 * j;
+      if (ti < NKT) {
+        const int dk0 = 16 * ti + (lane >> 4) * 4;
+        store4<TI>(sHt + (lane & 15) * LK + dk0, hacc[j][0], hacc[j][1], hacc[j][2], hacc[j][3]);
+      }
+    }
+    __syncthreads();
+    const int tok = tok0 + (cc - c_begin) * C;
+    const int n = min(C, tok_end - tok);
+    if (wave < NB) {
+      // U = U~ - W H   (rows r of this wave's tile, columns = the slice)
+      f32x4 au = zero4();
+      mma16<DK>(au, sW + 16 * wave * LK, LK, sHt, LK, lane);
+      store4<TI>(sUt + (lane & 15) * LC + 16 * wave + (lane >> 4) * 4,
+                 ut_c[0] - au[0], ut_c[1] - au[1], ut_c[2] - au[2], ut_c[3] - au[3]);
+      // O^T = H^T Q'^T + O_loc^T
+      f32x4 ao = zero4();
+      mma16<DK>(ao, sHt, LK, sQp + 16 * wave * LK, LK, lane);
+      const int r = 16 * wave + (lane & 15);
+      if (r < n) {
+        store4<TI>(outg + (int64_t)(tok + r) * p.o_st + (int64_t)h * p.o_sh + dv0 + (lane >> 4) * 4,
+                   ao[0] + ol_c[0], ao[1] + ol_c[1], ao[2] + ol_c[2], ao[3] + ol_c[3]);
+      }
+    }
+    __syncthreads();
+    // H <- e^gamma_last H + K~^T U
+#pragma unroll
+    for (int j = 0; j < NHW; ++j) {
+      const int ti = wave + 4 * j;
+      if (ti < NKT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hacc[j][e] *= dec_c;
+        mma16<C>(hacc[j], sKt + 16 * ti * LC, LC, sUt, LC, lane);
+      }
+    }
+    if (has_next) {
+      GDN_SCAN_COMMIT(buf ^ 1);
+      ut_c = ut_n;
+      ol_c = ol_n;
+      dec_c = dec_n;
+    }
+  }
+#undef GDN_SCAN_ISSUE
+#undef GDN_SCAN_COMMIT
+#undef GDN_SCAN_SMALL
+
+  if (p.final_state) {
+#pragma unroll
+    for (int j = 0; j < NHW; ++j) {
+      const int ti = wave + 4 * j;
+      if (ti < NKT) {
+        const int dk0 = 16 * ti + (lane >> 4) * 4, dv = dv0 + (lane & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p.final_state[sbase + (int64_t)(dk0 + e) * DV + dv] = hacc[j][e];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+
+template <typename TI, int C, int DK>
+static constexpr bool fits() {
+  return WyLayout<TI, C, DK>::total <= kLdsLimit && ScanLayout<TI, C, DK>::total <= kLdsLimit;
+}
+
+template <typename TI, int C, int DK>
+static int launch_pair(int stage, const WyParams* wy, const ScanParams* sc,
+                       dim3 grid, hipStream_t s) {
+  if constexpr (fits<TI, C, DK>()) {
+    if (stage == 0) hipLaunchKernelGGL((wy_kernel<TI, C, DK>), grid, dim3(kThreads), 0, s, *wy);
+    else hipLaunchKernelGGL((scan_kernel<TI, C, DK>), grid, dim3(kThreads), 0, s, *sc);
+    return 0;
+  } else {
+    return -1;
+  }
+}
+
+template <typename TI, int C>
+static int dispatch_dk(int dk, int stage, const WyParams* wy, const ScanParams* sc,
+                       dim3 grid, hipStream_t s) {
+  switch (dk) {
+    case 16: return launch_pair<TI, C, 16>(stage, wy, sc, grid, s);
+    case 32: return launch_pair<TI, C, 32>(stage, wy, sc, grid, s);
+    case 64: return launch_pair<TI, C, 64>(stage, wy, sc, grid, s);
+    case 128: return launch_pair<TI, C, 128>(stage, wy, sc, grid, s);
+  }
+  return -1;
+}
+
+template <typename TI>
+static int dispatch_c(int chunk, int dk, int stage, const WyParams* wy,
+                      const ScanParams* sc, dim3 grid, hipStream_t s) {
+  switch (chunk) {
+    case 16: return dispatch_dk<TI, 16>(dk, stage, wy, sc, grid, s);
+    case 32: return dispatch_dk<TI, 32>(dk, stage, wy, sc, grid, s);
+    case 64: return dispatch_dk<TI, 64>(dk, stage, wy, sc, grid, s);
+  }
+  return -1;
+}
+
+template <typename TI>
+static bool fits_any(int chunk, int dk) {
+#define GDN_FITS(CC, DD) if (chunk == CC && dk == DD) return fits<TI, CC, DD>();
+  GDN_FITS(16, 16) GDN_FITS(16, 32) GDN_FITS(16, 64) GDN_FITS(16, 128)
+  GDN_FITS(32, 16) GDN_FITS(32, 32) GDN_FITS(32, 64) GDN_FITS(32, 128)
+  GDN_FITS(64, 16) GDN_FITS(64, 32) GDN_FITS(64, 64) GDN_FITS(64, 128)
+#undef GDN_FITS
+  return false;
+}
+
+bool kernels_available(bool bf16, int chunk, int dk) {
+  return bf16 ? fits_any<gdn::bf16>(chunk, dk) : fits_any<float>(chunk, dk);
+}
+
+hipError_t launch_table(const TableParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(table_kernel, dim3(1), dim3(1024), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_wy(bool bf16, int chunk, int dk, const WyParams& p,
+                     int grid_x, int grid_y, hipStream_t s) {
+  const dim3 grid(grid_x, grid_y);
+  const int rc = bf16 ? dispatch_c<gdn::bf16>(chunk, dk, 0, &p, nullptr, grid, s)
+                      : dispatch_c<float>(chunk, dk, 0, &p, nullptr, grid, s);
+  if (rc) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(bool bf16, int chunk, int dk, const ScanParams& p,
+                       int grid_x, hipStream_t s) {
+  const dim3 grid(grid_x);
+  const int rc = bf16 ? dispatch_c<gdn::bf16>(chunk, dk, 1, nullptr, &p, grid, s)
+                      : dispatch_c<float>(chunk, dk, 1, nullptr, &p, grid, s);
+  if (rc) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace gdn

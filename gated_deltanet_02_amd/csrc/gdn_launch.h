@@ -1,0 +1,20 @@
+// Host-side launchers of the gfx950 kernels (defined in gdn_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+
+// True when kernels for this element type / chunk / d_k were built (some
+// fp32 combinations exceed the 160 KiB of LDS and are not).
+bool kernels_available(bool bf16, int chunk, int dk);
+
+hipError_t launch_table(const TableParams& p, hipStream_t s);
+hipError_t launch_wy(bool bf16, int chunk, int dk, const WyParams& p,
+                     int grid_x, int grid_y, hipStream_t s);
+hipError_t launch_scan(bool bf16, int chunk, int dk, const ScanParams& p,
+                       int grid_x, hipStream_t s);
+
+}  // namespace gdn

@@ -1,0 +1,186 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) chunked Gated DeltaNet prefill.
+ *
+ * The operation.  For every sequence i (tokens cu[i] .. cu[i+1]-1 of a packed
+ * batch) and every value head h (reading key head h / (Hv/Hk)), starting from
+ * the d_k x d_v state H = init_state[i, h] (or zeros):
+ *
+ *     q^ = q_t / sqrt(|q_t|^2 + eps),  k^ = k_t / sqrt(|k_t|^2 + eps)
+ *     H  = exp(g_t) (I - beta_t k^ k^T) H + beta_t k^ v_t^T
+ *     out[t, h] = scale * H^T q^
+ *
+ * and final_state[i, h] = H after the sequence's last token.  This is the
+ * gated delta rule ("Gated Delta Networks: Improving Mamba2 with Delta
+ * Rule", Yang, Kautz, Hatamizadeh, ICLR 2025, section 3) with the state
+ * stored as d_k x d_v.  The serving pages name the operation as the
+ * "chunked Gated DeltaNet prefill" of their native Qwen3.5 backend ("Cua-S1
+ * 4B 0.2 native text worker"; "Open-Jev-27B-v1.1 native text worker",
+ * section "Validation and optimization scope") and test it against float64
+ * references, as this library's tests do.
+ *
+ * The library evaluates it chunk by chunk (chunk C in {16, 32, 64}, default
+ * 64) on the caller's HIP stream with three kernels: a chunk table, a fused
+ * L2-norm / gate-prep / intra-chunk WY kernel, and a fused inter-chunk
+ * state-scan / output kernel.
+ *
+ * Conventions taken from the pages:
+ *   - a versioned ABI that callers are rebuilt against ("Cua-S1 4B 0.2
+ *     native text worker"; "Open-Jev-27B-v1.1 native text worker", section
+ *     "Build and serve");
+ *   - invalid or oversize inputs are rejected before any work starts
+ *     (same page, section "Prepare the checkpoint");
+ *   - vector memory paths only where width, stride and pointers permit
+ *     (same page, section "Validation and optimization scope"); here
+ *     layouts that do not permit them are rejected with GDN_ERR_LAYOUT.
+ *
+ * Error behaviour (all entry points): arguments are validated on the host
+ * before any HIP call; a failed validation returns a negative status and
+ * enqueues nothing.  No exception crosses the ABI.  gdn_last_error() gives a
+ * message for the calling thread's last failure.  The contents of
+ * cu_seqlens are a precondition (cu[0] = 0, non-decreasing, cu[N] = T); the
+ * library never reads device memory on the host, so it cannot check them,
+ * but the kernels clamp them so that a bad table cannot make them access
+ * memory outside the tensors.  Faults of enqueued work surface at the
+ * caller's next synchronisation of the stream.  No call synchronises the
+ * device.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+/* Status codes. */
+#define GDN_OK 0
+#define GDN_ERR_NULL_ARG (-1)    /* a required tensor or pointer is NULL      */
+#define GDN_ERR_DTYPE (-2)       /* unsupported or mismatched element types   */
+#define GDN_ERR_SHAPE (-3)       /* inconsistent or out-of-range sizes        */
+#define GDN_ERR_LAYOUT (-4)      /* strides / alignment the kernels cannot use */
+#define GDN_ERR_UNSUPPORTED (-5) /* valid but not built: head size, chunk ... */
+#define GDN_ERR_WORKSPACE (-6)   /* workspace missing, too small or misaligned */
+#define GDN_ERR_HIP (-7)         /* a HIP call or kernel launch failed        */
+
+/* Element types. */
+#define GDN_DTYPE_BF16 1
+#define GDN_DTYPE_F32 2
+#define GDN_DTYPE_I32 3
+
+/* A strided view of caller-owned memory (device memory for every tensor
+ * argument).  shape/stride have ndim valid entries, outermost first; strides
+ * are in elements.  The library never frees, retains or reallocates it. */
+typedef struct gdn_tensor {
+  void* data;
+  int32_t dtype;
+  int32_t ndim;
+  int64_t shape[4];
+  int64_t stride[4];
+} gdn_tensor;
+
+/* Stage mask bits for gdn_options.stages.  A full call runs all of them; a
+ * caller-owned workspace keeps the intermediates between partial calls so a
+ * caller may run (and time) the stages one at a time, in order. */
+#define GDN_STAGE_TABLE 1u /* chunk table from cu_seqlens                   */
+#define GDN_STAGE_WY 2u    /* L2 norms, gate cumsum, (I+A)^-1, W, U~, Q', K~ */
+#define GDN_STAGE_SCAN 4u  /* sequential state scan fused with the output   */
+#define GDN_STAGE_ALL 7u
+
+typedef struct gdn_options {
+  int32_t chunk;   /* 16, 32 or 64 (default 64)                             */
+  float scale;     /* output multiplier (default 1.0)                        */
+  float l2_eps;    /* epsilon inside the L2 norm's square root (1e-6)        */
+  uint32_t stages; /* GDN_STAGE_* mask (default GDN_STAGE_ALL)               */
+} gdn_options;
+
+/* Returns GDN_ABI_VERSION of the built library. */
+int gdn_abi_version(void);
+
+/* Fills *opts with the defaults listed in gdn_options. */
+void gdn_default_options(gdn_options* opts);
+
+/*
+ * gdn_prefill -- the whole prefill on `stream` (a hipStream_t; NULL = the
+ * null stream), with default options and a workspace the library allocates
+ * and frees stream-ordered (hipMallocAsync / hipFreeAsync on `stream`).
+ *
+ *   q, k        [T, Hk, dk] or [B, T/B, Hk, dk]; bf16 or f32
+ *   v, out      [T, Hv, dv] (or 4-D like q); same dtype as q
+ *   g, beta     [T, Hv] (or [B, T/B, Hv]) f32: g is the log-decay (<= 0,
+ *               alpha = exp(g)), beta the write strength in [0, 1] (already
+ *               passed through the sigmoid).  These ranges are
+ *               preconditions, not checked.
+ *   cu_seqlens  int32 [N+1] device array of sequence starts, or NULL: one
+ *               sequence of T tokens (3-D inputs) or B sequences of T/B
+ *               tokens each (4-D inputs).  With cu_seqlens, 4-D inputs need
+ *               B == 1.
+ *   init_state  f32 [N, Hv, dk, dv] contiguous, or NULL for zeros
+ *   final_state f32 [N, Hv, dk, dv] contiguous, or NULL (not written); it
+ *               may be the same memory as init_state.
+ * Sizes: dk, dv in {16, 32, 64, 128}; Hv a multiple of Hk; N, T < 2^31.
+ * Layout: unit stride in the last dimension; other strides multiples of 8
+ * elements (bf16) or 4 (f32); 16-byte aligned data pointers; for 4-D
+ * tensors stride[0] == shape[1] * stride[1].  Otherwise GDN_ERR_LAYOUT.
+ * All tensors are caller-owned device memory that must stay valid until
+ * the stream reaches the end of the enqueued work.  Returns a GDN_* status.
+ */
+int gdn_prefill(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
+                const gdn_tensor* g, const gdn_tensor* beta,
+                const gdn_tensor* cu_seqlens, const gdn_tensor* init_state,
+                gdn_tensor* out, gdn_tensor* final_state, void* stream);
+
+/*
+ * gdn_prefill_ex -- as gdn_prefill, with options (NULL = defaults) and a
+ * caller-owned device workspace of at least gdn_workspace_size() bytes,
+ * 256-byte aligned.  It allocates nothing.  The workspace must not be used
+ * by another call that overlaps on the device.
+ */
+int gdn_prefill_ex(const gdn_tensor* q, const gdn_tensor* k,
+                   const gdn_tensor* v, const gdn_tensor* g,
+                   const gdn_tensor* beta, const gdn_tensor* cu_seqlens,
+                   const gdn_tensor* init_state, gdn_tensor* out,
+                   gdn_tensor* final_state, const gdn_options* opts,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Byte offsets of the intermediates inside the workspace (for inspection and
+ * tests).  Per (chunk c, value head h) block, all in the input dtype:
+ *   w       [C][dk]  W  = T diag(beta e^gamma) K^
+ *   qp      [C][dk]  Q' = scale diag(e^gamma) Q^ - P W
+ *   kt      [dk][C]  K~^T, K~_r = e^(gamma_last - gamma_r) k^_r
+ *   ut      [dv][C]  U~^T, U~ = T diag(beta) V
+ *   oloc    [C][dv]  O_loc = P U~
+ * and f32 decay[c][h] = e^(gamma_last).  Chunk c's blocks start at
+ * offset + (c * Hv + h) * block_elems * element_size.  Rows past the end of
+ * a short chunk are zero.  chunk_table is int32 [max_chunks][4] =
+ * (sequence, first token, length, 0) in packed mode. */
+typedef struct gdn_workspace_layout {
+  size_t total_bytes;
+  int64_t max_chunks;
+  size_t chunk_table, chunk_offsets, seq_starts, decay, w, qp, kt, ut, oloc;
+} gdn_workspace_layout;
+
+/* Computes the workspace size / layout for the given tensors and options
+ * (host only; data pointers are not read). */
+int gdn_workspace_size(const gdn_tensor* q, const gdn_tensor* k,
+                       const gdn_tensor* v, const gdn_tensor* cu_seqlens,
+                       const gdn_options* opts, size_t* bytes);
+int gdn_get_workspace_layout(const gdn_tensor* q, const gdn_tensor* k,
+                             const gdn_tensor* v, const gdn_tensor* cu_seqlens,
+                             const gdn_options* opts,
+                             gdn_workspace_layout* layout);
+
+/* Short description of a status code (static storage). */
+const char* gdn_status_string(int status);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

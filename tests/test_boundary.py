@@ -1,0 +1,157 @@
+"""The C-ABI library on the host: it loads, exports every function that
+include/gdn.h declares, and rejects bad arguments with the documented status
+before making any HIP call (no GPU needed: descriptors carry fake device
+addresses that are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import gated_deltanet_02_amd as G
+from gated_deltanet_02_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.library_path()):
+        pytest.fail("libgdn.so is not built (run __graft_entry__.build())")
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED), names
+
+
+def test_library_exports_every_declared_function(lib):
+    raw = ctypes.CDLL(B.library_path())
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} not exported"
+
+
+def test_abi_version_and_defaults(lib):
+    src = open(HEADER).read()
+    ver = int(re.search(r"#define GDN_ABI_VERSION (\d+)", src).group(1))
+    assert G.gdn_abi_version() == ver
+    o = G.gdn_default_options()
+    assert (o.chunk, o.scale, o.stages) == (0, 1.0, 7)
+    assert abs(o.l2_eps - 1e-6) < 1e-12
+    for s in range(-7, 1):
+        assert G.gdn_status_string(s) != "unknown status"
+    assert G.gdn_status_string(5) == "unknown status"
+
+
+def fake(shape, dtype, addr=0x10000, strides=None):
+    """A descriptor with a fake device address (never dereferenced)."""
+    d = B.GdnTensor()
+    d.data = addr
+    d.dtype = {torch.bfloat16: 1, torch.float32: 2, torch.int32: 3}[dtype]
+    d.ndim = len(shape)
+    if strides is None:
+        strides, acc = [], 1
+        for s in reversed(shape):
+            strides.insert(0, acc)
+            acc *= s
+    for i, (s, st) in enumerate(zip(shape, strides)):
+        d.shape[i] = s
+        d.stride[i] = st
+    return d
+
+
+def call(lib, q, k, v, g, b, cu=None, init=None, out=None, fin=None, opts=None,
+         ws=0x100000, ws_bytes=1 << 40):
+    r = lambda x: ctypes.byref(x) if x is not None else None  # noqa: E731
+    return lib.gdn_prefill_ex(r(q), r(k), r(v), r(g), r(b), r(cu), r(init), r(out), r(fin),
+                              r(opts), ws, ws_bytes, None)
+
+
+def base(T=128, hk=2, hv=4, dk=64, dv=64, dt=torch.bfloat16):
+    return dict(q=fake((T, hk, dk), dt), k=fake((T, hk, dk), dt), v=fake((T, hv, dv), dt),
+                g=fake((T, hv), torch.float32), b=fake((T, hv), torch.float32),
+                out=fake((T, hv, dv), dt))
+
+
+CASES = {
+    "null_q": (lambda a: a.update(q=None), -1),
+    "null_out": (lambda a: a.update(out=None), -1),
+    "dtype_k": (lambda a: a.update(k=fake((128, 2, 64), torch.float32)), -2),
+    "dtype_g": (lambda a: a.update(g=fake((128, 4), torch.bfloat16)), -2),
+    "shape_k": (lambda a: a.update(k=fake((128, 2, 32), torch.bfloat16)), -3),
+    "shape_v_tokens": (lambda a: a.update(v=fake((127, 4, 64), torch.bfloat16)), -3),
+    "heads_not_multiple": (lambda a: a.update(v=fake((128, 3, 64), torch.bfloat16),
+                                              out=fake((128, 3, 64), torch.bfloat16),
+                                              g=fake((128, 3), torch.float32),
+                                              b=fake((128, 3), torch.float32)), -3),
+    "head_dim_96": (lambda a: a.update(q=fake((128, 2, 96), torch.bfloat16),
+                                       k=fake((128, 2, 96), torch.bfloat16)), -5),
+    "misaligned_q": (lambda a: a.update(q=fake((128, 2, 64), torch.bfloat16, addr=0x10002)), -4),
+    "token_stride_not_16B": (lambda a: a.update(
+        q=fake((128, 2, 64), torch.bfloat16, strides=(132, 66, 1)),
+        k=fake((128, 2, 64), torch.bfloat16, strides=(132, 66, 1))), -4),
+    "last_stride": (lambda a: a.update(v=fake((128, 4, 64), torch.bfloat16, strides=(512, 128, 2))), -4),
+    "g_shape": (lambda a: a.update(g=fake((128, 2), torch.float32)), -3),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_validation_errors(lib, case):
+    a = base()
+    mutate, want = CASES[case]
+    mutate(a)
+    rc = call(lib, a["q"], a["k"], a["v"], a["g"], a["b"], out=a["out"])
+    assert rc == want, (case, rc, G.gdn_last_error())
+    assert G.gdn_last_error() != ""
+
+
+def test_state_and_cu_validation(lib):
+    a = base()
+    cu = fake((4,), torch.int32)
+    st_ok = fake((3, 4, 64, 64), torch.float32)
+    assert call(lib, a["q"], a["k"], a["v"], a["g"], a["b"], cu=cu, init=fake((2, 4, 64, 64), torch.float32),
+                out=a["out"]) == -3
+    assert call(lib, a["q"], a["k"], a["v"], a["g"], a["b"], cu=fake((4,), torch.float32),
+                out=a["out"]) == -2
+    bad_stride = fake((3, 4, 64, 64), torch.float32, strides=(4 * 64 * 65, 64 * 65, 65, 1))
+    assert call(lib, a["q"], a["k"], a["v"], a["g"], a["b"], cu=cu, fin=bad_stride,
+                out=a["out"]) == -4
+    # fp32 with a 64-token chunk and d_k = 128 exceeds LDS: unsupported
+    f = base(dt=torch.float32, dk=128, dv=128)
+    o = B.options(chunk=64)
+    assert call(lib, f["q"], f["k"], f["v"], f["g"], f["b"], out=f["out"], opts=o) == -5
+    o = B.options(chunk=48)
+    assert call(lib, a["q"], a["k"], a["v"], a["g"], a["b"], out=a["out"], opts=o) == -5
+    # workspace too small / misaligned
+    assert call(lib, a["q"], a["k"], a["v"], a["g"], a["b"], out=a["out"], ws_bytes=10) == -6
+    assert call(lib, a["q"], a["k"], a["v"], a["g"], a["b"], out=a["out"], ws=0x100010) == -6
+    assert st_ok is not None
+
+
+def test_workspace_size_formula(lib):
+    q = torch.empty(4096, 16, 128, dtype=torch.bfloat16)
+    v = torch.empty(4096, 16, 128, dtype=torch.bfloat16)
+    n = G.gdn_workspace_size(q, q, v)
+    # 64 chunks x 16 heads x (3 C*dk + 2 C*dv) bf16 + decay, 256-byte aligned
+    per = 64 * 16 * (5 * 64 * 128) * 2
+    assert per <= n <= per + 64 * 16 * 4 + 6 * 256
+    lay = G.gdn_get_workspace_layout(q, q, v)
+    assert lay.max_chunks == 64 and lay.total_bytes == n
+    offs = [lay.decay, lay.w, lay.qp, lay.kt, lay.ut, lay.oloc]
+    assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+
+
+def test_binding_refuses_host_tensors(lib):
+    x = torch.zeros(64, 1, 16)
+    g = torch.zeros(64, 1)
+    with pytest.raises(ValueError):
+        G.gdn_prefill(x, x, x, g, g)

@@ -1,0 +1,167 @@
+"""Invariances and edge cases of the HIP path (GPU): determinism, packing,
+split/continuation, aliasing, strides, batch layout, empty and one-token
+sequences, chunk-size agreement, entry-point agreement, error paths."""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_02_amd as G
+from gated_deltanet_02_amd import workloads as W
+from oracle import oracle
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    U.need_gpu()
+
+
+def test_bitwise_deterministic():
+    w = W.make_workload("edge_mix", hk=2, hv=4)
+    o1, f1, d = U.run_gpu(w)
+    o2, f2, _ = U.run_gpu(w, dev=d)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+
+
+def test_packed_equals_separate_calls():
+    w = W.make_workload("packed_255", lengths=[130, 1, 64, 200, 63], hk=2, hv=2)
+    out, fin, _ = U.run_gpu(w)
+    starts = np.concatenate([[0], np.cumsum(w.lengths)])
+    for i in range(w.n_seqs):
+        s = W.select_sequences(w, [i])
+        o, f, _ = U.run_gpu(s)
+        assert np.array_equal(o, out[starts[i]:starts[i + 1]]), f"sequence {i}"
+        assert np.array_equal(f[0], fin[i])
+
+
+def test_empty_sequences_and_init_passthrough():
+    w = W.make_workload("long_16k_gqa", lengths=[0, 50, 0, 0, 70, 0], hk=1, hv=3)
+    assert w.init_state is not None
+    out, fin, _ = U.run_gpu(w)
+    init = w.init_state.numpy()
+    for i in (0, 2, 3, 5):
+        assert np.array_equal(fin[i], init[i])
+    ro, rf = oracle.reference_workload(w)
+    U.check_bf16(out, fin, ro, rf, label="empty sequences")
+
+
+def test_all_sequences_empty():
+    w = W.make_workload("long_16k_gqa", lengths=[0, 0], hk=1, hv=1)
+    out, fin, _ = U.run_gpu(w)
+    assert np.array_equal(fin, w.init_state.numpy())
+
+
+def test_single_token_and_cu_with_one_sequence():
+    w = W.make_workload("prompt_4k", lengths=[1], hk=1, hv=1)
+    o1, f1, d = U.run_gpu(w)
+    o2, f2, _ = U.run_gpu(w, with_cu=True, dev=d)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+    ro, rf = oracle.reference_workload(w)
+    U.check_bf16(o1, f1, ro, rf, label="one token")
+
+
+def test_split_continuation():
+    """[0, t) then [t, T) with the final state passed as the next initial state."""
+    w = W.make_workload("long_16k_gqa", lengths=[333], hk=1, hv=3)
+    out, fin, _ = U.run_gpu(w)
+    for t in (1, 64, 100):
+        a = W.make_workload("long_16k_gqa", lengths=[333], hk=1, hv=3)
+        a.q, a.k, a.v, a.g, a.beta, a.lengths = a.q[:t], a.k[:t], a.v[:t], a.g[:t], a.beta[:t], [t]
+        oa, fa, _ = U.run_gpu(a)
+        b = W.make_workload("long_16k_gqa", lengths=[333], hk=1, hv=3)
+        b.q, b.k, b.v, b.g, b.beta, b.lengths = b.q[t:], b.k[t:], b.v[t:], b.g[t:], b.beta[t:], [333 - t]
+        b.init_state = torch.from_numpy(fa)
+        ob, fb, _ = U.run_gpu(b)
+        both = np.concatenate([oa, ob])
+        U.check_bf16(both, fb, out, fin, label=f"split at {t} vs unsplit")
+
+
+def test_final_state_may_alias_init_state():
+    w = W.make_workload("long_16k_gqa", lengths=[40, 100], hk=1, hv=3)
+    o1, f1, _ = U.run_gpu(w)
+    o2, f2, _ = U.run_gpu(w, init_alias=True)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+
+
+def test_strided_views_and_4d_batch():
+    w = W.make_workload("prompt_4k", lengths=[96, 96, 96], hk=2, hv=2)
+    base_o, base_f, d = U.run_gpu(w)
+    # q/k/v/out as head slices of wider tensors (non-contiguous head/token strides)
+    T = w.t_total
+    def wide(x):
+        big = torch.zeros((T, 3 * x.shape[1], x.shape[2]), dtype=x.dtype, device="cuda")
+        big[:, x.shape[1]:2 * x.shape[1]] = x.to("cuda")
+        return big[:, x.shape[1]:2 * x.shape[1]]
+    q, k, v = wide(w.q), wide(w.k), wide(w.v)
+    out = wide(torch.zeros_like(w.v))
+    fin = torch.empty_like(d["final_state"])
+    G.gdn_prefill_ex(q, k, v, d["g"], d["beta"], d["cu_seqlens"], None, out, fin,
+                     opts=G.options(chunk=64))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy(), base_o)
+    assert np.array_equal(fin.cpu().numpy(), base_f)
+    # [B, T, H, d] with equal lengths and no cu_seqlens
+    q4 = d["q"].reshape(3, 96, *d["q"].shape[1:])
+    k4 = d["k"].reshape(3, 96, *d["k"].shape[1:])
+    v4 = d["v"].reshape(3, 96, *d["v"].shape[1:])
+    o4 = torch.empty_like(v4)
+    fin4 = torch.empty_like(d["final_state"])
+    G.gdn_prefill_ex(q4, k4, v4, d["g"].reshape(3, 96, -1), d["beta"].reshape(3, 96, -1),
+                     None, None, o4, fin4, opts=G.options(chunk=64))
+    torch.cuda.synchronize()
+    assert np.array_equal(o4.reshape(T, *o4.shape[2:]).float().cpu().numpy(), base_o)
+    assert np.array_equal(fin4.cpu().numpy(), base_f)
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_chunk_sizes_agree_with_oracle(chunk):
+    w = W.make_workload("edge_mix", lengths=[65, 130, 7], hk=1, hv=2)
+    out, fin, _ = U.run_gpu(w, chunk=chunk)
+    ro, rf = oracle.reference_workload(w)
+    U.check_bf16(out, fin, ro, rf, label=f"chunk {chunk}")
+
+
+def test_library_allocated_workspace_matches_caller_workspace():
+    w = W.make_workload("packed_255", lengths=[100, 200, 3], hk=2, hv=4)
+    o1, f1, d = U.run_gpu(w)
+    o2, f2, _ = U.run_gpu(w, entry="plain", dev=d)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+
+
+def test_scale_option_is_linear():
+    w = W.make_workload("prompt_4k", lengths=[100], hk=1, hv=1)
+    o1, f1, d = U.run_gpu(w)
+    o2, f2, _ = U.run_gpu(w, scale=0.25, dev=d)
+    assert np.array_equal(f1, f2)
+    assert U.max_abs(o2, 0.25 * o1) <= 0.25 * 2e-2
+
+
+def test_rejects_bad_arguments_before_launch():
+    w = W.make_workload("prompt_4k", lengths=[64], hk=1, hv=1)
+    d = W.to_device(w)
+    args = [d["q"], d["k"], d["v"], d["g"], d["beta"], None, None, d["out"], d["final_state"]]
+
+    def status_of(*a, **kw):
+        with pytest.raises(G.GdnError) as ei:
+            G.gdn_prefill_ex(*a, **kw)
+        return ei.value.status
+
+    bad = list(args)
+    bad[1] = d["k"][:, :, :64]                       # k narrower than q
+    assert status_of(*bad) == -3
+    odd = torch.zeros((65, 1, 128), dtype=torch.bfloat16, device="cuda")
+    bad = list(args)
+    bad[0] = odd.view(-1)[1:1 + 64 * 128].view(64, 1, 128)   # 2-byte misaligned
+    assert status_of(*bad) == -4
+    bad = list(args)
+    bad[2] = d["v"].float()                           # dtype mismatch
+    assert status_of(*bad) == -2
+    f32 = W.make_workload("tiny_fp32", lengths=[64], hk=1, hv=1, dk=128, dv=128)
+    fd = W.to_device(f32)
+    assert status_of(fd["q"], fd["k"], fd["v"], fd["g"], fd["beta"], None, None, fd["out"],
+                     fd["final_state"], opts=G.options(chunk=64)) == -5
+    small = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    assert status_of(*args, workspace=small) == -6
+    torch.cuda.synchronize()

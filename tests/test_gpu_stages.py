@@ -1,0 +1,93 @@
+"""Each stage's intermediates vs the float64 chunked evaluator (GPU).
+
+The chunk table and the WY stage run alone on a caller-owned workspace; the
+per-(chunk, value head) blocks are then read back through the documented
+workspace layout and compared with oracle/chunked.py's intermediates.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_02_amd as G
+from gated_deltanet_02_amd import workloads as W
+from oracle import chunked
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    U.need_gpu()
+
+
+def _blocks(ws, off, count, shape, dtype):
+    n = int(np.prod(shape)) * count
+    es = torch.tensor([], dtype=dtype).element_size()
+    return ws[off:off + n * es].view(dtype).view(count, *shape).float().cpu().numpy()
+
+
+CASES = [
+    ("bf16-single", "prompt_4k", dict(lengths=[150], hk=2, hv=4, dk=64, dv=64), 2e-2),
+    ("bf16-packed", "edge_mix", dict(lengths=[70, 1, 64, 30, 0, 129], hk=1, hv=2, dk=128, dv=128), 2e-2),
+    ("bf16-c32", "prompt_4k", dict(lengths=[100], hk=1, hv=1, dk=32, dv=64, chunk=32), 2e-2),
+    ("f32-c16", "tiny_fp32", dict(lengths=[64, 7], hk=2, hv=2), 2e-6),
+    ("f32-c32", "tiny_fp32", dict(lengths=[75], hk=1, hv=3, dk=128, dv=32, chunk=32), 2e-6),
+]
+
+
+@pytest.mark.parametrize("label,name,kw,tol", CASES, ids=[c[0] for c in CASES])
+def test_wy_intermediates(label, name, kw, tol):
+    w = W.make_workload(name, **kw)
+    d = W.to_device(w)
+    C = w.chunk
+    cu = d["cu_seqlens"] if w.n_seqs > 1 else None
+    opts = G.options(chunk=C, stages=G.STAGE_TABLE | G.STAGE_WY)
+    lay = G.gdn_get_workspace_layout(d["q"], d["k"], d["v"], cu, opts)
+    ws = torch.zeros(lay.total_bytes, dtype=torch.uint8, device="cuda")
+    U.say(f"  {label}: stages table+wy, max_chunks={lay.max_chunks}")
+    G.gdn_prefill_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, d["init_state"],
+                     d["out"], d["final_state"], opts=opts, workspace=ws)
+    torch.cuda.synchronize()
+    keep = []
+    chunked.chunked_reference(w.q, w.k, w.v, w.g, w.beta, w.lengths, w.init_state,
+                              chunk=C, keep=keep)
+    hv, dk, dv = w.v.shape[1], w.q.shape[2], w.v.shape[2]
+    mc = lay.max_chunks
+    dt = w.q.dtype
+    Wb = _blocks(ws, lay.w, mc * hv, (C, dk), dt)
+    Qp = _blocks(ws, lay.qp, mc * hv, (C, dk), dt)
+    Kt = _blocks(ws, lay.kt, mc * hv, (dk, C), dt)
+    Ut = _blocks(ws, lay.ut, mc * hv, (dv, C), dt)
+    Ol = _blocks(ws, lay.oloc, mc * hv, (C, dv), dt)
+    dec = _blocks(ws, lay.decay, mc * hv, (1,), torch.float32)[:, 0]
+    if w.n_seqs > 1:
+        table = _blocks(ws, lay.chunk_table, mc, (4,), torch.int32).astype(np.int64)
+    nchunks = [-(-L // C) for L in w.lengths]
+    first = np.concatenate([[0], np.cumsum(nchunks)])
+    starts = np.concatenate([[0], np.cumsum(w.lengths)])
+
+    def close(a, b, what):
+        scale_ = max(float(np.abs(b).max()), 1e-30)
+        err = float(np.abs(a - b).max()) / scale_
+        assert err <= tol, f"{label} {what}: relative error {err:.3e} > {tol}"
+        return err
+
+    worst = {}
+    for it in keep:
+        c = int(first[it["seq"]] + it["chunk"])
+        n = it["n"]
+        blk = c * hv + it["head"]
+        if w.n_seqs > 1:
+            assert table[c, 0] == it["seq"] and table[c, 1] == it["t0"] and table[c, 2] == n
+            assert it["t0"] == starts[it["seq"]] + it["chunk"] * C
+        for what, got, ref in (("W", Wb[blk, :n], it["W"]), ("Qprime", Qp[blk, :n], it["Qprime"]),
+                               ("Ktilde^T", Kt[blk][:, :n], it["Ktilde"].T),
+                               ("Utilde^T", Ut[blk][:, :n], it["Utilde"].T),
+                               ("Oloc", Ol[blk, :n], it["Oloc"])):
+            worst[what] = max(worst.get(what, 0.0), close(got, ref, what))
+        # rows past the chunk's end are zero
+        assert not Wb[blk, n:].any() and not Qp[blk, n:].any() and not Kt[blk][:, n:].any()
+        assert not Ut[blk][:, n:].any() and not Ol[blk, n:].any()
+        assert abs(dec[blk] - np.exp(it["gamma"][-1])) <= 1e-5 * max(1.0, np.exp(it["gamma"][-1]))
+    U.say(f"  {label}: worst relative errors {worst}")
