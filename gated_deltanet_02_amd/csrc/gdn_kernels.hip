@@ -27,9 +27,11 @@
 //                 Fully parallel over chunks.
 //   scan_kernel   one workgroup per (sequence, value head, 16-column slice of
 //                 d_v): the only sequential part.  The state slice lives in
-//                 MFMA accumulators; each step stages the next chunk's W, Q'
-//                 and K~^T from global memory into LDS while the current one
-//                 is consumed.  The output is produced in the same step.
+//                 MFMA accumulators.  W, Q' and K~^T are stored by the WY
+//                 kernel in MFMA fragment order, so each wave loads its
+//                 operands straight into registers, three chunks ahead; LDS
+//                 only carries the two exchanges per step (H and U).  The
+//                 output is produced in the same step.
 //
 // bf16 inputs use bf16 MFMA operands with fp32 accumulation; the triangular
 // solve and every gate exponential are fp32.  fp32 inputs use fp32 MFMA
@@ -237,6 +239,9 @@ __global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
   constexpr int GR = Gran<TI>::n;
   constexpr int NB = C / 16;    // 16-row tiles along the chunk
   constexpr int NKT = DK / 16;  // 16-row tiles along d_k
+  constexpr int GPR = DK / GR;  // 16-byte granules per q / k row
+  constexpr int NQK = (C * GPR + kThreads - 1) / kThreads;
+  constexpr int NVG = (C * (128 / GR) + kThreads - 1) / kThreads;  // v granules per thread (d_v <= 128)
   __shared__ __attribute__((aligned(16))) char smem[L::total];
   TI* sKt = (TI*)(smem + L::r_kt);
   TI* sQ = (TI*)(smem + L::r_q);
@@ -266,19 +271,51 @@ __global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
   const TI* kg = (const TI*)p.k;
   const TI* vg = (const TI*)p.v;
   const int DV = p.dv;
+  const int GPRV = DV / GR;
+  const int NVT = DV / 16;
+  const int grp = p.hv / p.hk;
 
-  // Q and K rows of the chunk (zero past the chunk's end).
-  constexpr int GPR = DK / GR;
-  for (int idx = tid; idx < C * GPR; idx += kThreads) {
+  // All global inputs of the chunk are requested up front: q and k rows,
+  // the v rows and gates of the first value head (zeros past the chunk end).
+  uint4 kreg[NQK], qreg[NQK], vreg[NVG];
+  float gv = 0.f, bv = 0.f;
+#pragma unroll
+  for (int i = 0; i < NQK; ++i) {
+    const int idx = tid + i * kThreads;
     const int r = idx / GPR, gc = idx % GPR;
-    uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-    if (r < n) {
+    kreg[i] = qreg[i] = make_uint4(0, 0, 0, 0);
+    if (idx < C * GPR && r < n) {
       const int64_t t = t0 + r;
-      kv = ld16(kg + t * p.k_st + kh * p.k_sh + gc * GR);
-      qv = ld16(qg + t * p.q_st + kh * p.q_sh + gc * GR);
+      kreg[i] = ld16(kg + t * p.k_st + kh * p.k_sh + gc * GR);
+      qreg[i] = ld16(qg + t * p.q_st + kh * p.q_sh + gc * GR);
     }
-    st16(sKV + r * LK + gc * GR, kv);
-    st16(sQ + r * LK + gc * GR, qv);
+  }
+  auto load_head = [&](int h) {
+#pragma unroll
+    for (int i = 0; i < NVG; ++i) {
+      const int idx = tid + i * kThreads;
+      const int r = idx / GPRV, gc = idx % GPRV;
+      vreg[i] = make_uint4(0, 0, 0, 0);
+      if (idx < C * GPRV && r < n) vreg[i] = ld16(vg + (int64_t)(t0 + r) * p.v_st + h * p.v_sh + gc * GR);
+    }
+    if (wave == 0 && lane < n) {
+      gv = p.g[(int64_t)(t0 + lane) * p.g_st + h * p.g_sh];
+      bv = p.beta[(int64_t)(t0 + lane) * p.b_st + h * p.b_sh];
+    } else {
+      gv = 0.f;
+      bv = 0.f;
+    }
+  };
+  load_head(kh * grp);
+
+#pragma unroll
+  for (int i = 0; i < NQK; ++i) {
+    const int idx = tid + i * kThreads;
+    if (idx < C * GPR) {
+      const int r = idx / GPR, gc = idx % GPR;
+      st16(sKV + r * LK + gc * GR, kreg[i]);
+      st16(sQ + r * LK + gc * GR, qreg[i]);
+    }
   }
   __syncthreads();
   transpose_lds<TI>(sKV, LK, sKt, LC, C, DK, tid);
@@ -286,46 +323,43 @@ __global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
   row_inv_norms<TI, DK>(sQ, LK, C, p.eps, sRq, tid);
   __syncthreads();
 
-  // K^K^T and Q^K^T, lower-triangular tiles only (diagonal included).
-  constexpr int NTRI = NB * (NB + 1) / 2;
-  for (int t = wave; t < 2 * NTRI; t += 4) {
-    const bool is_s = t >= NTRI;
-    const int tt = is_s ? t - NTRI : t;
-    int i = 0;
-    while ((i + 1) * (i + 2) / 2 <= tt) ++i;
-    const int j = tt - i * (i + 1) / 2;
-    f32x4 acc = zero4();
-    mma16<DK>(acc, (is_s ? sQ : sKV) + 16 * i * LK, LK, sKV + 16 * j * LK, LK, lane);
-    float* dst = is_s ? sS : sG;
-    const float* ra = is_s ? sRq : sRk;
-    const int col = 16 * j + (lane & 15);
+  // K^K^T and Q^K^T: wave w computes row tile w against every column tile
+  // and keeps the lower triangle (diagonal included).
+  if (wave < NB) {
+    f32x4 ag[1][NB], as[1][NB];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 16 * i + (lane >> 4) * 4 + e;
-      dst[row * LF + col] = acc[e] * ra[row] * sRk[col];
+    for (int j = 0; j < NB; ++j) ag[0][j] = as[0][j] = zero4();
+    mma_block<1, NB, DK>(ag, sKV + 16 * wave * LK, LK, sKV, LK, lane);
+    mma_block<1, NB, DK>(as, sQ + 16 * wave * LK, LK, sKV, LK, lane);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      settle(ag[0][j]);
+      settle(as[0][j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (j > wave) continue;
+      const int col = 16 * j + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * wave + (lane >> 4) * 4 + e;
+        sG[row * LF + col] = ag[0][j][e] * sRk[row] * sRk[col];
+        sS[row * LF + col] = as[0][j][e] * sRq[row] * sRk[col];
+      }
     }
   }
-  __syncthreads();
 
-  const int grp = p.hv / p.hk;
   for (int gi = 0; gi < grp; ++gi) {
     const int h = kh * grp + gi;
     const int64_t blk = (int64_t)c * p.hv + h;
 
-    // V rows (row-major, into the U~ region for now) and the gates.
-    const int GPRV = DV / GR;
-    for (int idx = tid; idx < C * GPRV; idx += kThreads) {
-      const int r = idx / GPRV, gc = idx % GPRV;
-      uint4 vv = make_uint4(0, 0, 0, 0);
-      if (r < n) vv = ld16(vg + (int64_t)(t0 + r) * p.v_st + h * p.v_sh + gc * GR);
-      st16(sUT + r * LV + gc * GR, vv);
+    // v rows into the U~ region (row-major for now) and the gate scan.
+#pragma unroll
+    for (int i = 0; i < NVG; ++i) {
+      const int idx = tid + i * kThreads;
+      if (idx < C * GPRV) st16(sUT + (idx / GPRV) * LV + (idx % GPRV) * GR, vreg[i]);
     }
     if (wave == 0) {
-      float gv = 0.f, bv = 0.f;
-      if (lane < n) {
-        gv = p.g[(int64_t)(t0 + lane) * p.g_st + h * p.g_sh];
-        bv = p.beta[(int64_t)(t0 + lane) * p.b_st + h * p.b_sh];
-      }
       float x = gv;  // inclusive scan over the chunk
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -336,10 +370,11 @@ __global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
       if (lane < C) {
         sGam[lane] = x;
         sBeta[lane] = bv;
-        sEg[lane] = expf(x);
-        sKs[lane] = sRk[lane] * expf(glast - x);
+        sEg[lane] = fast_exp(x);
+        sKs[lane] = sRk[lane] * fast_exp(glast - x);
       }
     }
+    if (gi + 1 < grp) load_head(h + 1);  // next value head's inputs, in flight meanwhile
     __syncthreads();
     transpose_lds<TI>(sUT, LV, sKV, LC, C, DV, tid);  // V^T [dv][s]
 
@@ -347,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
     for (int idx = tid; idx < C * C; idx += kThreads) {
       const int r = idx / C, s = idx % C;
       float a = 0.f;
-      if (s < r) a = sBeta[r] * expf(sGam[r] - sGam[s]) * sG[r * LF + s];
+      if (s < r) a = sBeta[r] * fast_exp(sGam[r] - sGam[s]) * sG[r * LF + s];
       sA[r * LF + s] = a;
     }
     __syncthreads();
@@ -382,6 +417,7 @@ __global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
         f32x4 acc = zero4();
         for (int bk = bj; bk < bi; ++bk)
           mma16_f32_kn(acc, sA + (16 * bi) * LF + 16 * bk, LF, sT + (16 * bk) * LF + 16 * bj, LF, lane);
+        settle(acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) scr[((lane >> 4) * 4 + e) * 20 + (lane & 15)] = acc[e];
       }
@@ -403,67 +439,147 @@ __global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
       const float tv = (s <= r) ? sT[r * LF + s] : 0.f;
       sTb[r * LC + s] = from_float<TI>(tv * sBeta[s] * sEg[s] * sRk[s]);
       sTv[r * LC + s] = from_float<TI>(tv * sBeta[s]);
-      const float pv = (s <= r) ? p.scale * sS[r * LF + s] * expf(sGam[r] - sGam[s]) : 0.f;
+      const float pv = (s <= r) ? p.scale * sS[r * LF + s] * fast_exp(sGam[r] - sGam[s]) : 0.f;
       sP[r * LC + s] = from_float<TI>(pv);
     }
     __syncthreads();
 
-    // U~ = Tv V, stored as U~^T [dv][r] (global and LDS).
+    // U~ = Tv V: all chunk row tiles x this wave's d_v tiles.  Stored as
+    // accumulator tiles (global) and as U~^T [dv][r] (LDS).
     TI* ut_g = (TI*)p.im.ut + blk * DV * C;
-    const int NVT = DV / 16;
-    for (int t = wave; t < NB * NVT; t += 4) {
-      const int i = t % NB, j = t / NB;
-      f32x4 acc = zero4();
-      mma16<C>(acc, sTv + 16 * i * LC, LC, sKV + 16 * j * LC, LC, lane);
-      const int dv = 16 * j + (lane & 15), r0 = 16 * i + (lane >> 4) * 4;
-      store4<TI>(ut_g + dv * C + r0, acc[0], acc[1], acc[2], acc[3]);
-      store4<TI>(sUT + dv * LC + r0, acc[0], acc[1], acc[2], acc[3]);
+    {
+      const int per = NVT >= 8 ? 2 : 1;
+      const int j0 = wave * per;
+      if (j0 < NVT) {
+        f32x4 acc[NB][2];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) acc[i][0] = acc[i][1] = zero4();
+        if (per == 2) {
+          mma_block<NB, 2, C>(acc, sTv, LC, sKV + 16 * j0 * LC, LC, lane);
+#pragma unroll
+          for (int i = 0; i < NB; ++i) {
+            settle(acc[i][0]);
+            settle(acc[i][1]);
+          }
+        } else {
+          f32x4 tmp[NB][1];
+#pragma unroll
+          for (int i = 0; i < NB; ++i) tmp[i][0] = zero4();
+          mma_block<NB, 1, C>(tmp, sTv, LC, sKV + 16 * j0 * LC, LC, lane);
+#pragma unroll
+          for (int i = 0; i < NB; ++i) {
+            settle(tmp[i][0]);
+            acc[i][0] = tmp[i][0];
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          if (jj >= per) break;
+          const int j = j0 + jj;
+#pragma unroll
+          for (int i = 0; i < NB; ++i) {
+            const int dv = 16 * j + (lane & 15), r0 = 16 * i + (lane >> 4) * 4;
+            store_acc_tile<TI>(ut_g + (i * NVT + j) * 256, acc[i][jj], lane);
+            store4<TI>(sUT + dv * LC + r0, acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]);
+          }
+        }
+      }
     }
     __syncthreads();
 
-    // W^T tiles (rows d_k, columns r): W[r][dk] = sum_s Tb[r][s] K[s][dk].
+    // W^T tiles (rows d_k, columns r): W[r][dk] = sum_s Tb[r][s] K[s][dk],
+    // this wave's d_k tiles x all chunk row tiles.  Stored as W in fragment
+    // order (global) and as W^T [dk][r] (LDS, over the dead V^T).
+    constexpr int KPW = NKT >= 8 ? 2 : 1;   // d_k tiles per wave
     TI* w_g = (TI*)p.im.w + blk * C * DK;
-    for (int t = wave; t < NKT * NB; t += 4) {
-      const int i = t % NKT, j = t / NKT;
-      f32x4 acc = zero4();
-      mma16<C>(acc, sKt + 16 * i * LC, LC, sTb + 16 * j * LC, LC, lane);
-      const int r = 16 * j + (lane & 15), dk0 = 16 * i + (lane >> 4) * 4;
-      store4<TI>(w_g + r * DK + dk0, acc[0], acc[1], acc[2], acc[3]);
+    if (wave * KPW < NKT) {
+      const int i0 = wave * KPW;
+      f32x4 acc[KPW][NB];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sKV[(dk0 + e) * LC + r] = from_float<TI>(acc[e]);
+      for (int i = 0; i < KPW; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = zero4();
+      mma_block<KPW, NB, C>(acc, sKt + 16 * i0 * LC, LC, sTb, LC, lane);
+#pragma unroll
+      for (int i = 0; i < KPW; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int r = 16 * j + (lane & 15), dk0 = 16 * (i0 + i) + (lane >> 4) * 4;
+          store4<TI>(w_g + j * 16 * DK + frag_pos<DK>(lane & 15, dk0), acc[i][j][0], acc[i][j][1],
+                     acc[i][j][2], acc[i][j][3]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sKV[(dk0 + e) * LC + r] = from_float<TI>(acc[i][j][e]);
+        }
     }
     __syncthreads();
 
-    // Q' = scale diag(e^gamma rq) Q - P W (as Q'^T tiles) and O_loc = P U~.
+    // Q' = scale diag(e^gamma rq) Q - P W (as Q'^T tiles, fragment order).
     TI* qp_g = (TI*)p.im.qp + blk * C * DK;
-    for (int t = wave; t < NKT * NB; t += 4) {
-      const int i = t % NKT, j = t / NKT;
-      f32x4 acc = zero4();
-      mma16<C>(acc, sKV + 16 * i * LC, LC, sP + 16 * j * LC, LC, lane);
-      const int r = 16 * j + (lane & 15), dk0 = 16 * i + (lane >> 4) * 4;
-      const float qs = p.scale * sEg[r] * sRq[r];
-      const f32x4 qv = load4<TI>(sQ + r * LK + dk0);
-      store4<TI>(qp_g + r * DK + dk0, qs * qv[0] - acc[0], qs * qv[1] - acc[1],
-                 qs * qv[2] - acc[2], qs * qv[3] - acc[3]);
-    }
-    TI* ol_g = (TI*)p.im.oloc + blk * C * DV;
-    for (int t = wave; t < NVT * NB; t += 4) {
-      const int i = t % NVT, j = t / NVT;
-      f32x4 acc = zero4();
-      mma16<C>(acc, sUT + 16 * i * LC, LC, sP + 16 * j * LC, LC, lane);
-      const int r = 16 * j + (lane & 15), dv0 = 16 * i + (lane >> 4) * 4;
-      store4<TI>(ol_g + r * DV + dv0, acc[0], acc[1], acc[2], acc[3]);
-    }
-    // K~^T [dk][r] = K^T[dk][r] rk_r e^(gamma_last - gamma_r).
-    TI* kt_g = (TI*)p.im.kt + blk * DK * C;
-    constexpr int GPC = C / GR;
-    for (int idx = tid; idx < DK * GPC; idx += kThreads) {
-      const int dk = idx / GPC, gc = idx % GPC;
-      uint4 kv = ld16(sKt + dk * LC + gc * GR);
-      TI* e = (TI*)&kv;
+    if (wave * KPW < NKT) {
+      const int i0 = wave * KPW;
+      f32x4 acc[KPW][NB];
 #pragma unroll
-      for (int j = 0; j < GR; ++j) e[j] = from_float<TI>(to_float(e[j]) * sKs[gc * GR + j]);
-      st16(kt_g + dk * C + gc * GR, kv);
+      for (int i = 0; i < KPW; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = zero4();
+      mma_block<KPW, NB, C>(acc, sKV + 16 * i0 * LC, LC, sP, LC, lane);
+#pragma unroll
+      for (int i = 0; i < KPW; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int r = 16 * j + (lane & 15), dk0 = 16 * (i0 + i) + (lane >> 4) * 4;
+          const float qs = p.scale * sEg[r] * sRq[r];
+          const f32x4 qv = load4<TI>(sQ + r * LK + dk0);
+          store4<TI>(qp_g + j * 16 * DK + frag_pos<DK>(lane & 15, dk0), qs * qv[0] - acc[i][j][0],
+                     qs * qv[1] - acc[i][j][1], qs * qv[2] - acc[i][j][2], qs * qv[3] - acc[i][j][3]);
+        }
+    }
+    // O_loc = P U~ (as O_loc^T tiles: rows d_v, columns r).
+    TI* ol_g = (TI*)p.im.oloc + blk * C * DV;
+    {
+      const int per = NVT >= 8 ? 2 : 1;
+      const int i0 = wave * per;
+      if (i0 < NVT) {
+        f32x4 acc[2][NB];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = zero4();
+        if (per == 2) {
+          mma_block<2, NB, C>(acc, sUT + 16 * i0 * LC, LC, sP, LC, lane);
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            settle(acc[0][j]);
+            settle(acc[1][j]);
+          }
+        } else {
+          f32x4 tmp[1][NB];
+#pragma unroll
+          for (int j = 0; j < NB; ++j) tmp[0][j] = zero4();
+          mma_block<1, NB, C>(tmp, sUT + 16 * i0 * LC, LC, sP, LC, lane);
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            settle(tmp[0][j]);
+            acc[0][j] = tmp[0][j];
+          }
+        }
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          if (ii >= per) break;
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            store_acc_tile<TI>(ol_g + ((i0 + ii) * NB + j) * 256, acc[ii][j], lane);
+        }
+      }
+    }
+    // K~^T [dk][r] = K^T[dk][r] rk_r e^(gamma_last - gamma_r), in fragment
+    // order per 16-row tile of d_k (contraction over r).
+    TI* kt_g = (TI*)p.im.kt + blk * DK * C;
+    for (int idx = tid; idx < DK * (C / 4); idx += kThreads) {
+      const int dk = idx / (C / 4), r0 = (idx % (C / 4)) * 4;
+      const f32x4 kv = load4<TI>(sKt + dk * LC + r0);
+      store4<TI>(kt_g + (dk / 16) * 16 * C + frag_pos<C>(dk % 16, r0), kv[0] * sKs[r0],
+                 kv[1] * sKs[r0 + 1], kv[2] * sKs[r0 + 2], kv[3] * sKs[r0 + 3]);
     }
     if (tid == 0) p.im.decay[blk] = sEg[C - 1];
     __syncthreads();
@@ -479,25 +595,54 @@ struct ScanLayout {
   static constexpr int PADE = 16 / S;
   static constexpr int LK = DK + PADE;
   static constexpr int LC = C + PADE;
-  static constexpr int sz_w = C * LK * S;   // W or Q' [C][LK]
-  static constexpr int sz_kt = DK * LC * S; // K~^T [DK][LC]
-  static constexpr int sz_buf = 2 * sz_w + sz_kt;
-  static constexpr int r_ht = 2 * sz_buf;   // H^T slice [16][LK]
-  static constexpr int r_ut = r_ht + 16 * LK * S;  // U^T slice [16][LC]
+  static constexpr int r_ht = 0;                   // H^T slice [16][LK]
+  static constexpr int r_ut = 16 * LK * S;         // U^T slice [16][LC]
   static constexpr int total = r_ut + 16 * LC * S;
 };
+
+// Everything one wave needs from global memory for one chunk step.  The
+// values are kept exactly as loaded (no conversion) so that issuing the loads
+// never waits for them; they are consumed a few steps later.
+template <typename TI, int C, int DK>
+struct ScanStage {
+  static constexpr int NHW = (DK / 16 + 3) / 4;
+  Frag<TI, DK> w, q;                 // this wave's 16 rows of W and Q'
+  Frag<TI, C> kt[NHW];               // this wave's 16-row tiles of K~^T
+  typename Raw4<TI>::type ut, ol;    // U~ (U layout) and O_loc (O^T layout)
+  float dec;                         // e^gamma_last
+};
+
+// Every wave issues the same loads whatever its share of the work (tile
+// indices are clamped; a clamped tile is loaded but not used), so the
+// number of loads in flight is fixed and the compiler can wait for exactly
+// the stage it needs.
+template <typename TI, int C, int DK>
+__device__ __forceinline__ void scan_load(ScanStage<TI, C, DK>& st, const ScanParams& p,
+                                          int cc, int h, int sl, int wave, int lane) {
+  constexpr int NB = C / 16, NKT = DK / 16;
+  const int64_t blk = (int64_t)cc * p.hv + h;
+  const int NVT = p.dv / 16;
+  const int wt = NB >= 4 ? wave : min(wave, NB - 1);
+  st.w.load((const TI*)p.im.w + blk * C * DK + wt * 16 * DK, lane);
+  st.q.load((const TI*)p.im.qp + blk * C * DK + wt * 16 * DK, lane);
+  st.ut = load_raw4<TI>((const TI*)p.im.ut + blk * C * p.dv + (wt * NVT + sl) * 256 + lane * 4);
+  st.ol = load_raw4<TI>((const TI*)p.im.oloc + blk * C * p.dv + (sl * NB + wt) * 256 + lane * 4);
+#pragma unroll
+  for (int j = 0; j < ScanStage<TI, C, DK>::NHW; ++j) {
+    const int ti = min(wave + 4 * j, NKT - 1);
+    st.kt[j].load((const TI*)p.im.kt + blk * DK * C + ti * 16 * C, lane);
+  }
+  st.dec = p.im.decay[blk];
+}
 
 template <typename TI, int C, int DK>
 __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
   using L = ScanLayout<TI, C, DK>;
+  using Stage = ScanStage<TI, C, DK>;
   constexpr int LK = L::LK, LC = L::LC;
-  constexpr int GR = Gran<TI>::n;
   constexpr int NB = C / 16;
   constexpr int NKT = DK / 16;
-  constexpr int NHW = (NKT + 3) / 4;      // state tiles per wave
-  constexpr int NGW = C * DK / GR;        // granules in one W / Q' / K~^T block
-  constexpr int NG = 3 * NGW;
-  constexpr int NPT = (NG + kThreads - 1) / kThreads;
+  constexpr int NHW = Stage::NHW;
   __shared__ __attribute__((aligned(16))) char smem[L::total];
   TI* sHt = (TI*)(smem + L::r_ht);
   TI* sUt = (TI*)(smem + L::r_ut);
@@ -528,119 +673,64 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
       for (int e = 0; e < 4; ++e) hacc[j][e] = p.init[sbase + (int64_t)(dk0 + e) * DV + dv];
     }
   }
-
-  const TI* wg = (const TI*)p.im.w;
-  const TI* qpg = (const TI*)p.im.qp;
-  const TI* ktg = (const TI*)p.im.kt;
-  const TI* utg = (const TI*)p.im.ut;
-  const TI* olg = (const TI*)p.im.oloc;
   TI* outg = (TI*)p.out;
 
-  // Register staging of the next chunk's W, Q' and K~^T (granule g of the
-  // three consecutive blocks goes to thread g % 256, slot g / 256).
-  uint4 stg[NPT];
-#define GDN_SCAN_ISSUE(CC)                                                      \
-  {                                                                             \
-    const int64_t blk_ = (int64_t)(CC) * p.hv + h;                              \
-    _Pragma("unroll") for (int k = 0; k < NPT; ++k) {                           \
-      const int g = tid + k * kThreads;                                         \
-      if (g < NG) {                                                             \
-        const int a = g / NGW, gg = g - a * NGW;                                \
-        const TI* src = (a == 0 ? wg : (a == 1 ? qpg : ktg)) + blk_ * C * DK + gg * GR; \
-        stg[k] = ld16(src);                                                     \
-      }                                                                         \
-    }                                                                           \
-  }
-#define GDN_SCAN_COMMIT(BUF)                                                    \
-  {                                                                             \
-    TI* base_ = (TI*)(smem + (BUF) * L::sz_buf);                                \
-    _Pragma("unroll") for (int k = 0; k < NPT; ++k) {                           \
-      const int g = tid + k * kThreads;                                         \
-      if (g < NG) {                                                             \
-        const int a = g / NGW, gg = g - a * NGW;                                \
-        TI* dst = (a < 2)                                                       \
-            ? base_ + a * (L::sz_w / L::S) + (gg / (DK / GR)) * LK + (gg % (DK / GR)) * GR \
-            : base_ + 2 * (L::sz_w / L::S) + (gg / (C / GR)) * LC + (gg % (C / GR)) * GR;  \
-        st16(dst, stg[k]);                                                      \
-      }                                                                         \
-    }                                                                           \
-  }
-  // Per-lane U~ (U layout) and O_loc (O^T layout) pieces of this slice.
-#define GDN_SCAN_SMALL(CC, UT, OL, DEC)                                         \
-  {                                                                             \
-    const int64_t blk_ = (int64_t)(CC) * p.hv + h;                              \
-    DEC = p.im.decay[blk_];                                                     \
-    if (wave < NB) {                                                            \
-      UT = load4<TI>(utg + blk_ * DV * C + (int64_t)(dv0 + (lane & 15)) * C + 16 * wave + (lane >> 4) * 4); \
-      OL = load4<TI>(olg + blk_ * C * DV + (int64_t)(16 * wave + (lane & 15)) * DV + dv0 + (lane >> 4) * 4); \
-    }                                                                           \
-  }
-  f32x4 ut_c = zero4(), ol_c = zero4(), ut_n = zero4(), ol_n = zero4();
-  float dec_c = 1.f, dec_n = 1.f;
-
-  if (c_begin < c_end) {
-    GDN_SCAN_ISSUE(c_begin);
-    GDN_SCAN_SMALL(c_begin, ut_c, ol_c, dec_c);
-    GDN_SCAN_COMMIT(0);
-  }
-  for (int cc = c_begin; cc < c_end; ++cc) {
-    const int buf = (cc - c_begin) & 1;
-    const bool has_next = cc + 1 < c_end;
-    if (has_next) {
-      GDN_SCAN_ISSUE(cc + 1);
-      GDN_SCAN_SMALL(cc + 1, ut_n, ol_n, dec_n);
-    }
-    const TI* sW = (const TI*)(smem + buf * L::sz_buf);
-    const TI* sQp = sW + L::sz_w / L::S;
-    const TI* sKt = sW + 2 * (L::sz_w / L::S);
-    // H (as operand precision) -> sHt[dv][dk]
+  // One chunk step: H -> LDS; U = U~ - W H and O = Q' H + O_loc; U -> LDS;
+  // H <- e^gamma_last H + K~^T U.
+  auto step = [&](const Stage& st, int cc) {
 #pragma unroll
     for (int j = 0; j < NHW; ++j) {
       const int ti = wave + 4 * j;
-      if (ti < NKT) {
-        const int dk0 = 16 * ti + (lane >> 4) * 4;
-        store4<TI>(sHt + (lane & 15) * LK + dk0, hacc[j][0], hacc[j][1], hacc[j][2], hacc[j][3]);
-      }
+      if (ti < NKT)
+        store4<TI>(sHt + (lane & 15) * LK + 16 * ti + (lane >> 4) * 4, hacc[j][0], hacc[j][1],
+                   hacc[j][2], hacc[j][3]);
     }
     __syncthreads();
-    const int tok = tok0 + (cc - c_begin) * C;
-    const int n = min(C, tok_end - tok);
-    if (wave < NB) {
-      // U = U~ - W H   (rows r of this wave's tile, columns = the slice)
-      f32x4 au = zero4();
-      mma16<DK>(au, sW + 16 * wave * LK, LK, sHt, LK, lane);
-      store4<TI>(sUt + (lane & 15) * LC + 16 * wave + (lane >> 4) * 4,
-                 ut_c[0] - au[0], ut_c[1] - au[1], ut_c[2] - au[2], ut_c[3] - au[3]);
-      // O^T = H^T Q'^T + O_loc^T
-      f32x4 ao = zero4();
-      mma16<DK>(ao, sHt, LK, sQp + 16 * wave * LK, LK, lane);
+    if (NB >= 4 || wave < NB) {
+      f32x4 au = zero4(), ao = zero4();
+      mma_pair_lds<DK>(au, ao, st.w, st.q, sHt, LK, lane);
+      settle(au);
+      settle(ao);
+      const f32x4 ut = raw4_to_f32<TI>(st.ut), ol = raw4_to_f32<TI>(st.ol);
+      store4<TI>(sUt + (lane & 15) * LC + 16 * wave + (lane >> 4) * 4, ut[0] - au[0],
+                 ut[1] - au[1], ut[2] - au[2], ut[3] - au[3]);
+      const int tok = tok0 + (cc - c_begin) * C;
       const int r = 16 * wave + (lane & 15);
-      if (r < n) {
+      if (r < tok_end - tok)
         store4<TI>(outg + (int64_t)(tok + r) * p.o_st + (int64_t)h * p.o_sh + dv0 + (lane >> 4) * 4,
-                   ao[0] + ol_c[0], ao[1] + ol_c[1], ao[2] + ol_c[2], ao[3] + ol_c[3]);
-      }
+                   ao[0] + ol[0], ao[1] + ol[1], ao[2] + ol[2], ao[3] + ol[3]);
     }
     __syncthreads();
-    // H <- e^gamma_last H + K~^T U
 #pragma unroll
     for (int j = 0; j < NHW; ++j) {
       const int ti = wave + 4 * j;
       if (ti < NKT) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hacc[j][e] *= dec_c;
-        mma16<C>(hacc[j], sKt + 16 * ti * LC, LC, sUt, LC, lane);
+        for (int e = 0; e < 4; ++e) hacc[j][e] *= st.dec;
+        mma_frag_lds<C>(hacc[j], st.kt[j], sUt, LC, lane);
+        settle(hacc[j]);
       }
     }
-    if (has_next) {
-      GDN_SCAN_COMMIT(buf ^ 1);
-      ut_c = ut_n;
-      ol_c = ol_n;
-      dec_c = dec_n;
+  };
+
+  // Three stages in flight: the loads for chunk c + 3 are issued as soon as
+  // chunk c's registers are consumed.  Loads past the last chunk re-read it
+  // (clamped) so that every iteration issues the same loads.
+  if (c_begin < c_end) {
+    const int last = c_end - 1;
+    Stage s0, s1, s2;
+    scan_load(s0, p, c_begin, h, sl, wave, lane);
+    scan_load(s1, p, min(c_begin + 1, last), h, sl, wave, lane);
+    scan_load(s2, p, min(c_begin + 2, last), h, sl, wave, lane);
+    for (int cc = c_begin; cc < c_end; cc += 3) {
+      step(s0, cc);
+      scan_load(s0, p, min(cc + 3, last), h, sl, wave, lane);
+      if (cc + 1 < c_end) step(s1, cc + 1);
+      scan_load(s1, p, min(cc + 4, last), h, sl, wave, lane);
+      if (cc + 2 < c_end) step(s2, cc + 2);
+      scan_load(s2, p, min(cc + 5, last), h, sl, wave, lane);
     }
   }
-#undef GDN_SCAN_ISSUE
-#undef GDN_SCAN_COMMIT
-#undef GDN_SCAN_SMALL
 
   if (p.final_state) {
 #pragma unroll

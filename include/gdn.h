@@ -148,15 +148,22 @@ int gdn_prefill_ex(const gdn_tensor* q, const gdn_tensor* k,
 
 /* Byte offsets of the intermediates inside the workspace (for inspection and
  * tests).  Per (chunk c, value head h) block, all in the input dtype:
- *   w       [C][dk]  W  = T diag(beta e^gamma) K^
- *   qp      [C][dk]  Q' = scale diag(e^gamma) Q^ - P W
- *   kt      [dk][C]  K~^T, K~_r = e^(gamma_last - gamma_r) k^_r
- *   ut      [dv][C]  U~^T, U~ = T diag(beta) V
- *   oloc    [C][dv]  O_loc = P U~
- * and f32 decay[c][h] = e^(gamma_last).  Chunk c's blocks start at
- * offset + (c * Hv + h) * block_elems * element_size.  Rows past the end of
- * a short chunk are zero.  chunk_table is int32 [max_chunks][4] =
- * (sequence, first token, length, 0) in packed mode. */
+ *   w     W  = T diag(beta e^gamma) K^             C x dk, fragment order
+ *   qp    Q' = scale diag(e^gamma) Q^ - P W        C x dk, fragment order
+ *   kt    K~^T, K~_r = e^(gamma_last - gamma_r) k^_r   dk x C, fragment order
+ *   ut    U~ = T diag(beta) V                      C x dv, accumulator tiles
+ *   oloc  O_loc = P U~                             C x dv, transposed tiles
+ * and f32 decay[c][h] = e^(gamma_last).  A block starts at
+ * offset + (c * Hv + h) * (its element count) * element_size.
+ * "Fragment order": 16-row tiles one after another; inside a tile, for each
+ * 32-wide group of the second index, lane l = m + 16 ((k % 32) / 8) holds the
+ * 8 consecutive elements k (a trailing 16-wide group: 4 per lane).
+ * "Accumulator tiles": 16 x 16 tiles (row-tile major) of 64 lanes x 4, lane
+ * l holding rows 4 (l / 16) .. +3 of column l % 16; "transposed tiles" hold
+ * the tiles of the transpose (column-tile major), lane l holding columns
+ * 4 (l / 16) .. +3 of row l % 16.  Rows past the end of a short chunk are
+ * zero.  chunk_table is int32 [max_chunks][4] = (sequence, first token,
+ * length, 0) in packed mode. */
 typedef struct gdn_workspace_layout {
   size_t total_bytes;
   int64_t max_chunks;

@@ -27,6 +27,44 @@ def _blocks(ws, off, count, shape, dtype):
     return ws[off:off + n * es].view(dtype).view(count, *shape).float().cpu().numpy()
 
 
+def frag_pos(K, m, k):
+    """Position of element (m, k) of a 16 x K tile stored in fragment order:
+    per 32-wide k-group, lane (m + 16 ((k % 32) // 8)) holds 8 consecutive k;
+    a trailing 16-wide group holds 4 per lane."""
+    K32 = (K // 32) * 32
+    full = (k // 32) * 512 + (m + 16 * ((k % 32) // 8)) * 8 + (k % 8)
+    tail = K32 * 16 + (m + 16 * ((k - K32) // 4)) * 4 + ((k - K32) % 4)
+    return np.where(k < K32, full, tail)
+
+
+def unfrag(blocks, rows, K):
+    """[count, rows*K] in fragment order (16-row tiles) -> [count, rows, K]."""
+    r = np.arange(rows)[:, None]
+    k = np.arange(K)[None, :]
+    idx = (r // 16) * 16 * K + frag_pos(K, r % 16, k)
+    return blocks.reshape(blocks.shape[0], -1)[:, idx]
+
+
+def unacc(blocks, rows, cols, transposed):
+    """Accumulator-layout tiles ([tile][lane][4]) -> dense [count, rows, cols].
+    Not transposed: tile (rt, ct) = rt * (cols/16) + ct, lane l holds rows
+    4 (l/16) + e, column l % 16.  Transposed (O^T tiles of a [rows][cols]
+    matrix): tile (ct, rt) = ct * (rows/16) + rt, lane l holds columns
+    4 (l/16) + e of row l % 16."""
+    r = np.arange(rows)[:, None]
+    c = np.arange(cols)[None, :]
+    if not transposed:
+        tile = (r // 16) * (cols // 16) + c // 16
+        lane = (c % 16) + 16 * ((r % 16) // 4)
+        e = (r % 16) % 4
+    else:
+        tile = (c // 16) * (rows // 16) + r // 16
+        lane = (r % 16) + 16 * ((c % 16) // 4)
+        e = (c % 16) % 4
+    idx = tile * 256 + lane * 4 + e
+    return blocks.reshape(blocks.shape[0], -1)[:, idx]
+
+
 CASES = [
     ("bf16-single", "prompt_4k", dict(lengths=[150], hk=2, hv=4, dk=64, dv=64), 2e-2),
     ("bf16-packed", "edge_mix", dict(lengths=[70, 1, 64, 30, 0, 129], hk=1, hv=2, dk=128, dv=128), 2e-2),
@@ -55,11 +93,11 @@ def test_wy_intermediates(label, name, kw, tol):
     hv, dk, dv = w.v.shape[1], w.q.shape[2], w.v.shape[2]
     mc = lay.max_chunks
     dt = w.q.dtype
-    Wb = _blocks(ws, lay.w, mc * hv, (C, dk), dt)
-    Qp = _blocks(ws, lay.qp, mc * hv, (C, dk), dt)
-    Kt = _blocks(ws, lay.kt, mc * hv, (dk, C), dt)
-    Ut = _blocks(ws, lay.ut, mc * hv, (dv, C), dt)
-    Ol = _blocks(ws, lay.oloc, mc * hv, (C, dv), dt)
+    Wb = unfrag(_blocks(ws, lay.w, mc * hv, (C, dk), dt), C, dk)
+    Qp = unfrag(_blocks(ws, lay.qp, mc * hv, (C, dk), dt), C, dk)
+    Kt = unfrag(_blocks(ws, lay.kt, mc * hv, (dk, C), dt), dk, C)
+    Ut = np.swapaxes(unacc(_blocks(ws, lay.ut, mc * hv, (C, dv), dt), C, dv, False), 1, 2)
+    Ol = unacc(_blocks(ws, lay.oloc, mc * hv, (C, dv), dt), C, dv, True)
     dec = _blocks(ws, lay.decay, mc * hv, (1,), torch.float32)[:, 0]
     if w.n_seqs > 1:
         table = _blocks(ws, lay.chunk_table, mc, (4,), torch.int32).astype(np.int64)
