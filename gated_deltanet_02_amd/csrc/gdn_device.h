@@ -425,3 +425,84 @@ __device__ __forceinline__ void mma_block(f32x4 (&acc)[MT][NT], const float* A, 
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 }  // namespace gdn
+
+namespace gdn {
+
+// Row-swizzled LDS matrices.  A matrix of rows of `ld` elements is stored
+// without padding; the 16-byte granule g of row r lives at granule
+// g ^ (r & SW).  SW = (granules per row - 1) makes the 16 rows read by one
+// MFMA fragment load land on distinct banks.  SW = 0 is a plain layout
+// (used with padded rows).
+template <typename T, int SW>
+__device__ __forceinline__ int swz(int row, int col) {
+  constexpr int GE = 16 / (int)sizeof(T);
+  if constexpr (SW == 0) return col;
+  return ((((col / GE) ^ (row & SW))) * GE) + (col % GE);
+}
+
+// mma_block on swizzled operands: acc[i][j] += A_i * Bt_j^T, A rows start
+// at row a0 of A, Bt rows at row b0 of Bt.
+template <int MT, int NT, int K, int SWA, int SWB>
+__device__ __forceinline__ void mma_block_sw(f32x4 (&acc)[MT][NT], const bf16* A, int lda, int a0,
+                                             const bf16* Bt, int ldb, int b0, int lane) {
+  const int r = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 + 32 <= K; k0 += 32) {
+    bf16x8 a[MT], b[NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int row = a0 + 16 * i + r;
+      a[i] = *(const bf16x8*)(A + row * lda + swz<bf16, SWA>(row, k0 + q * 8));
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int row = b0 + 16 * j + r;
+      b[j] = *(const bf16x8*)(Bt + row * ldb + swz<bf16, SWB>(row, k0 + q * 8));
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+  if constexpr (K % 32 == 16) {
+    constexpr int k0 = K - 16;
+    bf16x4 a[MT], b[NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int row = a0 + 16 * i + r;
+      a[i] = *(const bf16x4*)(A + row * lda + swz<bf16, SWA>(row, k0 + q * 4));
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int row = b0 + 16 * j + r;
+      b[j] = *(const bf16x4*)(Bt + row * ldb + swz<bf16, SWB>(row, k0 + q * 4));
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+template <int MT, int NT, int K, int SWA, int SWB>
+__device__ __forceinline__ void mma_block_sw(f32x4 (&acc)[MT][NT], const float* A, int lda, int a0,
+                                             const float* Bt, int ldb, int b0, int lane) {
+  static_assert(SWA == 0 && SWB == 0, "fp32 operands use padded rows");
+  mma_block<MT, NT, K>(acc, A + a0 * lda, lda, Bt + b0 * ldb, ldb, lane);
+}
+
+// acc += A_blk * B where B is a 16 x 16 fp32 tile held in accumulator
+// layout by this wave (lane (q, r) holds B[4q + e][r]); with the contraction
+// order of instruction e taken as k = 4q + e this is exactly the operand
+// layout of v_mfma_f32_16x16x4_f32, so no LDS round trip is needed.
+__device__ __forceinline__ void mma16_f32_acc_b(f32x4& acc, const float* A, int lda, const f32x4& b,
+                                                int lane) {
+  const int r = lane & 15, q = lane >> 4;
+  const float* a = A + r * lda + q * 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc, 0, 0, 0);
+}
+
+}  // namespace gdn

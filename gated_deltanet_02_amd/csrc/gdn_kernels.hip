@@ -158,13 +158,13 @@ __global__ __launch_bounds__(1024) void table_kernel(TableParams p) {
 
 // dst[d][r] = src[r][d] for r < R (even), d < D (multiple of a granule).
 // Pairs of rows are packed so each LDS write carries two elements.
-template <typename TI>
+template <typename TI, int NT = kThreads>
 __device__ __forceinline__ void transpose_lds(const TI* src, int lds, TI* dst,
                                               int ldd, int R, int D, int tid) {
   constexpr int GR = Gran<TI>::n;
   typedef TI pair_t __attribute__((ext_vector_type(2)));
   const int npair = R / 2, ngran = D / GR;
-  for (int idx = tid; idx < npair * ngran; idx += kThreads) {
+  for (int idx = tid; idx < npair * ngran; idx += NT) {
     const int m = idx % npair, gc = idx / npair;
     const uint4 va = ld16(src + (2 * m) * lds + gc * GR);
     const uint4 vb = ld16(src + (2 * m + 1) * lds + gc * GR);
@@ -180,20 +180,35 @@ __device__ __forceinline__ void transpose_lds(const TI* src, int lds, TI* dst,
   }
 }
 
-// out[r] = 1 / sqrt(sum_d src[r][d]^2 + eps); four lanes per row.
-template <typename TI, int D>
+// out[r] = 1 / sqrt(sum_d src[r][d]^2 + eps); four lanes per row, each
+// reading its quarter of the row in 16-byte pieces.
+template <typename TI, int D, int NT = kThreads>
 __device__ __forceinline__ void row_inv_norms(const TI* src, int lds, int R,
                                               float eps, float* out, int tid) {
-  for (int base = 0; base < R * 4; base += kThreads) {
+  constexpr int GR = Gran<TI>::n;
+  for (int base = 0; base < R * 4; base += NT) {
     const int idx = base + tid;
     const int r = idx >> 2, part = idx & 3;
     float s = 0.f;
     if (r < R) {
       const TI* row = src + r * lds + part * (D / 4);
+      if constexpr ((D / 4) % GR == 0) {
 #pragma unroll
-      for (int d = 0; d < D / 4; ++d) {
-        const float x = to_float(row[d]);
-        s += x * x;
+        for (int g = 0; g < D / 4 / GR; ++g) {
+          const uint4 v = ld16(row + g * GR);
+          const TI* e = (const TI*)&v;
+#pragma unroll
+          for (int j = 0; j < GR; ++j) {
+            const float x = to_float(e[j]);
+            s += x * x;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int d = 0; d < D / 4; ++d) {
+          const float x = to_float(row[d]);
+          s += x * x;
+        }
       }
     }
     s += __shfl_xor(s, 1);
@@ -205,62 +220,96 @@ __device__ __forceinline__ void row_inv_norms(const TI* src, int lds, int R,
 // ---------------------------------------------------------------------------
 // WY kernel
 
+constexpr int kWyThreads = 512;  // 8 waves, one workgroup per CU
+
+// LDS plan of the WY kernel (bytes).  bf16 tiles are stored unpadded with
+// row-swizzled 16-byte granules; fp32 tiles (and fp32 inputs) use rows padded
+// by 16 bytes.  Regions are reused as their contents die:
+//   kt  K^T [dk][C]                                          whole kernel
+//   kv  K rows [C][dk] -> V^T [dv][C] -> W^T [dk][C]
+//   t   V rows [C][128] -> T (f32) -> U~^T [dv][C]
+//   x   Q rows [C][dk] -> A (f32) -> Tb, Tv, P [C][C]
 template <typename TI, int C, int DK>
 struct WyLayout {
   static constexpr int S = sizeof(TI);
-  static constexpr int PADE = 16 / S;
+  static constexpr bool SWIZ = S == 2;
+  static constexpr int PK = SWIZ ? 0 : 16 / S;
   static constexpr int DVM = 128;  // largest d_v
-  static constexpr int LK = DK + PADE;
-  static constexpr int LV = DVM + PADE;
-  static constexpr int LC = C + PADE;
+  static constexpr int LK = DK + PK;
+  static constexpr int LV = DVM + PK;
+  static constexpr int LC = C + PK;
   static constexpr int LF = C + 4;
+  static constexpr int SWK = SWIZ ? DK / 8 - 1 : 0;
+  static constexpr int SWC = SWIZ ? C / 8 - 1 : 0;
+  static constexpr int SWV = SWIZ ? DVM / 8 - 1 : 0;
   static constexpr int cmax(int a, int b) { return a > b ? a : b; }
-  static constexpr int sz_f = C * LF * 4;
-  static constexpr int r_kt = 0;                      // K^T [DK][LC]
-  static constexpr int r_q = r_kt + DK * LC * S;      // Q [C][LK]
-  static constexpr int r_g = r_q + C * LK * S;        // K^K^T (f32)
-  static constexpr int r_s = r_g + sz_f;              // Q^K^T (f32)
-  static constexpr int r_t = r_s + sz_f;              // T (f32)
-  static constexpr int r_kv = r_t + sz_f;             // K | V^T | W^T
+  static constexpr int r_kt = 0;
+  static constexpr int r_kv = r_kt + DK * LC * S;
   static constexpr int sz_kv = cmax(cmax(C * LK, DVM * LC), DK * LC) * S;
-  static constexpr int r_x = r_kv + sz_kv;            // A (f32) | Tb, Tv, P
-  static constexpr int sz_x = cmax(sz_f, 3 * C * LC * S);
-  static constexpr int r_ut = r_x + sz_x;             // V | U~^T
-  static constexpr int sz_ut = cmax(C * LV, DVM * LC) * S;
-  static constexpr int r_scr = r_ut + sz_ut;          // per-wave 16x20 f32
-  static constexpr int r_vec = r_scr + 4 * 16 * 20 * 4;
-  static constexpr int total = r_vec + 6 * C * 4;
+  static constexpr int r_t = r_kv + sz_kv;
+  static constexpr int sz_t = cmax(cmax(C * LF * 4, DVM * LC * S), C * LV * S);
+  static constexpr int r_x = r_t + sz_t;
+  static constexpr int sz_x = cmax(cmax(C * LK * S, C * LF * 4), 3 * C * LC * S);
+  static constexpr int r_vec = r_x + sz_x;
+  static constexpr int total = r_vec + 7 * C * 4;
 };
 
+// dst[d][r] = src[r][d] for r < R (even), d < D (whole granules), with the
+// source and destination row swizzles.  Pairs of rows are packed so each LDS
+// write carries two elements.
+template <typename TI, int NT, int SWS, int SWD>
+__device__ __forceinline__ void transpose_sw(const TI* src, int lds, TI* dst, int ldd, int R, int D,
+                                             int tid) {
+  constexpr int GR = Gran<TI>::n;
+  typedef TI pair_t __attribute__((ext_vector_type(2)));
+  const int npair = R / 2, ngran = D / GR;
+  for (int idx = tid; idx < npair * ngran; idx += NT) {
+    const int m = idx % npair, gc = idx / npair;
+    const uint4 va = ld16(src + (2 * m) * lds + swz<TI, SWS>(2 * m, gc * GR));
+    const uint4 vb = ld16(src + (2 * m + 1) * lds + swz<TI, SWS>(2 * m + 1, gc * GR));
+    const TI* ea = (const TI*)&va;
+    const TI* eb = (const TI*)&vb;
+#pragma unroll
+    for (int j = 0; j < GR; ++j) {
+      pair_t pr;
+      pr[0] = ea[j];
+      pr[1] = eb[j];
+      const int row = gc * GR + j;
+      *(pair_t*)(dst + row * ldd + swz<TI, SWD>(row, 2 * m)) = pr;
+    }
+  }
+}
+
 template <typename TI, int C, int DK>
-__global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
+__global__ __launch_bounds__(kWyThreads) void wy_kernel(WyParams p) {
   using L = WyLayout<TI, C, DK>;
+  constexpr int NT = kWyThreads;
   constexpr int LK = L::LK, LV = L::LV, LC = L::LC, LF = L::LF;
+  constexpr int SWK = L::SWK, SWC = L::SWC, SWV = L::SWV;
   constexpr int GR = Gran<TI>::n;
   constexpr int NB = C / 16;    // 16-row tiles along the chunk
   constexpr int NKT = DK / 16;  // 16-row tiles along d_k
   constexpr int GPR = DK / GR;  // 16-byte granules per q / k row
-  constexpr int NQK = (C * GPR + kThreads - 1) / kThreads;
-  constexpr int NVG = (C * (128 / GR) + kThreads - 1) / kThreads;  // v granules per thread (d_v <= 128)
+  constexpr int NQK = (C * GPR + NT - 1) / NT;
+  constexpr int NVG = (C * (128 / GR) + NT - 1) / NT;  // v granules per thread (d_v <= 128)
   __shared__ __attribute__((aligned(16))) char smem[L::total];
   TI* sKt = (TI*)(smem + L::r_kt);
-  TI* sQ = (TI*)(smem + L::r_q);
-  float* sG = (float*)(smem + L::r_g);
-  float* sS = (float*)(smem + L::r_s);
+  TI* sKV = (TI*)(smem + L::r_kv);   // K rows | V^T | W^T
+  TI* sVr = (TI*)(smem + L::r_t);    // V rows
   float* sT = (float*)(smem + L::r_t);
-  TI* sKV = (TI*)(smem + L::r_kv);
+  TI* sUt = (TI*)(smem + L::r_t);    // U~^T
+  TI* sQ = (TI*)(smem + L::r_x);     // Q rows
   float* sA = (float*)(smem + L::r_x);
   TI* sTb = (TI*)(smem + L::r_x);
   TI* sTv = sTb + C * LC;
   TI* sP = sTv + C * LC;
-  TI* sUT = (TI*)(smem + L::r_ut);
-  float* sScr = (float*)(smem + L::r_scr);
   float* sRq = (float*)(smem + L::r_vec);
   float* sRk = sRq + C;
   float* sGam = sRk + C;
   float* sBeta = sGam + C;
   float* sEg = sBeta + C;   // e^gamma_r
   float* sKs = sEg + C;     // rk_r e^(gamma_last - gamma_r)
+  float* sCb = sKs + C;     // beta_s e^gamma_s rk_s  (column scale of Tb)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x, kh = blockIdx.y;
@@ -281,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
   float gv = 0.f, bv = 0.f;
 #pragma unroll
   for (int i = 0; i < NQK; ++i) {
-    const int idx = tid + i * kThreads;
+    const int idx = tid + i * NT;
     const int r = idx / GPR, gc = idx % GPR;
     kreg[i] = qreg[i] = make_uint4(0, 0, 0, 0);
     if (idx < C * GPR && r < n) {
@@ -293,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
   auto load_head = [&](int h) {
 #pragma unroll
     for (int i = 0; i < NVG; ++i) {
-      const int idx = tid + i * kThreads;
+      const int idx = tid + i * NT;
       const int r = idx / GPRV, gc = idx % GPRV;
       vreg[i] = make_uint4(0, 0, 0, 0);
       if (idx < C * GPRV && r < n) vreg[i] = ld16(vg + (int64_t)(t0 + r) * p.v_st + h * p.v_sh + gc * GR);
@@ -310,54 +359,47 @@ __global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
 
 #pragma unroll
   for (int i = 0; i < NQK; ++i) {
-    const int idx = tid + i * kThreads;
+    const int idx = tid + i * NT;
     if (idx < C * GPR) {
       const int r = idx / GPR, gc = idx % GPR;
-      st16(sKV + r * LK + gc * GR, kreg[i]);
-      st16(sQ + r * LK + gc * GR, qreg[i]);
+      st16(sKV + r * LK + swz<TI, SWK>(r, gc * GR), kreg[i]);
+      st16(sQ + r * LK + swz<TI, SWK>(r, gc * GR), qreg[i]);
     }
   }
   __syncthreads();
-  transpose_lds<TI>(sKV, LK, sKt, LC, C, DK, tid);
-  row_inv_norms<TI, DK>(sKV, LK, C, p.eps, sRk, tid);
-  row_inv_norms<TI, DK>(sQ, LK, C, p.eps, sRq, tid);
-  __syncthreads();
+  transpose_sw<TI, NT, SWK, SWC>(sKV, LK, sKt, LC, C, DK, tid);
+  row_inv_norms<TI, DK, NT>(sKV, LK, C, p.eps, sRk, tid);  // sums are order-free: the
+  row_inv_norms<TI, DK, NT>(sQ, LK, C, p.eps, sRq, tid);   // swizzle only permutes a row
 
-  // K^K^T and Q^K^T: wave w computes row tile w against every column tile
-  // and keeps the lower triangle (diagonal included).
-  if (wave < NB) {
-    f32x4 ag[1][NB], as[1][NB];
+  // Raw K K^T (waves 0..NB-1) and Q K^T (waves 4..4+NB-1), one row tile
+  // against every column tile.  The tiles stay in registers for all value
+  // heads of the group; norms and gates are applied when A and P are built.
+  const bool g_wave = wave < NB;
+  const bool s_wave = wave >= 4 && wave - 4 < NB;
+  const int rt = g_wave ? wave : wave - 4;
+  f32x4 acc_gs[1][NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) ag[0][j] = as[0][j] = zero4();
-    mma_block<1, NB, DK>(ag, sKV + 16 * wave * LK, LK, sKV, LK, lane);
-    mma_block<1, NB, DK>(as, sQ + 16 * wave * LK, LK, sKV, LK, lane);
+  for (int j = 0; j < NB; ++j) acc_gs[0][j] = zero4();
+  if (g_wave || s_wave) {
+    mma_block_sw<1, NB, DK, SWK, SWK>(acc_gs, g_wave ? sKV : sQ, LK, 16 * rt, sKV, LK, 0, lane);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      settle(ag[0][j]);
-      settle(as[0][j]);
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if (j > wave) continue;
-      const int col = 16 * j + (lane & 15);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * wave + (lane >> 4) * 4 + e;
-        sG[row * LF + col] = ag[0][j][e] * sRk[row] * sRk[col];
-        sS[row * LF + col] = as[0][j][e] * sRq[row] * sRk[col];
-      }
-    }
+    for (int j = 0; j < NB; ++j) settle(acc_gs[0][j]);
   }
+  __syncthreads();
 
   for (int gi = 0; gi < grp; ++gi) {
     const int h = kh * grp + gi;
     const int64_t blk = (int64_t)c * p.hv + h;
 
-    // v rows into the U~ region (row-major for now) and the gate scan.
+    // v rows into the T region and the gate scan; then the next value
+    // head's inputs are requested.
 #pragma unroll
     for (int i = 0; i < NVG; ++i) {
-      const int idx = tid + i * kThreads;
-      if (idx < C * GPRV) st16(sUT + (idx / GPRV) * LV + (idx % GPRV) * GR, vreg[i]);
+      const int idx = tid + i * NT;
+      if (idx < C * GPRV) {
+        const int r = idx / GPRV, gc = idx % GPRV;
+        st16(sVr + r * LV + swz<TI, SWV>(r, gc * GR), vreg[i]);
+      }
     }
     if (wave == 0) {
       float x = gv;  // inclusive scan over the chunk
@@ -368,28 +410,41 @@ __global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
       }
       const float glast = __shfl(x, C - 1);
       if (lane < C) {
+        const float eg = fast_exp(x);
         sGam[lane] = x;
         sBeta[lane] = bv;
-        sEg[lane] = fast_exp(x);
+        sEg[lane] = eg;
         sKs[lane] = sRk[lane] * fast_exp(glast - x);
+        sCb[lane] = bv * eg * sRk[lane];
       }
     }
-    if (gi + 1 < grp) load_head(h + 1);  // next value head's inputs, in flight meanwhile
+    if (gi + 1 < grp) load_head(h + 1);
     __syncthreads();
-    transpose_lds<TI>(sUT, LV, sKV, LC, C, DV, tid);  // V^T [dv][s]
 
-    // A_rs = beta_r exp(gamma_r - gamma_s) (k^_r . k^_s), s < r.
-    for (int idx = tid; idx < C * C; idx += kThreads) {
-      const int r = idx / C, s = idx % C;
-      float a = 0.f;
-      if (s < r) a = sBeta[r] * fast_exp(sGam[r] - sGam[s]) * sG[r * LF + s];
-      sA[r * LF + s] = a;
+    // V^T [dv][s] from the v rows, and A from the K K^T tiles:
+    // A_rs = beta_r exp(gamma_r - gamma_s) rk_r rk_s (k_r . k_s), s < r
+    // (only the strictly lower part is ever read).
+    transpose_sw<TI, NT, SWV, SWC>(sVr, LV, sKV, LC, C, DV, tid);
+    if (g_wave) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (j > rt) continue;
+        const int col = 16 * j + (lane & 15);
+        const float gc = sGam[col], rkc = sRk[col];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * rt + (lane >> 4) * 4 + e;
+          if (col < row)
+            sA[row * LF + col] = sBeta[row] * sRk[row] * rkc * fast_exp(sGam[row] - gc) * acc_gs[0][j][e];
+        }
+      }
     }
     __syncthreads();
 
     // T = (I + A)^-1.  Diagonal 16x16 blocks by forward substitution, one
     // lane per column; then block rows i = 1.. by
-    //   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj   (fp32 MFMA).
+    //   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj   (fp32 MFMA; the inner sum
+    // stays in registers as the second operand).
     if (wave == 0) {
       const int b = lane >> 4, col = lane & 15;
       if (b < NB) {
@@ -401,8 +456,10 @@ __global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
         for (int r = 1; r < 16; ++r) {
           float acc = x[r];
 #pragma unroll
-          for (int s = 0; s < r; ++s) acc -= Ab[r * LF + s] * x[s];
+          for (int s2 = 0; s2 < r; ++s2) acc -= Ab[r * LF + s2] * x[s2];
           x[r] = acc;
+          // one row's operands at a time: keeps the register footprint small
+          __builtin_amdgcn_sched_barrier(0);
         }
         float* Tb = sT + (16 * b) * LF + 16 * b;
 #pragma unroll
@@ -411,95 +468,101 @@ __global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
     }
     __syncthreads();
     for (int bi = 1; bi < NB; ++bi) {
-      float* scr = sScr + wave * 16 * 20;
       if (wave < bi) {
         const int bj = wave;
-        f32x4 acc = zero4();
+        f32x4 m = zero4();
         for (int bk = bj; bk < bi; ++bk)
-          mma16_f32_kn(acc, sA + (16 * bi) * LF + 16 * bk, LF, sT + (16 * bk) * LF + 16 * bj, LF, lane);
-        settle(acc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) scr[((lane >> 4) * 4 + e) * 20 + (lane & 15)] = acc[e];
-      }
-      __syncthreads();
-      if (wave < bi) {
-        const int bj = wave;
-        f32x4 acc = zero4();
-        mma16_f32_kn(acc, sT + (16 * bi) * LF + 16 * bi, LF, scr, 20, lane);
+          mma16_f32_kn(m, sA + (16 * bi) * LF + 16 * bk, LF, sT + (16 * bk) * LF + 16 * bj, LF, lane);
+        settle(m);
+        f32x4 t = zero4();
+        mma16_f32_acc_b(t, sT + (16 * bi) * LF + 16 * bi, LF, m, lane);
+        settle(t);
         float* dst = sT + (16 * bi) * LF + 16 * bj;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[((lane >> 4) * 4 + e) * LF + (lane & 15)] = -acc[e];
+        for (int e = 0; e < 4; ++e) dst[((lane >> 4) * 4 + e) * LF + (lane & 15)] = -t[e];
       }
       __syncthreads();
     }
 
-    // Tb = T diag(beta e^gamma rk), Tv = T diag(beta), P = scale D o (Q^K^T).
-    for (int idx = tid; idx < C * C; idx += kThreads) {
-      const int r = idx / C, s = idx % C;
-      const float tv = (s <= r) ? sT[r * LF + s] : 0.f;
-      sTb[r * LC + s] = from_float<TI>(tv * sBeta[s] * sEg[s] * sRk[s]);
-      sTv[r * LC + s] = from_float<TI>(tv * sBeta[s]);
-      const float pv = (s <= r) ? p.scale * sS[r * LF + s] * fast_exp(sGam[r] - sGam[s]) : 0.f;
-      sP[r * LC + s] = from_float<TI>(pv);
+    // Tb = T diag(beta e^gamma rk), Tv = T diag(beta) (8 columns per item),
+    // and P = scale D o (Q^K^T) from the Q K^T tiles.
+    for (int idx = tid; idx < C * (C / 8); idx += NT) {
+      const int r = idx / (C / 8), s0 = (idx % (C / 8)) * 8;
+      typedef TI vec8 __attribute__((ext_vector_type(8)));
+      vec8 tb, tv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float t = (s0 + j <= r) ? sT[r * LF + s0 + j] : 0.f;
+        tb[j] = from_float<TI>(t * sCb[s0 + j]);
+        tv[j] = from_float<TI>(t * sBeta[s0 + j]);
+      }
+      if constexpr (sizeof(TI) == 2) {
+        *(vec8*)(sTb + r * LC + swz<TI, SWC>(r, s0)) = tb;
+        *(vec8*)(sTv + r * LC + swz<TI, SWC>(r, s0)) = tv;
+      } else {
+        *(f32x4*)(sTb + r * LC + s0) = __builtin_shufflevector(tb, tb, 0, 1, 2, 3);
+        *(f32x4*)(sTb + r * LC + s0 + 4) = __builtin_shufflevector(tb, tb, 4, 5, 6, 7);
+        *(f32x4*)(sTv + r * LC + s0) = __builtin_shufflevector(tv, tv, 0, 1, 2, 3);
+        *(f32x4*)(sTv + r * LC + s0 + 4) = __builtin_shufflevector(tv, tv, 4, 5, 6, 7);
+      }
     }
-    __syncthreads();
-
-    // U~ = Tv V: all chunk row tiles x this wave's d_v tiles.  Stored as
-    // accumulator tiles (global) and as U~^T [dv][r] (LDS).
-    TI* ut_g = (TI*)p.im.ut + blk * DV * C;
-    {
-      const int per = NVT >= 8 ? 2 : 1;
-      const int j0 = wave * per;
-      if (j0 < NVT) {
-        f32x4 acc[NB][2];
+    if (s_wave) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i) acc[i][0] = acc[i][1] = zero4();
-        if (per == 2) {
-          mma_block<NB, 2, C>(acc, sTv, LC, sKV + 16 * j0 * LC, LC, lane);
+      for (int j = 0; j < NB; ++j) {
+        const int col = 16 * j + (lane & 15);
+        const float gc = sGam[col], rkc = sRk[col];
 #pragma unroll
-          for (int i = 0; i < NB; ++i) {
-            settle(acc[i][0]);
-            settle(acc[i][1]);
-          }
-        } else {
-          f32x4 tmp[NB][1];
-#pragma unroll
-          for (int i = 0; i < NB; ++i) tmp[i][0] = zero4();
-          mma_block<NB, 1, C>(tmp, sTv, LC, sKV + 16 * j0 * LC, LC, lane);
-#pragma unroll
-          for (int i = 0; i < NB; ++i) {
-            settle(tmp[i][0]);
-            acc[i][0] = tmp[i][0];
-          }
-        }
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          if (jj >= per) break;
-          const int j = j0 + jj;
-#pragma unroll
-          for (int i = 0; i < NB; ++i) {
-            const int dv = 16 * j + (lane & 15), r0 = 16 * i + (lane >> 4) * 4;
-            store_acc_tile<TI>(ut_g + (i * NVT + j) * 256, acc[i][jj], lane);
-            store4<TI>(sUT + dv * LC + r0, acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * rt + (lane >> 4) * 4 + e;
+          const float pv = (col <= row)
+              ? p.scale * sRq[row] * rkc * fast_exp(sGam[row] - gc) * acc_gs[0][j][e] : 0.f;
+          sP[row * LC + swz<TI, SWC>(row, col)] = from_float<TI>(pv);
         }
       }
     }
     __syncthreads();
 
-    // W^T tiles (rows d_k, columns r): W[r][dk] = sum_s Tb[r][s] K[s][dk],
-    // this wave's d_k tiles x all chunk row tiles.  Stored as W in fragment
-    // order (global) and as W^T [dk][r] (LDS, over the dead V^T).
-    constexpr int KPW = NKT >= 8 ? 2 : 1;   // d_k tiles per wave
-    TI* w_g = (TI*)p.im.w + blk * C * DK;
-    if (wave * KPW < NKT) {
-      const int i0 = wave * KPW;
+    // U~ = Tv V (all chunk row tiles x d_v tile `wave`): accumulator tiles
+    // to global memory, U~^T [dv][r] into the T region.
+    TI* ut_g = (TI*)p.im.ut + blk * DV * C;
+    if (wave < NVT) {
+      const int j = wave;
+      f32x4 acc[NB][1];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) acc[i][0] = zero4();
+      mma_block_sw<NB, 1, C, SWC, SWC>(acc, sTv, LC, 0, sKV, LC, 16 * j, lane);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int dv = 16 * j + (lane & 15), r0 = 16 * i + (lane >> 4) * 4;
+        store_acc_tile<TI>(ut_g + (i * NVT + j) * 256, acc[i][0], lane);
+        store4<TI>(sUt + dv * LC + swz<TI, SWC>(dv, r0), acc[i][0][0], acc[i][0][1], acc[i][0][2],
+                   acc[i][0][3]);
+      }
+    }
+    __syncthreads();
+
+    // W^T tiles (rows d_k, columns r): W[r][dk] = sum_s Tb[r][s] K[s][dk].
+    // W in fragment order to global memory, W^T [dk][r] over the dead V^T.
+    // The q rows for Q' are requested here and used after the next barrier.
+    constexpr int KPW = 1;  // d_k tiles per wave
+    const int i0 = wave;
+    typename Raw4<TI>::type qraw[KPW][NB];
+    if (i0 < NKT) {
+#pragma unroll
+      for (int i = 0; i < KPW; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int r = 16 * j + (lane & 15), dk0 = 16 * (i0 + i) + (lane >> 4) * 4;
+          qraw[i][j] = typename Raw4<TI>::type{};
+          if (r < n) qraw[i][j] = load_raw4<TI>(qg + (int64_t)(t0 + r) * p.q_st + kh * p.q_sh + dk0);
+        }
+      TI* w_g = (TI*)p.im.w + blk * C * DK;
       f32x4 acc[KPW][NB];
 #pragma unroll
       for (int i = 0; i < KPW; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = zero4();
-      mma_block<KPW, NB, C>(acc, sKt + 16 * i0 * LC, LC, sTb, LC, lane);
+      mma_block_sw<KPW, NB, C, SWC, SWC>(acc, sKt, LC, 16 * i0, sTb, LC, 0, lane);
 #pragma unroll
       for (int i = 0; i < KPW; ++i)
 #pragma unroll
@@ -508,78 +571,52 @@ __global__ __launch_bounds__(kThreads) void wy_kernel(WyParams p) {
           store4<TI>(w_g + j * 16 * DK + frag_pos<DK>(lane & 15, dk0), acc[i][j][0], acc[i][j][1],
                      acc[i][j][2], acc[i][j][3]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sKV[(dk0 + e) * LC + r] = from_float<TI>(acc[i][j][e]);
+          for (int e = 0; e < 4; ++e)
+            sKV[(dk0 + e) * LC + swz<TI, SWC>(dk0 + e, r)] = from_float<TI>(acc[i][j][e]);
         }
     }
     __syncthreads();
 
-    // Q' = scale diag(e^gamma rq) Q - P W (as Q'^T tiles, fragment order).
-    TI* qp_g = (TI*)p.im.qp + blk * C * DK;
-    if (wave * KPW < NKT) {
-      const int i0 = wave * KPW;
+    // Q' = scale diag(e^gamma rq) Q - P W (Q'^T tiles, fragment order), and
+    // O_loc = P U~ (O_loc^T tiles).
+    if (i0 < NKT) {
+      TI* qp_g = (TI*)p.im.qp + blk * C * DK;
       f32x4 acc[KPW][NB];
 #pragma unroll
       for (int i = 0; i < KPW; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = zero4();
-      mma_block<KPW, NB, C>(acc, sKV + 16 * i0 * LC, LC, sP, LC, lane);
+      mma_block_sw<KPW, NB, C, SWC, SWC>(acc, sKV, LC, 16 * i0, sP, LC, 0, lane);
 #pragma unroll
       for (int i = 0; i < KPW; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           const int r = 16 * j + (lane & 15), dk0 = 16 * (i0 + i) + (lane >> 4) * 4;
           const float qs = p.scale * sEg[r] * sRq[r];
-          const f32x4 qv = load4<TI>(sQ + r * LK + dk0);
+          const f32x4 qv = raw4_to_f32<TI>(qraw[i][j]);
           store4<TI>(qp_g + j * 16 * DK + frag_pos<DK>(lane & 15, dk0), qs * qv[0] - acc[i][j][0],
                      qs * qv[1] - acc[i][j][1], qs * qv[2] - acc[i][j][2], qs * qv[3] - acc[i][j][3]);
         }
     }
-    // O_loc = P U~ (as O_loc^T tiles: rows d_v, columns r).
     TI* ol_g = (TI*)p.im.oloc + blk * C * DV;
-    {
-      const int per = NVT >= 8 ? 2 : 1;
-      const int i0 = wave * per;
-      if (i0 < NVT) {
-        f32x4 acc[2][NB];
+    if (wave < NVT) {
+      const int v0 = wave;
+      f32x4 acc[1][NB];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < NB; ++j) acc[0][j] = zero4();
+      mma_block_sw<1, NB, C, SWC, SWC>(acc, sUt, LC, 16 * v0, sP, LC, 0, lane);
 #pragma unroll
-          for (int j = 0; j < NB; ++j) acc[i][j] = zero4();
-        if (per == 2) {
-          mma_block<2, NB, C>(acc, sUT + 16 * i0 * LC, LC, sP, LC, lane);
-#pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            settle(acc[0][j]);
-            settle(acc[1][j]);
-          }
-        } else {
-          f32x4 tmp[1][NB];
-#pragma unroll
-          for (int j = 0; j < NB; ++j) tmp[0][j] = zero4();
-          mma_block<1, NB, C>(tmp, sUT + 16 * i0 * LC, LC, sP, LC, lane);
-#pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            settle(tmp[0][j]);
-            acc[0][j] = tmp[0][j];
-          }
-        }
-#pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-          if (ii >= per) break;
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-            store_acc_tile<TI>(ol_g + ((i0 + ii) * NB + j) * 256, acc[ii][j], lane);
-        }
-      }
+      for (int j = 0; j < NB; ++j) store_acc_tile<TI>(ol_g + (v0 * NB + j) * 256, acc[0][j], lane);
     }
     // K~^T [dk][r] = K^T[dk][r] rk_r e^(gamma_last - gamma_r), in fragment
-    // order per 16-row tile of d_k (contraction over r).
+    // order per 16-row tile of d_k (contraction over r), four at a time.
     TI* kt_g = (TI*)p.im.kt + blk * DK * C;
-    for (int idx = tid; idx < DK * (C / 4); idx += kThreads) {
+    for (int idx = tid; idx < DK * (C / 4); idx += NT) {
       const int dk = idx / (C / 4), r0 = (idx % (C / 4)) * 4;
-      const f32x4 kv = load4<TI>(sKt + dk * LC + r0);
-      store4<TI>(kt_g + (dk / 16) * 16 * C + frag_pos<C>(dk % 16, r0), kv[0] * sKs[r0],
-                 kv[1] * sKs[r0 + 1], kv[2] * sKs[r0 + 2], kv[3] * sKs[r0 + 3]);
+      const f32x4 kv = load4<TI>(sKt + dk * LC + swz<TI, SWC>(dk, r0));
+      const f32x4 ks = *(const f32x4*)(sKs + r0);
+      store4<TI>(kt_g + (dk / 16) * 16 * C + frag_pos<C>(dk % 16, r0), kv[0] * ks[0],
+                 kv[1] * ks[1], kv[2] * ks[2], kv[3] * ks[3]);
     }
     if (tid == 0) p.im.decay[blk] = sEg[C - 1];
     __syncthreads();
@@ -748,16 +785,19 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
 // ---------------------------------------------------------------------------
 // dispatch
 
+// fp32 inputs are built for chunks of 16 and 32 only (their WY tiles at 64
+// would exceed the LDS or the register budget).
 template <typename TI, int C, int DK>
 static constexpr bool fits() {
-  return WyLayout<TI, C, DK>::total <= kLdsLimit && ScanLayout<TI, C, DK>::total <= kLdsLimit;
+  return WyLayout<TI, C, DK>::total <= kLdsLimit && ScanLayout<TI, C, DK>::total <= kLdsLimit &&
+         (sizeof(TI) == 2 || C <= 32);
 }
 
 template <typename TI, int C, int DK>
 static int launch_pair(int stage, const WyParams* wy, const ScanParams* sc,
                        dim3 grid, hipStream_t s) {
   if constexpr (fits<TI, C, DK>()) {
-    if (stage == 0) hipLaunchKernelGGL((wy_kernel<TI, C, DK>), grid, dim3(kThreads), 0, s, *wy);
+    if (stage == 0) hipLaunchKernelGGL((wy_kernel<TI, C, DK>), grid, dim3(kWyThreads), 0, s, *wy);
     else hipLaunchKernelGGL((scan_kernel<TI, C, DK>), grid, dim3(kThreads), 0, s, *sc);
     return 0;
   } else {
