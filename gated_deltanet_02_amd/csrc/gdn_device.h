@@ -189,146 +189,89 @@ __device__ __forceinline__ f32x4 zero4() {
 namespace gdn {
 
 // ---------------------------------------------------------------------------
-// Fragment order.  A 16 x K operand tile (rows m, contraction index k) is
-// stored so that one wavefront reads its MFMA operand registers with
-// contiguous 16-byte (or 8-byte) loads: for every 32-wide k-group g, the 64
-// lanes' eight consecutive elements (lane l: row l % 16, k = 32 g + 8 (l/16)
-// + j) follow each other; a trailing 16-wide group stores four elements per
-// lane (k = K32 + 4 (l/16) + j).  The same order serves as the A or the B
-// operand, since both take row/column l % 16 and the same k range per lane.
-template <int K>
-__host__ __device__ constexpr int frag_pos(int m, int k) {
-  constexpr int K32 = (K / 32) * 32;
-  return k < K32 ? (k / 32) * 512 + (m + 16 * ((k % 32) / 8)) * 8 + (k % 8)
-                 : K32 * 16 + (m + 16 * ((k - K32) / 4)) * 4 + ((k - K32) % 4);
-}
-
-// Per-lane registers of one 16 x K fragment tile.
+// k-tile order.  The scan's stored MFMA operands follow the accumulator
+// layout along the contraction index: for a 16-row tile (rows m) and a
+// 16-wide k-tile t, lane m + 16 g holds the four elements k = 16 t + 4 g + e
+// (e = 0..3), which are the rows an accumulator tile gives that lane.  A
+// product whose other operand is an accumulator (the state H, the U rows)
+// then feeds its registers to the MFMA without moving data between lanes;
+// the contraction order is permuted identically on both operands.  bf16
+// pairs k-tiles (2u, 2u + 1) into one 16-byte unit per lane (the eight
+// contraction indices of one v_mfma_f32_16x16x32_bf16); a trailing single
+// bf16 k-tile is an 8-byte half unit (v_mfma_f32_16x16x16_bf16).  fp32 puts
+// one k-tile in a 16-byte unit (four v_mfma_f32_16x16x4_f32, one per e).
+// A full unit is 64 lanes x 16 bytes = 1 KiB.
 template <typename TI, int K>
-struct Frag {
-  static constexpr int NG = K / 32;                 // full 32-wide groups
-  static constexpr bool TAIL = (K % 32) == 16;
-  static constexpr int U4_PER_G = sizeof(TI) == 2 ? 1 : 2;   // uint4 per lane per group
-  static constexpr int NV = NG * U4_PER_G + (TAIL ? 1 : 0);  // uint4 slots (tail: bf16 uses .xy)
-  uint4 v[NV > 0 ? NV : 1];
-
-  __device__ __forceinline__ void load(const TI* tile, int lane) {
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const TI* p = tile + g * 512 + lane * 8;
-      v[g * U4_PER_G] = ld16(p);
-      if constexpr (U4_PER_G == 2) v[g * U4_PER_G + 1] = ld16(p + 4);
-    }
-    if constexpr (TAIL) {
-      const TI* p = tile + NG * 512 + lane * 4;
-      if constexpr (sizeof(TI) == 2) {
-        const uint2 t = *(const uint2*)p;
-        v[NV - 1] = make_uint4(t.x, t.y, 0, 0);
-      } else {
-        v[NV - 1] = ld16(p);
-      }
-    }
+struct KTile {
+  static_assert(K % 16 == 0, "contraction must be a multiple of 16");
+  static constexpr int TPU = sizeof(TI) == 2 ? 2 : 1;       // k-tiles per unit
+  static constexpr int NT = K / 16;                          // k-tiles
+  static constexpr int NU = (NT + TPU - 1) / TPU;            // units
+  static constexpr bool HALF_TAIL = TPU == 2 && (NT % 2) == 1;
+  static constexpr int UNIT = 64 * 4 * TPU;                  // elements per full unit
+  // Element offset of (m, k) inside one 16 x K tile (16 K elements).
+  __host__ __device__ static constexpr int pos(int m, int k) {
+    const int t = k / 16, g = (k % 16) / 4, e = k % 4, u = t / TPU, h = t % TPU;
+    return (HALF_TAIL && u == NU - 1) ? u * UNIT + (m + 16 * g) * 4 + e
+                                      : u * UNIT + (m + 16 * g) * 4 * TPU + 4 * h + e;
   }
 };
 
-// acc += A * B^T with A from fragment registers and B^T rows from LDS
-// (16 rows, leading dimension ldb, contraction contiguous).
-template <int K>
-__device__ __forceinline__ void mma_frag_lds(f32x4& acc, const Frag<bf16, K>& a,
-                                             const bf16* Bt, int ldb, int lane) {
-  const bf16* b = Bt + (lane & 15) * ldb + (lane >> 4) * 8;
-#pragma unroll
-  for (int g = 0; g < Frag<bf16, K>::NG; ++g) {
-    const bf16x8 bv = *(const bf16x8*)(b + g * 32);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v[g]), bv, acc, 0, 0, 0);
-  }
-  if constexpr (Frag<bf16, K>::TAIL) {
-    constexpr int NG = Frag<bf16, K>::NG;
-    const bf16x4 bv = *(const bf16x4*)(Bt + (lane & 15) * ldb + NG * 32 + (lane >> 4) * 4);
-    const uint2 t = make_uint2(a.v[Frag<bf16, K>::NV - 1].x, a.v[Frag<bf16, K>::NV - 1].y);
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, t), bv, acc, 0, 0, 0);
+// One unit's operand registers: a full bf16 unit (8 elements), a bf16 half
+// unit (4; the upper half unused) or an fp32 unit (4).
+template <typename TI>
+struct Unit;
+template <>
+struct Unit<bf16> {
+  typedef bf16x8 type;
+};
+template <>
+struct Unit<float> {
+  typedef f32x4 type;
+};
+
+// acc += A * B over one unit of the contraction (see KTile).
+template <bool HALF>
+__device__ __forceinline__ void mma_unit(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  if constexpr (HALF) {
+    const bf16x4 a4 = __builtin_shufflevector(a, a, 0, 1, 2, 3);
+    const bf16x4 b4 = __builtin_shufflevector(b, b, 0, 1, 2, 3);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a4, b4, acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
   }
 }
-
-template <int K>
-__device__ __forceinline__ void mma_frag_lds(f32x4& acc, const Frag<float, K>& a,
-                                             const float* Bt, int ldb, int lane) {
-  const float* b = Bt + (lane & 15) * ldb + (lane >> 4) * 8;
+template <bool HALF>
+__device__ __forceinline__ void mma_unit(f32x4& acc, const f32x4& a, const f32x4& b) {
 #pragma unroll
-  for (int g = 0; g < Frag<float, K>::NG; ++g) {
-    const f32x4 b0 = *(const f32x4*)(b + g * 32);
-    const f32x4 b1 = *(const f32x4*)(b + g * 32 + 4);
-    const f32x4 a0 = __builtin_bit_cast(f32x4, a.v[2 * g]);
-    const f32x4 a1 = __builtin_bit_cast(f32x4, a.v[2 * g + 1]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[j], b0[j], acc, 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[j], b1[j], acc, 0, 0, 0);
-  }
-  if constexpr (Frag<float, K>::TAIL) {
-    constexpr int NG = Frag<float, K>::NG;
-    const f32x4 b0 = *(const f32x4*)(Bt + (lane & 15) * ldb + NG * 32 + (lane >> 4) * 4);
-    const f32x4 a0 = __builtin_bit_cast(f32x4, a.v[Frag<float, K>::NV - 1]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[j], b0[j], acc, 0, 0, 0);
-  }
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
 }
 
-// Two products sharing one LDS operand H (16 rows of H^T, contraction d_k):
-//   accu += A * H^T-rows   (A from fragments: U = W H)
-//   acco += H^T-rows * B   (B from fragments: O^T = H^T Q'^T)
-template <int K>
-__device__ __forceinline__ void mma_pair_lds(f32x4& accu, f32x4& acco, const Frag<bf16, K>& a,
-                                             const Frag<bf16, K>& b, const bf16* Ht, int ldh,
-                                             int lane) {
-  const bf16* h = Ht + (lane & 15) * ldh + (lane >> 4) * 8;
+// Operand unit from accumulator tiles: k-tiles (2u, 2u + 1) for bf16 (a
+// half unit takes one), k-tile u for fp32.
+template <bool HALF>
+__device__ __forceinline__ bf16x8 acc_unit(const f32x4& t0, const f32x4& t1, bf16) {
+  bf16x8 v;
 #pragma unroll
-  for (int g = 0; g < Frag<bf16, K>::NG; ++g) {
-    const bf16x8 hv = *(const bf16x8*)(h + g * 32);
-    accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v[g]), hv, accu, 0, 0, 0);
-    acco = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, __builtin_bit_cast(bf16x8, b.v[g]), acco, 0, 0, 0);
+  for (int e = 0; e < 4; ++e) {
+    v[e] = (bf16)t0[e];
+    v[4 + e] = HALF ? (bf16)0.f : (bf16)t1[e];
   }
-  if constexpr (Frag<bf16, K>::TAIL) {
-    constexpr int NG = Frag<bf16, K>::NG, NV = Frag<bf16, K>::NV;
-    const bf16x4 hv = *(const bf16x4*)(Ht + (lane & 15) * ldh + NG * 32 + (lane >> 4) * 4);
-    const bf16x4 av = __builtin_bit_cast(bf16x4, make_uint2(a.v[NV - 1].x, a.v[NV - 1].y));
-    const bf16x4 bv = __builtin_bit_cast(bf16x4, make_uint2(b.v[NV - 1].x, b.v[NV - 1].y));
-    accu = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, hv, accu, 0, 0, 0);
-    acco = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hv, bv, acco, 0, 0, 0);
-  }
+  return v;
+}
+template <bool HALF>
+__device__ __forceinline__ f32x4 acc_unit(const f32x4& t0, const f32x4&, float) {
+  return t0;
 }
 
-template <int K>
-__device__ __forceinline__ void mma_pair_lds(f32x4& accu, f32x4& acco, const Frag<float, K>& a,
-                                             const Frag<float, K>& b, const float* Ht, int ldh,
-                                             int lane) {
-  const float* h = Ht + (lane & 15) * ldh + (lane >> 4) * 8;
-#pragma unroll
-  for (int g = 0; g < Frag<float, K>::NG; ++g) {
-    const f32x4 h0 = *(const f32x4*)(h + g * 32);
-    const f32x4 h1 = *(const f32x4*)(h + g * 32 + 4);
-    const f32x4 a0 = __builtin_bit_cast(f32x4, a.v[2 * g]), a1 = __builtin_bit_cast(f32x4, a.v[2 * g + 1]);
-    const f32x4 b0 = __builtin_bit_cast(f32x4, b.v[2 * g]), b1 = __builtin_bit_cast(f32x4, b.v[2 * g + 1]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      accu = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[j], h0[j], accu, 0, 0, 0);
-      acco = __builtin_amdgcn_mfma_f32_16x16x4f32(h0[j], b0[j], acco, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      accu = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[j], h1[j], accu, 0, 0, 0);
-      acco = __builtin_amdgcn_mfma_f32_16x16x4f32(h1[j], b1[j], acco, 0, 0, 0);
-    }
-  }
-  if constexpr (Frag<float, K>::TAIL) {
-    constexpr int NG = Frag<float, K>::NG, NV = Frag<float, K>::NV;
-    const f32x4 h0 = *(const f32x4*)(Ht + (lane & 15) * ldh + NG * 32 + (lane >> 4) * 4);
-    const f32x4 a0 = __builtin_bit_cast(f32x4, a.v[NV - 1]), b0 = __builtin_bit_cast(f32x4, b.v[NV - 1]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      accu = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[j], h0[j], accu, 0, 0, 0);
-      acco = __builtin_amdgcn_mfma_f32_16x16x4f32(h0[j], b0[j], acco, 0, 0, 0);
-    }
+// Reads one unit of a k-tile-order tile from LDS (byte address of the unit).
+template <typename TI, bool HALF>
+__device__ __forceinline__ typename Unit<TI>::type lds_unit(const char* unit, int lane) {
+  if constexpr (sizeof(TI) == 2 && HALF) {
+    const uint2 r = *(const uint2*)(unit + lane * 8);
+    return __builtin_bit_cast(bf16x8, make_uint4(r.x, r.y, 0u, 0u));
+  } else {
+    return __builtin_bit_cast(typename Unit<TI>::type, *(const uint4*)(unit + lane * 16));
   }
 }
 

@@ -26,12 +26,15 @@
 //                 blocked triangular inverse and every per-chunk matrix above.
 //                 Fully parallel over chunks.
 //   scan_kernel   one workgroup per (sequence, value head, 16-column slice of
-//                 d_v): the only sequential part.  The state slice lives in
-//                 MFMA accumulators.  W, Q' and K~^T are stored by the WY
-//                 kernel in MFMA fragment order, so each wave loads its
-//                 operands straight into registers, three chunks ahead; LDS
-//                 only carries the two exchanges per step (H and U).  The
-//                 output is produced in the same step.
+//                 d_v): the only sequential part.  One wave runs the
+//                 recurrence with the state slice in its MFMA accumulators;
+//                 W, Q' and K~^T are stored by the WY kernel in k-tile order
+//                 (the contraction index follows the accumulator layout), so
+//                 the state and the U rows feed the MFMAs from the
+//                 registers they were accumulated in, with no exchange
+//                 through LDS.  Three more waves stream the chunks' operands
+//                 into an LDS ring with LDS-direct loads, two or three chunks
+//                 ahead.  The output is produced in the same step.
 //
 // bf16 inputs use bf16 MFMA operands with fp32 accumulation; the triangular
 // solve and every gate exponential are fp32.  fp32 inputs use fp32 MFMA
@@ -534,7 +537,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(WyParams p) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int dv = 16 * j + (lane & 15), r0 = 16 * i + (lane >> 4) * 4;
-        store_acc_tile<TI>(ut_g + (i * NVT + j) * 256, acc[i][0], lane);
+        store_acc_tile<TI>(ut_g + (j * NB + i) * 256, acc[i][0], lane);
         store4<TI>(sUt + dv * LC + swz<TI, SWC>(dv, r0), acc[i][0][0], acc[i][0][1], acc[i][0][2],
                    acc[i][0][3]);
       }
@@ -542,7 +545,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(WyParams p) {
     __syncthreads();
 
     // W^T tiles (rows d_k, columns r): W[r][dk] = sum_s Tb[r][s] K[s][dk].
-    // W in fragment order to global memory, W^T [dk][r] over the dead V^T.
+    // W in k-tile order to global memory, W^T [dk][r] over the dead V^T.
     // The q rows for Q' are requested here and used after the next barrier.
     constexpr int KPW = 1;  // d_k tiles per wave
     const int i0 = wave;
@@ -568,7 +571,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(WyParams p) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           const int r = 16 * j + (lane & 15), dk0 = 16 * (i0 + i) + (lane >> 4) * 4;
-          store4<TI>(w_g + j * 16 * DK + frag_pos<DK>(lane & 15, dk0), acc[i][j][0], acc[i][j][1],
+          store4<TI>(w_g + j * 16 * DK + KTile<TI, DK>::pos(lane & 15, dk0), acc[i][j][0], acc[i][j][1],
                      acc[i][j][2], acc[i][j][3]);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -577,7 +580,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(WyParams p) {
     }
     __syncthreads();
 
-    // Q' = scale diag(e^gamma rq) Q - P W (Q'^T tiles, fragment order), and
+    // Q' = scale diag(e^gamma rq) Q - P W (Q'^T tiles, k-tile order), and
     // O_loc = P U~ (O_loc^T tiles).
     if (i0 < NKT) {
       TI* qp_g = (TI*)p.im.qp + blk * C * DK;
@@ -594,7 +597,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(WyParams p) {
           const int r = 16 * j + (lane & 15), dk0 = 16 * (i0 + i) + (lane >> 4) * 4;
           const float qs = p.scale * sEg[r] * sRq[r];
           const f32x4 qv = raw4_to_f32<TI>(qraw[i][j]);
-          store4<TI>(qp_g + j * 16 * DK + frag_pos<DK>(lane & 15, dk0), qs * qv[0] - acc[i][j][0],
+          store4<TI>(qp_g + j * 16 * DK + KTile<TI, DK>::pos(lane & 15, dk0), qs * qv[0] - acc[i][j][0],
                      qs * qv[1] - acc[i][j][1], qs * qv[2] - acc[i][j][2], qs * qv[3] - acc[i][j][3]);
         }
     }
@@ -608,14 +611,14 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(WyParams p) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) store_acc_tile<TI>(ol_g + (v0 * NB + j) * 256, acc[0][j], lane);
     }
-    // K~^T [dk][r] = K^T[dk][r] rk_r e^(gamma_last - gamma_r), in fragment
+    // K~^T [dk][r] = K^T[dk][r] rk_r e^(gamma_last - gamma_r), in k-tile
     // order per 16-row tile of d_k (contraction over r), four at a time.
     TI* kt_g = (TI*)p.im.kt + blk * DK * C;
     for (int idx = tid; idx < DK * (C / 4); idx += NT) {
       const int dk = idx / (C / 4), r0 = (idx % (C / 4)) * 4;
       const f32x4 kv = load4<TI>(sKt + dk * LC + swz<TI, SWC>(dk, r0));
       const f32x4 ks = *(const f32x4*)(sKs + r0);
-      store4<TI>(kt_g + (dk / 16) * 16 * C + frag_pos<C>(dk % 16, r0), kv[0] * ks[0],
+      store4<TI>(kt_g + (dk / 16) * 16 * C + KTile<TI, C>::pos(dk % 16, r0), kv[0] * ks[0],
                  kv[1] * ks[1], kv[2] * ks[2], kv[3] * ks[3]);
     }
     if (tid == 0) p.im.decay[blk] = sEg[C - 1];
@@ -625,66 +628,139 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(WyParams p) {
 
 // ---------------------------------------------------------------------------
 // state scan fused with the output
+//
+// One workgroup per (sequence, value head, 16-column slice of d_v), four
+// waves with fixed roles:
+//   wave 0  the recurrence: U = U~ - W H and H <- e^gamma_last H + K~^T U,
+//           with the state slice in its MFMA accumulators; after each chunk
+//           it leaves H (as bf16 / fp32 operand units) in LDS for wave 1;
+//   wave 1  the output of the same chunk, O = Q' H + O_loc, off the
+//           recurrence's critical path;
+//   waves 2, 3 copy each chunk's W, Q', K~^T, U~ slice and decay from
+//           global memory into a ring of LDS stages with LDS-direct loads
+//           (no registers), `lead` chunks ahead.
+// One barrier per chunk hands a stage (and the H copy) over.
+
+constexpr int kScanCopyWaves = 2;
 
 template <typename TI, int C, int DK>
-struct ScanLayout {
+struct ScanRing {
   static constexpr int S = sizeof(TI);
-  static constexpr int PADE = 16 / S;
-  static constexpr int LK = DK + PADE;
-  static constexpr int LC = C + PADE;
-  static constexpr int r_ht = 0;                   // H^T slice [16][LK]
-  static constexpr int r_ut = 16 * LK * S;         // U^T slice [16][LC]
-  static constexpr int total = r_ut + 16 * LC * S;
+  static constexpr int BIG = C * DK * S;            // W, Q', K~^T of one chunk
+  static constexpr int SMALL = C * 16 * S;          // U~ / O_loc tiles of one slice
+  static constexpr int w = 0, qp = BIG, kt = 2 * BIG, ut = 3 * BIG;
+  static constexpr int dec = ut + SMALL;            // e^gamma_last (4 bytes)
+  static constexpr int stage = dec + 16;
+  static constexpr int HB = KTile<TI, DK>::NU * 1024;  // H as operand units
+  static constexpr int room = (kLdsLimit - 2 * HB) / stage;
+  static constexpr int slots = room < 4 ? room : 4;
+  static constexpr int lead = slots - 1;
+  static constexpr int hbuf = slots * stage;        // two H buffers
+  static constexpr int total = hbuf + 2 * HB;
+  // 1 KiB copies per stage (the last of a region may be 512 bytes), plus
+  // one 4-byte copy of the decay
+  static constexpr int PB = (BIG + 1023) / 1024, PS = (SMALL + 1023) / 1024;
+  static constexpr int pieces = 3 * PB + PS + 1;
+  static constexpr int per_wave = (pieces + kScanCopyWaves - 1) / kScanCopyWaves;
+  static_assert(slots < 2 || per_wave * lead <= 63, "loads in flight exceed the wave's counter");
 };
 
-// Everything one wave needs from global memory for one chunk step.  The
-// values are kept exactly as loaded (no conversion) so that issuing the loads
-// never waits for them; they are consumed a few steps later.
-template <typename TI, int C, int DK>
-struct ScanStage {
-  static constexpr int NHW = (DK / 16 + 3) / 4;
-  Frag<TI, DK> w, q;                 // this wave's 16 rows of W and Q'
-  Frag<TI, C> kt[NHW];               // this wave's 16-row tiles of K~^T
-  typename Raw4<TI>::type ut, ol;    // U~ (U layout) and O_loc (O^T layout)
-  float dec;                         // e^gamma_last
-};
+// Workgroup barrier that the compiler may not move memory accesses across;
+// the waits it needs are issued explicitly before it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
-// Every wave issues the same loads whatever its share of the work (tile
-// indices are clamped; a clamped tile is loaded but not used), so the
-// number of loads in flight is fixed and the compiler can wait for exactly
-// the stage it needs.
-template <typename TI, int C, int DK>
-__device__ __forceinline__ void scan_load(ScanStage<TI, C, DK>& st, const ScanParams& p,
-                                          int cc, int h, int sl, int wave, int lane) {
-  constexpr int NB = C / 16, NKT = DK / 16;
+// s_waitcnt immediates (gfx9 encoding): vmcnt <= n only; lgkmcnt == 0 only.
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+__host__ __device__ constexpr int lgkmcnt0_imm() { return 15 | (3 << 14) | (7 << 4); }
+
+// Copies chunk cc's operands into one LDS stage: copying wave CW's share of
+// the stage's pieces (CW, CW + kScanCopyWaves, ...), each a coalesced 16
+// bytes per lane.  Indices beyond the stage repeat its last piece (same
+// bytes, same place), so that every copying wave issues exactly per_wave
+// loads per stage.  All piece indices are compile-time constants.
+template <typename TI, int C, int DK, int CW>
+__device__ __forceinline__ void ring_copy(char* stage, const ScanParams& p, int cc, int h,
+                                          int sl, int lane) {
+  using R = ScanRing<TI, C, DK>;
+  constexpr int NB = C / 16;
   const int64_t blk = (int64_t)cc * p.hv + h;
-  const int NVT = p.dv / 16;
-  const int wt = NB >= 4 ? wave : min(wave, NB - 1);
-  st.w.load((const TI*)p.im.w + blk * C * DK + wt * 16 * DK, lane);
-  st.q.load((const TI*)p.im.qp + blk * C * DK + wt * 16 * DK, lane);
-  st.ut = load_raw4<TI>((const TI*)p.im.ut + blk * C * p.dv + (wt * NVT + sl) * 256 + lane * 4);
-  st.ol = load_raw4<TI>((const TI*)p.im.oloc + blk * C * p.dv + (sl * NB + wt) * 256 + lane * 4);
+  const int64_t big = blk * R::BIG, small = (blk * C * p.dv + (int64_t)sl * NB * 256) * R::S;
+  const char* bases[4] = {(const char*)p.im.w + big, (const char*)p.im.qp + big,
+                          (const char*)p.im.kt + big, (const char*)p.im.ut + small};
 #pragma unroll
-  for (int j = 0; j < ScanStage<TI, C, DK>::NHW; ++j) {
-    const int ti = min(wave + 4 * j, NKT - 1);
-    st.kt[j].load((const TI*)p.im.kt + blk * DK * C + ti * 16 * C, lane);
+  for (int j = 0; j < R::per_wave; ++j) {
+    const int i = min(CW + kScanCopyWaves * j, R::pieces - 1);
+    if (i == R::pieces - 1) {
+      if (lane == 0)
+        __builtin_amdgcn_global_load_lds((const void*)(p.im.decay + blk),
+                                         (__attribute__((address_space(3))) void*)(stage + R::dec),
+                                         4, 0, 0);
+      continue;
+    }
+    const int r = i < 3 * R::PB ? i / R::PB : 3;
+    const int k = i - r * R::PB;
+    const int bytes = r < 3 ? R::BIG : R::SMALL;
+    const int lds_off = r * R::BIG + k * 1024;
+    const bool half = (bytes % 1024) != 0 && k == (bytes - 1) / 1024;
+    if (!half || lane < 32)
+      __builtin_amdgcn_global_load_lds((const void*)(bases[r] + k * 1024 + lane * 16),
+                                       (__attribute__((address_space(3))) void*)(stage + lds_off),
+                                       16, 0, 0);
   }
-  st.dec = p.im.decay[blk];
+}
+
+// Copying wave CW: fills the first `lead` stages, then one stage per chunk,
+// and meets the other waves at one barrier per chunk once the stage they
+// need next has landed.  Loads past the last chunk re-read it.
+template <typename TI, int C, int DK, int CW>
+__device__ __forceinline__ void ring_producer(char* smem, const ScanParams& p, int c_begin,
+                                              int c_end, int h, int sl, int lane) {
+  using R = ScanRing<TI, C, DK>;
+  const int last = c_end - 1;
+#pragma unroll
+  for (int k = 0; k < R::lead; ++k)
+    ring_copy<TI, C, DK, CW>(smem + k * R::stage, p, min(c_begin + k, last), h, sl, lane);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::per_wave * (R::lead - 1)));
+  ring_barrier();
+  int slot = R::lead;
+  for (int cc = c_begin; cc < c_end; ++cc) {
+    ring_copy<TI, C, DK, CW>(smem + slot * R::stage, p, min(cc + R::lead, last), h, sl, lane);
+    slot = slot + 1 == R::slots ? 0 : slot + 1;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::per_wave * (R::lead - 1)));
+    ring_barrier();
+  }
+}
+
+// H as operand units (B of U = W H, A of O^T = H^T Q'^T) from the state's
+// accumulator tiles.
+template <typename TI, int DK, typename UT>
+__device__ __forceinline__ void state_units(UT* hb, const f32x4* hacc) {
+  using KD = KTile<TI, DK>;
+#pragma unroll
+  for (int q = 0; q < KD::NU; ++q)
+    hb[q] = (KD::HALF_TAIL && q == KD::NU - 1)
+                ? acc_unit<true>(hacc[KD::TPU * q], hacc[KD::TPU * q], TI{})
+                : acc_unit<false>(hacc[KD::TPU * q], hacc[KD::TPU * q + KD::TPU - 1], TI{});
 }
 
 template <typename TI, int C, int DK>
 __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
-  using L = ScanLayout<TI, C, DK>;
-  using Stage = ScanStage<TI, C, DK>;
-  constexpr int LK = L::LK, LC = L::LC;
-  constexpr int NB = C / 16;
-  constexpr int NKT = DK / 16;
-  constexpr int NHW = Stage::NHW;
-  __shared__ __attribute__((aligned(16))) char smem[L::total];
-  TI* sHt = (TI*)(smem + L::r_ht);
-  TI* sUt = (TI*)(smem + L::r_ut);
+  using R = ScanRing<TI, C, DK>;
+  using KD = KTile<TI, DK>;
+  using KC = KTile<TI, C>;
+  using UT = typename Unit<TI>::type;
+  constexpr int NB = C / 16, NKT = DK / 16;
+  constexpr int S = R::S;
+  __shared__ __attribute__((aligned(1024))) char smem[R::total];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int NS = p.n_slices;
   // XCD-aware: the slices of one (sequence, head) share blockIdx % 8 and so
   // land on the same XCD, where they share W, Q' and K~^T through its L2.
@@ -697,87 +773,164 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
   const int dv0 = 16 * sl;
   int c_begin, c_end, tok0, tok_end;
   seq_range(p.map, seq, C, c_begin, c_end, tok0, tok_end);
+  const int nch = c_end - c_begin;
 
+  if (wave >= 2) {
+    if (nch <= 0) return;
+    if (wave == 2) ring_producer<TI, C, DK, 0>(smem, p, c_begin, c_end, h, sl, lane);
+    else ring_producer<TI, C, DK, 1>(smem, p, c_begin, c_end, h, sl, lane);
+    return;
+  }
+
+  if (wave == 1) {
+    // the output: O^T tiles = H^T Q'^T + O_loc^T, lane holding row
+    // 16 rt + lane % 16, columns dv0 + 4 (lane / 16) + 0..3.
+    if (nch <= 0) return;
+    TI* outg = (TI*)p.out;
+    typedef typename Raw4<TI>::type RT;
+    auto load_ol = [&](RT (&o)[NB], int cc) {
+      const TI* src = (const TI*)p.im.oloc +
+                      (((int64_t)cc * p.hv + h) * C * p.dv + (int64_t)sl * NB * 256) + lane * 4;
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) o[rt] = load_raw4<TI>(src + rt * 256);
+    };
+    RT ol0[NB], ol1[NB];
+    load_ol(ol0, c_begin);
+    load_ol(ol1, min(c_begin + 1, c_end - 1));
+    ring_barrier();
+    int slot = 0;
+    for (int i = 0; i < nch; ++i) {
+      const char* st = smem + slot * R::stage;
+      const char* hsrc = smem + R::hbuf + (i & 1) * R::HB;
+      UT ha[KD::NU];
+#pragma unroll
+      for (int q = 0; q < KD::NU; ++q) ha[q] = lds_unit<TI, false>(hsrc + q * 1024, lane);
+      f32x4 ao[NB];
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) ao[rt] = zero4();
+#pragma unroll
+      for (int q = 0; q < KD::NU; ++q)
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+          const char* qu = st + R::qp + rt * 16 * DK * S + q * KD::UNIT * S;
+          if (KD::HALF_TAIL && q == KD::NU - 1)
+            mma_unit<true>(ao[rt], ha[q], lds_unit<TI, true>(qu, lane));
+          else
+            mma_unit<false>(ao[rt], ha[q], lds_unit<TI, false>(qu, lane));
+        }
+      RT olc[NB];
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        olc[rt] = ol0[rt];
+        ol0[rt] = ol1[rt];
+      }
+      load_ol(ol1, min(c_begin + i + 2, c_end - 1));
+      const int tok = tok0 + i * C;
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        settle(ao[rt]);
+        const f32x4 ol = raw4_to_f32<TI>(olc[rt]);
+        const int r = 16 * rt + (lane & 15);
+        if (r < tok_end - tok)
+          store4<TI>(outg + (int64_t)(tok + r) * p.o_st + (int64_t)h * p.o_sh + dv0 + (lane >> 4) * 4,
+                     ao[rt][0] + ol[0], ao[rt][1] + ol[1], ao[rt][2] + ol[2], ao[rt][3] + ol[3]);
+      }
+      slot = slot + 1 == R::slots ? 0 : slot + 1;
+      __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+      ring_barrier();
+    }
+    return;
+  }
+
+  // wave 0: the recurrence.  hacc[t] holds rows 16 t + 4 (lane / 16) + e of
+  // the state slice, column dv0 + lane % 16.
   const int64_t sbase = ((int64_t)seq * p.hv + h) * DK * DV;
-  f32x4 hacc[NHW];
+  f32x4 hacc[NKT];
 #pragma unroll
-  for (int j = 0; j < NHW; ++j) {
-    hacc[j] = zero4();
-    const int ti = wave + 4 * j;
-    if (ti < NKT && p.init) {
-      const int dk0 = 16 * ti + (lane >> 4) * 4, dv = dv0 + (lane & 15);
+  for (int t = 0; t < NKT; ++t) {
+    hacc[t] = zero4();
+    if (p.init) {
+      const int dk0 = 16 * t + (lane >> 4) * 4, dv = dv0 + (lane & 15);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) hacc[j][e] = p.init[sbase + (int64_t)(dk0 + e) * DV + dv];
+      for (int e = 0; e < 4; ++e) hacc[t][e] = p.init[sbase + (int64_t)(dk0 + e) * DV + dv];
     }
   }
-  TI* outg = (TI*)p.out;
 
-  // One chunk step: H -> LDS; U = U~ - W H and O = Q' H + O_loc; U -> LDS;
-  // H <- e^gamma_last H + K~^T U.
-  auto step = [&](const Stage& st, int cc) {
+  if (nch > 0) {
+    UT hb[KD::NU];
+    state_units<TI, DK>(hb, hacc);
 #pragma unroll
-    for (int j = 0; j < NHW; ++j) {
-      const int ti = wave + 4 * j;
-      if (ti < NKT)
-        store4<TI>(sHt + (lane & 15) * LK + 16 * ti + (lane >> 4) * 4, hacc[j][0], hacc[j][1],
-                   hacc[j][2], hacc[j][3]);
-    }
-    __syncthreads();
-    if (NB >= 4 || wave < NB) {
-      f32x4 au = zero4(), ao = zero4();
-      mma_pair_lds<DK>(au, ao, st.w, st.q, sHt, LK, lane);
-      settle(au);
-      settle(ao);
-      const f32x4 ut = raw4_to_f32<TI>(st.ut), ol = raw4_to_f32<TI>(st.ol);
-      store4<TI>(sUt + (lane & 15) * LC + 16 * wave + (lane >> 4) * 4, ut[0] - au[0],
-                 ut[1] - au[1], ut[2] - au[2], ut[3] - au[3]);
-      const int tok = tok0 + (cc - c_begin) * C;
-      const int r = 16 * wave + (lane & 15);
-      if (r < tok_end - tok)
-        store4<TI>(outg + (int64_t)(tok + r) * p.o_st + (int64_t)h * p.o_sh + dv0 + (lane >> 4) * 4,
-                   ao[0] + ol[0], ao[1] + ol[1], ao[2] + ol[2], ao[3] + ol[3]);
-    }
-    __syncthreads();
+    for (int q = 0; q < KD::NU; ++q) *(UT*)(smem + R::hbuf + q * 1024 + lane * 16) = hb[q];
+    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+    ring_barrier();
+    int slot = 0;
+    for (int i = 0; i < nch; ++i) {
+      const char* st = smem + slot * R::stage;
+      const float dec = *(const float*)(st + R::dec);
+      // U = W H over the d_k units.
+      f32x4 au[NB];
 #pragma unroll
-    for (int j = 0; j < NHW; ++j) {
-      const int ti = wave + 4 * j;
-      if (ti < NKT) {
+      for (int rt = 0; rt < NB; ++rt) au[rt] = zero4();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hacc[j][e] *= st.dec;
-        mma_frag_lds<C>(hacc[j], st.kt[j], sUt, LC, lane);
-        settle(hacc[j]);
+      for (int q = 0; q < KD::NU; ++q)
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+          const char* wu = st + R::w + rt * 16 * DK * S + q * KD::UNIT * S;
+          if (KD::HALF_TAIL && q == KD::NU - 1)
+            mma_unit<true>(au[rt], lds_unit<TI, true>(wu, lane), hb[q]);
+          else
+            mma_unit<false>(au[rt], lds_unit<TI, false>(wu, lane), hb[q]);
+        }
+#pragma unroll
+      for (int t = 0; t < NKT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hacc[t][e] *= dec;
+      // U = U~ - W H (accumulator tiles), as operand units over chunk rows.
+      f32x4 uu[NB];
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        const f32x4 ut = load4<TI>((const TI*)(st + R::ut + rt * 256 * S) + lane * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) uu[rt][e] = ut[e] - au[rt][e];
       }
-    }
-  };
-
-  // Three stages in flight: the loads for chunk c + 3 are issued as soon as
-  // chunk c's registers are consumed.  Loads past the last chunk re-read it
-  // (clamped) so that every iteration issues the same loads.
-  if (c_begin < c_end) {
-    const int last = c_end - 1;
-    Stage s0, s1, s2;
-    scan_load(s0, p, c_begin, h, sl, wave, lane);
-    scan_load(s1, p, min(c_begin + 1, last), h, sl, wave, lane);
-    scan_load(s2, p, min(c_begin + 2, last), h, sl, wave, lane);
-    for (int cc = c_begin; cc < c_end; cc += 3) {
-      step(s0, cc);
-      scan_load(s0, p, min(cc + 3, last), h, sl, wave, lane);
-      if (cc + 1 < c_end) step(s1, cc + 1);
-      scan_load(s1, p, min(cc + 4, last), h, sl, wave, lane);
-      if (cc + 2 < c_end) step(s2, cc + 2);
-      scan_load(s2, p, min(cc + 5, last), h, sl, wave, lane);
+      UT ub[KC::NU];
+#pragma unroll
+      for (int q = 0; q < KC::NU; ++q)
+        ub[q] = (KC::HALF_TAIL && q == KC::NU - 1)
+                    ? acc_unit<true>(uu[KC::TPU * q], uu[KC::TPU * q], TI{})
+                    : acc_unit<false>(uu[KC::TPU * q], uu[KC::TPU * q + KC::TPU - 1], TI{});
+      // H <- e^gamma_last H + K~^T U.
+#pragma unroll
+      for (int q = 0; q < KC::NU; ++q)
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) {
+          const char* ku = st + R::kt + t * 16 * C * S + q * KC::UNIT * S;
+          if (KC::HALF_TAIL && q == KC::NU - 1)
+            mma_unit<true>(hacc[t], lds_unit<TI, true>(ku, lane), ub[q]);
+          else
+            mma_unit<false>(hacc[t], lds_unit<TI, false>(ku, lane), ub[q]);
+        }
+#pragma unroll
+      for (int t = 0; t < NKT; ++t) settle(hacc[t]);
+      // the next chunk's H operand, also for wave 1
+      state_units<TI, DK>(hb, hacc);
+      char* hdst = smem + R::hbuf + ((i + 1) & 1) * R::HB;
+#pragma unroll
+      for (int q = 0; q < KD::NU; ++q) *(UT*)(hdst + q * 1024 + lane * 16) = hb[q];
+      slot = slot + 1 == R::slots ? 0 : slot + 1;
+      // every LDS access of this chunk has completed before the copying
+      // waves may refill the stage
+      __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+      ring_barrier();
     }
   }
 
   if (p.final_state) {
 #pragma unroll
-    for (int j = 0; j < NHW; ++j) {
-      const int ti = wave + 4 * j;
-      if (ti < NKT) {
-        const int dk0 = 16 * ti + (lane >> 4) * 4, dv = dv0 + (lane & 15);
+    for (int t = 0; t < NKT; ++t) {
+      const int dk0 = 16 * t + (lane >> 4) * 4, dv = dv0 + (lane & 15);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p.final_state[sbase + (int64_t)(dk0 + e) * DV + dv] = hacc[j][e];
-      }
+      for (int e = 0; e < 4; ++e) p.final_state[sbase + (int64_t)(dk0 + e) * DV + dv] = hacc[t][e];
     }
   }
 }
@@ -789,7 +942,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
 // would exceed the LDS or the register budget).
 template <typename TI, int C, int DK>
 static constexpr bool fits() {
-  return WyLayout<TI, C, DK>::total <= kLdsLimit && ScanLayout<TI, C, DK>::total <= kLdsLimit &&
+  return WyLayout<TI, C, DK>::total <= kLdsLimit && ScanRing<TI, C, DK>::slots >= 2 &&
          (sizeof(TI) == 2 || C <= 32);
 }
 

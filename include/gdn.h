@@ -148,22 +148,25 @@ int gdn_prefill_ex(const gdn_tensor* q, const gdn_tensor* k,
 
 /* Byte offsets of the intermediates inside the workspace (for inspection and
  * tests).  Per (chunk c, value head h) block, all in the input dtype:
- *   w     W  = T diag(beta e^gamma) K^             C x dk, fragment order
- *   qp    Q' = scale diag(e^gamma) Q^ - P W        C x dk, fragment order
- *   kt    K~^T, K~_r = e^(gamma_last - gamma_r) k^_r   dk x C, fragment order
+ *   w     W  = T diag(beta e^gamma) K^             C x dk, k-tile order
+ *   qp    Q' = scale diag(e^gamma) Q^ - P W        C x dk, k-tile order
+ *   kt    K~^T, K~_r = e^(gamma_last - gamma_r) k^_r   dk x C, k-tile order
  *   ut    U~ = T diag(beta) V                      C x dv, accumulator tiles
  *   oloc  O_loc = P U~                             C x dv, transposed tiles
  * and f32 decay[c][h] = e^(gamma_last).  A block starts at
  * offset + (c * Hv + h) * (its element count) * element_size.
- * "Fragment order": 16-row tiles one after another; inside a tile, for each
- * 32-wide group of the second index, lane l = m + 16 ((k % 32) / 8) holds the
- * 8 consecutive elements k (a trailing 16-wide group: 4 per lane).
- * "Accumulator tiles": 16 x 16 tiles (row-tile major) of 64 lanes x 4, lane
- * l holding rows 4 (l / 16) .. +3 of column l % 16; "transposed tiles" hold
- * the tiles of the transpose (column-tile major), lane l holding columns
- * 4 (l / 16) .. +3 of row l % 16.  Rows past the end of a short chunk are
- * zero.  chunk_table is int32 [max_chunks][4] = (sequence, first token,
- * length, 0) in packed mode. */
+ * "k-tile order": 16-row tiles one after another; inside a tile, for the
+ * 16-wide k-tile t of the second index, lane l = m + 16 ((k % 16) / 4)
+ * holds the 4 elements k % 4 = 0..3.  bf16 pairs k-tiles 2u and 2u+1 into
+ * one unit of 8 elements per lane (4 of k-tile 2u, then 4 of 2u+1; a
+ * trailing single k-tile has 4); f32 has one k-tile (4 elements) per unit.
+ * Units follow each other, lanes in order inside a unit.
+ * "Accumulator tiles": 16 x 16 tiles, column-tile major (tile (ct, rt) at
+ * ct * C/16 + rt), of 64 lanes x 4, lane l holding rows 4 (l / 16) .. +3 of
+ * column l % 16; "transposed tiles" hold the same tiles with lane l holding
+ * columns 4 (l / 16) .. +3 of row l % 16.  Rows past the end of a short
+ * chunk are zero.  chunk_table is int32 [max_chunks][4] = (sequence, first
+ * token, length, 0) in packed mode. */
 typedef struct gdn_workspace_layout {
   size_t total_bytes;
   int64_t max_chunks;

@@ -27,34 +27,39 @@ def _blocks(ws, off, count, shape, dtype):
     return ws[off:off + n * es].view(dtype).view(count, *shape).float().cpu().numpy()
 
 
-def frag_pos(K, m, k):
-    """Position of element (m, k) of a 16 x K tile stored in fragment order:
-    per 32-wide k-group, lane (m + 16 ((k % 32) // 8)) holds 8 consecutive k;
-    a trailing 16-wide group holds 4 per lane."""
-    K32 = (K // 32) * 32
-    full = (k // 32) * 512 + (m + 16 * ((k % 32) // 8)) * 8 + (k % 8)
-    tail = K32 * 16 + (m + 16 * ((k - K32) // 4)) * 4 + ((k - K32) % 4)
-    return np.where(k < K32, full, tail)
+def ktile_pos(K, m, k, two_byte):
+    """Position of element (m, k) of a 16 x K tile stored in k-tile order:
+    for the 16-wide k-tile t = k // 16, lane m + 16 ((k % 16) // 4) holds
+    the four elements k % 4 = 0..3.  Two-byte types pair k-tiles (2u, 2u+1)
+    into one 8-element unit per lane (a trailing single k-tile: 4 elements);
+    fp32 has one k-tile per unit."""
+    t, g, e = k // 16, (k % 16) // 4, k % 4
+    lane = m + 16 * g
+    if not two_byte:
+        return t * 256 + lane * 4 + e
+    nt = K // 16
+    u, h = t // 2, t % 2
+    half_tail = (nt % 2 == 1) & (u == nt // 2)
+    return np.where(half_tail, u * 512 + lane * 4 + e, u * 512 + lane * 8 + 4 * h + e)
 
 
-def unfrag(blocks, rows, K):
-    """[count, rows*K] in fragment order (16-row tiles) -> [count, rows, K]."""
+def unfrag(blocks, rows, K, two_byte):
+    """[count, rows*K] in k-tile order (16-row tiles) -> [count, rows, K]."""
     r = np.arange(rows)[:, None]
     k = np.arange(K)[None, :]
-    idx = (r // 16) * 16 * K + frag_pos(K, r % 16, k)
+    idx = (r // 16) * 16 * K + ktile_pos(K, r % 16, k, two_byte)
     return blocks.reshape(blocks.shape[0], -1)[:, idx]
 
 
 def unacc(blocks, rows, cols, transposed):
-    """Accumulator-layout tiles ([tile][lane][4]) -> dense [count, rows, cols].
-    Not transposed: tile (rt, ct) = rt * (cols/16) + ct, lane l holds rows
-    4 (l/16) + e, column l % 16.  Transposed (O^T tiles of a [rows][cols]
-    matrix): tile (ct, rt) = ct * (rows/16) + rt, lane l holds columns
-    4 (l/16) + e of row l % 16."""
+    """Accumulator-layout tiles ([tile][lane][4]) -> dense [count, rows, cols],
+    tiles column-tile major: tile (ct, rt) = ct * (rows/16) + rt.  Not
+    transposed: lane l holds rows 4 (l/16) + e, column l % 16.  Transposed
+    (O^T tiles): lane l holds columns 4 (l/16) + e of row l % 16."""
     r = np.arange(rows)[:, None]
     c = np.arange(cols)[None, :]
     if not transposed:
-        tile = (r // 16) * (cols // 16) + c // 16
+        tile = (c // 16) * (rows // 16) + r // 16
         lane = (c % 16) + 16 * ((r % 16) // 4)
         e = (r % 16) % 4
     else:
@@ -93,9 +98,10 @@ def test_wy_intermediates(label, name, kw, tol):
     hv, dk, dv = w.v.shape[1], w.q.shape[2], w.v.shape[2]
     mc = lay.max_chunks
     dt = w.q.dtype
-    Wb = unfrag(_blocks(ws, lay.w, mc * hv, (C, dk), dt), C, dk)
-    Qp = unfrag(_blocks(ws, lay.qp, mc * hv, (C, dk), dt), C, dk)
-    Kt = unfrag(_blocks(ws, lay.kt, mc * hv, (dk, C), dt), dk, C)
+    two = dt == torch.bfloat16
+    Wb = unfrag(_blocks(ws, lay.w, mc * hv, (C, dk), dt), C, dk, two)
+    Qp = unfrag(_blocks(ws, lay.qp, mc * hv, (C, dk), dt), C, dk, two)
+    Kt = unfrag(_blocks(ws, lay.kt, mc * hv, (dk, C), dt), dk, C, two)
     Ut = np.swapaxes(unacc(_blocks(ws, lay.ut, mc * hv, (C, dv), dt), C, dv, False), 1, 2)
     Ol = unacc(_blocks(ws, lay.oloc, mc * hv, (C, dv), dt), C, dv, True)
     dec = _blocks(ws, lay.decay, mc * hv, (1,), torch.float32)[:, 0]
