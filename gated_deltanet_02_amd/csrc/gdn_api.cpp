@@ -228,7 +228,7 @@ int validate(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
     P->chunks_per_seq = (P->seq_len + P->chunk - 1) / P->chunk;
     P->max_chunks = (int64_t)P->n_seq * P->chunks_per_seq;
   }
-  if (P->max_chunks >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "too many chunks");
+  if (P->max_chunks * P->hk >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "too many chunks");
   const int64_t n_slices = P->dv / 16;
   const int64_t scan_blocks = ((int64_t)P->n_seq * P->hv + 7) / 8 * 8 * n_slices;
   if (scan_blocks >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "too many (sequence, head) pairs");
@@ -329,7 +329,8 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
     wp.eps = P.eps;
     wp.map = map;
     wp.im = im;
-    if ((e = gdn::launch_wy(P.bf16, P.chunk, P.dk, wp, (int)P.max_chunks, P.hk, s)) != hipSuccess)
+    wp.n_items = (int32_t)(P.max_chunks * P.hk);
+    if ((e = gdn::launch_wy(P.bf16, P.chunk, P.dk, wp, s)) != hipSuccess)
       return fail(GDN_ERR_HIP, "WY launch: %s", hipGetErrorString(e));
   }
   if (P.stages & GDN_STAGE_SCAN) {

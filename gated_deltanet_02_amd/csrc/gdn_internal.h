@@ -51,6 +51,7 @@ struct WyParams {
   int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh;
   int64_t g_st, g_sh, b_st, b_sh;
   int32_t hk, hv, dv;
+  int32_t n_items;    // (chunk, key head) work items: max_chunks * hk
   float scale, eps;
   ChunkMap map;
   Intermediates im;

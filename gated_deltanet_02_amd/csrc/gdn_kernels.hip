@@ -254,8 +254,32 @@ struct WyLayout {
   static constexpr int r_x = r_t + sz_t;
   static constexpr int sz_x = cmax(cmax(C * LK * S, C * LF * 4), 3 * C * LC * S);
   static constexpr int r_vec = r_x + sz_x;
-  static constexpr int total = r_vec + 7 * C * 4;
+  static constexpr int r_gate = r_vec + 7 * C * 4;  // g, beta of the first value head
+  static constexpr int total = r_gate + 2 * C * 4;
 };
+
+// Issues LDS-direct copies of rows 0 .. R-1 of a row-major LDS region (row
+// stride LDR elements, granule swizzle SW) from global rows src + r * st,
+// D elements each: every 16-byte slot of the region fetches the global
+// granule stored there, so the copy lands in the swizzled layout directly.
+// Rows r >= n and slots past the data are left alone (the caller zeroes the
+// rows).  The 1 KiB pieces are spread over the NW waves.
+template <typename TI, int R, int LDR, int SW, int NW>
+__device__ __forceinline__ void dma_rows(char* region, const TI* src, int64_t st, int D, int n,
+                                         int wave, int lane) {
+  constexpr int S = sizeof(TI), GE = 16 / S;
+  constexpr int BYTES = R * LDR * S;
+  constexpr int PIECES = (BYTES + 1023) / 1024;
+  for (int pc = wave; pc < PIECES; pc += NW) {
+    const int o = pc * 1024 + lane * 16;
+    const int row = o / (LDR * S), ce = (o % (LDR * S)) / S;
+    const int gcol = ((ce / GE) ^ (row & SW)) * GE;
+    if (o < BYTES && row < n && gcol < D)
+      __builtin_amdgcn_global_load_lds((const void*)(src + row * st + gcol),
+                                       (__attribute__((address_space(3))) void*)(region + pc * 1024),
+                                       16, 0, 0);
+  }
+}
 
 // dst[d][r] = src[r][d] for r < R (even), d < D (whole granules), with the
 // source and destination row swizzles.  Pairs of rows are packed so each LDS
@@ -283,8 +307,35 @@ __device__ __forceinline__ void transpose_sw(const TI* src, int lds, TI* dst, in
   }
 }
 
+// The inputs of the chunk (first token t0, n tokens) for key head kh: q, k
+// rows and the first value head's v rows and gates, copied straight into
+// their LDS regions (no registers).
 template <typename TI, int C, int DK>
-__global__ __launch_bounds__(kWyThreads) void wy_kernel(WyParams p) {
+__device__ __forceinline__ void wy_fetch(char* buf, const WyParams& p, int kh, int t0, int n,
+                                         int wave, int lane) {
+  using L = WyLayout<TI, C, DK>;
+  constexpr int NW = kWyThreads / 64;
+  const int h = kh * (p.hv / p.hk);
+  dma_rows<TI, C, L::LK, L::SWK, NW>(buf + L::r_kv, (const TI*)p.k + (int64_t)t0 * p.k_st + kh * p.k_sh,
+                                     p.k_st, DK, n, wave, lane);
+  dma_rows<TI, C, L::LK, L::SWK, NW>(buf + L::r_x, (const TI*)p.q + (int64_t)t0 * p.q_st + kh * p.q_sh,
+                                     p.q_st, DK, n, wave, lane);
+  dma_rows<TI, C, L::LV, L::SWV, NW>(buf + L::r_t, (const TI*)p.v + (int64_t)t0 * p.v_st + h * p.v_sh,
+                                     p.v_st, p.dv, n, wave, lane);
+  if (wave == NW - 1 && lane < n) {
+    __builtin_amdgcn_global_load_lds((const void*)(p.g + (int64_t)(t0 + lane) * p.g_st + h * p.g_sh),
+                                     (__attribute__((address_space(3))) void*)(buf + L::r_gate), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(p.beta + (int64_t)(t0 + lane) * p.b_st + h * p.b_sh),
+                                     (__attribute__((address_space(3))) void*)(buf + L::r_gate + C * 4),
+                                     4, 0, 0);
+  }
+}
+
+// One workgroup per (chunk, key head) item, under 128 VGPRs and 80 KiB of
+// LDS so that two workgroups share a compute unit and hide each other's
+// barriers and latencies.
+template <typename TI, int C, int DK>
+__global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   using L = WyLayout<TI, C, DK>;
   constexpr int NT = kWyThreads;
   constexpr int LK = L::LK, LV = L::LV, LC = L::LC, LF = L::LF;
@@ -292,10 +343,19 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(WyParams p) {
   constexpr int GR = Gran<TI>::n;
   constexpr int NB = C / 16;    // 16-row tiles along the chunk
   constexpr int NKT = DK / 16;  // 16-row tiles along d_k
-  constexpr int GPR = DK / GR;  // 16-byte granules per q / k row
-  constexpr int NQK = (C * GPR + NT - 1) / NT;
   constexpr int NVG = (C * (128 / GR) + NT - 1) / NT;  // v granules per thread (d_v <= 128)
-  __shared__ __attribute__((aligned(16))) char smem[L::total];
+  __shared__ __attribute__((aligned(1024))) char smem[L::total];
+
+  const int it = blockIdx.x;
+  if (it >= p.n_items) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const TI* qg = (const TI*)p.q;
+  const TI* vg = (const TI*)p.v;
+  const int DV = p.dv;
+  const int GPRV = DV / GR;
+  const int NVT = DV / 16;
+  const int grp = p.hv / p.hk;
   TI* sKt = (TI*)(smem + L::r_kt);
   TI* sKV = (TI*)(smem + L::r_kv);   // K rows | V^T | W^T
   TI* sVr = (TI*)(smem + L::r_t);    // V rows
@@ -313,35 +373,33 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(WyParams p) {
   float* sEg = sBeta + C;   // e^gamma_r
   float* sKs = sEg + C;     // rk_r e^(gamma_last - gamma_r)
   float* sCb = sKs + C;     // beta_s e^gamma_s rk_s  (column scale of Tb)
+  const float* sGate = (const float*)(smem + L::r_gate);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = blockIdx.x, kh = blockIdx.y;
+  const int c = it / p.hk, kh = it % p.hk;
   int seq, t0, n;
   if (!chunk_info(p.map, c, C, seq, t0, n)) return;
   (void)seq;
-  const TI* qg = (const TI*)p.q;
-  const TI* kg = (const TI*)p.k;
-  const TI* vg = (const TI*)p.v;
-  const int DV = p.dv;
-  const int GPRV = DV / GR;
-  const int NVT = DV / 16;
-  const int grp = p.hv / p.hk;
-
-  // All global inputs of the chunk are requested up front: q and k rows,
-  // the v rows and gates of the first value head (zeros past the chunk end).
-  uint4 kreg[NQK], qreg[NQK], vreg[NVG];
-  float gv = 0.f, bv = 0.f;
-#pragma unroll
-  for (int i = 0; i < NQK; ++i) {
-    const int idx = tid + i * NT;
-    const int r = idx / GPR, gc = idx % GPR;
-    kreg[i] = qreg[i] = make_uint4(0, 0, 0, 0);
-    if (idx < C * GPR && r < n) {
-      const int64_t t = t0 + r;
-      kreg[i] = ld16(kg + t * p.k_st + kh * p.k_sh + gc * GR);
-      qreg[i] = ld16(qg + t * p.q_st + kh * p.q_sh + gc * GR);
+  wy_fetch<TI, C, DK>(smem, p, kh, t0, n, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (n < C) {
+    // rows past the chunk's end are zero (the copies skipped them)
+    for (int idx = tid; idx < (C - n) * LK; idx += NT) {
+      sKV[n * LK + idx] = from_float<TI>(0.f);
+      sQ[n * LK + idx] = from_float<TI>(0.f);
     }
+    for (int idx = tid; idx < (C - n) * LV; idx += NT) sVr[n * LV + idx] = from_float<TI>(0.f);
+    if (tid < C - n) {
+      ((float*)sGate)[n + tid] = 0.f;
+      ((float*)sGate)[C + n + tid] = 0.f;
+    }
+    __syncthreads();
   }
+
+  uint4 vreg[NVG];
+  float gv = 0.f, bv = 0.f;
+  // v rows and gates of value head h (heads after the first of a group go
+  // through registers, one head ahead)
   auto load_head = [&](int h) {
 #pragma unroll
     for (int i = 0; i < NVG; ++i) {
@@ -358,18 +416,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(WyParams p) {
       bv = 0.f;
     }
   };
-  load_head(kh * grp);
 
-#pragma unroll
-  for (int i = 0; i < NQK; ++i) {
-    const int idx = tid + i * NT;
-    if (idx < C * GPR) {
-      const int r = idx / GPR, gc = idx % GPR;
-      st16(sKV + r * LK + swz<TI, SWK>(r, gc * GR), kreg[i]);
-      st16(sQ + r * LK + swz<TI, SWK>(r, gc * GR), qreg[i]);
-    }
-  }
-  __syncthreads();
   transpose_sw<TI, NT, SWK, SWC>(sKV, LK, sKt, LC, C, DK, tid);
   row_inv_norms<TI, DK, NT>(sKV, LK, C, p.eps, sRk, tid);  // sums are order-free: the
   row_inv_norms<TI, DK, NT>(sQ, LK, C, p.eps, sRq, tid);   // swizzle only permutes a row
@@ -388,20 +435,33 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(WyParams p) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) settle(acc_gs[0][j]);
   }
+  if (wave == 0) {
+    gv = sGate[lane < C ? lane : 0];
+    bv = sGate[C + (lane < C ? lane : 0)];
+    if (lane >= C) gv = bv = 0.f;
+  }
   __syncthreads();
 
   for (int gi = 0; gi < grp; ++gi) {
     const int h = kh * grp + gi;
     const int64_t blk = (int64_t)c * p.hv + h;
+    // re-read thread indices per head (see the item loop): the addresses of
+    // each phase are computed where they are used, not all up front
+    int tid_h;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid_h) : "v"(tid));
+    const int tid = tid_h, lane = tid_h & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid_h >> 6);
 
-    // v rows into the T region and the gate scan; then the next value
-    // head's inputs are requested.
+    // v rows into the T region (the first head's are there already) and
+    // the gate scan; then the next value head's inputs are requested.
+    if (gi > 0) {
 #pragma unroll
-    for (int i = 0; i < NVG; ++i) {
-      const int idx = tid + i * NT;
-      if (idx < C * GPRV) {
-        const int r = idx / GPRV, gc = idx % GPRV;
-        st16(sVr + r * LV + swz<TI, SWV>(r, gc * GR), vreg[i]);
+      for (int i = 0; i < NVG; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < C * GPRV) {
+          const int r = idx / GPRV, gc = idx % GPRV;
+          st16(sVr + r * LV + swz<TI, SWV>(r, gc * GR), vreg[i]);
+        }
       }
     }
     if (wave == 0) {
@@ -1000,9 +1060,8 @@ hipError_t launch_table(const TableParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_wy(bool bf16, int chunk, int dk, const WyParams& p,
-                     int grid_x, int grid_y, hipStream_t s) {
-  const dim3 grid(grid_x, grid_y);
+hipError_t launch_wy(bool bf16, int chunk, int dk, const WyParams& p, hipStream_t s) {
+  const dim3 grid(p.n_items);
   const int rc = bf16 ? dispatch_c<gdn::bf16>(chunk, dk, 0, &p, nullptr, grid, s)
                       : dispatch_c<float>(chunk, dk, 0, &p, nullptr, grid, s);
   if (rc) return hipErrorInvalidValue;

@@ -12,8 +12,8 @@ namespace gdn {
 bool kernels_available(bool bf16, int chunk, int dk);
 
 hipError_t launch_table(const TableParams& p, hipStream_t s);
-hipError_t launch_wy(bool bf16, int chunk, int dk, const WyParams& p,
-                     int grid_x, int grid_y, hipStream_t s);
+// One WY workgroup per (chunk, key head) item.
+hipError_t launch_wy(bool bf16, int chunk, int dk, const WyParams& p, hipStream_t s);
 hipError_t launch_scan(bool bf16, int chunk, int dk, const ScanParams& p,
                        int grid_x, hipStream_t s);
 
