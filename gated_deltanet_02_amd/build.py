@@ -20,8 +20,13 @@ LIB = os.path.join(HERE, "libgdn.so")
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
+# -packed-fp32-ops: no packed fp32 arithmetic in the generated code.
+# -amdgpu-mfma-vgpr-form: MFMA results in VGPRs, so accumulators that VALU
+# code also updates (the scan's state) are not copied between the
+# accumulator and vector register files.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 SOURCES = ["gdn_kernels.hip", "gdn_api.cpp"]
 

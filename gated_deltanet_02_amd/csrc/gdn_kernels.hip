@@ -797,16 +797,18 @@ __device__ __forceinline__ void ring_producer(char* smem, const ScanParams& p, i
   }
 }
 
-// H as operand units (B of U = W H, A of O^T = H^T Q'^T) from the state's
-// accumulator tiles.
+// -H as operand units (B of U = U~ + W (-H), A of -O^T = (-H)^T Q'^T) from
+// the state's accumulator tiles.  Carrying the negated state lets U~ enter
+// the MFMA as its accumulator input, so no subtraction follows the product.
 template <typename TI, int DK, typename UT>
 __device__ __forceinline__ void state_units(UT* hb, const f32x4* hacc) {
   using KD = KTile<TI, DK>;
 #pragma unroll
-  for (int q = 0; q < KD::NU; ++q)
-    hb[q] = (KD::HALF_TAIL && q == KD::NU - 1)
-                ? acc_unit<true>(hacc[KD::TPU * q], hacc[KD::TPU * q], TI{})
-                : acc_unit<false>(hacc[KD::TPU * q], hacc[KD::TPU * q + KD::TPU - 1], TI{});
+  for (int q = 0; q < KD::NU; ++q) {
+    const f32x4 a = -hacc[KD::TPU * q], b = -hacc[KD::TPU * q + KD::TPU - 1];
+    hb[q] = (KD::HALF_TAIL && q == KD::NU - 1) ? acc_unit<true>(a, a, TI{})
+                                               : acc_unit<false>(a, b, TI{});
+  }
 }
 
 template <typename TI, int C, int DK>
@@ -843,7 +845,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
   }
 
   if (wave == 1) {
-    // the output: O^T tiles = H^T Q'^T + O_loc^T, lane holding row
+    // the output: O^T tiles = O_loc^T - (-H)^T Q'^T, lane holding row
     // 16 rt + lane % 16, columns dv0 + 4 (lane / 16) + 0..3.
     if (nch <= 0) return;
     TI* outg = (TI*)p.out;
@@ -893,7 +895,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
         const int r = 16 * rt + (lane & 15);
         if (r < tok_end - tok)
           store4<TI>(outg + (int64_t)(tok + r) * p.o_st + (int64_t)h * p.o_sh + dv0 + (lane >> 4) * 4,
-                     ao[rt][0] + ol[0], ao[rt][1] + ol[1], ao[rt][2] + ol[2], ao[rt][3] + ol[3]);
+                     ol[0] - ao[rt][0], ol[1] - ao[rt][1], ol[2] - ao[rt][2], ol[3] - ao[rt][3]);
       }
       slot = slot + 1 == R::slots ? 0 : slot + 1;
       __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
@@ -927,10 +929,10 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
     for (int i = 0; i < nch; ++i) {
       const char* st = smem + slot * R::stage;
       const float dec = *(const float*)(st + R::dec);
-      // U = W H over the d_k units.
+      // U = U~ + W (-H) over the d_k units, U~ as the accumulator input.
       f32x4 au[NB];
 #pragma unroll
-      for (int rt = 0; rt < NB; ++rt) au[rt] = zero4();
+      for (int rt = 0; rt < NB; ++rt) au[rt] = load4<TI>((const TI*)(st + R::ut + rt * 256 * S) + lane * 4);
 #pragma unroll
       for (int q = 0; q < KD::NU; ++q)
 #pragma unroll
@@ -945,20 +947,13 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
       for (int t = 0; t < NKT; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) hacc[t][e] *= dec;
-      // U = U~ - W H (accumulator tiles), as operand units over chunk rows.
-      f32x4 uu[NB];
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        const f32x4 ut = load4<TI>((const TI*)(st + R::ut + rt * 256 * S) + lane * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) uu[rt][e] = ut[e] - au[rt][e];
-      }
+      // U (accumulator tiles) as operand units over chunk rows.
       UT ub[KC::NU];
 #pragma unroll
       for (int q = 0; q < KC::NU; ++q)
         ub[q] = (KC::HALF_TAIL && q == KC::NU - 1)
-                    ? acc_unit<true>(uu[KC::TPU * q], uu[KC::TPU * q], TI{})
-                    : acc_unit<false>(uu[KC::TPU * q], uu[KC::TPU * q + KC::TPU - 1], TI{});
+                    ? acc_unit<true>(au[KC::TPU * q], au[KC::TPU * q], TI{})
+                    : acc_unit<false>(au[KC::TPU * q], au[KC::TPU * q + KC::TPU - 1], TI{});
       // H <- e^gamma_last H + K~^T U.
 #pragma unroll
       for (int q = 0; q < KC::NU; ++q)
