@@ -692,10 +692,11 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
 // One workgroup per (sequence, value head, 16-column slice of d_v), four
 // waves with fixed roles:
 //   wave 0  the recurrence: U = U~ - W H and H <- e^gamma_last H + K~^T U,
-//           with the state slice in its MFMA accumulators; after each chunk
-//           it leaves H (as bf16 / fp32 operand units) in LDS for wave 1;
-//   wave 1  the output of the same chunk, O = Q' H + O_loc, off the
-//           recurrence's critical path;
+//           with the state slice in its MFMA accumulators; at the start of
+//           each chunk it leaves -H (as bf16 / fp32 operand units) in LDS;
+//   wave 1  the output, one chunk behind: O = Q' H + O_loc from Q' held in
+//           registers since the previous chunk, off the recurrence's
+//           critical path;
 //   waves 2, 3 copy each chunk's W, Q', K~^T, U~ slice and decay from
 //           global memory into a ring of LDS stages with LDS-direct loads
 //           (no registers), `lead` chunks ahead.
@@ -845,24 +846,34 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
   }
 
   if (wave == 1) {
-    // the output: O^T tiles = O_loc^T - (-H)^T Q'^T, lane holding row
-    // 16 rt + lane % 16, columns dv0 + 4 (lane / 16) + 0..3.
+    // The output, one chunk behind the recurrence: during chunk i it reads
+    // Q'_i (LDS) and O_loc_i (global) into registers and forms
+    //   O_{i-1}^T = O_loc^T - (-H_{i-1})^T Q'^T
+    // with -H_{i-1} as wave 0 left it in LDS during chunk i - 1.  Lane holds
+    // row 16 rt + lane % 16, columns dv0 + 4 (lane / 16) + 0..3.
     if (nch <= 0) return;
     TI* outg = (TI*)p.out;
     typedef typename Raw4<TI>::type RT;
-    auto load_ol = [&](RT (&o)[NB], int cc) {
-      const TI* src = (const TI*)p.im.oloc +
-                      (((int64_t)cc * p.hv + h) * C * p.dv + (int64_t)sl * NB * 256) + lane * 4;
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) o[rt] = load_raw4<TI>(src + rt * 256);
+    struct OBuf {
+      UT q[NB][KD::NU];
+      RT ol[NB];
     };
-    RT ol0[NB], ol1[NB];
-    load_ol(ol0, c_begin);
-    load_ol(ol1, min(c_begin + 1, c_end - 1));
-    ring_barrier();
-    int slot = 0;
-    for (int i = 0; i < nch; ++i) {
+    auto fetch = [&](OBuf& o, int i, int slot) {
       const char* st = smem + slot * R::stage;
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+        for (int q = 0; q < KD::NU; ++q) {
+          const char* qu = st + R::qp + rt * 16 * DK * S + q * KD::UNIT * S;
+          o.q[rt][q] = (KD::HALF_TAIL && q == KD::NU - 1) ? lds_unit<TI, true>(qu, lane)
+                                                          : lds_unit<TI, false>(qu, lane);
+        }
+      const TI* src = (const TI*)p.im.oloc +
+                      (((int64_t)(c_begin + i) * p.hv + h) * C * p.dv + (int64_t)sl * NB * 256) + lane * 4;
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) o.ol[rt] = load_raw4<TI>(src + rt * 256);
+    };
+    auto emit = [&](const OBuf& o, int i) {
       const char* hsrc = smem + R::hbuf + (i & 1) * R::HB;
       UT ha[KD::NU];
 #pragma unroll
@@ -874,32 +885,39 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
       for (int q = 0; q < KD::NU; ++q)
 #pragma unroll
         for (int rt = 0; rt < NB; ++rt) {
-          const char* qu = st + R::qp + rt * 16 * DK * S + q * KD::UNIT * S;
-          if (KD::HALF_TAIL && q == KD::NU - 1)
-            mma_unit<true>(ao[rt], ha[q], lds_unit<TI, true>(qu, lane));
-          else
-            mma_unit<false>(ao[rt], ha[q], lds_unit<TI, false>(qu, lane));
+          if (KD::HALF_TAIL && q == KD::NU - 1) mma_unit<true>(ao[rt], ha[q], o.q[rt][q]);
+          else mma_unit<false>(ao[rt], ha[q], o.q[rt][q]);
         }
-      RT olc[NB];
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        olc[rt] = ol0[rt];
-        ol0[rt] = ol1[rt];
-      }
-      load_ol(ol1, min(c_begin + i + 2, c_end - 1));
       const int tok = tok0 + i * C;
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
         settle(ao[rt]);
-        const f32x4 ol = raw4_to_f32<TI>(olc[rt]);
+        const f32x4 ol = raw4_to_f32<TI>(o.ol[rt]);
         const int r = 16 * rt + (lane & 15);
         if (r < tok_end - tok)
           store4<TI>(outg + (int64_t)(tok + r) * p.o_st + (int64_t)h * p.o_sh + dv0 + (lane >> 4) * 4,
                      ol[0] - ao[rt][0], ol[1] - ao[rt][1], ol[2] - ao[rt][2], ol[3] - ao[rt][3]);
       }
+    };
+    auto iter = [&](OBuf& cur, const OBuf& prev, int i, int& slot) {
+      fetch(cur, i, slot);
+      if (i > 0) emit(prev, i - 1);
       slot = slot + 1 == R::slots ? 0 : slot + 1;
       __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
       ring_barrier();
+    };
+    OBuf oa, ob;
+    ring_barrier();
+    int slot = 0, i = 0;
+    for (; i + 1 < nch; i += 2) {
+      iter(oa, ob, i, slot);
+      iter(ob, oa, i + 1, slot);
+    }
+    if (i < nch) {
+      iter(oa, ob, i, slot);
+      emit(oa, nch - 1);
+    } else {
+      emit(ob, nch - 1);
     }
     return;
   }
@@ -930,19 +948,30 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
       const char* st = smem + slot * R::stage;
       const float dec = *(const float*)(st + R::dec);
       // U = U~ + W (-H) over the d_k units, U~ as the accumulator input.
+      // Row tiles are finished in pairs, so that the state update for the
+      // first 32 rows can start while the MFMAs for the rest run.
       f32x4 au[NB];
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) au[rt] = load4<TI>((const TI*)(st + R::ut + rt * 256 * S) + lane * 4);
 #pragma unroll
-      for (int q = 0; q < KD::NU; ++q)
+      for (int r0 = 0; r0 < NB; r0 += 2)
 #pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
-          const char* wu = st + R::w + rt * 16 * DK * S + q * KD::UNIT * S;
-          if (KD::HALF_TAIL && q == KD::NU - 1)
-            mma_unit<true>(au[rt], lds_unit<TI, true>(wu, lane), hb[q]);
-          else
-            mma_unit<false>(au[rt], lds_unit<TI, false>(wu, lane), hb[q]);
-        }
+        for (int q = 0; q < KD::NU; ++q)
+#pragma unroll
+          for (int rt = r0; rt < r0 + 2 && rt < NB; ++rt) {
+            const char* wu = st + R::w + rt * 16 * DK * S + q * KD::UNIT * S;
+            if (KD::HALF_TAIL && q == KD::NU - 1)
+              mma_unit<true>(au[rt], lds_unit<TI, true>(wu, lane), hb[q]);
+            else
+              mma_unit<false>(au[rt], lds_unit<TI, false>(wu, lane), hb[q]);
+          }
+      // -H_i for wave 1, which reads it after the next barrier (written
+      // behind this chunk's operand reads)
+      if (i > 0) {
+        char* hdst = smem + R::hbuf + (i & 1) * R::HB;
+#pragma unroll
+        for (int q = 0; q < KD::NU; ++q) *(UT*)(hdst + q * 1024 + lane * 16) = hb[q];
+      }
 #pragma unroll
       for (int t = 0; t < NKT; ++t)
 #pragma unroll
@@ -967,11 +996,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
         }
 #pragma unroll
       for (int t = 0; t < NKT; ++t) settle(hacc[t]);
-      // the next chunk's H operand, also for wave 1
+      // the next chunk's operand -H
       state_units<TI, DK>(hb, hacc);
-      char* hdst = smem + R::hbuf + ((i + 1) & 1) * R::HB;
-#pragma unroll
-      for (int q = 0; q < KD::NU; ++q) *(UT*)(hdst + q * 1024 + lane * 16) = hb[q];
       slot = slot + 1 == R::slots ? 0 : slot + 1;
       // every LDS access of this chunk has completed before the copying
       // waves may refill the stage
