@@ -11,6 +11,7 @@ dominant kernel (HIP events around its launches on the stream it runs on)
 and the float64 oracle's throughput on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --mode decode     # the single-token decode step instead
 """
 from __future__ import annotations
 
@@ -103,6 +104,62 @@ def cpu_baseline(w, budget_s: float = 12.0):
                       f"one thread per (sequence, head) of {units}, {cores} host cores visible"}
 
 
+DECODE_METRIC = "GDN decode tokens/sec, 256 sequences x 16 heads, d=128, bf16 (state in HBM)"
+
+
+def decode_bytes(w) -> int:
+    """Bytes one decode step must move: read and write the fp32 state; read
+    q, k, v, g, beta; write out."""
+    es = w.q.element_size()
+    N, hk, dk = w.q.shape
+    hv, dv = w.v.shape[1], w.v.shape[2]
+    return N * (2 * hv * dk * dv * 4 + 2 * hk * dk * es + 2 * hv * dv * es + 2 * hv * 4)
+
+
+def decode_main(args, torch, G, W, dev):
+    """One step = gdn_decode for every sequence (the state updated in place)."""
+    w = W.make_workload(args.workload)
+    log(f"decode workload {args.workload}: N={w.n_seqs} dims={w.dims}")
+    q, k, v, g, b = (getattr(w, x).to(dev) for x in ("q", "k", "v", "g", "beta"))
+    state = w.init_state.to(dev).contiguous()
+    out = torch.empty_like(v)
+    for _ in range(args.warmup):
+        G.gdn_decode(q, k, v, g, b, state, out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(K):
+        G.gdn_decode(q, k, v, g, b, state, out)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / K
+    t_k = ev[0].elapsed_time(ev[K]) / K
+    nbytes = decode_bytes(w)
+    achieved = nbytes / (t_k * 1e-3) / 1e9
+    result = {
+        "metric": DECODE_METRIC, "value": w.n_seqs / (ms_step * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 (bf16 inputs)", "data": "synthetic (seeded; state ~ N(0, 0.5^2))",
+        "config": {"workload": args.workload, "n_seqs": w.n_seqs, "hk": int(w.q.shape[1]),
+                   "hv": int(w.v.shape[1]), "dk": int(w.q.shape[2]), "dv": int(w.v.shape[2]),
+                   "seed": 0, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "gdn_decode_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": t_k},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on the host cores ...")
+        result["cpu_baseline"] = cpu_baseline(w)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +167,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prompt_4k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill",
+                    help="decode: time gdn_decode on --workload (default decode_256)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -138,6 +197,12 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         log(f"copy calibration: 5 copies of {n} bytes")
+        return
+
+    if args.mode == "decode":
+        if args.workload == "prompt_4k":
+            args.workload = "decode_256"
+        decode_main(args, torch, G, W, dev)
         return
 
     w = W.make_workload(args.workload)

@@ -9,7 +9,7 @@ from ._binding import (GdnError, GdnOptions, GdnTensor, GdnWorkspaceLayout,  # n
                        STAGE_ALL, STAGE_SCAN, STAGE_TABLE, STAGE_WY, EXPORTED,
                        alloc_workspace, describe, gdn_abi_version,
                        gdn_default_options, gdn_get_workspace_layout,
-                       gdn_last_error, gdn_prefill, gdn_prefill_ex,
+                       gdn_decode, gdn_last_error, gdn_prefill, gdn_prefill_ex,
                        gdn_status_string, gdn_workspace_size, library_path,
                        options)
 from ._binding import PreparedPrefill  # noqa: F401,E402

@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "GDN_OK", -1: "GDN_ERR_NULL_ARG", -2: "GDN_ERR_DTYPE",
 STAGE_TABLE, STAGE_WY, STAGE_SCAN, STAGE_ALL = 1, 2, 4, 7
 EXPORTED = ("gdn_abi_version", "gdn_default_options", "gdn_prefill",
             "gdn_prefill_ex", "gdn_workspace_size", "gdn_get_workspace_layout",
-            "gdn_status_string", "gdn_last_error")
+            "gdn_decode", "gdn_status_string", "gdn_last_error")
 
 _DTYPES = {torch.bfloat16: 1, torch.float32: 2, torch.int32: 3}
 
@@ -84,6 +84,8 @@ def lib():
         L.gdn_workspace_size.restype = ctypes.c_int
         L.gdn_get_workspace_layout.argtypes = [T, T, T, T, P(GdnOptions), P(GdnWorkspaceLayout)]
         L.gdn_get_workspace_layout.restype = ctypes.c_int
+        L.gdn_decode.argtypes = [T] * 7 + [P(GdnOptions), ctypes.c_void_p]
+        L.gdn_decode.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_last_error.restype = ctypes.c_char_p
@@ -210,6 +212,23 @@ def gdn_prefill_ex(q, k, v, g, beta, cu_seqlens=None, init_state=None,
                                 workspace.data_ptr(), workspace.numel(),
                                 _stream_handle(stream, v)))
     return out, final_state
+
+
+def gdn_decode(q, k, v, g, beta, state, out=None, opts: Optional[GdnOptions] = None,
+               stream=None):
+    """One recurrent step per sequence on ``state`` (updated in place).
+    q, k [N, Hk, dk]; v [N, Hv, dv]; g, beta [N, Hv]; state [N, Hv, dk, dv]
+    f32.  Returns out [N, Hv, dv]."""
+    if out is None:
+        out = torch.empty_like(v)
+    ts = (q, k, v, g, beta, state, out)
+    for name, t in zip(("q", "k", "v", "g", "beta", "state", "out"), ts):
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    ds = [describe(x) for x in ts]
+    _check(lib().gdn_decode(*[_ref(d) for d in ds], ctypes.byref(opts) if opts else None,
+                            _stream_handle(stream, v)))
+    return out
 
 
 class PreparedPrefill:

@@ -274,6 +274,72 @@ int validate(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
   return GDN_OK;
 }
 
+// Decode: one token per sequence.  q, k [N, Hk, dk]; v, out [N, Hv, dv];
+// g, beta [N, Hv] f32; state [N, Hv, dk, dv] f32 contiguous.
+int validate_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
+                    const gdn_tensor* g, const gdn_tensor* beta, const gdn_tensor* state,
+                    const gdn_tensor* out, const gdn_options* opts, gdn::DecodeParams* d,
+                    bool* bf16, int* dk) {
+  if (!q || !k || !v || !g || !beta || !state || !out)
+    return fail(GDN_ERR_NULL_ARG, "q, k, v, g, beta, state and out are required");
+  if (q->dtype != GDN_DTYPE_BF16 && q->dtype != GDN_DTYPE_F32)
+    return fail(GDN_ERR_DTYPE, "q must be bf16 or f32");
+  if (k->dtype != q->dtype || v->dtype != q->dtype || out->dtype != q->dtype)
+    return fail(GDN_ERR_DTYPE, "q, k, v and out must share one dtype");
+  if (g->dtype != GDN_DTYPE_F32 || beta->dtype != GDN_DTYPE_F32 || state->dtype != GDN_DTYPE_F32)
+    return fail(GDN_ERR_DTYPE, "g, beta and state must be f32");
+  const gdn_tensor* vecs[4] = {q, k, v, out};
+  const char* names[4] = {"q", "k", "v", "out"};
+  for (int i = 0; i < 4; ++i)
+    if (vecs[i]->ndim != 3) return fail(GDN_ERR_SHAPE, "%s must be [N, H, D]", names[i]);
+  if (g->ndim != 2 || beta->ndim != 2) return fail(GDN_ERR_SHAPE, "g and beta must be [N, Hv]");
+  const int64_t N = q->shape[0], hk = q->shape[1], dkk = q->shape[2];
+  const int64_t hv = v->shape[1], dv = v->shape[2];
+  if (N < 0 || hk < 1 || hv < 1) return fail(GDN_ERR_SHAPE, "bad sizes");
+  if (k->shape[0] != N || k->shape[1] != hk || k->shape[2] != dkk) return fail(GDN_ERR_SHAPE, "q and k shapes differ");
+  if (v->shape[0] != N || out->shape[0] != N || out->shape[1] != hv || out->shape[2] != dv)
+    return fail(GDN_ERR_SHAPE, "v and out must be [N, Hv, dv]");
+  if (g->shape[0] != N || g->shape[1] != hv || beta->shape[0] != N || beta->shape[1] != hv)
+    return fail(GDN_ERR_SHAPE, "g and beta must be [N, Hv]");
+  if (!supported_head_dim(dkk) || !supported_head_dim(dv))
+    return fail(GDN_ERR_UNSUPPORTED, "d_k and d_v must be 16, 32, 64 or 128");
+  if (hv % hk) return fail(GDN_ERR_SHAPE, "value heads must be a multiple of key heads");
+  if (state->ndim != 4 || state->shape[0] != N || state->shape[1] != hv || state->shape[2] != dkk ||
+      state->shape[3] != dv)
+    return fail(GDN_ERR_SHAPE, "state must be [N, Hv, dk, dv]");
+  if (N * hv * (dv / (dv < 64 ? dv : 64)) >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "too many (sequence, head) pairs");
+  if (N > 0) {
+    for (int i = 0; i < 4; ++i) {
+      if (!vecs[i]->data) return fail(GDN_ERR_NULL_ARG, "%s data is NULL", names[i]);
+      if (vecs[i]->stride[2] != 1 || vecs[i]->stride[0] < 0 || vecs[i]->stride[1] < 0)
+        return fail(GDN_ERR_LAYOUT, "%s: last dimension must have unit stride", names[i]);
+    }
+    if (!g->data || !beta->data || !state->data) return fail(GDN_ERR_NULL_ARG, "g, beta or state data is NULL");
+    if (g->stride[0] < 0 || g->stride[1] < 0 || beta->stride[0] < 0 || beta->stride[1] < 0)
+      return fail(GDN_ERR_LAYOUT, "negative stride");
+    if (state->stride[3] != 1 || state->stride[2] != dv || state->stride[1] != dkk * dv ||
+        state->stride[0] != hv * dkk * dv)
+      return fail(GDN_ERR_LAYOUT, "state must be contiguous");
+  }
+  gdn_options o;
+  gdn_default_options(&o);
+  if (opts) o = *opts;
+  if (!(o.l2_eps >= 0.f)) return fail(GDN_ERR_SHAPE, "l2_eps must be >= 0");
+  d->q = q->data; d->k = k->data; d->v = v->data; d->out = out->data;
+  d->g = (const float*)g->data; d->beta = (const float*)beta->data; d->state = (float*)state->data;
+  d->q_st = q->stride[0]; d->q_sh = q->stride[1];
+  d->k_st = k->stride[0]; d->k_sh = k->stride[1];
+  d->v_st = v->stride[0]; d->v_sh = v->stride[1];
+  d->o_st = out->stride[0]; d->o_sh = out->stride[1];
+  d->g_st = g->stride[0]; d->g_sh = g->stride[1];
+  d->b_st = beta->stride[0]; d->b_sh = beta->stride[1];
+  d->n = (int32_t)N; d->hk = (int32_t)hk; d->hv = (int32_t)hv; d->dv = (int32_t)dv;
+  d->scale = o.scale; d->eps = o.l2_eps;
+  *bf16 = q->dtype == GDN_DTYPE_BF16;
+  *dk = (int)dkk;
+  return GDN_OK;
+}
+
 int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
         const gdn_tensor* v, const gdn_tensor* g, const gdn_tensor* beta,
         const gdn_tensor* cu, const gdn_tensor* init, gdn_tensor* out,
@@ -451,6 +517,21 @@ int gdn_prefill(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
     if (rc == GDN_OK && e != hipSuccess) rc = fail(GDN_ERR_HIP, "workspace release: %s", hipGetErrorString(e));
   }
   return rc;
+}
+
+int gdn_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
+               const gdn_tensor* g, const gdn_tensor* beta, gdn_tensor* state,
+               gdn_tensor* out, const gdn_options* opts, void* stream) {
+  gdn::DecodeParams d{};
+  bool bf16 = true;
+  int dk = 0;
+  const int rc = validate_decode(q, k, v, g, beta, state, out, opts, &d, &bf16, &dk);
+  if (rc) return rc;
+  g_last_error.clear();
+  if (d.n == 0) return GDN_OK;
+  const hipError_t e = gdn::launch_decode(bf16, dk, d, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return GDN_OK;
 }
 
 }  // extern "C"

@@ -68,4 +68,19 @@ struct ScanParams {
   Intermediates im;
 };
 
+// One recurrent step per sequence (decode).
+struct DecodeParams {
+  const void* q;         // [N, Hk, dk] strides q_st, q_sh
+  const void* k;
+  const void* v;         // [N, Hv, dv]
+  const float* g;        // [N, Hv] strides g_st, g_sh
+  const float* beta;
+  float* state;          // [N, Hv, dk, dv], read and written in place
+  void* out;             // [N, Hv, dv] strides o_st, o_sh
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;
+  int64_t g_st, g_sh, b_st, b_sh;
+  int32_t n, hk, hv, dv;
+  float scale, eps;
+};
+
 }  // namespace gdn

@@ -1017,6 +1017,98 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// decode: one token per sequence
+//
+// The same recurrence for a single token, applied to a state carried in
+// memory (the step a generator runs after the prefill):
+//   H <- exp(g) (I - beta k^ k^T) H + beta k^ v^T,   out = scale H^T q^.
+// It reads and writes the whole fp32 state once, so it is bound by HBM: one
+// workgroup per (sequence, value head, slice of up to 64 columns), each
+// thread holding DK / (256 / cols) rows of one column in registers.  The
+// two contractions over d_k (k^T H before the update, q^T H after it) are
+// reduced across the row groups through LDS.  Everything is fp32.
+
+constexpr int kDecodeThreads = 256;
+
+template <typename TI, int DK>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) {
+  constexpr int NT = kDecodeThreads;
+  constexpr int MAXR = DK / 4;  // rows per thread when a slice has 64 columns
+  __shared__ float sq[DK], sk[DK], sred[NT], snorm[2];
+  const int tid = threadIdx.x;
+  const int cols = p.dv < 64 ? p.dv : 64;
+  const int ngrp = NT / cols;            // row groups
+  const int rpt = DK / ngrp;             // rows per thread (<= MAXR)
+  const int n_sl = p.dv / cols;
+  const int u = blockIdx.x / n_sl, sl = blockIdx.x % n_sl;
+  if (u >= p.n * p.hv) return;
+  const int i = u / p.hv, h = u % p.hv, kh = h / (p.hv / p.hk);
+  const int col = tid % cols, grp = tid / cols;
+  const int j = sl * cols + col;         // this thread's state column
+
+  // q and k rows and their inverse norms
+  const TI* qr = (const TI*)p.q + (int64_t)i * p.q_st + (int64_t)kh * p.q_sh;
+  const TI* kr = (const TI*)p.k + (int64_t)i * p.k_st + (int64_t)kh * p.k_sh;
+  for (int d = tid; d < DK; d += NT) {
+    sq[d] = to_float(qr[d]);
+    sk[d] = to_float(kr[d]);
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const float* src = tid < 64 ? sq : sk;
+    const int l = tid & 63;
+    float s2 = 0.f;
+    for (int d = l; d < DK; d += 64) s2 += src[d] * src[d];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s2 += __shfl_xor(s2, off);
+    if (l == 0) snorm[tid >> 6] = 1.0f / sqrtf(s2 + p.eps);
+  }
+  __syncthreads();
+  const float rq = snorm[0], rk = snorm[1];
+  const float g = p.g[(int64_t)i * p.g_st + (int64_t)h * p.g_sh];
+  const float beta = p.beta[(int64_t)i * p.b_st + (int64_t)h * p.b_sh];
+  const float alpha = expf(g);
+  const float vj = to_float(((const TI*)p.v)[(int64_t)i * p.v_st + (int64_t)h * p.v_sh + j]);
+
+  // this thread's rows r = grp * rpt .. + rpt - 1 of column j
+  float* Hc = p.state + ((int64_t)i * p.hv + h) * DK * p.dv + j;
+  const int r0 = grp * rpt;
+  float hreg[MAXR];
+  float part = 0.f;
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r) {
+    if (r < rpt) {
+      hreg[r] = Hc[(int64_t)(r0 + r) * p.dv];
+      part += sk[r0 + r] * hreg[r];
+    }
+  }
+  sred[tid] = part;
+  __syncthreads();
+  float kth = 0.f;  // (k^T H)_j with the raw k; the norm is applied below
+  for (int gq = 0; gq < ngrp; ++gq) kth += sred[gq * cols + col];
+  kth *= rk;
+  __syncthreads();
+  // H' = alpha (H - beta k^ (k^T H)) + beta k^ v^T, and q^T H'
+  part = 0.f;
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r) {
+    if (r < rpt) {
+      const float kh_r = sk[r0 + r] * rk;
+      const float hn = alpha * (hreg[r] - beta * kh_r * kth) + beta * kh_r * vj;
+      Hc[(int64_t)(r0 + r) * p.dv] = hn;
+      part += sq[r0 + r] * hn;
+    }
+  }
+  sred[tid] = part;
+  __syncthreads();
+  if (grp == 0) {
+    float o = 0.f;
+    for (int gq = 0; gq < ngrp; ++gq) o += sred[gq * cols + col];
+    ((TI*)p.out)[(int64_t)i * p.o_st + (int64_t)h * p.o_sh + j] = from_float<TI>(p.scale * rq * o);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dispatch
 
 // fp32 inputs are built for chunks of 16 and 32 only (their WY tiles at 64
@@ -1096,6 +1188,20 @@ hipError_t launch_scan(bool bf16, int chunk, int dk, const ScanParams& p,
                       : dispatch_c<float>(chunk, dk, 1, nullptr, &p, grid, s);
   if (rc) return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_decode(bool bf16, int dk, const DecodeParams& p, hipStream_t s) {
+  const int cols = p.dv < 64 ? p.dv : 64;
+  const dim3 grid((unsigned)((int64_t)p.n * p.hv * (p.dv / cols)));
+#define GDN_DECODE(D)                                                                       \
+  if (dk == D) {                                                                           \
+    if (bf16) hipLaunchKernelGGL((decode_kernel<gdn::bf16, D>), grid, dim3(kDecodeThreads), 0, s, p); \
+    else hipLaunchKernelGGL((decode_kernel<float, D>), grid, dim3(kDecodeThreads), 0, s, p);          \
+    return hipGetLastError();                                                              \
+  }
+  GDN_DECODE(16) GDN_DECODE(32) GDN_DECODE(64) GDN_DECODE(128)
+#undef GDN_DECODE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace gdn

@@ -17,4 +17,6 @@ hipError_t launch_wy(bool bf16, int chunk, int dk, const WyParams& p, hipStream_
 hipError_t launch_scan(bool bf16, int chunk, int dk, const ScanParams& p,
                        int grid_x, hipStream_t s);
 
+hipError_t launch_decode(bool bf16, int dk, const DecodeParams& p, hipStream_t s);
+
 }  // namespace gdn

@@ -70,6 +70,11 @@ SPECS = {
                      dv=128, chunk=64, dtype="bf16", g_low=-8.0,
                      beta="three_class", init_std=None, g_zero_frac=0.25,
                      token_offset=1),
+    # decode: one token for each of 256 sequences, 16 heads, d=128, bf16,
+    # against a carried fp32 state (the step after a prefill)
+    "decode_256": dict(lengths=[1] * 256, hk=16, hv=16, dk=128, dv=128,
+                       chunk=64, dtype="bf16", g_low=-1.0, beta="sigmoid_normal",
+                       init_std=0.5, g_zero_frac=0.0, token_offset=0),
 }
 
 

@@ -183,6 +183,26 @@ int gdn_get_workspace_layout(const gdn_tensor* q, const gdn_tensor* k,
                              const gdn_options* opts,
                              gdn_workspace_layout* layout);
 
+/*
+ * gdn_decode -- one recurrent step per sequence: the single-token form of
+ * the same gated delta rule ("Gated Delta Networks", section 3), as a
+ * generator runs it after the prefill, on the state the prefill returned.
+ * For every sequence i and value head h (key head h / (Hv/Hk)):
+ *     H = state[i, h];  H <- exp(g) (I - beta k^ k^T) H + beta k^ v^T;
+ *     out[i, h] = scale * H^T q^;  state[i, h] = H (in place)
+ * with q^, k^ L2-normalised as in gdn_prefill.  Computed in fp32.
+ *   q, k     [N, Hk, dk]; v, out [N, Hv, dv]; one dtype, bf16 or f32; unit
+ *            stride in the last dimension
+ *   g, beta  [N, Hv] f32 (same preconditions as gdn_prefill)
+ *   state    f32 [N, Hv, dk, dv] contiguous, read and written in place
+ *   opts     NULL or options; only scale and l2_eps are used
+ * dk, dv in {16, 32, 64, 128}.  N = 0 enqueues nothing.  Allocates nothing.
+ * Returns a GDN_* status; validation errors enqueue nothing.
+ */
+int gdn_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
+               const gdn_tensor* g, const gdn_tensor* beta, gdn_tensor* state,
+               gdn_tensor* out, const gdn_options* opts, void* stream);
+
 /* Short description of a status code (static storage). */
 const char* gdn_status_string(int status);
 

@@ -155,3 +155,33 @@ def test_binding_refuses_host_tensors(lib):
     g = torch.zeros(64, 1)
     with pytest.raises(ValueError):
         G.gdn_prefill(x, x, x, g, g)
+
+
+def test_decode_validation_errors(lib):
+    """gdn_decode rejects bad arguments before any device work."""
+    N, hk, hv, dk, dv = 3, 2, 4, 64, 32
+    q = fake((N, hk, dk), torch.bfloat16)
+    v = fake((N, hv, dv), torch.bfloat16)
+    g = fake((N, hv), torch.float32)
+    st = fake((N, hv, dk, dv), torch.float32)
+    out = fake((N, hv, dv), torch.bfloat16)
+    r = ctypes.byref
+
+    def dec(q_=q, k_=q, v_=v, g_=g, b_=g, s_=st, o_=out):
+        args = [r(x) if x is not None else None for x in (q_, k_, v_, g_, b_, s_, o_)]
+        return lib.gdn_decode(*args, None, None)
+
+    NULL, DTYPE, SHAPE, LAYOUT, UNSUPPORTED = -1, -2, -3, -4, -5
+    assert dec(q_=None) == NULL
+    assert dec(v_=fake((N, hv, dv), torch.float32)) == DTYPE
+    assert dec(s_=fake((N, hv, dk, dv), torch.bfloat16)) == DTYPE
+    assert dec(k_=fake((N, hk, 32), torch.bfloat16)) == SHAPE
+    assert dec(g_=fake((N, hv + 1), torch.float32)) == SHAPE
+    assert dec(s_=fake((N, hv, dk, dv + 16), torch.float32)) == SHAPE
+    assert dec(q_=fake((N, 3, dk), torch.bfloat16), k_=fake((N, 3, dk), torch.bfloat16)) == SHAPE
+    assert dec(q_=fake((N, hk, 48), torch.bfloat16), k_=fake((N, hk, 48), torch.bfloat16)) == UNSUPPORTED
+    tr = fake((N, hv, dk, dv), torch.float32, strides=(hv * dk * dv, dk * dv, 1, dk))
+    assert dec(s_=tr) == LAYOUT
+    lv = fake((N, hv, dv), torch.bfloat16, strides=(hv * dv * 2, dv * 2, 2))
+    assert dec(v_=lv) == LAYOUT
+    assert G.gdn_last_error() != ""
