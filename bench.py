@@ -167,6 +167,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prompt_4k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the prefill replayed from a captured HIP graph")
     ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill",
                     help="decode: time gdn_decode on --workload (default decode_256)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -276,6 +278,24 @@ def main():
         "kernel_ms": {k: round(v, 5) for k, v in kernels.items()},
         "gpu_event_ms_per_step": t_gpu,
     }
+    if args.graph:
+        # the whole prefill as one replay of a captured graph (same buffers)
+        cache = G.GraphCache()
+        ws = full.workspace
+        def gstep():
+            cache.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, d["init_state"],
+                          d["out"], d["final_state"], opts=opts, workspace=ws)
+        for _ in range(max(1, args.warmup)):
+            gstep()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            gstep()
+        torch.cuda.synchronize()
+        g_ms = (time.perf_counter() - t0) * 1e3 / K
+        result["graph"] = {"ms_per_step": g_ms, "tokens_per_s": w.t_total / (g_ms * 1e-3),
+                           "eager_ms_per_step": ms_step, "cache": cache.stats()}
+        cache.close()
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host cores ...")
         result["cpu_baseline"] = cpu_baseline(w)

@@ -12,4 +12,4 @@ from ._binding import (GdnError, GdnOptions, GdnTensor, GdnWorkspaceLayout,  # n
                        gdn_decode, gdn_last_error, gdn_prefill, gdn_prefill_ex,
                        gdn_status_string, gdn_workspace_size, library_path,
                        options)
-from ._binding import PreparedPrefill  # noqa: F401,E402
+from ._binding import GraphCache, PreparedPrefill  # noqa: F401,E402

@@ -22,7 +22,9 @@ STATUS_NAMES = {0: "GDN_OK", -1: "GDN_ERR_NULL_ARG", -2: "GDN_ERR_DTYPE",
 STAGE_TABLE, STAGE_WY, STAGE_SCAN, STAGE_ALL = 1, 2, 4, 7
 EXPORTED = ("gdn_abi_version", "gdn_default_options", "gdn_prefill",
             "gdn_prefill_ex", "gdn_workspace_size", "gdn_get_workspace_layout",
-            "gdn_decode", "gdn_status_string", "gdn_last_error")
+            "gdn_decode", "gdn_graph_cache_create", "gdn_graph_cache_destroy",
+            "gdn_graph_cache_clear", "gdn_graph_cache_stats", "gdn_prefill_graph",
+            "gdn_status_string", "gdn_last_error")
 
 _DTYPES = {torch.bfloat16: 1, torch.float32: 2, torch.int32: 3}
 
@@ -86,6 +88,18 @@ def lib():
         L.gdn_get_workspace_layout.restype = ctypes.c_int
         L.gdn_decode.argtypes = [T] * 7 + [P(GdnOptions), ctypes.c_void_p]
         L.gdn_decode.restype = ctypes.c_int
+        L.gdn_graph_cache_create.argtypes = [ctypes.c_int, P(ctypes.c_void_p)]
+        L.gdn_graph_cache_create.restype = ctypes.c_int
+        L.gdn_graph_cache_destroy.argtypes = [ctypes.c_void_p]
+        L.gdn_graph_cache_destroy.restype = None
+        L.gdn_graph_cache_clear.argtypes = [ctypes.c_void_p]
+        L.gdn_graph_cache_clear.restype = None
+        L.gdn_graph_cache_stats.argtypes = [ctypes.c_void_p, P(ctypes.c_int), P(ctypes.c_int64),
+                                            P(ctypes.c_int64), P(ctypes.c_int64)]
+        L.gdn_graph_cache_stats.restype = ctypes.c_int
+        L.gdn_prefill_graph.argtypes = [ctypes.c_void_p] + [T] * 9 + [
+            P(GdnOptions), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.gdn_prefill_graph.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_last_error.restype = ctypes.c_char_p
@@ -229,6 +243,51 @@ def gdn_decode(q, k, v, g, beta, state, out=None, opts: Optional[GdnOptions] = N
     _check(lib().gdn_decode(*[_ref(d) for d in ds], ctypes.byref(opts) if opts else None,
                             _stream_handle(stream, v)))
     return out
+
+
+class GraphCache:
+    """A gdn_graph_cache: captured replays of gdn_prefill_ex keyed by all of
+    its arguments (see include/gdn.h).  ``prefill`` takes the arguments of
+    gdn_prefill_ex; the workspace is required."""
+
+    def __init__(self, capacity: int = 64):
+        self._h = ctypes.c_void_p()
+        self._lib = lib()
+        _check(self._lib.gdn_graph_cache_create(capacity, ctypes.byref(self._h)))
+
+    def prefill(self, q, k, v, g, beta, cu_seqlens=None, init_state=None, out=None,
+                final_state=None, opts: Optional[GdnOptions] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None):
+        if out is None:
+            raise ValueError("out is required (it is part of the captured launches)")
+        if workspace is None or workspace.device.type != "cuda":
+            raise ValueError("a GPU workspace is required")
+        ds = _descs(q, k, v, g, beta, cu_seqlens, init_state, out, final_state)
+        _check(self._lib.gdn_prefill_graph(self._h, *[_ref(d) for d in ds],
+                                           ctypes.byref(opts) if opts else None,
+                                           workspace.data_ptr(), workspace.numel(),
+                                           _stream_handle(stream, v)))
+        return out, final_state
+
+    def stats(self) -> dict:
+        n, h, m, f = ctypes.c_int(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(self._lib.gdn_graph_cache_stats(self._h, ctypes.byref(n), ctypes.byref(h),
+                                               ctypes.byref(m), ctypes.byref(f)))
+        return {"entries": n.value, "hits": h.value, "misses": m.value, "fallbacks": f.value}
+
+    def clear(self):
+        self._lib.gdn_graph_cache_clear(self._h)
+
+    def close(self):
+        if self._h:
+            self._lib.gdn_graph_cache_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class PreparedPrefill:

@@ -10,6 +10,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <list>
+#include <mutex>
 #include <string>
 
 #include "gdn.h"
@@ -531,6 +533,161 @@ int gdn_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
   if (d.n == 0) return GDN_OK;
   const hipError_t e = gdn::launch_decode(bf16, dk, d, (hipStream_t)stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return GDN_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Captured replays (HIP graphs) of gdn_prefill_ex.
+
+namespace {
+
+struct GraphEntry {
+  std::string key;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+void release(GraphEntry& e) {
+  if (e.exec) (void)hipGraphExecDestroy(e.exec);
+  if (e.graph) (void)hipGraphDestroy(e.graph);
+  e.exec = nullptr;
+  e.graph = nullptr;
+}
+
+void append(std::string& k, const void* p, size_t n) { k.append((const char*)p, n); }
+
+void append_tensor(std::string& k, const gdn_tensor* t) {
+  const int32_t none = -1;
+  if (!t) {
+    append(k, &none, sizeof none);
+    return;
+  }
+  append(k, &t->data, sizeof t->data);
+  append(k, &t->dtype, sizeof t->dtype);
+  append(k, &t->ndim, sizeof t->ndim);
+  append(k, t->shape, sizeof(int64_t) * (size_t)(t->ndim > 0 && t->ndim <= 4 ? t->ndim : 0));
+  append(k, t->stride, sizeof(int64_t) * (size_t)(t->ndim > 0 && t->ndim <= 4 ? t->ndim : 0));
+}
+
+}  // namespace
+
+struct gdn_graph_cache {
+  std::mutex mu;
+  int capacity = 64;
+  std::list<GraphEntry> entries;  // most recently used first
+  int64_t hits = 0, misses = 0, fallbacks = 0;
+};
+
+extern "C" {
+
+int gdn_graph_cache_create(int capacity, gdn_graph_cache** cache) {
+  if (!cache) return fail(GDN_ERR_NULL_ARG, "cache pointer is NULL");
+  if (capacity < 1 || capacity > 4096) return fail(GDN_ERR_SHAPE, "capacity must be 1..4096");
+  gdn_graph_cache* c = new (std::nothrow) gdn_graph_cache;
+  if (!c) return fail(GDN_ERR_HIP, "out of host memory");
+  c->capacity = capacity;
+  *cache = c;
+  return GDN_OK;
+}
+
+void gdn_graph_cache_destroy(gdn_graph_cache* cache) {
+  if (!cache) return;
+  for (auto& e : cache->entries) release(e);
+  delete cache;
+}
+
+void gdn_graph_cache_clear(gdn_graph_cache* cache) {
+  if (!cache) return;
+  std::lock_guard<std::mutex> lock(cache->mu);
+  for (auto& e : cache->entries) release(e);
+  cache->entries.clear();
+}
+
+int gdn_graph_cache_stats(gdn_graph_cache* cache, int* entries, int64_t* hits,
+                          int64_t* misses, int64_t* fallbacks) {
+  if (!cache) return fail(GDN_ERR_NULL_ARG, "cache is NULL");
+  std::lock_guard<std::mutex> lock(cache->mu);
+  if (entries) *entries = (int)cache->entries.size();
+  if (hits) *hits = cache->hits;
+  if (misses) *misses = cache->misses;
+  if (fallbacks) *fallbacks = cache->fallbacks;
+  return GDN_OK;
+}
+
+int gdn_prefill_graph(gdn_graph_cache* cache, const gdn_tensor* q, const gdn_tensor* k,
+                      const gdn_tensor* v, const gdn_tensor* g, const gdn_tensor* beta,
+                      const gdn_tensor* cu_seqlens, const gdn_tensor* init_state,
+                      gdn_tensor* out, gdn_tensor* final_state, const gdn_options* opts,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cache) return fail(GDN_ERR_NULL_ARG, "cache is NULL");
+  Problem P;
+  int rc = validate(q, k, v, g, beta, cu_seqlens, init_state, out, final_state, opts, true, &P);
+  if (rc) return rc;
+  const size_t need = make_layout(P).total;
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if ((uintptr_t)workspace % kAlign) return fail(GDN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  g_last_error.clear();
+  hipStream_t s = (hipStream_t)stream;
+
+  // The key: every argument the launches depend on.  The kernels read the
+  // sequence lengths from device memory, so a capture stays valid for any
+  // lengths with the same shapes and buffers.
+  std::string key;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  append(key, &dev, sizeof dev);
+  const gdn_tensor* ts[9] = {q, k, v, g, beta, cu_seqlens, init_state, out, final_state};
+  for (const gdn_tensor* t : ts) append_tensor(key, t);
+  gdn_options o;
+  gdn_default_options(&o);
+  if (opts) o = *opts;
+  append(key, &o, sizeof o);
+  append(key, &workspace, sizeof workspace);
+  append(key, &workspace_bytes, sizeof workspace_bytes);
+
+  std::lock_guard<std::mutex> lock(cache->mu);
+  for (auto it = cache->entries.begin(); it != cache->entries.end(); ++it) {
+    if (it->key == key) {
+      cache->entries.splice(cache->entries.begin(), cache->entries, it);
+      ++cache->hits;
+      const hipError_t e = hipGraphLaunch(cache->entries.front().exec, s);
+      if (e != hipSuccess) return fail(GDN_ERR_HIP, "graph launch: %s", hipGetErrorString(e));
+      return GDN_OK;
+    }
+  }
+  ++cache->misses;
+  // Capture on a private stream (the caller's may be the null stream, which
+  // cannot be captured), then launch on the caller's.
+  GraphEntry ent;
+  ent.key = key;
+  hipStream_t cs = nullptr;
+  bool ok = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) == hipSuccess;
+  if (ok) ok = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) == hipSuccess;
+  if (ok) {
+    const int rrc = run(P, q, k, v, g, beta, cu_seqlens, init_state, out, final_state, workspace, cs);
+    const hipError_t ec = hipStreamEndCapture(cs, &ent.graph);
+    ok = rrc == GDN_OK && ec == hipSuccess && ent.graph != nullptr;
+  }
+  if (ok) ok = hipGraphInstantiate(&ent.exec, ent.graph, nullptr, nullptr, 0) == hipSuccess;
+  if (cs) (void)hipStreamDestroy(cs);
+  if (!ok) {
+    // fall back to the eager launches
+    release(ent);
+    (void)hipGetLastError();
+    ++cache->fallbacks;
+    g_last_error.clear();
+    return run(P, q, k, v, g, beta, cu_seqlens, init_state, out, final_state, workspace, s);
+  }
+  const hipError_t e = hipGraphLaunch(ent.exec, s);
+  cache->entries.push_front(ent);
+  while ((int)cache->entries.size() > cache->capacity) {
+    release(cache->entries.back());
+    cache->entries.pop_back();
+  }
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "graph launch: %s", hipGetErrorString(e));
   return GDN_OK;
 }
 

@@ -203,6 +203,40 @@ int gdn_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
                const gdn_tensor* g, const gdn_tensor* beta, gdn_tensor* state,
                gdn_tensor* out, const gdn_options* opts, void* stream);
 
+/*
+ * Captured replays.  gdn_prefill_graph behaves as gdn_prefill_ex, but keeps
+ * a HIP graph of the launches in `cache`, keyed by every argument (device,
+ * tensor descriptors including data pointers, options, workspace pointer and
+ * size).  A miss captures the launches on a private stream (stream capture),
+ * instantiates the graph and launches it on `stream`; a hit only launches
+ * the stored graph, which removes the per-kernel launch cost.  If capture or
+ * instantiation fails the call runs the launches eagerly (and counts a
+ * fallback).  The sequence lengths are read from cu_seqlens on the device by
+ * the kernels themselves, so one capture stays valid for any lengths with
+ * the same shapes and buffers (the serving pages key their captures by the
+ * length tuple: "Cua-S1 4B 0.2 native text worker"; "Open-Jev-27B-v1.1
+ * native text worker", section "Build and serve").  The cache holds at most
+ * `capacity` graphs and drops the least recently used.  Buffers named by a
+ * stored graph must stay allocated while it may be replayed: call
+ * gdn_graph_cache_clear after freeing or growing any of them.  A cache may be
+ * shared by threads (calls are serialised); entries of one cache must not be
+ * replayed on overlapping streams with the same workspace.
+ */
+typedef struct gdn_graph_cache gdn_graph_cache;
+
+int gdn_graph_cache_create(int capacity, gdn_graph_cache** cache);
+void gdn_graph_cache_destroy(gdn_graph_cache* cache);
+void gdn_graph_cache_clear(gdn_graph_cache* cache);
+int gdn_graph_cache_stats(gdn_graph_cache* cache, int* entries, int64_t* hits,
+                          int64_t* misses, int64_t* fallbacks);
+int gdn_prefill_graph(gdn_graph_cache* cache, const gdn_tensor* q,
+                      const gdn_tensor* k, const gdn_tensor* v,
+                      const gdn_tensor* g, const gdn_tensor* beta,
+                      const gdn_tensor* cu_seqlens, const gdn_tensor* init_state,
+                      gdn_tensor* out, gdn_tensor* final_state,
+                      const gdn_options* opts, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Short description of a status code (static storage). */
 const char* gdn_status_string(int status);
 

@@ -185,3 +185,31 @@ def test_decode_validation_errors(lib):
     lv = fake((N, hv, dv), torch.bfloat16, strides=(hv * dv * 2, dv * 2, 2))
     assert dec(v_=lv) == LAYOUT
     assert G.gdn_last_error() != ""
+
+
+def test_graph_cache_host_side(lib):
+    """Create / stats / clear / destroy need no device; bad arguments are
+    rejected before any capture."""
+    cache = ctypes.c_void_p()
+    assert lib.gdn_graph_cache_create(0, ctypes.byref(cache)) == -3
+    assert lib.gdn_graph_cache_create(4, None) == -1
+    assert lib.gdn_graph_cache_create(4, ctypes.byref(cache)) == 0
+    n, h, m, f = ctypes.c_int(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    assert lib.gdn_graph_cache_stats(cache, ctypes.byref(n), ctypes.byref(h), ctypes.byref(m),
+                                     ctypes.byref(f)) == 0
+    assert (n.value, h.value, m.value, f.value) == (0, 0, 0, 0)
+    a = base()
+    r = ctypes.byref
+    # a bad argument: missing workspace
+    rc = lib.gdn_prefill_graph(cache, r(a["q"]), r(a["k"]), r(a["v"]), r(a["g"]), r(a["b"]),
+                               None, None, r(a["out"]), None, None, None, 0, None)
+    assert rc == -6, G.gdn_last_error()
+    # a bad shape
+    a["g"] = fake((128, 2), torch.float32)
+    rc = lib.gdn_prefill_graph(cache, r(a["q"]), r(a["k"]), r(a["v"]), r(a["g"]), r(a["b"]),
+                               None, None, r(a["out"]), None, None, None, 0, None)
+    assert rc == -3
+    assert lib.gdn_prefill_graph(None, r(a["q"]), r(a["k"]), r(a["v"]), r(a["g"]), r(a["b"]),
+                                 None, None, r(a["out"]), None, None, None, 0, None) == -1
+    lib.gdn_graph_cache_clear(cache)
+    lib.gdn_graph_cache_destroy(cache)
