@@ -430,8 +430,21 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   f32x4 acc_gs[1][NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc_gs[0][j] = zero4();
+  if (g_wave) {
+    // K K^T row tile rt against every column tile
+    mma_block_sw<1, NB, DK, SWK, SWK>(acc_gs, sKV, LK, 16 * rt, sKV, LK, 0, lane);
+  } else if (s_wave) {
+    // (Q K^T)^T = K Q^T: column tile rt of Q K^T, as the row tiles of its
+    // transpose, so that each lane later holds four consecutive keys of
+    // one query row
+    f32x4 acc_t[NB][1];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc_t[j][0] = zero4();
+    mma_block_sw<NB, 1, DK, SWK, SWK>(acc_t, sKV, LK, 0, sQ, LK, 16 * rt, lane);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc_gs[0][j] = acc_t[j][0];
+  }
   if (g_wave || s_wave) {
-    mma_block_sw<1, NB, DK, SWK, SWK>(acc_gs, g_wave ? sKV : sQ, LK, 16 * rt, sKV, LK, 0, lane);
 #pragma unroll
     for (int j = 0; j < NB; ++j) settle(acc_gs[0][j]);
   }
@@ -489,17 +502,21 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     // (only the strictly lower part is ever read).
     transpose_sw<TI, NT, SWV, SWC>(sVr, LV, sKV, LC, C, DV, tid);
     if (g_wave) {
+      // The Gram tile (rt, j) read transposed (K K^T is symmetric): lane
+      // holds rows r = 16 j + lane % 16 (tiles j >= rt) and the four
+      // consecutive columns c = 16 rt + 4 (lane / 16) + e.
+      const int c0 = 16 * rt + (lane >> 4) * 4;
+      const f32x4 gc = *(const f32x4*)(sGam + c0), rkc = *(const f32x4*)(sRk + c0);
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        if (j > rt) continue;
-        const int col = 16 * j + (lane & 15);
-        const float gc = sGam[col], rkc = sRk[col];
+        if (j < rt) continue;
+        const int r = 16 * j + (lane & 15);
+        const float br = sBeta[r] * sRk[r], gr = sGam[r];
+        f32x4 a;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 16 * rt + (lane >> 4) * 4 + e;
-          if (col < row)
-            sA[row * LF + col] = sBeta[row] * sRk[row] * rkc * fast_exp(sGam[row] - gc) * acc_gs[0][j][e];
-        }
+        for (int e = 0; e < 4; ++e)
+          a[e] = (c0 + e < r) ? br * rkc[e] * fast_exp(gr - gc[e]) * acc_gs[0][j][e] : 0.f;
+        *(f32x4*)(sA + r * LF + c0) = a;
       }
     }
     __syncthreads();
@@ -570,17 +587,19 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       }
     }
     if (s_wave) {
+      // (Q K^T)^T tiles: lane holds query row r = 16 rt + lane % 16 and the
+      // four consecutive keys s = 16 j + 4 (lane / 16) + e.
+      const int r = 16 * rt + (lane & 15);
+      const float qr = p.scale * sRq[r], gr = sGam[r];
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int col = 16 * j + (lane & 15);
-        const float gc = sGam[col], rkc = sRk[col];
+        const int s0 = 16 * j + (lane >> 4) * 4;
+        const f32x4 gs = *(const f32x4*)(sGam + s0), rks = *(const f32x4*)(sRk + s0);
+        f32x4 pv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 16 * rt + (lane >> 4) * 4 + e;
-          const float pv = (col <= row)
-              ? p.scale * sRq[row] * rkc * fast_exp(sGam[row] - gc) * acc_gs[0][j][e] : 0.f;
-          sP[row * LC + swz<TI, SWC>(row, col)] = from_float<TI>(pv);
-        }
+        for (int e = 0; e < 4; ++e)
+          pv[e] = (s0 + e <= r) ? qr * rks[e] * fast_exp(gr - gs[e]) * acc_gs[0][j][e] : 0.f;
+        store4<TI>(sP + r * LC + swz<TI, SWC>(r, s0), pv[0], pv[1], pv[2], pv[3]);
       }
     }
     __syncthreads();
