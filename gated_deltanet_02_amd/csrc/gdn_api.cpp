@@ -410,7 +410,8 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
     sp.final_state = fin ? (float*)fin->data : nullptr;
     sp.hv = P.hv;
     sp.dv = P.dv;
-    sp.n_slices = P.dv / 16;
+    sp.nsl = gdn::scan_slices_per_group(P.bf16, P.chunk, P.dk, P.dv, (int64_t)P.n_seq * P.hv);
+    sp.n_slices = P.dv / (16 * sp.nsl);
     sp.map = map;
     sp.im = im;
     const int64_t blocks = ((int64_t)P.n_seq * P.hv + 7) / 8 * 8 * sp.n_slices;

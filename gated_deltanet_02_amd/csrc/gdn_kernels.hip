@@ -42,6 +42,8 @@
 // only formed for s <= r and never factored into exp(gamma_r) exp(-gamma_s).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_launch.h"
@@ -708,41 +710,54 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
 // ---------------------------------------------------------------------------
 // state scan fused with the output
 //
-// One workgroup per (sequence, value head, 16-column slice of d_v), four
-// waves with fixed roles:
-//   wave 0  the recurrence: U = U~ - W H and H <- e^gamma_last H + K~^T U,
-//           with the state slice in its MFMA accumulators; at the start of
-//           each chunk it leaves -H (as bf16 / fp32 operand units) in LDS;
-//   wave 1  the output, one chunk behind: O = Q' H + O_loc from Q' held in
-//           registers since the previous chunk, off the recurrence's
-//           critical path;
-//   waves 2, 3 copy each chunk's W, Q', K~^T, U~ slice and decay from
-//           global memory into a ring of LDS stages with LDS-direct loads
-//           (no registers), `lead` chunks ahead.
-// One barrier per chunk hands a stage (and the H copy) over.
+// One workgroup per (sequence, value head, group of NSL 16-column slices of
+// d_v), 2 NSL + 2 waves with fixed roles:
+//   wave s < NSL       the recurrence of slice s: U = U~ - W H and
+//                      H <- e^gamma_last H + K~^T U, with the state slice in
+//                      its MFMA accumulators; at the start of each chunk it
+//                      leaves -H (as bf16 / fp32 operand units) in LDS;
+//   wave NSL + s       the output of slice s, one chunk behind:
+//                      O = Q' H + O_loc from Q' held in registers since the
+//                      previous chunk, off the recurrence's critical path;
+//   the last two waves copy each chunk's W, Q' and K~^T (one slice: also its
+//                      U~ tiles and the decay) from global memory into a ring
+//                      of LDS stages with LDS-direct loads (no registers),
+//                      `lead` chunks ahead.
+// One barrier per chunk hands a stage (and the H copies) over.  With more
+// than one slice the recurrence waves take their U~ tiles and the decay into
+// registers, two chunks ahead.
+//
+// A wave reads LDS at about half of what its SIMD's LDS port delivers, and
+// the recurrence of one slice reads 32 KiB of W and K~^T per chunk, so its
+// chunk step is bound by that wave's reads, not by its MFMAs.  Slices of one
+// workgroup share the ring's copies and run on separate SIMDs: two slices
+// cost the compute unit about what one does.
 
 constexpr int kScanCopyWaves = 2;
 
-template <typename TI, int C, int DK>
+template <typename TI, int C, int DK, int NSL>
 struct ScanRing {
   static constexpr int S = sizeof(TI);
   static constexpr int BIG = C * DK * S;            // W, Q', K~^T of one chunk
-  static constexpr int SMALL = C * 16 * S;          // U~ / O_loc tiles of one slice
+  static constexpr int SMALL = C * 16 * S;          // U~ tiles of one slice
+  static constexpr bool UTR = NSL == 1;             // U~ and the decay staged too
   static constexpr int w = 0, qp = BIG, kt = 2 * BIG, ut = 3 * BIG;
   static constexpr int dec = ut + SMALL;            // e^gamma_last (4 bytes)
-  static constexpr int stage = dec + 16;
-  static constexpr int HB = KTile<TI, DK>::NU * 1024;  // H as operand units
-  static constexpr int room = (kLdsLimit - 2 * HB) / stage;
+  static constexpr int stage = UTR ? dec + 16 : 3 * BIG;
+  static constexpr int HB = KTile<TI, DK>::NU * 1024;  // -H of one slice as operand units
+  static constexpr int room = (kLdsLimit - 2 * NSL * HB) / stage;
   static constexpr int slots = room < 4 ? room : 4;
   static constexpr int lead = slots - 1;
-  static constexpr int hbuf = slots * stage;        // two H buffers
-  static constexpr int total = hbuf + 2 * HB;
+  static constexpr int hbuf = slots * stage;        // two H buffers per slice
+  static constexpr int total = hbuf + 2 * NSL * HB;
   // 1 KiB copies per stage (the last of a region may be 512 bytes), plus
   // one 4-byte copy of the decay
   static constexpr int PB = (BIG + 1023) / 1024, PS = (SMALL + 1023) / 1024;
-  static constexpr int pieces = 3 * PB + PS + 1;
+  static constexpr int pieces = 3 * PB + (UTR ? PS + 1 : 0);
   static constexpr int per_wave = (pieces + kScanCopyWaves - 1) / kScanCopyWaves;
   static_assert(slots < 2 || per_wave * lead <= 63, "loads in flight exceed the wave's counter");
+  // slice s's copy b of -H
+  static constexpr int hcopy(int s, int b) { return hbuf + (2 * s + b) * HB; }
 };
 
 // Workgroup barrier that the compiler may not move memory accesses across;
@@ -764,19 +779,18 @@ __host__ __device__ constexpr int lgkmcnt0_imm() { return 15 | (3 << 14) | (7 <<
 // bytes per lane.  Indices beyond the stage repeat its last piece (same
 // bytes, same place), so that every copying wave issues exactly per_wave
 // loads per stage.  All piece indices are compile-time constants.
-template <typename TI, int C, int DK, int CW>
+template <typename R, int C, int CW>
 __device__ __forceinline__ void ring_copy(char* stage, const ScanParams& p, int cc, int h,
-                                          int sl, int lane) {
-  using R = ScanRing<TI, C, DK>;
+                                          int ctile, int lane) {
   constexpr int NB = C / 16;
   const int64_t blk = (int64_t)cc * p.hv + h;
-  const int64_t big = blk * R::BIG, small = (blk * C * p.dv + (int64_t)sl * NB * 256) * R::S;
+  const int64_t big = blk * R::BIG, small = (blk * C * p.dv + (int64_t)ctile * NB * 256) * R::S;
   const char* bases[4] = {(const char*)p.im.w + big, (const char*)p.im.qp + big,
                           (const char*)p.im.kt + big, (const char*)p.im.ut + small};
 #pragma unroll
   for (int j = 0; j < R::per_wave; ++j) {
     const int i = min(CW + kScanCopyWaves * j, R::pieces - 1);
-    if (i == R::pieces - 1) {
+    if (R::UTR && i == R::pieces - 1) {
       if (lane == 0)
         __builtin_amdgcn_global_load_lds((const void*)(p.im.decay + blk),
                                          (__attribute__((address_space(3))) void*)(stage + R::dec),
@@ -798,19 +812,18 @@ __device__ __forceinline__ void ring_copy(char* stage, const ScanParams& p, int 
 // Copying wave CW: fills the first `lead` stages, then one stage per chunk,
 // and meets the other waves at one barrier per chunk once the stage they
 // need next has landed.  Loads past the last chunk re-read it.
-template <typename TI, int C, int DK, int CW>
+template <typename R, int C, int CW>
 __device__ __forceinline__ void ring_producer(char* smem, const ScanParams& p, int c_begin,
-                                              int c_end, int h, int sl, int lane) {
-  using R = ScanRing<TI, C, DK>;
+                                              int c_end, int h, int ctile, int lane) {
   const int last = c_end - 1;
 #pragma unroll
   for (int k = 0; k < R::lead; ++k)
-    ring_copy<TI, C, DK, CW>(smem + k * R::stage, p, min(c_begin + k, last), h, sl, lane);
+    ring_copy<R, C, CW>(smem + k * R::stage, p, min(c_begin + k, last), h, ctile, lane);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::per_wave * (R::lead - 1)));
   ring_barrier();
   int slot = R::lead;
   for (int cc = c_begin; cc < c_end; ++cc) {
-    ring_copy<TI, C, DK, CW>(smem + slot * R::stage, p, min(cc + R::lead, last), h, sl, lane);
+    ring_copy<R, C, CW>(smem + slot * R::stage, p, min(cc + R::lead, last), h, ctile, lane);
     slot = slot + 1 == R::slots ? 0 : slot + 1;
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::per_wave * (R::lead - 1)));
     ring_barrier();
@@ -831,127 +844,116 @@ __device__ __forceinline__ void state_units(UT* hb, const f32x4* hacc) {
   }
 }
 
-template <typename TI, int C, int DK>
-__global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
-  using R = ScanRing<TI, C, DK>;
+// The output wave of slice s (column tile ctile), one chunk behind the
+// recurrence: during chunk i it reads Q'_i (LDS) and O_loc_i (global) into
+// registers and forms
+//   O_{i-1}^T = O_loc^T - (-H_{i-1})^T Q'^T
+// with -H_{i-1} as the recurrence wave left it in LDS during chunk i - 1.
+// Lane holds row 16 rt + lane % 16, columns 16 ctile + 4 (lane / 16) + 0..3.
+template <typename TI, int C, int DK, int NSL>
+__device__ __forceinline__ void scan_output(char* smem, const ScanParams& p, int h, int s,
+                                            int ctile, int c_begin, int nch, int tok0,
+                                            int tok_end, int lane) {
+  using R = ScanRing<TI, C, DK, NSL>;
+  using KD = KTile<TI, DK>;
+  using UT = typename Unit<TI>::type;
+  typedef typename Raw4<TI>::type RT;
+  constexpr int NB = C / 16;
+  constexpr int S = R::S;
+  const int DV = p.dv;
+  TI* outg = (TI*)p.out;
+  struct OBuf {
+    UT q[NB][KD::NU];
+    RT ol[NB];
+  };
+  auto fetch = [&](OBuf& o, int i, int slot) {
+    const char* st = smem + slot * R::stage;
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+      for (int q = 0; q < KD::NU; ++q) {
+        const char* qu = st + R::qp + rt * 16 * DK * S + q * KD::UNIT * S;
+        o.q[rt][q] = (KD::HALF_TAIL && q == KD::NU - 1) ? lds_unit<TI, true>(qu, lane)
+                                                        : lds_unit<TI, false>(qu, lane);
+      }
+    const TI* src = (const TI*)p.im.oloc + ((int64_t)(c_begin + i) * p.hv + h) * C * DV +
+                    (int64_t)ctile * NB * 256 + lane * 4;
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) o.ol[rt] = load_raw4<TI>(src + rt * 256);
+  };
+  auto emit = [&](const OBuf& o, int i) {
+    const char* hsrc = smem + R::hcopy(s, i & 1);
+    UT ha[KD::NU];
+#pragma unroll
+    for (int q = 0; q < KD::NU; ++q) ha[q] = lds_unit<TI, false>(hsrc + q * 1024, lane);
+    f32x4 ao[NB];
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) ao[rt] = zero4();
+#pragma unroll
+    for (int q = 0; q < KD::NU; ++q)
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        if (KD::HALF_TAIL && q == KD::NU - 1) mma_unit<true>(ao[rt], ha[q], o.q[rt][q]);
+        else mma_unit<false>(ao[rt], ha[q], o.q[rt][q]);
+      }
+    const int tok = tok0 + i * C;
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) {
+      settle(ao[rt]);
+      const f32x4 ol = raw4_to_f32<TI>(o.ol[rt]);
+      const int r = 16 * rt + (lane & 15);
+      if (r < tok_end - tok)
+        store4<TI>(outg + (int64_t)(tok + r) * p.o_st + (int64_t)h * p.o_sh + 16 * ctile + (lane >> 4) * 4,
+                   ol[0] - ao[rt][0], ol[1] - ao[rt][1], ol[2] - ao[rt][2], ol[3] - ao[rt][3]);
+    }
+  };
+  auto iter = [&](OBuf& cur, const OBuf& prev, int i, int& slot) {
+    fetch(cur, i, slot);
+    if (i > 0) emit(prev, i - 1);
+    slot = slot + 1 == R::slots ? 0 : slot + 1;
+    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+    ring_barrier();
+  };
+  OBuf oa, ob;
+  ring_barrier();
+  int slot = 0, i = 0;
+  for (; i + 1 < nch; i += 2) {
+    iter(oa, ob, i, slot);
+    iter(ob, oa, i + 1, slot);
+  }
+  if (i < nch) {
+    iter(oa, ob, i, slot);
+    emit(oa, nch - 1);
+  } else {
+    emit(ob, nch - 1);
+  }
+}
+
+// The recurrence wave of slice s (column tile ctile).  hacc[t] holds rows
+// 16 t + 4 (lane / 16) + e of the state slice, column 16 ctile + lane % 16.
+template <typename TI, int C, int DK, int NSL>
+__device__ __forceinline__ void scan_recurrence(char* smem, const ScanParams& p, int seq, int h,
+                                                int s, int ctile, int c_begin, int c_end,
+                                                int lane) {
+  using R = ScanRing<TI, C, DK, NSL>;
   using KD = KTile<TI, DK>;
   using KC = KTile<TI, C>;
   using UT = typename Unit<TI>::type;
+  typedef typename Raw4<TI>::type RT;
   constexpr int NB = C / 16, NKT = DK / 16;
   constexpr int S = R::S;
-  __shared__ __attribute__((aligned(1024))) char smem[R::total];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int NS = p.n_slices;
-  // XCD-aware: the slices of one (sequence, head) share blockIdx % 8 and so
-  // land on the same XCD, where they share W, Q' and K~^T through its L2.
-  const int b = blockIdx.x;
-  const int u = (b / (8 * NS)) * 8 + (b % 8);
-  const int sl = (b / 8) % NS;
-  if (u >= p.map.n_seq * p.hv) return;
-  const int seq = u / p.hv, h = u % p.hv;
   const int DV = p.dv;
-  const int dv0 = 16 * sl;
-  int c_begin, c_end, tok0, tok_end;
-  seq_range(p.map, seq, C, c_begin, c_end, tok0, tok_end);
   const int nch = c_end - c_begin;
-
-  if (wave >= 2) {
-    if (nch <= 0) return;
-    if (wave == 2) ring_producer<TI, C, DK, 0>(smem, p, c_begin, c_end, h, sl, lane);
-    else ring_producer<TI, C, DK, 1>(smem, p, c_begin, c_end, h, sl, lane);
-    return;
-  }
-
-  if (wave == 1) {
-    // The output, one chunk behind the recurrence: during chunk i it reads
-    // Q'_i (LDS) and O_loc_i (global) into registers and forms
-    //   O_{i-1}^T = O_loc^T - (-H_{i-1})^T Q'^T
-    // with -H_{i-1} as wave 0 left it in LDS during chunk i - 1.  Lane holds
-    // row 16 rt + lane % 16, columns dv0 + 4 (lane / 16) + 0..3.
-    if (nch <= 0) return;
-    TI* outg = (TI*)p.out;
-    typedef typename Raw4<TI>::type RT;
-    struct OBuf {
-      UT q[NB][KD::NU];
-      RT ol[NB];
-    };
-    auto fetch = [&](OBuf& o, int i, int slot) {
-      const char* st = smem + slot * R::stage;
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-        for (int q = 0; q < KD::NU; ++q) {
-          const char* qu = st + R::qp + rt * 16 * DK * S + q * KD::UNIT * S;
-          o.q[rt][q] = (KD::HALF_TAIL && q == KD::NU - 1) ? lds_unit<TI, true>(qu, lane)
-                                                          : lds_unit<TI, false>(qu, lane);
-        }
-      const TI* src = (const TI*)p.im.oloc +
-                      (((int64_t)(c_begin + i) * p.hv + h) * C * p.dv + (int64_t)sl * NB * 256) + lane * 4;
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) o.ol[rt] = load_raw4<TI>(src + rt * 256);
-    };
-    auto emit = [&](const OBuf& o, int i) {
-      const char* hsrc = smem + R::hbuf + (i & 1) * R::HB;
-      UT ha[KD::NU];
-#pragma unroll
-      for (int q = 0; q < KD::NU; ++q) ha[q] = lds_unit<TI, false>(hsrc + q * 1024, lane);
-      f32x4 ao[NB];
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) ao[rt] = zero4();
-#pragma unroll
-      for (int q = 0; q < KD::NU; ++q)
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
-          if (KD::HALF_TAIL && q == KD::NU - 1) mma_unit<true>(ao[rt], ha[q], o.q[rt][q]);
-          else mma_unit<false>(ao[rt], ha[q], o.q[rt][q]);
-        }
-      const int tok = tok0 + i * C;
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        settle(ao[rt]);
-        const f32x4 ol = raw4_to_f32<TI>(o.ol[rt]);
-        const int r = 16 * rt + (lane & 15);
-        if (r < tok_end - tok)
-          store4<TI>(outg + (int64_t)(tok + r) * p.o_st + (int64_t)h * p.o_sh + dv0 + (lane >> 4) * 4,
-                     ol[0] - ao[rt][0], ol[1] - ao[rt][1], ol[2] - ao[rt][2], ol[3] - ao[rt][3]);
-      }
-    };
-    auto iter = [&](OBuf& cur, const OBuf& prev, int i, int& slot) {
-      fetch(cur, i, slot);
-      if (i > 0) emit(prev, i - 1);
-      slot = slot + 1 == R::slots ? 0 : slot + 1;
-      __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
-      ring_barrier();
-    };
-    OBuf oa, ob;
-    ring_barrier();
-    int slot = 0, i = 0;
-    for (; i + 1 < nch; i += 2) {
-      iter(oa, ob, i, slot);
-      iter(ob, oa, i + 1, slot);
-    }
-    if (i < nch) {
-      iter(oa, ob, i, slot);
-      emit(oa, nch - 1);
-    } else {
-      emit(ob, nch - 1);
-    }
-    return;
-  }
-
-  // wave 0: the recurrence.  hacc[t] holds rows 16 t + 4 (lane / 16) + e of
-  // the state slice, column dv0 + lane % 16.
   const int64_t sbase = ((int64_t)seq * p.hv + h) * DK * DV;
+  const int col = 16 * ctile + (lane & 15);
   f32x4 hacc[NKT];
 #pragma unroll
   for (int t = 0; t < NKT; ++t) {
     hacc[t] = zero4();
     if (p.init) {
-      const int dk0 = 16 * t + (lane >> 4) * 4, dv = dv0 + (lane & 15);
+      const int dk0 = 16 * t + (lane >> 4) * 4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) hacc[t][e] = p.init[sbase + (int64_t)(dk0 + e) * DV + dv];
+      for (int e = 0; e < 4; ++e) hacc[t][e] = p.init[sbase + (int64_t)(dk0 + e) * DV + col];
     }
   }
 
@@ -959,19 +961,14 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
     UT hb[KD::NU];
     state_units<TI, DK>(hb, hacc);
 #pragma unroll
-    for (int q = 0; q < KD::NU; ++q) *(UT*)(smem + R::hbuf + q * 1024 + lane * 16) = hb[q];
-    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
-    ring_barrier();
+    for (int q = 0; q < KD::NU; ++q) *(UT*)(smem + R::hcopy(s, 0) + q * 1024 + lane * 16) = hb[q];
     int slot = 0;
-    for (int i = 0; i < nch; ++i) {
+    // One chunk step, given U~ (the accumulator input of U) and the decay.
+    auto rstep = [&](int i, f32x4 (&au)[NB], float dec) {
       const char* st = smem + slot * R::stage;
-      const float dec = *(const float*)(st + R::dec);
-      // U = U~ + W (-H) over the d_k units, U~ as the accumulator input.
-      // Row tiles are finished in pairs, so that the state update for the
-      // first 32 rows can start while the MFMAs for the rest run.
-      f32x4 au[NB];
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) au[rt] = load4<TI>((const TI*)(st + R::ut + rt * 256 * S) + lane * 4);
+      // U = U~ + W (-H) over the d_k units.  Row tiles are finished in
+      // pairs, so that the state update for the first 32 rows can start
+      // while the MFMAs for the rest run.
 #pragma unroll
       for (int r0 = 0; r0 < NB; r0 += 2)
 #pragma unroll
@@ -984,10 +981,10 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
             else
               mma_unit<false>(au[rt], lds_unit<TI, false>(wu, lane), hb[q]);
           }
-      // -H_i for wave 1, which reads it after the next barrier (written
-      // behind this chunk's operand reads)
+      // -H_i for the output wave, which reads it after the next barrier
+      // (written behind this chunk's operand reads)
       if (i > 0) {
-        char* hdst = smem + R::hbuf + (i & 1) * R::HB;
+        char* hdst = smem + R::hcopy(s, i & 1);
 #pragma unroll
         for (int q = 0; q < KD::NU; ++q) *(UT*)(hdst + q * 1024 + lane * 16) = hb[q];
       }
@@ -1022,17 +1019,111 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanParams p) {
       // waves may refill the stage
       __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
       ring_barrier();
+    };
+    if constexpr (R::UTR) {
+      __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+      ring_barrier();
+      for (int i = 0; i < nch; ++i) {
+        const char* st = smem + slot * R::stage;
+        f32x4 au[NB];
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) au[rt] = load4<TI>((const TI*)(st + R::ut + rt * 256 * S) + lane * 4);
+        rstep(i, au, *(const float*)(st + R::dec));
+      }
+    } else {
+      // the slice's U~ tiles and the decay of chunk cc, requested two chunk
+      // steps before their use (past the last chunk the last is read again)
+      auto fetch_u = [&](RT (&un)[NB], float& dn, int cc) {
+        const int64_t blk = (int64_t)cc * p.hv + h;
+        const TI* src = (const TI*)p.im.ut + blk * C * DV + (int64_t)ctile * NB * 256 + lane * 4;
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) un[rt] = load_raw4<TI>(src + rt * 256);
+        dn = p.im.decay[blk];
+      };
+      auto take = [&](f32x4 (&au)[NB], const RT (&un)[NB]) {
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) au[rt] = raw4_to_f32<TI>(un[rt]);
+      };
+      RT pa[NB], pb[NB];
+      float da, db;
+      fetch_u(pa, da, c_begin);
+      fetch_u(pb, db, min(c_begin + 1, c_end - 1));
+      __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+      ring_barrier();
+      int i = 0;
+      for (; i + 1 < nch; i += 2) {
+        {
+          f32x4 au[NB];
+          take(au, pa);
+          // into a scalar register, so that the next load may reuse da's
+          const float dec = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(da)));
+          fetch_u(pa, da, min(c_begin + i + 2, c_end - 1));
+          __builtin_amdgcn_sched_barrier(0);
+          rstep(i, au, dec);
+        }
+        {
+          f32x4 au[NB];
+          take(au, pb);
+          const float dec = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(db)));
+          fetch_u(pb, db, min(c_begin + i + 3, c_end - 1));
+          __builtin_amdgcn_sched_barrier(0);
+          rstep(i + 1, au, dec);
+        }
+      }
+      if (i < nch) {
+        f32x4 au[NB];
+        take(au, pa);
+        rstep(i, au, da);
+      }
     }
   }
 
   if (p.final_state) {
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
-      const int dk0 = 16 * t + (lane >> 4) * 4, dv = dv0 + (lane & 15);
+      const int dk0 = 16 * t + (lane >> 4) * 4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p.final_state[sbase + (int64_t)(dk0 + e) * DV + dv] = hacc[t][e];
+      for (int e = 0; e < 4; ++e) p.final_state[sbase + (int64_t)(dk0 + e) * DV + col] = hacc[t][e];
     }
   }
+}
+
+template <int NSL>
+constexpr int scan_threads() { return 64 * (2 * NSL + kScanCopyWaves); }
+
+template <typename TI, int C, int DK, int NSL>
+__global__ __launch_bounds__(scan_threads<NSL>()) void scan_kernel(ScanParams p) {
+  using R = ScanRing<TI, C, DK, NSL>;
+  __shared__ __attribute__((aligned(1024))) char smem[R::total];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int NS = p.n_slices;
+  // XCD-aware: the slice groups of one (sequence, head) share blockIdx % 8
+  // and so land on the same XCD, where they share W, Q' and K~^T through its
+  // L2.
+  const int b = blockIdx.x;
+  const int u = (b / (8 * NS)) * 8 + (b % 8);
+  const int sl = (b / 8) % NS;
+  if (u >= p.map.n_seq * p.hv) return;
+  const int seq = u / p.hv, h = u % p.hv;
+  int c_begin, c_end, tok0, tok_end;
+  seq_range(p.map, seq, C, c_begin, c_end, tok0, tok_end);
+  const int nch = c_end - c_begin;
+
+  if (wave >= 2 * NSL) {
+    if (nch <= 0) return;
+    if (wave == 2 * NSL) ring_producer<R, C, 0>(smem, p, c_begin, c_end, h, NSL * sl, lane);
+    else ring_producer<R, C, 1>(smem, p, c_begin, c_end, h, NSL * sl, lane);
+    return;
+  }
+  if (wave >= NSL) {
+    if (nch <= 0) return;
+    const int s = wave - NSL;
+    scan_output<TI, C, DK, NSL>(smem, p, h, s, NSL * sl + s, c_begin, nch, tok0, tok_end, lane);
+    return;
+  }
+  scan_recurrence<TI, C, DK, NSL>(smem, p, seq, h, wave, NSL * sl + wave, c_begin, c_end, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1134,16 +1225,30 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
 // would exceed the LDS or the register budget).
 template <typename TI, int C, int DK>
 static constexpr bool fits() {
-  return WyLayout<TI, C, DK>::total <= kLdsLimit && ScanRing<TI, C, DK>::slots >= 2 &&
+  return WyLayout<TI, C, DK>::total <= kLdsLimit && ScanRing<TI, C, DK, 1>::slots >= 2 &&
          (sizeof(TI) == 2 || C <= 32);
+}
+
+// Workgroups of two slices are built for bf16 inputs.
+template <typename TI, int C, int DK>
+static constexpr bool fits_group() {
+  return fits<TI, C, DK>() && sizeof(TI) == 2 && ScanRing<TI, C, DK, 2>::slots >= 2;
 }
 
 template <typename TI, int C, int DK>
 static int launch_pair(int stage, const WyParams* wy, const ScanParams* sc,
                        dim3 grid, hipStream_t s) {
   if constexpr (fits<TI, C, DK>()) {
-    if (stage == 0) hipLaunchKernelGGL((wy_kernel<TI, C, DK>), grid, dim3(kWyThreads), 0, s, *wy);
-    else hipLaunchKernelGGL((scan_kernel<TI, C, DK>), grid, dim3(kThreads), 0, s, *sc);
+    if (stage == 0) {
+      hipLaunchKernelGGL((wy_kernel<TI, C, DK>), grid, dim3(kWyThreads), 0, s, *wy);
+    } else if (sc->nsl == 2) {
+      if constexpr (fits_group<TI, C, DK>())
+        hipLaunchKernelGGL((scan_kernel<TI, C, DK, 2>), grid, dim3(scan_threads<2>()), 0, s, *sc);
+      else
+        return -1;
+    } else {
+      hipLaunchKernelGGL((scan_kernel<TI, C, DK, 1>), grid, dim3(scan_threads<1>()), 0, s, *sc);
+    }
     return 0;
   } else {
     return -1;
@@ -1185,6 +1290,38 @@ static bool fits_any(int chunk, int dk) {
 
 bool kernels_available(bool bf16, int chunk, int dk) {
   return bf16 ? fits_any<gdn::bf16>(chunk, dk) : fits_any<float>(chunk, dk);
+}
+
+static bool group_available(int chunk, int dk) {
+#define GDN_FITS(CC, DD) if (chunk == CC && dk == DD) return fits_group<gdn::bf16, CC, DD>();
+  GDN_FITS(16, 16) GDN_FITS(16, 32) GDN_FITS(16, 64) GDN_FITS(16, 128)
+  GDN_FITS(32, 16) GDN_FITS(32, 32) GDN_FITS(32, 64) GDN_FITS(32, 128)
+  GDN_FITS(64, 16) GDN_FITS(64, 32) GDN_FITS(64, 64) GDN_FITS(64, 128)
+#undef GDN_FITS
+  return false;
+}
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Slices per scan workgroup.  The scan runs one workgroup per compute unit.
+// Where the 16-column slices fit the compute units at once, one slice per
+// workgroup spreads the chains widest.  Where they would queue, two slices
+// per workgroup share one copy of each chunk's operands and run on separate
+// SIMDs, for about the time per chunk of one.
+int scan_slices_per_group(bool bf16, int chunk, int dk, int dv, int64_t seq_heads) {
+  if (!bf16 || dv % 32 != 0 || !group_available(chunk, dk)) return 1;
+  return seq_heads * (dv / 16) > device_cus() ? 2 : 1;
 }
 
 hipError_t launch_table(const TableParams& p, hipStream_t s) {

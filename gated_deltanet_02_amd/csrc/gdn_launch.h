@@ -11,6 +11,10 @@ namespace gdn {
 // fp32 combinations exceed the 160 KiB of LDS and are not).
 bool kernels_available(bool bf16, int chunk, int dk);
 
+// 16-column state slices per scan workgroup (1 or 2) for this problem;
+// seq_heads = sequences x value heads.  Queries the current device.
+int scan_slices_per_group(bool bf16, int chunk, int dk, int dv, int64_t seq_heads);
+
 hipError_t launch_table(const TableParams& p, hipStream_t s);
 // One WY workgroup per (chunk, key head) item.
 hipError_t launch_wy(bool bf16, int chunk, int dk, const WyParams& p, hipStream_t s);
