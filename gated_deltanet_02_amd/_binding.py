@@ -20,6 +20,7 @@ STATUS_NAMES = {0: "GDN_OK", -1: "GDN_ERR_NULL_ARG", -2: "GDN_ERR_DTYPE",
                 -5: "GDN_ERR_UNSUPPORTED", -6: "GDN_ERR_WORKSPACE",
                 -7: "GDN_ERR_HIP"}
 STAGE_TABLE, STAGE_WY, STAGE_SCAN, STAGE_ALL = 1, 2, 4, 7
+SCAN_AUTO, SCAN_ONE_PASS, SCAN_TWO_LEVEL = 0, 1, 2
 EXPORTED = ("gdn_abi_version", "gdn_default_options", "gdn_prefill",
             "gdn_prefill_ex", "gdn_workspace_size", "gdn_get_workspace_layout",
             "gdn_decode", "gdn_graph_cache_create", "gdn_graph_cache_destroy",
@@ -37,13 +38,17 @@ class GdnTensor(ctypes.Structure):
 
 class GdnOptions(ctypes.Structure):
     _fields_ = [("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("l2_eps", ctypes.c_float), ("stages", ctypes.c_uint32)]
+                ("l2_eps", ctypes.c_float), ("stages", ctypes.c_uint32),
+                ("scan_split", ctypes.c_int32)]
 
 
 class GdnWorkspaceLayout(ctypes.Structure):
     _fields_ = [("total_bytes", ctypes.c_size_t), ("max_chunks", ctypes.c_int64)] + [
         (n, ctypes.c_size_t) for n in ("chunk_table", "chunk_offsets", "seq_starts",
-                                       "decay", "w", "qp", "kt", "ut", "oloc")]
+                                       "decay", "w", "qp", "kt", "ut", "oloc")] + [
+        ("split_chunks", ctypes.c_int32)] + [
+        (n, ctypes.c_size_t) for n in ("split_y", "split_hmid", "split_hmid_t", "split_psi",
+                                       "split_phi")]
 
 
 class GdnError(RuntimeError):
@@ -128,9 +133,10 @@ def _ref(d):
 
 
 def options(chunk: int = 0, scale: float = 1.0, l2_eps: float = 1e-6,
-            stages: int = STAGE_ALL) -> GdnOptions:
+            stages: int = STAGE_ALL, scan_split: int = 0) -> GdnOptions:
+    """scan_split: SCAN_AUTO (0), SCAN_ONE_PASS (1) or SCAN_TWO_LEVEL (2)."""
     o = GdnOptions()
-    o.chunk, o.scale, o.l2_eps, o.stages = chunk, scale, l2_eps, stages
+    o.chunk, o.scale, o.l2_eps, o.stages, o.scan_split = chunk, scale, l2_eps, stages, scan_split
     return o
 
 

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <list>
 #include <mutex>
 #include <string>
@@ -120,11 +121,14 @@ struct Problem {
   View q, k, v, o, g, b;
   float scale = 1.f, eps = 1e-6f;
   uint32_t stages = GDN_STAGE_ALL;
+  int scan_split = GDN_SCAN_AUTO;
+  int split = 0;  // two-level scan: chunks in the first segment (0: one pass)
 };
 
 struct Layout {
   size_t table = 0, chunk_off = 0, seq_start = 0, decay = 0;
-  size_t w = 0, qp = 0, kt = 0, ut = 0, oloc = 0, total = 0;
+  size_t w = 0, qp = 0, kt = 0, ut = 0, oloc = 0;
+  size_t y = 0, hmid = 0, hmid_t = 0, psi = 0, phi = 0, total = 0;
 };
 
 Layout make_layout(const Problem& P) {
@@ -146,6 +150,14 @@ Layout make_layout(const Problem& P) {
   L.kt = take(blocks * P.chunk * P.dk * es);
   L.ut = take(blocks * P.chunk * P.dv * es);
   L.oloc = take(blocks * P.chunk * P.dv * es);
+  if (P.split > 0) {
+    const size_t heads = (size_t)P.n_seq * P.hv;
+    L.y = take(blocks * P.chunk * P.dk * 2);
+    L.hmid = take(heads * P.dk * P.dv * 4);
+    L.hmid_t = take(heads * P.dv * P.dk * 2);
+    L.psi = take(heads * P.dk * P.dv * 4);
+    L.phi = take(heads * P.dk * P.dk * 4);
+  }
   L.total = off;
   return L;
 }
@@ -160,10 +172,31 @@ int resolve_options(const gdn_options* opts, bool bf16, Problem* P) {
     return fail(GDN_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64 (got %d)", chunk);
   if (!(o.l2_eps >= 0.f)) return fail(GDN_ERR_SHAPE, "l2_eps must be >= 0");
   if ((o.stages & ~GDN_STAGE_ALL) != 0) return fail(GDN_ERR_SHAPE, "unknown stage bits 0x%x", o.stages);
+  if (o.scan_split < GDN_SCAN_AUTO || o.scan_split > GDN_SCAN_TWO_LEVEL)
+    return fail(GDN_ERR_SHAPE, "unknown scan_split %d", o.scan_split);
   P->chunk = chunk;
   P->scale = o.scale;
   P->eps = o.l2_eps;
   P->stages = o.stages;
+  P->scan_split = o.scan_split;
+  return GDN_OK;
+}
+
+// The two-level scan's split point (see GDN_SCAN_TWO_LEVEL), 0 for one pass.
+// Only on request: measured on MI355X at the 4096-token, 16-head prompt, its
+// two launches take longer than the one-pass scan.
+int choose_split(Problem* P) {
+  P->split = 0;
+  if (P->scan_split != GDN_SCAN_TWO_LEVEL) return GDN_OK;
+  const bool ok = P->bf16 && !P->packed && P->dk % 32 == 0 && P->dv % 32 == 0 &&
+                  P->chunk >= 32 && P->chunks_per_seq >= 2 &&
+                  gdn::two_level_available(P->bf16, P->chunk, P->dk);
+  if (!ok)
+    return fail(GDN_ERR_UNSUPPORTED, "the two-level scan needs bf16 uniform sequences of 2 or more "
+                "chunks of 32 or 64, d_k and d_v multiples of 32");
+  // about 5/8 of the chunks to the first segment (its one-slice workgroups
+  // take about 5/8 of the time per chunk of the second's two-slice ones)
+  P->split = std::min(std::max((5 * P->chunks_per_seq + 4) / 8, 1), P->chunks_per_seq - 1);
   return GDN_OK;
 }
 
@@ -234,6 +267,7 @@ int validate(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
   const int64_t n_slices = P->dv / 16;
   const int64_t scan_blocks = ((int64_t)P->n_seq * P->hv + 7) / 8 * 8 * n_slices;
   if (scan_blocks >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "too many (sequence, head) pairs");
+  if ((rc = choose_split(P))) return rc;
   if (!full) return GDN_OK;
 
   // The remaining tensors.
@@ -410,13 +444,27 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
     sp.final_state = fin ? (float*)fin->data : nullptr;
     sp.hv = P.hv;
     sp.dv = P.dv;
-    sp.nsl = gdn::scan_slices_per_group(P.bf16, P.chunk, P.dk, P.dv, (int64_t)P.n_seq * P.hv);
-    sp.n_slices = P.dv / (16 * sp.nsl);
     sp.map = map;
     sp.im = im;
-    const int64_t blocks = ((int64_t)P.n_seq * P.hv + 7) / 8 * 8 * sp.n_slices;
-    if ((e = gdn::launch_scan(P.bf16, P.chunk, P.dk, sp, (int)blocks, s)) != hipSuccess)
-      return fail(GDN_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
+    const int64_t heads8 = ((int64_t)P.n_seq * P.hv + 7) / 8 * 8;
+    if (P.split > 0) {
+      sp.split = P.split;
+      sp.sp_y = base + L.y;
+      sp.sp_hmid = (float*)(base + L.hmid);
+      sp.sp_hmid_t = base + L.hmid_t;
+      sp.sp_psi = (float*)(base + L.psi);
+      sp.sp_phi = (float*)(base + L.phi);
+      sp.nsl = 2;
+      sp.n_slices = P.dv / 16 + (P.dv + P.dk) / 32;  // workgroups per (sequence, head)
+      if ((e = gdn::launch_scan_two_level(P.chunk, P.dk, sp, s)) != hipSuccess)
+        return fail(GDN_ERR_HIP, "two-level scan launch: %s", hipGetErrorString(e));
+    } else {
+      sp.nsl = gdn::scan_slices_per_group(P.bf16, P.chunk, P.dk, P.dv, (int64_t)P.n_seq * P.hv);
+      sp.n_slices = P.dv / (16 * sp.nsl);
+      const int64_t blocks = heads8 * sp.n_slices;
+      if ((e = gdn::launch_scan(P.bf16, P.chunk, P.dk, sp, (int)blocks, s)) != hipSuccess)
+        return fail(GDN_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
+    }
   }
   return GDN_OK;
 }
@@ -433,6 +481,7 @@ void gdn_default_options(gdn_options* opts) {
   opts->scale = 1.0f;
   opts->l2_eps = 1e-6f;
   opts->stages = GDN_STAGE_ALL;
+  opts->scan_split = GDN_SCAN_AUTO;
 }
 
 const char* gdn_status_string(int status) {
@@ -480,6 +529,12 @@ int gdn_get_workspace_layout(const gdn_tensor* q, const gdn_tensor* k, const gdn
   layout->kt = L.kt;
   layout->ut = L.ut;
   layout->oloc = L.oloc;
+  layout->split_chunks = P.split;
+  layout->split_y = L.y;
+  layout->split_hmid = L.hmid;
+  layout->split_hmid_t = L.hmid_t;
+  layout->split_psi = L.psi;
+  layout->split_phi = L.phi;
   return GDN_OK;
 }
 

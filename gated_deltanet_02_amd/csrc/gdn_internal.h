@@ -67,6 +67,14 @@ struct ScanParams {
   int32_t n_slices;      // workgroups per (sequence, head): dv / (16 nsl)
   ChunkMap map;
   Intermediates im;
+  // two-level scan (uniform sequences only): chunks in the first segment,
+  // 0 for the one-pass scan, and its workspace
+  int32_t split;
+  void* sp_y;            // Q'_c Phi_c of second-segment chunks [chunk][Hv][C][dk]
+  float* sp_hmid;        // state after the first segment [N][Hv][dk][dv]
+  void* sp_hmid_t;       // its bf16 transpose [N][Hv][dv][dk]
+  float* sp_psi;         // second segment's end state from zero [N][Hv][dk][dv]
+  float* sp_phi;         // second segment's transition [N][Hv][dk][dk]
 };
 
 // One recurrent step per sequence (decode).

@@ -844,16 +844,25 @@ __device__ __forceinline__ void state_units(UT* hb, const f32x4* hacc) {
   }
 }
 
+// One slice of the two-level scan (scan_split_kernel).
+struct SliceJob {
+  int first;  // 1: first segment, from the initial state; 0: second, from zero
+  int phi;    // 1: transition columns: U~ = 0, O_loc = 0, identity start, Q' Phi out
+  int ctile;  // column tile (of d_v; of d_k for transition columns)
+};
+
 // The output wave of slice s (column tile ctile), one chunk behind the
 // recurrence: during chunk i it reads Q'_i (LDS) and O_loc_i (global) into
 // registers and forms
 //   O_{i-1}^T = O_loc^T - (-H_{i-1})^T Q'^T
 // with -H_{i-1} as the recurrence wave left it in LDS during chunk i - 1.
 // Lane holds row 16 rt + lane % 16, columns 16 ctile + 4 (lane / 16) + 0..3.
-template <typename TI, int C, int DK, int NSL>
+// In the two-level scan (SPLIT) a transition slice writes Q'_i Phi_i (all
+// rows) to the workspace instead.
+template <typename TI, int C, int DK, int NSL, bool SPLIT = false>
 __device__ __forceinline__ void scan_output(char* smem, const ScanParams& p, int h, int s,
                                             int ctile, int c_begin, int nch, int tok0,
-                                            int tok_end, int lane) {
+                                            int tok_end, int lane, SliceJob job = {}) {
   using R = ScanRing<TI, C, DK, NSL>;
   using KD = KTile<TI, DK>;
   using UT = typename Unit<TI>::type;
@@ -878,8 +887,13 @@ __device__ __forceinline__ void scan_output(char* smem, const ScanParams& p, int
       }
     const TI* src = (const TI*)p.im.oloc + ((int64_t)(c_begin + i) * p.hv + h) * C * DV +
                     (int64_t)ctile * NB * 256 + lane * 4;
+    if (SPLIT && job.phi) {
 #pragma unroll
-    for (int rt = 0; rt < NB; ++rt) o.ol[rt] = load_raw4<TI>(src + rt * 256);
+      for (int rt = 0; rt < NB; ++rt) o.ol[rt] = RT{};
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) o.ol[rt] = load_raw4<TI>(src + rt * 256);
+    }
   };
   auto emit = [&](const OBuf& o, int i) {
     const char* hsrc = smem + R::hcopy(s, i & 1);
@@ -897,6 +911,16 @@ __device__ __forceinline__ void scan_output(char* smem, const ScanParams& p, int
         else mma_unit<false>(ao[rt], ha[q], o.q[rt][q]);
       }
     const int tok = tok0 + i * C;
+    if (SPLIT && job.phi) {
+      TI* y = (TI*)p.sp_y + ((int64_t)(c_begin + i) * p.hv + h) * C * DK + 16 * ctile + (lane >> 4) * 4;
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        settle(ao[rt]);
+        const int r = 16 * rt + (lane & 15);
+        store4<TI>(y + r * DK, -ao[rt][0], -ao[rt][1], -ao[rt][2], -ao[rt][3]);
+      }
+      return;
+    }
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt) {
       settle(ao[rt]);
@@ -931,10 +955,13 @@ __device__ __forceinline__ void scan_output(char* smem, const ScanParams& p, int
 
 // The recurrence wave of slice s (column tile ctile).  hacc[t] holds rows
 // 16 t + 4 (lane / 16) + e of the state slice, column 16 ctile + lane % 16.
-template <typename TI, int C, int DK, int NSL>
+// In the two-level scan (SPLIT) the slice starts from the initial state
+// (first segment), from zero, or from identity columns (transition), and its
+// end state goes to the workspace.
+template <typename TI, int C, int DK, int NSL, bool SPLIT = false>
 __device__ __forceinline__ void scan_recurrence(char* smem, const ScanParams& p, int seq, int h,
                                                 int s, int ctile, int c_begin, int c_end,
-                                                int lane) {
+                                                int lane, SliceJob job = {}) {
   using R = ScanRing<TI, C, DK, NSL>;
   using KD = KTile<TI, DK>;
   using KC = KTile<TI, C>;
@@ -947,13 +974,17 @@ __device__ __forceinline__ void scan_recurrence(char* smem, const ScanParams& p,
   const int64_t sbase = ((int64_t)seq * p.hv + h) * DK * DV;
   const int col = 16 * ctile + (lane & 15);
   f32x4 hacc[NKT];
+  const bool from_init = p.init && (!SPLIT || (job.first && !job.phi));
 #pragma unroll
   for (int t = 0; t < NKT; ++t) {
     hacc[t] = zero4();
-    if (p.init) {
-      const int dk0 = 16 * t + (lane >> 4) * 4;
+    const int dk0 = 16 * t + (lane >> 4) * 4;
+    if (from_init) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) hacc[t][e] = p.init[sbase + (int64_t)(dk0 + e) * DV + col];
+    } else if (SPLIT && job.phi) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hacc[t][e] = dk0 + e == col ? 1.f : 0.f;
     }
   }
 
@@ -1036,8 +1067,13 @@ __device__ __forceinline__ void scan_recurrence(char* smem, const ScanParams& p,
       auto fetch_u = [&](RT (&un)[NB], float& dn, int cc) {
         const int64_t blk = (int64_t)cc * p.hv + h;
         const TI* src = (const TI*)p.im.ut + blk * C * DV + (int64_t)ctile * NB * 256 + lane * 4;
+        if (SPLIT && job.phi) {
 #pragma unroll
-        for (int rt = 0; rt < NB; ++rt) un[rt] = load_raw4<TI>(src + rt * 256);
+          for (int rt = 0; rt < NB; ++rt) un[rt] = RT{};
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt) un[rt] = load_raw4<TI>(src + rt * 256);
+        }
         dn = p.im.decay[blk];
       };
       auto take = [&](f32x4 (&au)[NB], const RT (&un)[NB]) {
@@ -1078,7 +1114,22 @@ __device__ __forceinline__ void scan_recurrence(char* smem, const ScanParams& p,
     }
   }
 
-  if (p.final_state) {
+  if constexpr (SPLIT) {
+    // end of the first segment (fp32, and its bf16 transpose for the
+    // output correction), of the second from zero, or the transition
+    const int64_t u = (int64_t)seq * p.hv + h;
+    float* dst = job.phi ? p.sp_phi + u * DK * DK : job.first ? p.sp_hmid + sbase : p.sp_psi + sbase;
+    const int ld = job.phi ? DK : DV;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) {
+      const int dk0 = 16 * t + (lane >> 4) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(int64_t)(dk0 + e) * ld + col] = hacc[t][e];
+      if (job.first && !job.phi)
+        store4<TI>((TI*)p.sp_hmid_t + u * DV * DK + (int64_t)col * DK + dk0, hacc[t][0], hacc[t][1],
+                   hacc[t][2], hacc[t][3]);
+    }
+  } else if (p.final_state) {
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
       const int dk0 = 16 * t + (lane >> 4) * 4;
@@ -1124,6 +1175,169 @@ __global__ __launch_bounds__(scan_threads<NSL>()) void scan_kernel(ScanParams p)
     return;
   }
   scan_recurrence<TI, C, DK, NSL>(smem, p, seq, h, wave, NSL * sl + wave, c_begin, c_end, lane);
+}
+
+// ---------------------------------------------------------------------------
+// two-level scan
+//
+// Each chunk maps the incoming state affinely, H' = M_c H + B_c with
+// M_c = e^gamma_last I - K~^T W and B_c = K~^T U~.  A sequence is split at
+// chunk `split` into two segments scanned at the same time:
+//   first segment   the ordinary scan from the initial state (its outputs
+//                   are final), ending in H_mid;
+//   second segment  the ordinary scan from zero (local outputs O', end state
+//                   Psi), and beside it the same recurrence on identity
+//                   columns with U~ = 0 and O_loc = 0: Phi_i, the product of
+//                   the segment's M_c before chunk i, and Q'_i Phi_i.
+// Linearity in (U~, start) then gives, for second-segment chunk i,
+//   O_i = O'_i + (Q'_i Phi_i) H_mid   and   H_end = Phi_end H_mid + Psi,
+// which scan_fix_kernel applies.  The chain is half as long at the price of
+// the transition columns (d_k more state columns in the second segment).
+//
+// Per (sequence, head): d_v / 16 first-segment workgroups of one slice (the
+// second slice's waves leave at once; a barrier waits for live waves only),
+// then (d_v + d_k) / 32 second-segment workgroups of two slices (value
+// columns first, then transition columns).  A one-slice workgroup steps
+// faster, so the host gives the first segment more chunks.
+
+template <typename TI, int C, int DK>
+__global__ __launch_bounds__(scan_threads<2>()) void scan_split_kernel(ScanParams p) {
+  using R = ScanRing<TI, C, DK, 2>;
+  __shared__ __attribute__((aligned(1024))) char smem[R::total];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int NW = p.n_slices;  // workgroups per (sequence, head)
+  // XCD-aware: the workgroups of one (sequence, head) share blockIdx % 8.
+  const int b = blockIdx.x;
+  const int u = (b / (8 * NW)) * 8 + (b % 8);
+  const int wg = (b / 8) % NW;
+  if (u >= p.map.n_seq * p.hv) return;
+  const int seq = u / p.hv, h = u % p.hv;
+  int c_begin, c_end, tok0, tok_end;
+  seq_range(p.map, seq, C, c_begin, c_end, tok0, tok_end);
+  const int NV = p.dv / 16;  // value column tiles = first-segment workgroups
+  SliceJob job;
+  job.first = wg < NV;
+  if (job.first && wave < 4 && (wave & 1)) return;  // one slice: waves 0, 2 and the copiers
+  const int k0 = job.first ? wg : 2 * (wg - NV);  // this workgroup's first job in its segment
+  job.phi = !job.first && k0 >= NV;
+  const int cb = job.first ? c_begin : c_begin + p.split;
+  const int ce = job.first ? c_begin + p.split : c_end;
+  const int tb = tok0 + (cb - c_begin) * C;
+  const int te = job.first ? tb + p.split * C : tok_end;
+  if (ce <= cb) return;
+
+  if (wave >= 4) {
+    if (wave == 4) ring_producer<R, C, 0>(smem, p, cb, ce, h, 0, lane);
+    else ring_producer<R, C, 1>(smem, p, cb, ce, h, 0, lane);
+    return;
+  }
+  const int s = wave & 1;
+  job.ctile = k0 + s - (job.phi ? NV : 0);
+  if (wave >= 2)
+    scan_output<TI, C, DK, 2, true>(smem, p, h, s, job.ctile, cb, ce - cb, tb, te, lane, job);
+  else
+    scan_recurrence<TI, C, DK, 2, true>(smem, p, seq, h, s, job.ctile, cb, ce, lane, job);
+}
+
+// Applies the second segment's correction.  Output blocks: per (sequence,
+// head, kFixChunks chunks of the second segment) O^T += H_mid^T (Q' Phi)^T
+// with bf16 operands (the same rounding as the scan's Q' H); each wave keeps
+// H_mid^T's operand units in registers for its (chunk, row tile) jobs.
+// State blocks: per (sequence, head, 16 columns) H_end = Phi_end H_mid + Psi
+// in fp32, one thread per (row, 8 columns) with its row of Phi_end in
+// registers.
+constexpr int kFixThreads = 256;
+constexpr int kFixChunks = 4;
+
+__host__ __device__ constexpr int fix_groups(int l1) { return (l1 + kFixChunks - 1) / kFixChunks; }
+
+template <int C, int DK, int DV>
+__global__ __launch_bounds__(kFixThreads) void scan_fix_kernel(ScanParams p) {
+  constexpr int NW = kFixThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int L1 = p.map.chunks_per_seq - p.split;
+  const int NG = fix_groups(L1);
+  const int n_heads = p.map.n_seq * p.hv;
+  const int n_out = (n_heads + 7) / 8 * 8 * NG;
+  int b = blockIdx.x;
+  if (b < n_out) {
+    // XCD-aware: the blocks of one (sequence, head) share blockIdx % 8
+    const int u = (b / (8 * NG)) * 8 + (b % 8), gi = (b / 8) % NG;
+    if (u >= n_heads) return;
+    const int seq = u / p.hv, h = u % p.hv;
+    const bf16* ht = (const bf16*)p.sp_hmid_t + (int64_t)u * DV * DK + (lane & 15) * DK + (lane >> 4) * 8;
+    bf16x8 ha[DV / 16][DK / 32];
+#pragma unroll
+    for (int ct = 0; ct < DV / 16; ++ct)
+#pragma unroll
+      for (int q = 0; q < DK / 32; ++q) ha[ct][q] = *(const bf16x8*)(ht + 16 * ct * DK + 32 * q);
+    for (int jb = wave; jb < kFixChunks * (C / 16); jb += NW) {
+      const int i1 = gi * kFixChunks + jb / (C / 16), rt = jb % (C / 16);
+      if (i1 >= L1) break;
+      const int cc = seq * p.map.chunks_per_seq + p.split + i1;
+      const int tok = seq * p.map.seq_len + (p.split + i1) * C;
+      const int n = min(C, (seq + 1) * p.map.seq_len - tok);
+      const int r = 16 * rt + (lane & 15);
+      const bf16* yrow = (const bf16*)p.sp_y + (((int64_t)cc * p.hv + h) * C + r) * DK + (lane >> 4) * 8;
+      bf16x8 yb[DK / 32];
+#pragma unroll
+      for (int q = 0; q < DK / 32; ++q) yb[q] = *(const bf16x8*)(yrow + 32 * q);
+      bf16* orow = (bf16*)p.out + (int64_t)(tok + r) * p.o_st + (int64_t)h * p.o_sh + (lane >> 4) * 4;
+      // the row's outputs requested together, before the products
+      typename Raw4<bf16>::type ov[DV / 16];
+#pragma unroll
+      for (int ct = 0; ct < DV / 16; ++ct) ov[ct] = r < n ? load_raw4<bf16>(orow + 16 * ct) : uint2{};
+#pragma unroll
+      for (int ct = 0; ct < DV / 16; ++ct) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int q = 0; q < DK / 32; ++q)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[ct][q], yb[q], acc, 0, 0, 0);
+        if (r < n) {
+          const f32x4 o = raw4_to_f32<bf16>(ov[ct]);
+          store4<bf16>(orow + 16 * ct, o[0] + acc[0], o[1] + acc[1], o[2] + acc[2], o[3] + acc[3]);
+        }
+      }
+    }
+    return;
+  }
+  b -= n_out;
+  if (!p.final_state) return;
+  constexpr int NT = DV / 16;
+  const int u = b / NT, ct = b % NT;
+  if (u >= n_heads) return;
+  __shared__ float sH[DK][16];
+  const float* hm = p.sp_hmid + (int64_t)u * DK * DV + 16 * ct;
+  for (int idx = tid; idx < DK * 16; idx += kFixThreads) sH[idx / 16][idx % 16] = hm[(int64_t)(idx / 16) * DV + idx % 16];
+  __syncthreads();
+  const int k = tid / 2, j0 = (tid % 2) * 8;
+  if (k >= DK) return;
+  const float* phr = p.sp_phi + ((int64_t)u * DK + k) * DK;
+  f32x4 a[DK / 4];
+#pragma unroll
+  for (int i = 0; i < DK / 4; ++i) a[i] = *(const f32x4*)(phr + 4 * i);
+  const float* psr = p.sp_psi + ((int64_t)u * DK + k) * DV + 16 * ct + j0;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = psr[e];
+#pragma unroll
+  for (int i = 0; i < DK / 4; ++i)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const f32x4 h0 = *(const f32x4*)&sH[4 * i + ii][j0];
+      const f32x4 h1 = *(const f32x4*)&sH[4 * i + ii][j0 + 4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] = __builtin_fmaf(a[i][ii], h0[e], acc[e]);
+        acc[4 + e] = __builtin_fmaf(a[i][ii], h1[e], acc[4 + e]);
+      }
+    }
+  float* dst = p.final_state + ((int64_t)u * DK + k) * DV + 16 * ct + j0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[e] = acc[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -1344,6 +1558,38 @@ hipError_t launch_scan(bool bf16, int chunk, int dk, const ScanParams& p,
                       : dispatch_c<float>(chunk, dk, 1, nullptr, &p, grid, s);
   if (rc) return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+bool two_level_available(bool bf16, int chunk, int dk) { return bf16 && group_available(chunk, dk); }
+
+template <int C, int DK>
+static hipError_t launch_two_level_dk(const ScanParams& p, hipStream_t s) {
+  if constexpr (fits_group<gdn::bf16, C, DK>()) {
+    const int64_t heads = (int64_t)p.map.n_seq * p.hv, heads8 = (heads + 7) / 8 * 8;
+    const int64_t grid_a = heads8 * p.n_slices;
+    const int64_t grid_fix = heads8 * fix_groups(p.map.chunks_per_seq - p.split) + heads * (p.dv / 16);
+    hipLaunchKernelGGL((scan_split_kernel<gdn::bf16, C, DK>), dim3((unsigned)grid_a),
+                       dim3(scan_threads<2>()), 0, s, p);
+    switch (p.dv) {
+      case 32: hipLaunchKernelGGL((scan_fix_kernel<C, DK, 32>), dim3((unsigned)grid_fix), dim3(kFixThreads), 0, s, p); break;
+      case 64: hipLaunchKernelGGL((scan_fix_kernel<C, DK, 64>), dim3((unsigned)grid_fix), dim3(kFixThreads), 0, s, p); break;
+      case 128: hipLaunchKernelGGL((scan_fix_kernel<C, DK, 128>), dim3((unsigned)grid_fix), dim3(kFixThreads), 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_scan_two_level(int chunk, int dk, const ScanParams& p, hipStream_t s) {
+  if (chunk == 32 && dk == 32) return launch_two_level_dk<32, 32>(p, s);
+  if (chunk == 32 && dk == 64) return launch_two_level_dk<32, 64>(p, s);
+  if (chunk == 32 && dk == 128) return launch_two_level_dk<32, 128>(p, s);
+  if (chunk == 64 && dk == 32) return launch_two_level_dk<64, 32>(p, s);
+  if (chunk == 64 && dk == 64) return launch_two_level_dk<64, 64>(p, s);
+  if (chunk == 64 && dk == 128) return launch_two_level_dk<64, 128>(p, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(bool bf16, int dk, const DecodeParams& p, hipStream_t s) {

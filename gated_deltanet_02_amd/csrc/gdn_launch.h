@@ -21,6 +21,11 @@ hipError_t launch_wy(bool bf16, int chunk, int dk, const WyParams& p, hipStream_
 hipError_t launch_scan(bool bf16, int chunk, int dk, const ScanParams& p,
                        int grid_x, hipStream_t s);
 
+// The two-level scan: both segments in one launch, then the correction of
+// the second segment's outputs and the final state.
+bool two_level_available(bool bf16, int chunk, int dk);
+hipError_t launch_scan_two_level(int chunk, int dk, const ScanParams& p, hipStream_t s);
+
 hipError_t launch_decode(bool bf16, int dk, const DecodeParams& p, hipStream_t s);
 
 }  // namespace gdn

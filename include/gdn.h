@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 /* Status codes. */
 #define GDN_OK 0
@@ -91,11 +91,30 @@ typedef struct gdn_tensor {
 #define GDN_STAGE_ALL 7u
 
 typedef struct gdn_options {
-  int32_t chunk;   /* 16, 32 or 64 (default 64)                             */
-  float scale;     /* output multiplier (default 1.0)                        */
-  float l2_eps;    /* epsilon inside the L2 norm's square root (1e-6)        */
-  uint32_t stages; /* GDN_STAGE_* mask (default GDN_STAGE_ALL)               */
+  int32_t chunk;      /* 16, 32 or 64 (default 64)                          */
+  float scale;        /* output multiplier (default 1.0)                     */
+  float l2_eps;       /* epsilon inside the L2 norm's square root (1e-6)     */
+  uint32_t stages;    /* GDN_STAGE_* mask (default GDN_STAGE_ALL)            */
+  int32_t scan_split; /* GDN_SCAN_* (default GDN_SCAN_AUTO)                  */
 } gdn_options;
+
+/*
+ * The state scan's schedule.  Each chunk maps its incoming state affinely
+ * (the gated delta rule of "Gated Delta Networks", section 3, summed over a
+ * chunk): H' = M H + B with M = e^{gamma_last} I - K~^T W and B = K~^T U~.
+ * GDN_SCAN_TWO_LEVEL splits every sequence (at 5/8 of its chunks) and scans
+ * both halves at once: the second from zero, beside the product of its M
+ * (d_k more state columns), then adds M-product x (state at the split) to
+ * its outputs and final state.  The chain of dependent chunk steps halves;
+ * the arithmetic differs from the one-pass scan only in rounding.  Offered
+ * for bf16 inputs without cu_seqlens (uniform sequences), d_k and d_v
+ * multiples of 32 and chunks of 32 or 64; GDN_SCAN_TWO_LEVEL elsewhere is
+ * GDN_ERR_UNSUPPORTED.  GDN_SCAN_AUTO is the one-pass scan (on MI355X the
+ * two-level scan's two launches take longer at the sizes measured).
+ */
+#define GDN_SCAN_AUTO 0
+#define GDN_SCAN_ONE_PASS 1
+#define GDN_SCAN_TWO_LEVEL 2
 
 /* Returns GDN_ABI_VERSION of the built library. */
 int gdn_abi_version(void);
@@ -171,6 +190,14 @@ typedef struct gdn_workspace_layout {
   size_t total_bytes;
   int64_t max_chunks;
   size_t chunk_table, chunk_offsets, seq_starts, decay, w, qp, kt, ut, oloc;
+  /* two-level scan (split_chunks > 0: chunks in the first segment), else 0:
+   *   split_y      bf16 [chunk][Hv][C][dk]  Q' x M-product, second segment
+   *   split_hmid   f32 [N][Hv][dk][dv]      state at the split
+   *   split_hmid_t bf16 [N][Hv][dv][dk]     its transpose
+   *   split_psi    f32 [N][Hv][dk][dv]      second segment's end from zero
+   *   split_phi    f32 [N][Hv][dk][dk]      second segment's M-product   */
+  int32_t split_chunks;
+  size_t split_y, split_hmid, split_hmid_t, split_psi, split_phi;
 } gdn_workspace_layout;
 
 /* Computes the workspace size / layout for the given tensors and options

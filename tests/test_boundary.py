@@ -45,7 +45,7 @@ def test_abi_version_and_defaults(lib):
     ver = int(re.search(r"#define GDN_ABI_VERSION (\d+)", src).group(1))
     assert G.gdn_abi_version() == ver
     o = G.gdn_default_options()
-    assert (o.chunk, o.scale, o.stages) == (0, 1.0, 7)
+    assert (o.chunk, o.scale, o.stages, o.scan_split) == (0, 1.0, 7, 0)
     assert abs(o.l2_eps - 1e-6) < 1e-12
     for s in range(-7, 1):
         assert G.gdn_status_string(s) != "unknown status"
@@ -140,14 +140,50 @@ def test_state_and_cu_validation(lib):
 def test_workspace_size_formula(lib):
     q = torch.empty(4096, 16, 128, dtype=torch.bfloat16)
     v = torch.empty(4096, 16, 128, dtype=torch.bfloat16)
-    n = G.gdn_workspace_size(q, q, v)
-    # 64 chunks x 16 heads x (3 C*dk + 2 C*dv) bf16 + decay, 256-byte aligned
+    # one pass: 64 chunks x 16 heads x (3 C*dk + 2 C*dv) bf16 + decay, 256-byte aligned
+    one = G.options(scan_split=G.SCAN_ONE_PASS)
+    n = G.gdn_workspace_size(q, q, v, opts=one)
     per = 64 * 16 * (5 * 64 * 128) * 2
     assert per <= n <= per + 64 * 16 * 4 + 6 * 256
-    lay = G.gdn_get_workspace_layout(q, q, v)
-    assert lay.max_chunks == 64 and lay.total_bytes == n
+    lay = G.gdn_get_workspace_layout(q, q, v, opts=one)
+    assert lay.max_chunks == 64 and lay.total_bytes == n and lay.split_chunks == 0
     offs = [lay.decay, lay.w, lay.qp, lay.kt, lay.ut, lay.oloc]
     assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+    assert lay.split_y == lay.split_phi == 0
+    assert G.gdn_workspace_size(q, q, v) == n  # the default is one pass
+    # the two-level scan: the split at chunk 40 (5/8 of 64), plus Q' x transition per
+    # chunk (bf16 C x dk) and four (d x d) states per head (f32 H_mid, Psi,
+    # Phi and the bf16 transpose of H_mid)
+    two = G.options(scan_split=G.SCAN_TWO_LEVEL)
+    lay2 = G.gdn_get_workspace_layout(q, q, v, opts=two)
+    assert lay2.split_chunks == 40
+    extra = 64 * 16 * 64 * 128 * 2 + 16 * 128 * 128 * (4 + 2 + 4 + 4)
+    assert n + extra <= lay2.total_bytes <= n + extra + 5 * 256
+    offs2 = [lay2.oloc, lay2.split_y, lay2.split_hmid, lay2.split_hmid_t, lay2.split_psi, lay2.split_phi]
+    assert all(o % 256 == 0 for o in offs2) and offs2 == sorted(offs2)
+    assert G.gdn_workspace_size(q, q, v, opts=two) == lay2.total_bytes
+
+
+def test_scan_split_option(lib):
+    """scan_split: unknown values are rejected; the two-level scan, asked for
+    where it is not offered, is GDN_ERR_UNSUPPORTED; one pass is always
+    accepted."""
+    a = base()
+    for bad in (-1, 3):
+        o = B.options(scan_split=bad)
+        assert call(lib, a["q"], a["k"], a["v"], a["g"], a["b"], out=a["out"], opts=o) == -3
+    f = base(dt=torch.float32, dk=64, dv=64)
+    o = B.options(chunk=32, scan_split=2)
+    assert call(lib, f["q"], f["k"], f["v"], f["g"], f["b"], out=f["out"], opts=o) == -5
+    cu = fake((4,), torch.int32)
+    o = B.options(scan_split=2)
+    assert call(lib, a["q"], a["k"], a["v"], a["g"], a["b"], cu=cu, out=a["out"], opts=o) == -5
+    assert "two-level" in G.gdn_last_error()
+    o = B.options(chunk=16, scan_split=2)
+    assert call(lib, a["q"], a["k"], a["v"], a["g"], a["b"], out=a["out"], opts=o) == -5
+    # one chunk only: nothing to split
+    s = base(T=64)
+    assert call(lib, s["q"], s["k"], s["v"], s["g"], s["b"], out=s["out"], opts=B.options(scan_split=2)) == -5
 
 
 def test_binding_refuses_host_tensors(lib):
