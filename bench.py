@@ -147,7 +147,9 @@ def decode_main(args, torch, G, W, dev):
         "dtype": "f32 (bf16 inputs)", "data": "synthetic (seeded; state ~ N(0, 0.5^2))",
         "config": {"workload": args.workload, "n_seqs": w.n_seqs, "hk": int(w.q.shape[1]),
                    "hv": int(w.v.shape[1]), "dk": int(w.q.shape[2]), "dv": int(w.v.shape[2]),
-                   "seed": 0, "parallelism": "single GPU"},
+                   "seed": 0, "parallelism": "single GPU",
+                   "scan": (f"two-level (split at chunk {lay.split_chunks})" if lay.split_chunks
+                            else "one pass")},
         "roofline": {"bound": "hbm", "kernel": "gdn_decode_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None, "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": t_k},
@@ -173,6 +175,8 @@ def main():
                     help="decode: time gdn_decode on --workload (default decode_256)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--scan-split", choices=("auto", "one", "two"), default="auto",
+                    help="the state scan's schedule: the library's choice, one pass, or two-level")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -211,7 +215,9 @@ def main():
     log(f"workload {args.workload}: T={w.t_total} N={w.n_seqs} dims={w.dims} chunk={w.chunk}")
     d = W.to_device(w, dev)
     cu = d["cu_seqlens"] if w.n_seqs > 1 else None
-    opts = G.options(chunk=w.chunk)
+    split = {"auto": G.SCAN_AUTO, "one": G.SCAN_ONE_PASS, "two": G.SCAN_TWO_LEVEL}[args.scan_split]
+    opts = G.options(chunk=w.chunk, scan_split=split)
+    lay = G.gdn_get_workspace_layout(d["q"], d["k"], d["v"], cu, opts=opts)
     full = G.PreparedPrefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, d["init_state"],
                              d["out"], d["final_state"], opts=opts)
     pre = full.with_stages(G.STAGE_TABLE | G.STAGE_WY)
@@ -265,7 +271,9 @@ def main():
         "config": {"workload": args.workload, "T": w.t_total, "n_seqs": w.n_seqs,
                    "hk": int(w.q.shape[1]), "hv": int(w.v.shape[1]),
                    "dk": int(w.q.shape[2]), "dv": int(w.v.shape[2]), "chunk": w.chunk,
-                   "seed": 0, "parallelism": "single GPU"},
+                   "seed": 0, "parallelism": "single GPU",
+                   "scan": (f"two-level (split at chunk {lay.split_chunks})" if lay.split_chunks
+                            else "one pass")},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": nbytes,
