@@ -21,6 +21,7 @@ STATUS_NAMES = {0: "GDN_OK", -1: "GDN_ERR_NULL_ARG", -2: "GDN_ERR_DTYPE",
                 -7: "GDN_ERR_HIP"}
 STAGE_TABLE, STAGE_WY, STAGE_SCAN, STAGE_ALL = 1, 2, 4, 7
 SCAN_AUTO, SCAN_ONE_PASS, SCAN_TWO_LEVEL = 0, 1, 2
+FLAG_BETA_LOGITS = 1
 EXPORTED = ("gdn_abi_version", "gdn_default_options", "gdn_prefill",
             "gdn_prefill_ex", "gdn_workspace_size", "gdn_get_workspace_layout",
             "gdn_decode", "gdn_graph_cache_create", "gdn_graph_cache_destroy",
@@ -39,7 +40,7 @@ class GdnTensor(ctypes.Structure):
 class GdnOptions(ctypes.Structure):
     _fields_ = [("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("l2_eps", ctypes.c_float), ("stages", ctypes.c_uint32),
-                ("scan_split", ctypes.c_int32)]
+                ("scan_split", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
 class GdnWorkspaceLayout(ctypes.Structure):
@@ -133,10 +134,12 @@ def _ref(d):
 
 
 def options(chunk: int = 0, scale: float = 1.0, l2_eps: float = 1e-6,
-            stages: int = STAGE_ALL, scan_split: int = 0) -> GdnOptions:
-    """scan_split: SCAN_AUTO (0), SCAN_ONE_PASS (1) or SCAN_TWO_LEVEL (2)."""
+            stages: int = STAGE_ALL, scan_split: int = 0, beta_logits: bool = False) -> GdnOptions:
+    """scan_split: SCAN_AUTO (0), SCAN_ONE_PASS (1) or SCAN_TWO_LEVEL (2);
+    beta_logits: beta holds raw projections b and the kernels use sigmoid(b)."""
     o = GdnOptions()
     o.chunk, o.scale, o.l2_eps, o.stages, o.scan_split = chunk, scale, l2_eps, stages, scan_split
+    o.flags = FLAG_BETA_LOGITS if beta_logits else 0
     return o
 
 

@@ -122,6 +122,7 @@ struct Problem {
   float scale = 1.f, eps = 1e-6f;
   uint32_t stages = GDN_STAGE_ALL;
   int scan_split = GDN_SCAN_AUTO;
+  bool beta_logits = false;
   int split = 0;  // two-level scan: chunks in the first segment (0: one pass)
 };
 
@@ -174,11 +175,13 @@ int resolve_options(const gdn_options* opts, bool bf16, Problem* P) {
   if ((o.stages & ~GDN_STAGE_ALL) != 0) return fail(GDN_ERR_SHAPE, "unknown stage bits 0x%x", o.stages);
   if (o.scan_split < GDN_SCAN_AUTO || o.scan_split > GDN_SCAN_TWO_LEVEL)
     return fail(GDN_ERR_SHAPE, "unknown scan_split %d", o.scan_split);
+  if (o.flags & ~GDN_FLAG_BETA_LOGITS) return fail(GDN_ERR_SHAPE, "unknown flag bits 0x%x", o.flags);
   P->chunk = chunk;
   P->scale = o.scale;
   P->eps = o.l2_eps;
   P->stages = o.stages;
   P->scan_split = o.scan_split;
+  P->beta_logits = (o.flags & GDN_FLAG_BETA_LOGITS) != 0;
   return GDN_OK;
 }
 
@@ -361,6 +364,7 @@ int validate_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* 
   gdn_default_options(&o);
   if (opts) o = *opts;
   if (!(o.l2_eps >= 0.f)) return fail(GDN_ERR_SHAPE, "l2_eps must be >= 0");
+  if (o.flags & ~GDN_FLAG_BETA_LOGITS) return fail(GDN_ERR_SHAPE, "unknown flag bits 0x%x", o.flags);
   d->q = q->data; d->k = k->data; d->v = v->data; d->out = out->data;
   d->g = (const float*)g->data; d->beta = (const float*)beta->data; d->state = (float*)state->data;
   d->q_st = q->stride[0]; d->q_sh = q->stride[1];
@@ -371,6 +375,7 @@ int validate_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* 
   d->b_st = beta->stride[0]; d->b_sh = beta->stride[1];
   d->n = (int32_t)N; d->hk = (int32_t)hk; d->hv = (int32_t)hv; d->dv = (int32_t)dv;
   d->scale = o.scale; d->eps = o.l2_eps;
+  d->beta_logits = (o.flags & GDN_FLAG_BETA_LOGITS) ? 1 : 0;
   *bf16 = q->dtype == GDN_DTYPE_BF16;
   *dk = (int)dkk;
   return GDN_OK;
@@ -432,6 +437,7 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
     wp.map = map;
     wp.im = im;
     wp.n_items = (int32_t)(P.max_chunks * P.hk);
+    wp.beta_logits = P.beta_logits ? 1 : 0;
     if ((e = gdn::launch_wy(P.bf16, P.chunk, P.dk, wp, s)) != hipSuccess)
       return fail(GDN_ERR_HIP, "WY launch: %s", hipGetErrorString(e));
   }
@@ -482,6 +488,7 @@ void gdn_default_options(gdn_options* opts) {
   opts->l2_eps = 1e-6f;
   opts->stages = GDN_STAGE_ALL;
   opts->scan_split = GDN_SCAN_AUTO;
+  opts->flags = 0;
 }
 
 const char* gdn_status_string(int status) {

@@ -52,6 +52,7 @@ struct WyParams {
   int64_t g_st, g_sh, b_st, b_sh;
   int32_t hk, hv, dv;
   int32_t n_items;    // (chunk, key head) work items: max_chunks * hk
+  int32_t beta_logits;  // 1: beta holds logits b, the kernel takes sigmoid(b)
   float scale, eps;
   ChunkMap map;
   Intermediates im;
@@ -89,6 +90,7 @@ struct DecodeParams {
   int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;
   int64_t g_st, g_sh, b_st, b_sh;
   int32_t n, hk, hv, dv;
+  int32_t beta_logits;   // 1: beta holds logits b, the kernel takes sigmoid(b)
   float scale, eps;
 };
 

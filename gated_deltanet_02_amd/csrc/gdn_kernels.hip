@@ -490,6 +490,8 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       if (lane < C) {
         const float eg = fast_exp(x);
         sGam[lane] = x;
+        // a logit b of a real token becomes sigmoid(b); padded rows stay 0
+        if (p.beta_logits && lane < n) bv = 1.f / (1.f + fast_exp(-bv));
         sBeta[lane] = bv;
         sEg[lane] = eg;
         sKs[lane] = sRk[lane] * fast_exp(glast - x);
@@ -1390,7 +1392,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   __syncthreads();
   const float rq = snorm[0], rk = snorm[1];
   const float g = p.g[(int64_t)i * p.g_st + (int64_t)h * p.g_sh];
-  const float beta = p.beta[(int64_t)i * p.b_st + (int64_t)h * p.b_sh];
+  float beta = p.beta[(int64_t)i * p.b_st + (int64_t)h * p.b_sh];
+  if (p.beta_logits) beta = 1.f / (1.f + __expf(-beta));
   const float alpha = expf(g);
   const float vj = to_float(((const TI*)p.v)[(int64_t)i * p.v_st + (int64_t)h * p.v_sh + j]);
 

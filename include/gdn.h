@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 /* Status codes. */
 #define GDN_OK 0
@@ -96,7 +96,17 @@ typedef struct gdn_options {
   float l2_eps;       /* epsilon inside the L2 norm's square root (1e-6)     */
   uint32_t stages;    /* GDN_STAGE_* mask (default GDN_STAGE_ALL)            */
   int32_t scan_split; /* GDN_SCAN_* (default GDN_SCAN_AUTO)                  */
+  uint32_t flags;     /* GDN_FLAG_* (default 0)                              */
 } gdn_options;
+
+/*
+ * GDN_FLAG_BETA_LOGITS: `beta` holds the write gate's raw projection b, and
+ * the kernels use beta = sigmoid(b) = 1 / (1 + e^-b), computed in fp32 as the
+ * gate is loaded ("Gated Delta Networks": beta in (0, 1) from a sigmoid), so
+ * no separate activation pass over [T, Hv] runs before the prefill or the
+ * decode step.  b = +-inf give beta = 1 / 0.
+ */
+#define GDN_FLAG_BETA_LOGITS 1u
 
 /*
  * The state scan's schedule.  Each chunk maps its incoming state affinely

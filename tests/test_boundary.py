@@ -45,7 +45,7 @@ def test_abi_version_and_defaults(lib):
     ver = int(re.search(r"#define GDN_ABI_VERSION (\d+)", src).group(1))
     assert G.gdn_abi_version() == ver
     o = G.gdn_default_options()
-    assert (o.chunk, o.scale, o.stages, o.scan_split) == (0, 1.0, 7, 0)
+    assert (o.chunk, o.scale, o.stages, o.scan_split, o.flags) == (0, 1.0, 7, 0, 0)
     assert abs(o.l2_eps - 1e-6) < 1e-12
     for s in range(-7, 1):
         assert G.gdn_status_string(s) != "unknown status"
@@ -162,6 +162,22 @@ def test_workspace_size_formula(lib):
     offs2 = [lay2.oloc, lay2.split_y, lay2.split_hmid, lay2.split_hmid_t, lay2.split_psi, lay2.split_phi]
     assert all(o % 256 == 0 for o in offs2) and offs2 == sorted(offs2)
     assert G.gdn_workspace_size(q, q, v, opts=two) == lay2.total_bytes
+
+
+def test_flags_option(lib):
+    """Unknown flag bits are rejected by the prefill and the decode step."""
+    a = base()
+    o = B.options()
+    o.flags = 2
+    assert call(lib, a["q"], a["k"], a["v"], a["g"], a["b"], out=a["out"], opts=o) == -3
+    o.flags = B.FLAG_BETA_LOGITS
+    N, hk, hv, dk, dv = 2, 1, 1, 16, 16
+    r = ctypes.byref
+    q, v = fake((N, hk, dk), torch.bfloat16), fake((N, hv, dv), torch.bfloat16)
+    g, st = fake((N, hv), torch.float32), fake((N, hv, dk, dv), torch.float32)
+    bad = B.options()
+    bad.flags = 0x10
+    assert lib.gdn_decode(r(q), r(q), r(v), r(g), r(g), r(st), r(v), r(bad), None) == -3
 
 
 def test_scan_split_option(lib):
