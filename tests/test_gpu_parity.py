@@ -39,6 +39,26 @@ REDUCED = [
 ]
 
 
+# Enough (sequence, value head) pairs that 16-column slices would outnumber
+# the compute units, so the scan runs two slices per workgroup; every output
+# is checked.
+GROUPED = [
+    ("long_16k_gqa", dict(lengths=[300], hk=16, hv=48)),
+    ("packed_255", dict(lengths=("uniform", 40, 1, 200), hk=8, hv=8)),
+    ("prompt_4k", dict(lengths=[150] * 3, hk=12, hv=12, dk=64, dv=128)),
+]
+
+
+@pytest.mark.parametrize("name,kw", GROUPED, ids=[f"{n}-{i}" for i, (n, _) in enumerate(GROUPED)])
+def test_reduced_two_slice_groups(name, kw):
+    w = W.make_workload(name, **kw)
+    heads = w.n_seqs * w.v.shape[1]
+    assert heads * w.v.shape[2] // 16 > 256, "the case must queue one-slice workgroups"
+    out, fin, _ = U.run_gpu(w)
+    ro, rf = _ref(w)
+    U.check_bf16(out, fin, ro, rf, label=f"two-slice groups {name} {kw}")
+
+
 @pytest.mark.parametrize("name,kw", REDUCED, ids=[f"{n}-{i}" for i, (n, _) in enumerate(REDUCED)])
 def test_reduced_bf16(name, kw):
     w = W.make_workload(name, **kw)
