@@ -147,9 +147,7 @@ def decode_main(args, torch, G, W, dev):
         "dtype": "f32 (bf16 inputs)", "data": "synthetic (seeded; state ~ N(0, 0.5^2))",
         "config": {"workload": args.workload, "n_seqs": w.n_seqs, "hk": int(w.q.shape[1]),
                    "hv": int(w.v.shape[1]), "dk": int(w.q.shape[2]), "dv": int(w.v.shape[2]),
-                   "seed": 0, "parallelism": "single GPU",
-                   "scan": (f"two-level (split at chunk {lay.split_chunks})" if lay.split_chunks
-                            else "one pass")},
+                   "seed": 0, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "gdn_decode_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None, "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": t_k},

@@ -346,7 +346,7 @@ int validate_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* 
   if (state->ndim != 4 || state->shape[0] != N || state->shape[1] != hv || state->shape[2] != dkk ||
       state->shape[3] != dv)
     return fail(GDN_ERR_SHAPE, "state must be [N, Hv, dk, dv]");
-  if (N * hv * (dv / (dv < 64 ? dv : 64)) >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "too many (sequence, head) pairs");
+  if (N * hv >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "too many (sequence, head) pairs");
   if (N > 0) {
     for (int i = 0; i < 4; ++i) {
       if (!vecs[i]->data) return fail(GDN_ERR_NULL_ARG, "%s data is NULL", names[i]);
@@ -359,6 +359,12 @@ int validate_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* 
     if (state->stride[3] != 1 || state->stride[2] != dv || state->stride[1] != dkk * dv ||
         state->stride[0] != hv * dkk * dv)
       return fail(GDN_ERR_LAYOUT, "state must be contiguous");
+    // v and out are accessed four elements at a time, the state 16 bytes at a time
+    const int64_t es = q->dtype == GDN_DTYPE_BF16 ? 2 : 4;
+    for (const gdn_tensor* t : {v, out})
+      if ((uintptr_t)t->data % (4 * es) || t->stride[0] % 4 || t->stride[1] % 4)
+        return fail(GDN_ERR_LAYOUT, "v and out rows must start on 4-element boundaries");
+    if ((uintptr_t)state->data % 16) return fail(GDN_ERR_LAYOUT, "state must be 16-byte aligned");
   }
   gdn_options o;
   gdn_default_options(&o);

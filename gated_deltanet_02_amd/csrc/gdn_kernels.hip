@@ -1349,28 +1349,39 @@ __global__ __launch_bounds__(kFixThreads) void scan_fix_kernel(ScanParams p) {
 // memory (the step a generator runs after the prefill):
 //   H <- exp(g) (I - beta k^ k^T) H + beta k^ v^T,   out = scale H^T q^.
 // It reads and writes the whole fp32 state once, so it is bound by HBM: one
-// workgroup per (sequence, value head, slice of up to 64 columns), each
-// thread holding DK / (256 / cols) rows of one column in registers.  The
-// two contractions over d_k (k^T H before the update, q^T H after it) are
-// reduced across the row groups through LDS.  Everything is fp32.
+// workgroup per (sequence, value head); each thread holds four adjacent
+// columns of a band of DK / RG rows in registers, read and written with
+// 16-byte accesses (a row of the state is one coalesced run across the
+// threads of a row group).  The two contractions over d_k (k^T H before the
+// update, q^T H after it) are reduced across the row groups through LDS.
+// Everything is fp32.
 
-constexpr int kDecodeThreads = 256;
+template <int DK, int DV>
+struct DecodeShape {
+  static constexpr int CG = DV / 4;                                    // column groups
+  static constexpr int RG = (1024 / DV) < DK ? (1024 / DV) : DK;        // row groups
+  static constexpr int NT = CG * RG;                                   // threads
+  static constexpr int RPT = DK / RG;                                  // rows per thread
+};
 
-template <typename TI, int DK>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) {
-  constexpr int NT = kDecodeThreads;
-  constexpr int MAXR = DK / 4;  // rows per thread when a slice has 64 columns
-  __shared__ float sq[DK], sk[DK], sred[NT], snorm[2];
+template <typename TI, int DK, int DV>
+__global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(DecodeParams p) {
+  using D = DecodeShape<DK, DV>;
+  constexpr int NT = D::NT, CG = D::CG, RG = D::RG, RPT = D::RPT;
+  __shared__ float sq[DK], sk[DK], snorm[2];
+  __shared__ __attribute__((aligned(16))) float sred[RG][DV];
   const int tid = threadIdx.x;
-  const int cols = p.dv < 64 ? p.dv : 64;
-  const int ngrp = NT / cols;            // row groups
-  const int rpt = DK / ngrp;             // rows per thread (<= MAXR)
-  const int n_sl = p.dv / cols;
-  const int u = blockIdx.x / n_sl, sl = blockIdx.x % n_sl;
+  const int u = blockIdx.x;
   if (u >= p.n * p.hv) return;
   const int i = u / p.hv, h = u % p.hv, kh = h / (p.hv / p.hk);
-  const int col = tid % cols, grp = tid / cols;
-  const int j = sl * cols + col;         // this thread's state column
+  const int cg = tid % CG, rg = tid / CG;
+  const int c0 = 4 * cg, r0 = rg * RPT;
+
+  // this thread's band of the state, requested first
+  float* Hs = p.state + (int64_t)u * DK * DV + (int64_t)r0 * DV + c0;
+  f32x4 hreg[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) hreg[r] = *(const f32x4*)(Hs + (int64_t)r * DV);
 
   // q and k rows and their inverse norms
   const TI* qr = (const TI*)p.q + (int64_t)i * p.q_st + (int64_t)kh * p.q_sh;
@@ -1380,58 +1391,68 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
     sk[d] = to_float(kr[d]);
   }
   __syncthreads();
-  if (tid < 128) {
-    const float* src = tid < 64 ? sq : sk;
+  if (tid < 64 * (NT >= 128 ? 2 : 1)) {
     const int l = tid & 63;
-    float s2 = 0.f;
-    for (int d = l; d < DK; d += 64) s2 += src[d] * src[d];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s2 += __shfl_xor(s2, off);
-    if (l == 0) snorm[tid >> 6] = 1.0f / sqrtf(s2 + p.eps);
+    for (int which = 0; which < (NT >= 128 ? 1 : 2); ++which) {
+      const int sel = NT >= 128 ? (tid >> 6) : which;
+      const float* src = sel == 0 ? sq : sk;
+      float s2 = 0.f;
+      for (int d = l; d < DK; d += 64) s2 += src[d] * src[d];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) s2 += __shfl_xor(s2, off);
+      if (l == 0) snorm[sel] = 1.0f / sqrtf(s2 + p.eps);
+    }
   }
-  __syncthreads();
-  const float rq = snorm[0], rk = snorm[1];
   const float g = p.g[(int64_t)i * p.g_st + (int64_t)h * p.g_sh];
   float beta = p.beta[(int64_t)i * p.b_st + (int64_t)h * p.b_sh];
   if (p.beta_logits) beta = 1.f / (1.f + __expf(-beta));
   const float alpha = expf(g);
-  const float vj = to_float(((const TI*)p.v)[(int64_t)i * p.v_st + (int64_t)h * p.v_sh + j]);
+  const f32x4 vj = load4<TI>((const TI*)p.v + (int64_t)i * p.v_st + (int64_t)h * p.v_sh + c0);
 
-  // this thread's rows r = grp * rpt .. + rpt - 1 of column j
-  float* Hc = p.state + ((int64_t)i * p.hv + h) * DK * p.dv + j;
-  const int r0 = grp * rpt;
-  float hreg[MAXR];
-  float part = 0.f;
+  // (k^T H)_j over this band, with the raw k (the norm is applied below)
+  f32x4 part = zero4();
 #pragma unroll
-  for (int r = 0; r < MAXR; ++r) {
-    if (r < rpt) {
-      hreg[r] = Hc[(int64_t)(r0 + r) * p.dv];
-      part += sk[r0 + r] * hreg[r];
-    }
+  for (int r = 0; r < RPT; ++r) {
+    const float kv = sk[r0 + r];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) part[e] += kv * hreg[r][e];
   }
-  sred[tid] = part;
+  *(f32x4*)&sred[rg][c0] = part;
   __syncthreads();
-  float kth = 0.f;  // (k^T H)_j with the raw k; the norm is applied below
-  for (int gq = 0; gq < ngrp; ++gq) kth += sred[gq * cols + col];
-  kth *= rk;
+  const float rq = snorm[0], rk = snorm[1];
+  f32x4 kth = zero4();
+  for (int q = 0; q < RG; ++q) {
+    const f32x4 t = *(const f32x4*)&sred[q][c0];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kth[e] += t[e];
+  }
   __syncthreads();
   // H' = alpha (H - beta k^ (k^T H)) + beta k^ v^T, and q^T H'
-  part = 0.f;
+  part = zero4();
 #pragma unroll
-  for (int r = 0; r < MAXR; ++r) {
-    if (r < rpt) {
-      const float kh_r = sk[r0 + r] * rk;
-      const float hn = alpha * (hreg[r] - beta * kh_r * kth) + beta * kh_r * vj;
-      Hc[(int64_t)(r0 + r) * p.dv] = hn;
-      part += sq[r0 + r] * hn;
+  for (int r = 0; r < RPT; ++r) {
+    const float kh_r = sk[r0 + r] * rk, qv = sq[r0 + r];
+    f32x4 hn;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hn[e] = alpha * (hreg[r][e] - beta * kh_r * (kth[e] * rk)) + beta * kh_r * vj[e];
+      part[e] += qv * hn[e];
     }
+    *(f32x4*)(Hs + (int64_t)r * DV) = hn;
   }
-  sred[tid] = part;
+  *(f32x4*)&sred[rg][c0] = part;
   __syncthreads();
-  if (grp == 0) {
-    float o = 0.f;
-    for (int gq = 0; gq < ngrp; ++gq) o += sred[gq * cols + col];
-    ((TI*)p.out)[(int64_t)i * p.o_st + (int64_t)h * p.o_sh + j] = from_float<TI>(p.scale * rq * o);
+  if (rg == 0) {
+    f32x4 o = zero4();
+    for (int q = 0; q < RG; ++q) {
+      const f32x4 t = *(const f32x4*)&sred[q][c0];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += t[e];
+    }
+    const float sc = p.scale * rq;
+    store4<TI>((TI*)p.out + (int64_t)i * p.o_st + (int64_t)h * p.o_sh + c0, sc * o[0], sc * o[1],
+               sc * o[2], sc * o[3]);
   }
 }
 
@@ -1595,17 +1616,27 @@ hipError_t launch_scan_two_level(int chunk, int dk, const ScanParams& p, hipStre
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(bool bf16, int dk, const DecodeParams& p, hipStream_t s) {
-  const int cols = p.dv < 64 ? p.dv : 64;
-  const dim3 grid((unsigned)((int64_t)p.n * p.hv * (p.dv / cols)));
-#define GDN_DECODE(D)                                                                       \
-  if (dk == D) {                                                                           \
-    if (bf16) hipLaunchKernelGGL((decode_kernel<gdn::bf16, D>), grid, dim3(kDecodeThreads), 0, s, p); \
-    else hipLaunchKernelGGL((decode_kernel<float, D>), grid, dim3(kDecodeThreads), 0, s, p);          \
-    return hipGetLastError();                                                              \
-  }
-  GDN_DECODE(16) GDN_DECODE(32) GDN_DECODE(64) GDN_DECODE(128)
+template <typename TI, int DK>
+static hipError_t launch_decode_dv(const DecodeParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)p.n * p.hv));
+  switch (p.dv) {
+#define GDN_DECODE(V)                                                                           \
+    case V:                                                                                     \
+      hipLaunchKernelGGL((decode_kernel<TI, DK, V>), grid, dim3(DecodeShape<DK, V>::NT), 0, s, p); \
+      return hipGetLastError();
+    GDN_DECODE(16) GDN_DECODE(32) GDN_DECODE(64) GDN_DECODE(128)
 #undef GDN_DECODE
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(bool bf16, int dk, const DecodeParams& p, hipStream_t s) {
+  switch (dk) {
+#define GDN_DECODE(D) \
+    case D: return bf16 ? launch_decode_dv<gdn::bf16, D>(p, s) : launch_decode_dv<float, D>(p, s);
+    GDN_DECODE(16) GDN_DECODE(32) GDN_DECODE(64) GDN_DECODE(128)
+#undef GDN_DECODE
+  }
   return hipErrorInvalidValue;
 }
 

@@ -231,8 +231,10 @@ int gdn_get_workspace_layout(const gdn_tensor* q, const gdn_tensor* k,
  *   q, k     [N, Hk, dk]; v, out [N, Hv, dv]; one dtype, bf16 or f32; unit
  *            stride in the last dimension
  *   g, beta  [N, Hv] f32 (same preconditions as gdn_prefill)
- *   state    f32 [N, Hv, dk, dv] contiguous, read and written in place
- *   opts     NULL or options; only scale and l2_eps are used
+ *   state    f32 [N, Hv, dk, dv] contiguous and 16-byte aligned, read and
+ *            written in place; v and out rows start on 4-element
+ *            boundaries (address and strides)
+ *   opts     NULL or options; only scale, l2_eps and flags are used
  * dk, dv in {16, 32, 64, 128}.  N = 0 enqueues nothing.  Allocates nothing.
  * Returns a GDN_* status; validation errors enqueue nothing.
  */

@@ -236,6 +236,10 @@ def test_decode_validation_errors(lib):
     assert dec(s_=tr) == LAYOUT
     lv = fake((N, hv, dv), torch.bfloat16, strides=(hv * dv * 2, dv * 2, 2))
     assert dec(v_=lv) == LAYOUT
+    # four-element alignment of v and out rows, 16-byte state
+    assert dec(v_=fake((N, hv, dv), torch.bfloat16, addr=0x10002)) == LAYOUT
+    assert dec(o_=fake((N, hv, dv), torch.bfloat16, strides=(hv * (dv + 2), dv + 2, 1))) == LAYOUT
+    assert dec(s_=fake((N, hv, dk, dv), torch.float32, addr=0x10008)) == LAYOUT
     assert G.gdn_last_error() != ""
 
 
