@@ -105,3 +105,35 @@ def test_graph_cache_evicts_least_recently_used():
     cache.clear()
     assert cache.stats()["entries"] == 0
     cache.close()
+
+
+def test_graph_replays_two_level_scan_and_beta_logits():
+    """The two-level scan (two scan launches, its workspace regions) and the
+    write gate given as logits, captured once and replayed on new inputs:
+    bit for bit the eager result each time, and the oracle on the last."""
+    kw = dict(lengths=[640], hk=2, hv=4, g_low=-0.02)
+    w0 = W.make_workload("prompt_4k", seed=0, **kw)
+    d = W.to_device(w0)
+    opts = G.options(chunk=64, scan_split=G.SCAN_TWO_LEVEL, beta_logits=True)
+    ws = G.alloc_workspace(d["q"], d["k"], d["v"], None, opts)
+    assert G.gdn_get_workspace_layout(d["q"], d["k"], d["v"], opts=opts).split_chunks > 0
+    out_e, fin_e = torch.empty_like(d["out"]), torch.empty_like(d["final_state"])
+    cache = G.GraphCache(capacity=4)
+    for it in range(3):
+        w = W.make_workload("prompt_4k", seed=20 + it, **kw)
+        _copy_inputs(d, w)
+        b = w.beta.double().numpy()
+        d["beta"].copy_(torch.from_numpy((np.log(b) - np.log1p(-b)).astype(np.float32)))
+        G.gdn_prefill_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], None, d["init_state"],
+                         out_e, fin_e, opts=opts, workspace=ws)
+        torch.cuda.synchronize()
+        cache.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], None, d["init_state"],
+                      d["out"], d["final_state"], opts=opts, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(d["out"], out_e) and torch.equal(d["final_state"], fin_e), it
+    ro, rf = oracle.reference_workload(w)
+    U.check_bf16(d["out"].float().cpu().numpy(), d["final_state"].cpu().numpy(), ro, rf,
+                 "two-level replay vs oracle", out_tol=U.BF16_OUT_MAXABS * max(1.0, float(np.abs(ro).max()) / 2))
+    st = cache.stats()
+    assert st["misses"] == 1 and st["hits"] == 2 and st["fallbacks"] == 0
+    cache.close()
