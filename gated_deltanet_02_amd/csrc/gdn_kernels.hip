@@ -352,7 +352,6 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   if (it >= p.n_items) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const TI* qg = (const TI*)p.q;
   const TI* vg = (const TI*)p.v;
   const int DV = p.dv;
   const int GPRV = DV / GR;
@@ -454,6 +453,17 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     gv = sGate[lane < C ? lane : 0];
     bv = sGate[C + (lane < C ? lane : 0)];
     if (lane >= C) gv = bv = 0.f;
+  }
+  // The q elements this wave needs for Q' (d_k tile `wave`, rows
+  // 16 j + lane % 16, four columns from 4 (lane / 16)) for every value head
+  // of the group, read before their LDS region is reused: q leaves HBM once.
+  typename Raw4<TI>::type qraw[NB];
+  if (wave < NKT) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int r = 16 * j + (lane & 15), dk0 = 16 * wave + (lane >> 4) * 4;
+      qraw[j] = *(const typename Raw4<TI>::type*)(sQ + r * LK + swz<TI, SWK>(r, dk0));
+    }
   }
   __syncthreads();
 
@@ -629,19 +639,9 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
 
     // W^T tiles (rows d_k, columns r): W[r][dk] = sum_s Tb[r][s] K[s][dk].
     // W in k-tile order to global memory, W^T [dk][r] over the dead V^T.
-    // The q rows for Q' are requested here and used after the next barrier.
     constexpr int KPW = 1;  // d_k tiles per wave
     const int i0 = wave;
-    typename Raw4<TI>::type qraw[KPW][NB];
     if (i0 < NKT) {
-#pragma unroll
-      for (int i = 0; i < KPW; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const int r = 16 * j + (lane & 15), dk0 = 16 * (i0 + i) + (lane >> 4) * 4;
-          qraw[i][j] = typename Raw4<TI>::type{};
-          if (r < n) qraw[i][j] = load_raw4<TI>(qg + (int64_t)(t0 + r) * p.q_st + kh * p.q_sh + dk0);
-        }
       TI* w_g = (TI*)p.im.w + blk * C * DK;
       f32x4 acc[KPW][NB];
 #pragma unroll
@@ -679,7 +679,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
         for (int j = 0; j < NB; ++j) {
           const int r = 16 * j + (lane & 15), dk0 = 16 * (i0 + i) + (lane >> 4) * 4;
           const float qs = p.scale * sEg[r] * sRq[r];
-          const f32x4 qv = raw4_to_f32<TI>(qraw[i][j]);
+          const f32x4 qv = raw4_to_f32<TI>(qraw[j]);
           store4<TI>(qp_g + j * 16 * DK + KTile<TI, DK>::pos(lane & 15, dk0), qs * qv[0] - acc[i][j][0],
                      qs * qv[1] - acc[i][j][1], qs * qv[2] - acc[i][j][2], qs * qv[3] - acc[i][j][3]);
         }
