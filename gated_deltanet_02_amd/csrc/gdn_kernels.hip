@@ -25,16 +25,20 @@
 //                 cumulative sum, K^K^T and Q^K^T (shared by the group), the
 //                 blocked triangular inverse and every per-chunk matrix above.
 //                 Fully parallel over chunks.
-//   scan_kernel   one workgroup per (sequence, value head, 16-column slice of
-//                 d_v): the only sequential part.  One wave runs the
-//                 recurrence with the state slice in its MFMA accumulators;
-//                 W, Q' and K~^T are stored by the WY kernel in k-tile order
-//                 (the contraction index follows the accumulator layout), so
-//                 the state and the U rows feed the MFMAs from the
-//                 registers they were accumulated in, with no exchange
-//                 through LDS.  Three more waves stream the chunks' operands
-//                 into an LDS ring with LDS-direct loads, two or three chunks
-//                 ahead.  The output is produced in the same step.
+//   scan_kernel   one workgroup per (sequence, value head, one or two
+//                 16-column slices of d_v): the only sequential part.  Per
+//                 slice one wave runs the recurrence with the state slice in
+//                 its MFMA accumulators; W, Q' and K~^T are stored by the WY
+//                 kernel in k-tile order (the contraction index follows the
+//                 accumulator layout), so the state and the U rows feed the
+//                 MFMAs from the registers they were accumulated in, with no
+//                 exchange through LDS; a second wave forms the slice's
+//                 output.  Two more waves stream the chunks' operands into
+//                 an LDS ring with LDS-direct loads, two chunks ahead.
+//   scan_split_kernel, scan_fix_kernel
+//                 the two-level form of the scan, on request (both halves of
+//                 each sequence at once, then the second half's correction).
+//   decode_kernel one token per sequence on a state in memory.
 //
 // bf16 inputs use bf16 MFMA operands with fp32 accumulation; the triangular
 // solve and every gate exponential are fp32.  fp32 inputs use fp32 MFMA

@@ -21,7 +21,7 @@
  * The library evaluates it chunk by chunk (chunk C in {16, 32, 64}, default
  * 64) on the caller's HIP stream with three kernels: a chunk table, a fused
  * L2-norm / gate-prep / intra-chunk WY kernel, and a fused inter-chunk
- * state-scan / output kernel.
+ * state-scan / output kernel (two with GDN_SCAN_TWO_LEVEL).
  *
  * Conventions taken from the pages:
  *   - a versioned ABI that callers are rebuilt against ("Cua-S1 4B 0.2
@@ -115,8 +115,9 @@ typedef struct gdn_options {
  * GDN_SCAN_TWO_LEVEL splits every sequence (at 5/8 of its chunks) and scans
  * both halves at once: the second from zero, beside the product of its M
  * (d_k more state columns), then adds M-product x (state at the split) to
- * its outputs and final state.  The chain of dependent chunk steps halves;
- * the arithmetic differs from the one-pass scan only in rounding.  Offered
+ * its outputs and final state.  The chain of dependent chunk steps shortens
+ * to 5/8 of the chunks; the arithmetic differs from the one-pass scan only
+ * in rounding.  Offered
  * for bf16 inputs without cu_seqlens (uniform sequences), d_k and d_v
  * multiples of 32 and chunks of 32 or 64; GDN_SCAN_TWO_LEVEL elsewhere is
  * GDN_ERR_UNSUPPORTED.  GDN_SCAN_AUTO is the one-pass scan (on MI355X the
