@@ -237,7 +237,7 @@ constexpr int kWyThreads = 512;  // 8 waves, one workgroup per CU
 //   kt  K^T [dk][C]                                          whole kernel
 //   kv  K rows [C][dk] -> V^T [dv][C] -> W^T [dk][C]
 //   t   V rows [C][128] -> T (f32) -> U~^T [dv][C]
-//   x   Q rows [C][dk] -> A (f32) -> Tb, Tv, P [C][C]
+//   x   Q rows [C][dk] -> P [C][C] beside A (f32) -> P beside Tb, Tv
 template <typename TI, int C, int DK>
 struct WyLayout {
   static constexpr int S = sizeof(TI);
@@ -258,7 +258,8 @@ struct WyLayout {
   static constexpr int r_t = r_kv + sz_kv;
   static constexpr int sz_t = cmax(cmax(C * LF * 4, DVM * LC * S), C * LV * S);
   static constexpr int r_x = r_t + sz_t;
-  static constexpr int sz_x = cmax(cmax(C * LK * S, C * LF * 4), 3 * C * LC * S);
+  static constexpr int sz_p = C * LC * S;  // one [C][C] bf16 tile set (P, Tb or Tv)
+  static constexpr int sz_x = cmax(cmax(C * LK * S, sz_p + C * LF * 4), 3 * sz_p);
   static constexpr int r_vec = r_x + sz_x;
   static constexpr int r_gate = r_vec + 7 * C * 4;  // g, beta of the first value head
   static constexpr int total = r_gate + 2 * C * 4;
@@ -367,10 +368,10 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   float* sT = (float*)(smem + L::r_t);
   TI* sUt = (TI*)(smem + L::r_t);    // U~^T
   TI* sQ = (TI*)(smem + L::r_x);     // Q rows
-  float* sA = (float*)(smem + L::r_x);
-  TI* sTb = (TI*)(smem + L::r_x);
+  TI* sP = (TI*)(smem + L::r_x);
+  float* sA = (float*)(smem + L::r_x + L::sz_p);
+  TI* sTb = (TI*)(smem + L::r_x + L::sz_p);
   TI* sTv = sTb + C * LC;
-  TI* sP = sTv + C * LC;
   float* sRq = (float*)(smem + L::r_vec);
   float* sRk = sRq + C;
   float* sGam = sRk + C;
@@ -536,6 +537,22 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
           a[e] = (c0 + e < r) ? br * rkc[e] * fast_exp(gr - gc[e]) * acc_gs[0][j][e] : 0.f;
         *(f32x4*)(sA + r * LF + c0) = a;
       }
+    } else if (s_wave) {
+      // P = scale D o (Q^K^T) from the (Q K^T)^T tiles: lane holds query row
+      // r = 16 rt + lane % 16 and the four consecutive keys
+      // s = 16 j + 4 (lane / 16) + e.
+      const int r = 16 * rt + (lane & 15);
+      const float qr = p.scale * sRq[r], gr = sGam[r];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int s0 = 16 * j + (lane >> 4) * 4;
+        const f32x4 gs = *(const f32x4*)(sGam + s0), rks = *(const f32x4*)(sRk + s0);
+        f32x4 pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pv[e] = (s0 + e <= r) ? qr * rks[e] * fast_exp(gr - gs[e]) * acc_gs[0][j][e] : 0.f;
+        store4<TI>(sP + r * LC + swz<TI, SWC>(r, s0), pv[0], pv[1], pv[2], pv[3]);
+      }
     }
     __syncthreads();
 
@@ -543,6 +560,19 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     // lane per column; then block rows i = 1.. by
     //   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj   (fp32 MFMA; the inner sum
     // stays in registers as the second operand).
+    // Meanwhile waves 1.. write K~^T [dk][r] = K^T[dk][r] rk_r
+    // e^(gamma_last - gamma_r), in k-tile order per 16-row tile of d_k
+    // (contraction over r), four at a time.
+    if (wave > 0) {
+      TI* kt_g = (TI*)p.im.kt + blk * DK * C;
+      for (int idx = tid - 64; idx < DK * (C / 4); idx += NT - 64) {
+        const int dk = idx / (C / 4), r0 = (idx % (C / 4)) * 4;
+        const f32x4 kv = load4<TI>(sKt + dk * LC + swz<TI, SWC>(dk, r0));
+        const f32x4 ks = *(const f32x4*)(sKs + r0);
+        store4<TI>(kt_g + (dk / 16) * 16 * C + KTile<TI, C>::pos(dk % 16, r0), kv[0] * ks[0],
+                   kv[1] * ks[1], kv[2] * ks[2], kv[3] * ks[3]);
+      }
+    }
     if (wave == 0) {
       const int b = lane >> 4, col = lane & 15;
       if (b < NB) {
@@ -582,8 +612,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       __syncthreads();
     }
 
-    // Tb = T diag(beta e^gamma rk), Tv = T diag(beta) (8 columns per item),
-    // and P = scale D o (Q^K^T) from the Q K^T tiles.
+    // Tb = T diag(beta e^gamma rk), Tv = T diag(beta) (8 columns per item).
     for (int idx = tid; idx < C * (C / 8); idx += NT) {
       const int r = idx / (C / 8), s0 = (idx % (C / 8)) * 8;
       typedef TI vec8 __attribute__((ext_vector_type(8)));
@@ -602,22 +631,6 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
         *(f32x4*)(sTb + r * LC + s0 + 4) = __builtin_shufflevector(tb, tb, 4, 5, 6, 7);
         *(f32x4*)(sTv + r * LC + s0) = __builtin_shufflevector(tv, tv, 0, 1, 2, 3);
         *(f32x4*)(sTv + r * LC + s0 + 4) = __builtin_shufflevector(tv, tv, 4, 5, 6, 7);
-      }
-    }
-    if (s_wave) {
-      // (Q K^T)^T tiles: lane holds query row r = 16 rt + lane % 16 and the
-      // four consecutive keys s = 16 j + 4 (lane / 16) + e.
-      const int r = 16 * rt + (lane & 15);
-      const float qr = p.scale * sRq[r], gr = sGam[r];
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int s0 = 16 * j + (lane >> 4) * 4;
-        const f32x4 gs = *(const f32x4*)(sGam + s0), rks = *(const f32x4*)(sRk + s0);
-        f32x4 pv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pv[e] = (s0 + e <= r) ? qr * rks[e] * fast_exp(gr - gs[e]) * acc_gs[0][j][e] : 0.f;
-        store4<TI>(sP + r * LC + swz<TI, SWC>(r, s0), pv[0], pv[1], pv[2], pv[3]);
       }
     }
     __syncthreads();
@@ -697,16 +710,6 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       mma_block_sw<1, NB, C, SWC, SWC>(acc, sUt, LC, 16 * v0, sP, LC, 0, lane);
 #pragma unroll
       for (int j = 0; j < NB; ++j) store_acc_tile<TI>(ol_g + (v0 * NB + j) * 256, acc[0][j], lane);
-    }
-    // K~^T [dk][r] = K^T[dk][r] rk_r e^(gamma_last - gamma_r), in k-tile
-    // order per 16-row tile of d_k (contraction over r), four at a time.
-    TI* kt_g = (TI*)p.im.kt + blk * DK * C;
-    for (int idx = tid; idx < DK * (C / 4); idx += NT) {
-      const int dk = idx / (C / 4), r0 = (idx % (C / 4)) * 4;
-      const f32x4 kv = load4<TI>(sKt + dk * LC + swz<TI, SWC>(dk, r0));
-      const f32x4 ks = *(const f32x4*)(sKs + r0);
-      store4<TI>(kt_g + (dk / 16) * 16 * C + KTile<TI, C>::pos(dk % 16, r0), kv[0] * ks[0],
-                 kv[1] * ks[1], kv[2] * ks[2], kv[3] * ks[3]);
     }
     if (tid == 0) p.im.decay[blk] = sEg[C - 1];
     __syncthreads();
