@@ -562,8 +562,28 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     // stays in registers as the second operand).
     // Meanwhile waves 1.. write K~^T [dk][r] = K^T[dk][r] rk_r
     // e^(gamma_last - gamma_r), in k-tile order per 16-row tile of d_k
-    // (contraction over r), four at a time.
-    if (wave > 0) {
+    // (contraction over r).  bf16: one 16-byte operand unit per lane (rows
+    // 16 dt + m, r = 32 u + 4 g + {0..3} and the same + 16), so that a
+    // wave's stores cover one contiguous KiB; otherwise four at a time.
+    if constexpr (sizeof(TI) == 2 && C % 32 == 0) {
+      if (wave > 0) {
+        TI* kt_g = (TI*)p.im.kt + blk * DK * C;
+        for (int idx = tid - 64; idx < DK * (C / 8); idx += NT - 64) {
+          const int m = idx & 15, g = (idx >> 4) & 3, u = (idx >> 6) % (C / 32);
+          const int dk = 16 * (idx / (2 * C)) + m, ra = 32 * u + 4 * g;
+          const f32x4 ka = load4<TI>(sKt + dk * LC + swz<TI, SWC>(dk, ra));
+          const f32x4 kb = load4<TI>(sKt + dk * LC + swz<TI, SWC>(dk, ra + 16));
+          const f32x4 sa = *(const f32x4*)(sKs + ra), sb = *(const f32x4*)(sKs + ra + 16);
+          bf16x8 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] = from_float<TI>(ka[e] * sa[e]);
+            o[4 + e] = from_float<TI>(kb[e] * sb[e]);
+          }
+          *(bf16x8*)(kt_g + (dk / 16) * 16 * C + KTile<TI, C>::pos(m, ra)) = o;
+        }
+      }
+    } else if (wave > 0) {
       TI* kt_g = (TI*)p.im.kt + blk * DK * C;
       for (int idx = tid - 64; idx < DK * (C / 4); idx += NT - 64) {
         const int dk = idx / (C / 4), r0 = (idx % (C / 4)) * 4;
