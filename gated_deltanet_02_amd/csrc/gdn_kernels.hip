@@ -454,10 +454,28 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) settle(acc_gs[0][j]);
   }
+  // The gate cumulative sum gamma, beta (sigmoid of a logit for a real
+  // token; padded rows stay 0) and e^gamma of the value head whose g and
+  // beta are in gv, bv (wave 0).
+  auto gate_scan = [&]() {
+    float x = gv;  // inclusive scan over the chunk
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane < C) {
+      sGam[lane] = x;
+      if (p.beta_logits && lane < n) bv = 1.f / (1.f + fast_exp(-bv));
+      sBeta[lane] = bv;
+      sEg[lane] = fast_exp(x);
+    }
+  };
   if (wave == 0) {
     gv = sGate[lane < C ? lane : 0];
     bv = sGate[C + (lane < C ? lane : 0)];
     if (lane >= C) gv = bv = 0.f;
+    gate_scan();  // the first value head's, beside the Gram products
   }
   // The q elements this wave needs for Q' (d_k tile `wave`, rows
   // 16 j + lane % 16, four columns from 4 (lane / 16)) for every value head
@@ -482,8 +500,9 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     const int tid = tid_h, lane = tid_h & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid_h >> 6);
 
-    // v rows into the T region (the first head's are there already) and
-    // the gate scan; then the next value head's inputs are requested.
+    // Later value heads: v rows into the T region (the first head's are
+    // there already) and the gate scan.  Then the next value head's inputs
+    // are requested.
     if (gi > 0) {
 #pragma unroll
       for (int i = 0; i < NVG; ++i) {
@@ -493,28 +512,10 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
           st16(sVr + r * LV + swz<TI, SWV>(r, gc * GR), vreg[i]);
         }
       }
-    }
-    if (wave == 0) {
-      float x = gv;  // inclusive scan over the chunk
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-      }
-      const float glast = __shfl(x, C - 1);
-      if (lane < C) {
-        const float eg = fast_exp(x);
-        sGam[lane] = x;
-        // a logit b of a real token becomes sigmoid(b); padded rows stay 0
-        if (p.beta_logits && lane < n) bv = 1.f / (1.f + fast_exp(-bv));
-        sBeta[lane] = bv;
-        sEg[lane] = eg;
-        sKs[lane] = sRk[lane] * fast_exp(glast - x);
-        sCb[lane] = bv * eg * sRk[lane];
-      }
+      if (wave == 0) gate_scan();
     }
     if (gi + 1 < grp) load_head(h + 1);
-    __syncthreads();
+    if (gi > 0) __syncthreads();
 
     // V^T [dv][s] from the v rows, and A from the K K^T tiles:
     // A_rs = beta_r exp(gamma_r - gamma_s) rk_r rk_s (k_r . k_s), s < r
@@ -537,6 +538,13 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
           a[e] = (c0 + e < r) ? br * rkc[e] * fast_exp(gr - gc[e]) * acc_gs[0][j][e] : 0.f;
         *(f32x4*)(sA + r * LF + c0) = a;
       }
+      if (wave == NB - 1 && lane < C) {
+        // the K~ row scale rk_r e^(gamma_last - gamma_r) and Tb's column
+        // scale beta_s e^gamma_s rk_s
+        const float rk = sRk[lane];
+        sKs[lane] = rk * fast_exp(sGam[C - 1] - sGam[lane]);
+        sCb[lane] = sBeta[lane] * sEg[lane] * rk;
+      }
     } else if (s_wave) {
       // P = scale D o (Q^K^T) from the (Q K^T)^T tiles: lane holds query row
       // r = 16 rt + lane % 16 and the four consecutive keys
@@ -557,9 +565,9 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     __syncthreads();
 
     // T = (I + A)^-1.  Diagonal 16x16 blocks by forward substitution, one
-    // lane per column; then block rows i = 1.. by
-    //   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj   (fp32 MFMA; the inner sum
-    // stays in registers as the second operand).
+    // lane per column; then the blocks below the diagonal,
+    //   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj   (fp32 MFMA, block column j
+    // on wave j).
     // Meanwhile waves 1.. write K~^T [dk][r] = K^T[dk][r] rk_r
     // e^(gamma_last - gamma_r), in k-tile order per 16-row tile of d_k
     // (contraction over r).  bf16: one 16-byte operand unit per lane (rows
@@ -615,22 +623,38 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       }
     }
     __syncthreads();
-    for (int bi = 1; bi < NB; ++bi) {
-      if (wave < bi) {
-        const int bj = wave;
-        f32x4 m = zero4();
-        for (int bk = bj; bk < bi; ++bk)
-          mma16_f32_kn(m, sA + (16 * bi) * LF + 16 * bk, LF, sT + (16 * bk) * LF + 16 * bj, LF, lane);
-        settle(m);
-        f32x4 t = zero4();
-        mma16_f32_acc_b(t, sT + (16 * bi) * LF + 16 * bi, LF, m, lane);
-        settle(t);
-        float* dst = sT + (16 * bi) * LF + 16 * bj;
+    // Wave j takes block column j down the rows: every T_kj its sums need
+    // is one it made itself, kept in registers in the accumulator layout
+    // (lane (r, q) holds rows 4 q + e of column r), which is the second
+    // operand's layout for the next product, so the column needs no
+    // exchange and no barrier between block rows.
+    if (wave < NB - 1) {
+      const int bj = wave, r = lane & 15, q = lane >> 4;
+      f32x4 tcol[NB];  // T_(bj+d, bj), d = 0..
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[((lane >> 4) * 4 + e) * LF + (lane & 15)] = -t[e];
+      for (int e = 0; e < 4; ++e) tcol[0][e] = sT[(16 * bj + 4 * q + e) * LF + 16 * bj + r];
+#pragma unroll
+      for (int di = 1; di < NB; ++di) {
+        const int bi = bj + di;
+        if (bi < NB) {
+          f32x4 m = zero4();
+#pragma unroll
+          for (int dk = 0; dk < di; ++dk)
+            mma16_f32_acc_b(m, sA + (16 * bi) * LF + 16 * (bj + dk), LF, tcol[dk], lane);
+          settle(m);
+          f32x4 t = zero4();
+          mma16_f32_acc_b(t, sT + (16 * bi) * LF + 16 * bi, LF, m, lane);
+          settle(t);
+          float* dst = sT + (16 * bi) * LF + 16 * bj;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            tcol[di][e] = -t[e];
+            dst[(4 * q + e) * LF + r] = -t[e];
+          }
+        }
       }
-      __syncthreads();
     }
+    __syncthreads();
 
     // Tb = T diag(beta e^gamma rk), Tv = T diag(beta) (8 columns per item).
     for (int idx = tid; idx < C * (C / 8); idx += NT) {
