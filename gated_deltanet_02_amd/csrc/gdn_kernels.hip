@@ -229,21 +229,42 @@ __device__ __forceinline__ void row_inv_norms(const TI* src, int lds, int R,
 // ---------------------------------------------------------------------------
 // WY kernel
 
+// One k-tile-order operand unit (see KTile) of row `row` of a row-major LDS
+// matrix: bf16 elements 32 u + 4 q + {0..3} and 32 u + 16 + 4 q + {0..3}
+// (q = lane / 16; a half unit leaves the second four zero), fp32 elements
+// 16 u + 4 q + {0..3}.  It pairs with an operand unit built from
+// accumulator tiles (acc_unit) over the same contraction order.
+template <typename TI, bool HALF, int SW>
+__device__ __forceinline__ typename Unit<TI>::type row_unit(const TI* m, int ld, int row, int u,
+                                                            int lane) {
+  const int q = lane >> 4;
+  if constexpr (sizeof(TI) == 2) {
+    const TI* base = m + row * ld;
+    const uint2 lo = *(const uint2*)(base + swz<TI, SW>(row, 32 * u + 4 * q));
+    uint2 hi = make_uint2(0u, 0u);
+    if constexpr (!HALF) hi = *(const uint2*)(base + swz<TI, SW>(row, 32 * u + 16 + 4 * q));
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+  } else {
+    return *(const f32x4*)(m + row * ld + 16 * u + 4 * q);
+  }
+}
+
 constexpr int kWyThreads = 512;  // 8 waves, one workgroup per CU
 
 // LDS plan of the WY kernel (bytes).  bf16 tiles are stored unpadded with
 // row-swizzled 16-byte granules; fp32 tiles (and fp32 inputs) use rows padded
 // by 16 bytes.  Regions are reused as their contents die:
 //   kt  K^T [dk][C]                                          whole kernel
-//   kv  K rows [C][dk] -> V^T [dv][C] -> W^T [dk][C]
-//   t   V rows [C][128] -> T (f32) -> U~^T [dv][C]
+//   kv  K rows [C][dk] -> V^T [dv][C]
+//   t   V rows [C][128] -> T (f32) -> W^T [dk][C]
 //   x   Q rows [C][dk] -> P [C][C] beside A (f32) -> P beside Tb, Tv
 template <typename TI, int C, int DK>
 struct WyLayout {
   static constexpr int S = sizeof(TI);
   static constexpr bool SWIZ = S == 2;
   static constexpr int PK = SWIZ ? 0 : 16 / S;
-  static constexpr int DVM = 128;  // largest d_v
+  static constexpr int DVM = 128;  // largest d_v (and d_k: W^T [dk][C] uses the t region)
+  static_assert(DK <= DVM, "d_k up to 128");
   static constexpr int LK = DK + PK;
   static constexpr int LV = DVM + PK;
   static constexpr int LC = C + PK;
@@ -363,10 +384,10 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   const int NVT = DV / 16;
   const int grp = p.hv / p.hk;
   TI* sKt = (TI*)(smem + L::r_kt);
-  TI* sKV = (TI*)(smem + L::r_kv);   // K rows | V^T | W^T
+  TI* sKV = (TI*)(smem + L::r_kv);   // K rows | V^T
   TI* sVr = (TI*)(smem + L::r_t);    // V rows
   float* sT = (float*)(smem + L::r_t);
-  TI* sUt = (TI*)(smem + L::r_t);    // U~^T
+  TI* sWt = (TI*)(smem + L::r_t);    // W^T
   TI* sQ = (TI*)(smem + L::r_x);     // Q rows
   TI* sP = (TI*)(smem + L::r_x);
   float* sA = (float*)(smem + L::r_x + L::sz_p);
@@ -679,27 +700,47 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     }
     __syncthreads();
 
-    // U~ = Tv V (all chunk row tiles x d_v tile `wave`): accumulator tiles
-    // to global memory, U~^T [dv][r] into the T region.
+    // U~ = Tv V (all chunk row tiles x d_v tile `wave`), its accumulator
+    // tiles to global memory; then O_loc = P U~ as O_loc^T tiles (d_v tile
+    // `wave`, chunk tile jr) = sum_s U~^T[dv][s] P[r][s], with U~^T taken
+    // straight from the accumulators as operand units (contraction in
+    // k-tile order) and P's rows read in the same order.
     TI* ut_g = (TI*)p.im.ut + blk * DV * C;
+    TI* ol_g = (TI*)p.im.oloc + blk * C * DV;
     if (wave < NVT) {
-      const int j = wave;
+      using KT = KTile<TI, C>;
+      constexpr int NUF = KT::HALF_TAIL ? KT::NU - 1 : KT::NU;  // full units
+      const int j = wave, rr = lane & 15;
       f32x4 acc[NB][1];
 #pragma unroll
       for (int i = 0; i < NB; ++i) acc[i][0] = zero4();
       mma_block_sw<NB, 1, C, SWC, SWC>(acc, sTv, LC, 0, sKV, LC, 16 * j, lane);
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int dv = 16 * j + (lane & 15), r0 = 16 * i + (lane >> 4) * 4;
-        store_acc_tile<TI>(ut_g + (j * NB + i) * 256, acc[i][0], lane);
-        store4<TI>(sUt + dv * LC + swz<TI, SWC>(dv, r0), acc[i][0][0], acc[i][0][1], acc[i][0][2],
-                   acc[i][0][3]);
+      for (int i = 0; i < NB; ++i) store_acc_tile<TI>(ut_g + (j * NB + i) * 256, acc[i][0], lane);
+      f32x4 ol[NB];
+#pragma unroll
+      for (int jr = 0; jr < NB; ++jr) ol[jr] = zero4();
+#pragma unroll
+      for (int u = 0; u < NUF; ++u) {
+        constexpr int T1 = KT::TPU == 2 ? 1 : 0;
+        const auto ua = acc_unit<false>(acc[KT::TPU * u][0], acc[KT::TPU * u + T1][0], TI());
+#pragma unroll
+        for (int jr = 0; jr < NB; ++jr)
+          mma_unit<false>(ol[jr], ua, row_unit<TI, false, SWC>(sP, LC, 16 * jr + rr, u, lane));
       }
+      if constexpr (KT::HALF_TAIL) {
+        constexpr int u = KT::NU - 1;
+        const auto ua = acc_unit<true>(acc[KT::TPU * u][0], acc[KT::TPU * u][0], TI());
+#pragma unroll
+        for (int jr = 0; jr < NB; ++jr)
+          mma_unit<true>(ol[jr], ua, row_unit<TI, true, SWC>(sP, LC, 16 * jr + rr, u, lane));
+      }
+#pragma unroll
+      for (int jr = 0; jr < NB; ++jr) store_acc_tile<TI>(ol_g + (j * NB + jr) * 256, ol[jr], lane);
     }
-    __syncthreads();
 
     // W^T tiles (rows d_k, columns r): W[r][dk] = sum_s Tb[r][s] K[s][dk].
-    // W in k-tile order to global memory, W^T [dk][r] over the dead V^T.
+    // W in k-tile order to global memory, W^T [dk][r] over the dead T.
     constexpr int KPW = 1;  // d_k tiles per wave
     const int i0 = wave;
     if (i0 < NKT) {
@@ -719,13 +760,12 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
                      acc[i][j][2], acc[i][j][3]);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sKV[(dk0 + e) * LC + swz<TI, SWC>(dk0 + e, r)] = from_float<TI>(acc[i][j][e]);
+            sWt[(dk0 + e) * LC + swz<TI, SWC>(dk0 + e, r)] = from_float<TI>(acc[i][j][e]);
         }
     }
     __syncthreads();
 
-    // Q' = scale diag(e^gamma rq) Q - P W (Q'^T tiles, k-tile order), and
-    // O_loc = P U~ (O_loc^T tiles).
+    // Q' = scale diag(e^gamma rq) Q - P W (Q'^T tiles, k-tile order).
     if (i0 < NKT) {
       TI* qp_g = (TI*)p.im.qp + blk * C * DK;
       f32x4 acc[KPW][NB];
@@ -733,7 +773,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       for (int i = 0; i < KPW; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = zero4();
-      mma_block_sw<KPW, NB, C, SWC, SWC>(acc, sKV, LC, 16 * i0, sP, LC, 0, lane);
+      mma_block_sw<KPW, NB, C, SWC, SWC>(acc, sWt, LC, 16 * i0, sP, LC, 0, lane);
 #pragma unroll
       for (int i = 0; i < KPW; ++i)
 #pragma unroll
@@ -744,16 +784,6 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
           store4<TI>(qp_g + j * 16 * DK + KTile<TI, DK>::pos(lane & 15, dk0), qs * qv[0] - acc[i][j][0],
                      qs * qv[1] - acc[i][j][1], qs * qv[2] - acc[i][j][2], qs * qv[3] - acc[i][j][3]);
         }
-    }
-    TI* ol_g = (TI*)p.im.oloc + blk * C * DV;
-    if (wave < NVT) {
-      const int v0 = wave;
-      f32x4 acc[1][NB];
-#pragma unroll
-      for (int j = 0; j < NB; ++j) acc[0][j] = zero4();
-      mma_block_sw<1, NB, C, SWC, SWC>(acc, sUt, LC, 16 * v0, sP, LC, 0, lane);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) store_acc_tile<TI>(ol_g + (v0 * NB + j) * 256, acc[0][j], lane);
     }
     if (tid == 0) p.im.decay[blk] = sEg[C - 1];
     __syncthreads();
