@@ -165,30 +165,6 @@ __global__ __launch_bounds__(1024) void table_kernel(TableParams p) {
 // ---------------------------------------------------------------------------
 // LDS helpers (whole workgroup)
 
-// dst[d][r] = src[r][d] for r < R (even), d < D (multiple of a granule).
-// Pairs of rows are packed so each LDS write carries two elements.
-template <typename TI, int NT = kThreads>
-__device__ __forceinline__ void transpose_lds(const TI* src, int lds, TI* dst,
-                                              int ldd, int R, int D, int tid) {
-  constexpr int GR = Gran<TI>::n;
-  typedef TI pair_t __attribute__((ext_vector_type(2)));
-  const int npair = R / 2, ngran = D / GR;
-  for (int idx = tid; idx < npair * ngran; idx += NT) {
-    const int m = idx % npair, gc = idx / npair;
-    const uint4 va = ld16(src + (2 * m) * lds + gc * GR);
-    const uint4 vb = ld16(src + (2 * m + 1) * lds + gc * GR);
-    const TI* ea = (const TI*)&va;
-    const TI* eb = (const TI*)&vb;
-#pragma unroll
-    for (int j = 0; j < GR; ++j) {
-      pair_t pr;
-      pr[0] = ea[j];
-      pr[1] = eb[j];
-      *(pair_t*)(dst + (gc * GR + j) * ldd + 2 * m) = pr;
-    }
-  }
-}
-
 // out[r] = 1 / sqrt(sum_d src[r][d]^2 + eps); four lanes per row, each
 // reading its quarter of the row in 16-byte pieces.
 template <typename TI, int D, int NT = kThreads>
@@ -229,23 +205,74 @@ __device__ __forceinline__ void row_inv_norms(const TI* src, int lds, int R,
 // ---------------------------------------------------------------------------
 // WY kernel
 
-// One k-tile-order operand unit (see KTile) of row `row` of a row-major LDS
-// matrix: bf16 elements 32 u + 4 q + {0..3} and 32 u + 16 + 4 q + {0..3}
-// (q = lane / 16; a half unit leaves the second four zero), fp32 elements
-// 16 u + 4 q + {0..3}.  It pairs with an operand unit built from
-// accumulator tiles (acc_unit) over the same contraction order.
+// Column order of the bf16 [*][C] tiles of the WY kernel (P, Tb, Tv, W^T):
+// within each full 32-column block, column s = 32 u + 16 h + 4 q + e is
+// stored at 32 u + 8 q + 4 h + e, so that a k-tile-order operand unit (see
+// KTile: elements 32 u + 4 q + {0..3} and 32 u + 16 + 4 q + {0..3} for
+// lane group q) is 16 contiguous bytes.  A trailing half block (C % 32 ==
+// 16) and fp32 tiles keep the natural order.  kinv maps a stored position
+// back to its column.
+template <typename TI, int C>
+__device__ __forceinline__ int kperm(int s) {
+  if constexpr (sizeof(TI) != 2) return s;
+  if (s >= C / 32 * 32) return s;
+  return (s & ~31) + 8 * ((s >> 2) & 3) + 4 * ((s >> 4) & 1) + (s & 3);
+}
+template <typename TI, int C>
+__device__ __forceinline__ int kinv(int pos) {
+  if constexpr (sizeof(TI) != 2) return pos;
+  if (pos >= C / 32 * 32) return pos;
+  return (pos & ~31) + 16 * ((pos >> 2) & 1) + 4 * ((pos >> 3) & 3) + (pos & 3);
+}
+
+// One k-tile-order operand unit (see KTile) of row `row` of an LDS tile in
+// the kperm column order: bf16 columns 32 u + 4 q + {0..3} and 32 u + 16 +
+// 4 q + {0..3} (q = lane / 16; a half unit leaves the second four zero),
+// fp32 columns 16 u + 4 q + {0..3}.  It pairs with an operand unit built
+// from accumulator tiles (acc_unit) over the same contraction order.
 template <typename TI, bool HALF, int SW>
 __device__ __forceinline__ typename Unit<TI>::type row_unit(const TI* m, int ld, int row, int u,
                                                             int lane) {
   const int q = lane >> 4;
   if constexpr (sizeof(TI) == 2) {
     const TI* base = m + row * ld;
-    const uint2 lo = *(const uint2*)(base + swz<TI, SW>(row, 32 * u + 4 * q));
-    uint2 hi = make_uint2(0u, 0u);
-    if constexpr (!HALF) hi = *(const uint2*)(base + swz<TI, SW>(row, 32 * u + 16 + 4 * q));
-    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    if constexpr (HALF) {
+      const uint2 lo = *(const uint2*)(base + swz<TI, SW>(row, 32 * u + 4 * q));
+      return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, 0u, 0u));
+    } else {
+      return *(const bf16x8*)(base + swz<TI, SW>(row, 32 * u + 8 * q));
+    }
   } else {
     return *(const f32x4*)(m + row * ld + 16 * u + 4 * q);
+  }
+}
+
+// The same operand unit for column c0 + lane % 16 of a row-major LDS matrix,
+// contracting over its rows (the matrix read transposed): the unit holds
+// rows 32 u + 4 q + {0..3} and 32 u + 16 + 4 q + {0..3} (bf16), 16 u + 4 q
+// + {0..3} (fp32).  bf16 uses the LDS transpose read, which gives lane j of
+// each 16-lane group element j % 4 of the 8 bytes read by lane
+// 4 k + j / 4 as its element k: lane 4 k + c reads row 4 q + k (+ 32 u, then
+// + 16), columns c0 + 4 c .. + 3.
+template <typename TI, bool HALF, int SW>
+__device__ __forceinline__ typename Unit<TI>::type col_unit(const TI* m, int ld, int c0, int u,
+                                                            int lane) {
+  const int q = lane >> 4, j = lane & 15;
+  if constexpr (sizeof(TI) == 2) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int r = 32 * u + 4 * q + (j >> 2), c = c0 + 4 * (j & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(m + r * ld + swz<TI, SW>(r, c)));
+    s16x4 hi = {0, 0, 0, 0};
+    if constexpr (!HALF)
+      hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(m + (r + 16) * ld + swz<TI, SW>(r + 16, c)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  } else {
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = m[(16 * u + 4 * q + e) * ld + c0 + j];
+    return v;
   }
 }
 
@@ -253,17 +280,19 @@ constexpr int kWyThreads = 512;  // 8 waves, one workgroup per CU
 
 // LDS plan of the WY kernel (bytes).  bf16 tiles are stored unpadded with
 // row-swizzled 16-byte granules; fp32 tiles (and fp32 inputs) use rows padded
-// by 16 bytes.  Regions are reused as their contents die:
-//   kt  K^T [dk][C]                                          whole kernel
-//   kv  K rows [C][dk] -> V^T [dv][C]
-//   t   V rows [C][128] -> T (f32) -> W^T [dk][C]
+// by 16 bytes.  K and V stay as the rows they arrive in: the products that
+// contract over the chunk read them transposed (col_unit).  Regions are
+// reused as their contents die:
+//   kv  K rows [C][dk]                                       whole item
+//   v   V rows [C][128]                                      per value head
+//   t   T (f32) -> W^T [dk][C]
 //   x   Q rows [C][dk] -> P [C][C] beside A (f32) -> P beside Tb, Tv
 template <typename TI, int C, int DK>
 struct WyLayout {
   static constexpr int S = sizeof(TI);
   static constexpr bool SWIZ = S == 2;
   static constexpr int PK = SWIZ ? 0 : 16 / S;
-  static constexpr int DVM = 128;  // largest d_v (and d_k: W^T [dk][C] uses the t region)
+  static constexpr int DVM = 128;  // largest d_v and d_k
   static_assert(DK <= DVM, "d_k up to 128");
   static constexpr int LK = DK + PK;
   static constexpr int LV = DVM + PK;
@@ -273,13 +302,12 @@ struct WyLayout {
   static constexpr int SWC = SWIZ ? C / 8 - 1 : 0;
   static constexpr int SWV = SWIZ ? DVM / 8 - 1 : 0;
   static constexpr int cmax(int a, int b) { return a > b ? a : b; }
-  static constexpr int r_kt = 0;
-  static constexpr int r_kv = r_kt + DK * LC * S;
-  static constexpr int sz_kv = cmax(cmax(C * LK, DVM * LC), DK * LC) * S;
-  static constexpr int r_t = r_kv + sz_kv;
-  static constexpr int sz_t = cmax(cmax(C * LF * 4, DVM * LC * S), C * LV * S);
+  static constexpr int r_kv = 0;
+  static constexpr int r_v = r_kv + C * LK * S;
+  static constexpr int r_t = r_v + C * LV * S;
+  static constexpr int sz_t = cmax(C * LF * 4, DK * LC * S);
   static constexpr int r_x = r_t + sz_t;
-  static constexpr int sz_p = C * LC * S;  // one [C][C] bf16 tile set (P, Tb or Tv)
+  static constexpr int sz_p = C * LC * S;  // one [C][C] tile set (P, Tb or Tv)
   static constexpr int sz_x = cmax(cmax(C * LK * S, sz_p + C * LF * 4), 3 * sz_p);
   static constexpr int r_vec = r_x + sz_x;
   static constexpr int r_gate = r_vec + 7 * C * 4;  // g, beta of the first value head
@@ -309,32 +337,6 @@ __device__ __forceinline__ void dma_rows(char* region, const TI* src, int64_t st
   }
 }
 
-// dst[d][r] = src[r][d] for r < R (even), d < D (whole granules), with the
-// source and destination row swizzles.  Pairs of rows are packed so each LDS
-// write carries two elements.
-template <typename TI, int NT, int SWS, int SWD>
-__device__ __forceinline__ void transpose_sw(const TI* src, int lds, TI* dst, int ldd, int R, int D,
-                                             int tid) {
-  constexpr int GR = Gran<TI>::n;
-  typedef TI pair_t __attribute__((ext_vector_type(2)));
-  const int npair = R / 2, ngran = D / GR;
-  for (int idx = tid; idx < npair * ngran; idx += NT) {
-    const int m = idx % npair, gc = idx / npair;
-    const uint4 va = ld16(src + (2 * m) * lds + swz<TI, SWS>(2 * m, gc * GR));
-    const uint4 vb = ld16(src + (2 * m + 1) * lds + swz<TI, SWS>(2 * m + 1, gc * GR));
-    const TI* ea = (const TI*)&va;
-    const TI* eb = (const TI*)&vb;
-#pragma unroll
-    for (int j = 0; j < GR; ++j) {
-      pair_t pr;
-      pr[0] = ea[j];
-      pr[1] = eb[j];
-      const int row = gc * GR + j;
-      *(pair_t*)(dst + row * ldd + swz<TI, SWD>(row, 2 * m)) = pr;
-    }
-  }
-}
-
 // The inputs of the chunk (first token t0, n tokens) for key head kh: q, k
 // rows and the first value head's v rows and gates, copied straight into
 // their LDS regions (no registers).
@@ -348,7 +350,7 @@ __device__ __forceinline__ void wy_fetch(char* buf, const WyParams& p, int kh, i
                                      p.k_st, DK, n, wave, lane);
   dma_rows<TI, C, L::LK, L::SWK, NW>(buf + L::r_x, (const TI*)p.q + (int64_t)t0 * p.q_st + kh * p.q_sh,
                                      p.q_st, DK, n, wave, lane);
-  dma_rows<TI, C, L::LV, L::SWV, NW>(buf + L::r_t, (const TI*)p.v + (int64_t)t0 * p.v_st + h * p.v_sh,
+  dma_rows<TI, C, L::LV, L::SWV, NW>(buf + L::r_v, (const TI*)p.v + (int64_t)t0 * p.v_st + h * p.v_sh,
                                      p.v_st, p.dv, n, wave, lane);
   if (wave == NW - 1 && lane < n) {
     __builtin_amdgcn_global_load_lds((const void*)(p.g + (int64_t)(t0 + lane) * p.g_st + h * p.g_sh),
@@ -383,9 +385,8 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   const int GPRV = DV / GR;
   const int NVT = DV / 16;
   const int grp = p.hv / p.hk;
-  TI* sKt = (TI*)(smem + L::r_kt);
   TI* sKV = (TI*)(smem + L::r_kv);   // K rows | V^T
-  TI* sVr = (TI*)(smem + L::r_t);    // V rows
+  TI* sVr = (TI*)(smem + L::r_v);    // V rows
   float* sT = (float*)(smem + L::r_t);
   TI* sWt = (TI*)(smem + L::r_t);    // W^T
   TI* sQ = (TI*)(smem + L::r_x);     // Q rows
@@ -444,7 +445,6 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     }
   };
 
-  transpose_sw<TI, NT, SWK, SWC>(sKV, LK, sKt, LC, C, DK, tid);
   row_inv_norms<TI, DK, NT>(sKV, LK, C, p.eps, sRk, tid);  // sums are order-free: the
   row_inv_norms<TI, DK, NT>(sQ, LK, C, p.eps, sRq, tid);   // swizzle only permutes a row
 
@@ -538,10 +538,9 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     if (gi + 1 < grp) load_head(h + 1);
     if (gi > 0) __syncthreads();
 
-    // V^T [dv][s] from the v rows, and A from the K K^T tiles:
+    // A from the K K^T tiles:
     // A_rs = beta_r exp(gamma_r - gamma_s) rk_r rk_s (k_r . k_s), s < r
     // (only the strictly lower part is ever read).
-    transpose_sw<TI, NT, SWV, SWC>(sVr, LV, sKV, LC, C, DV, tid);
     if (g_wave) {
       // The Gram tile (rt, j) read transposed (K K^T is symmetric): lane
       // holds rows r = 16 j + lane % 16 (tiles j >= rt) and the four
@@ -580,7 +579,8 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           pv[e] = (s0 + e <= r) ? qr * rks[e] * fast_exp(gr - gs[e]) * acc_gs[0][j][e] : 0.f;
-        store4<TI>(sP + r * LC + swz<TI, SWC>(r, s0), pv[0], pv[1], pv[2], pv[3]);
+        const int ps = kperm<TI, C>(s0);
+        store4<TI>(sP + r * LC + swz<TI, SWC>(r, ps), pv[0], pv[1], pv[2], pv[3]);
       }
     }
     __syncthreads();
@@ -591,35 +591,38 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     // on wave j).
     // Meanwhile waves 1.. write K~^T [dk][r] = K^T[dk][r] rk_r
     // e^(gamma_last - gamma_r), in k-tile order per 16-row tile of d_k
-    // (contraction over r).  bf16: one 16-byte operand unit per lane (rows
-    // 16 dt + m, r = 32 u + 4 g + {0..3} and the same + 16), so that a
-    // wave's stores cover one contiguous KiB; otherwise four at a time.
-    if constexpr (sizeof(TI) == 2 && C % 32 == 0) {
-      if (wave > 0) {
-        TI* kt_g = (TI*)p.im.kt + blk * DK * C;
-        for (int idx = tid - 64; idx < DK * (C / 8); idx += NT - 64) {
-          const int m = idx & 15, g = (idx >> 4) & 3, u = (idx >> 6) % (C / 32);
-          const int dk = 16 * (idx / (2 * C)) + m, ra = 32 * u + 4 * g;
-          const f32x4 ka = load4<TI>(sKt + dk * LC + swz<TI, SWC>(dk, ra));
-          const f32x4 kb = load4<TI>(sKt + dk * LC + swz<TI, SWC>(dk, ra + 16));
-          const f32x4 sa = *(const f32x4*)(sKs + ra), sb = *(const f32x4*)(sKs + ra + 16);
+    // (contraction over r): one operand unit (16 d_k rows x 32 tokens for
+    // bf16) per wave and step, read transposed from the K rows and stored as
+    // one contiguous block.
+    if (wave > 0) {
+      using KC = KTile<TI, C>;
+      constexpr int TPU = KC::TPU;
+      TI* kt_g = (TI*)p.im.kt + blk * DK * C;
+      const int q = lane >> 4;
+      for (int w = wave - 1; w < (DK / 16) * KC::NU; w += NT / 64 - 1) {
+        const int dt = w / KC::NU, u = w % KC::NU;
+        const int k0 = 16 * TPU * u + 4 * q;  // first contraction index of the lane
+        TI* dst = kt_g + dt * 16 * C + KC::pos(lane & 15, k0);
+        const f32x4 sa = *(const f32x4*)(sKs + k0);
+        if (KC::HALF_TAIL && u == KC::NU - 1) {
+          const auto kv = col_unit<TI, true, SWK>(sKV, LK, 16 * dt, u, lane);
+          store4<TI>(dst, (float)kv[0] * sa[0], (float)kv[1] * sa[1], (float)kv[2] * sa[2],
+                     (float)kv[3] * sa[3]);
+        } else if constexpr (TPU == 2) {
+          const auto kv = col_unit<TI, false, SWK>(sKV, LK, 16 * dt, u, lane);
+          const f32x4 sb = *(const f32x4*)(sKs + k0 + 16);
           bf16x8 o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            o[e] = from_float<TI>(ka[e] * sa[e]);
-            o[4 + e] = from_float<TI>(kb[e] * sb[e]);
+            o[e] = from_float<TI>((float)kv[e] * sa[e]);
+            o[4 + e] = from_float<TI>((float)kv[4 + e] * sb[e]);
           }
-          *(bf16x8*)(kt_g + (dk / 16) * 16 * C + KTile<TI, C>::pos(m, ra)) = o;
+          *(bf16x8*)dst = o;
+        } else {
+          const auto kv = col_unit<TI, false, SWK>(sKV, LK, 16 * dt, u, lane);
+          store4<TI>(dst, (float)kv[0] * sa[0], (float)kv[1] * sa[1], (float)kv[2] * sa[2],
+                     (float)kv[3] * sa[3]);
         }
-      }
-    } else if (wave > 0) {
-      TI* kt_g = (TI*)p.im.kt + blk * DK * C;
-      for (int idx = tid - 64; idx < DK * (C / 4); idx += NT - 64) {
-        const int dk = idx / (C / 4), r0 = (idx % (C / 4)) * 4;
-        const f32x4 kv = load4<TI>(sKt + dk * LC + swz<TI, SWC>(dk, r0));
-        const f32x4 ks = *(const f32x4*)(sKs + r0);
-        store4<TI>(kt_g + (dk / 16) * 16 * C + KTile<TI, C>::pos(dk % 16, r0), kv[0] * ks[0],
-                   kv[1] * ks[1], kv[2] * ks[2], kv[3] * ks[3]);
       }
     }
     if (wave == 0) {
@@ -677,16 +680,18 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     }
     __syncthreads();
 
-    // Tb = T diag(beta e^gamma rk), Tv = T diag(beta) (8 columns per item).
+    // Tb = T diag(beta e^gamma rk), Tv = T diag(beta), 8 stored positions
+    // (kperm order) per item.
     for (int idx = tid; idx < C * (C / 8); idx += NT) {
       const int r = idx / (C / 8), s0 = (idx % (C / 8)) * 8;
       typedef TI vec8 __attribute__((ext_vector_type(8)));
       vec8 tb, tv;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float t = (s0 + j <= r) ? sT[r * LF + s0 + j] : 0.f;
-        tb[j] = from_float<TI>(t * sCb[s0 + j]);
-        tv[j] = from_float<TI>(t * sBeta[s0 + j]);
+        const int sc = kinv<TI, C>(s0 + j);
+        const float t = (sc <= r) ? sT[r * LF + sc] : 0.f;
+        tb[j] = from_float<TI>(t * sCb[sc]);
+        tv[j] = from_float<TI>(t * sBeta[sc]);
       }
       if constexpr (sizeof(TI) == 2) {
         *(vec8*)(sTb + r * LC + swz<TI, SWC>(r, s0)) = tb;
@@ -714,7 +719,21 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       f32x4 acc[NB][1];
 #pragma unroll
       for (int i = 0; i < NB; ++i) acc[i][0] = zero4();
-      mma_block_sw<NB, 1, C, SWC, SWC>(acc, sTv, LC, 0, sKV, LC, 16 * j, lane);
+      // B = V read transposed from its rows, A = Tv rows, both in k-tile order
+#pragma unroll
+      for (int u = 0; u < NUF; ++u) {
+        const auto vb = col_unit<TI, false, SWV>(sVr, LV, 16 * j, u, lane);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+          mma_unit<false>(acc[i][0], row_unit<TI, false, SWC>(sTv, LC, 16 * i + rr, u, lane), vb);
+      }
+      if constexpr (KT::HALF_TAIL) {
+        constexpr int u = KT::NU - 1;
+        const auto vb = col_unit<TI, true, SWV>(sVr, LV, 16 * j, u, lane);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+          mma_unit<true>(acc[i][0], row_unit<TI, true, SWC>(sTv, LC, 16 * i + rr, u, lane), vb);
+      }
 #pragma unroll
       for (int i = 0; i < NB; ++i) store_acc_tile<TI>(ut_g + (j * NB + i) * 256, acc[i][0], lane);
       f32x4 ol[NB];
@@ -750,7 +769,26 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       for (int i = 0; i < KPW; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = zero4();
-      mma_block_sw<KPW, NB, C, SWC, SWC>(acc, sKt, LC, 16 * i0, sTb, LC, 0, lane);
+      // A = K^T (K rows read transposed), B = Tb rows, in k-tile order
+      {
+        using KT = KTile<TI, C>;
+        constexpr int NUF = KT::HALF_TAIL ? KT::NU - 1 : KT::NU;
+        const int rr = lane & 15;
+#pragma unroll
+        for (int u = 0; u < NUF; ++u) {
+          const auto ka = col_unit<TI, false, SWK>(sKV, LK, 16 * i0, u, lane);
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            mma_unit<false>(acc[0][j], ka, row_unit<TI, false, SWC>(sTb, LC, 16 * j + rr, u, lane));
+        }
+        if constexpr (KT::HALF_TAIL) {
+          constexpr int u = KT::NU - 1;
+          const auto ka = col_unit<TI, true, SWK>(sKV, LK, 16 * i0, u, lane);
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            mma_unit<true>(acc[0][j], ka, row_unit<TI, true, SWC>(sTb, LC, 16 * j + rr, u, lane));
+        }
+      }
 #pragma unroll
       for (int i = 0; i < KPW; ++i)
 #pragma unroll
@@ -760,7 +798,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
                      acc[i][j][2], acc[i][j][3]);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sWt[(dk0 + e) * LC + swz<TI, SWC>(dk0 + e, r)] = from_float<TI>(acc[i][j][e]);
+            sWt[(dk0 + e) * LC + swz<TI, SWC>(dk0 + e, kperm<TI, C>(r))] = from_float<TI>(acc[i][j][e]);
         }
     }
     __syncthreads();
