@@ -205,54 +205,6 @@ __device__ __forceinline__ void row_inv_norms(const TI* src, int lds, int R,
 // ---------------------------------------------------------------------------
 // WY kernel
 
-// acc += A B for 16 x 16 fp32 tiles held in the accumulator layout (lane
-// (n, q) holds rows 4 q + e of column n): A given as its transpose's tile
-// (which puts A[m][4 q + e] in lane (m, q), the first operand's layout for
-// the contraction order k = 4 q + j of k-step j), B as its own tile.
-__device__ __forceinline__ void mma16_rr(f32x4& acc, const f32x4& at, const f32x4& b) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(at[j], b[j], acc, 0, 0, 0);
-}
-
-// (I + N)^-1 for a strictly lower 16 x 16 tile N (so N^16 = 0) as the
-// product (I - N)(I + N^2)(I + N^4)(I + N^8), every factor formed with fp32
-// MFMA in registers; n and nt are the tiles of N and N^T, the result is the
-// tile of the inverse (all in the accumulator layout).
-__device__ __forceinline__ f32x4 unit_lower_inverse16(const f32x4& n, const f32x4& nt, int lane) {
-  f32x4 id;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) id[e] = (4 * (lane >> 4) + e == (lane & 15)) ? 1.f : 0.f;
-  f32x4 x1 = zero4(), x1t = zero4(), nx1 = zero4(), x1tnt = zero4();
-  mma16_rr(x1, nt, n);     // N^2
-  mma16_rr(x1t, n, nt);    // (N^T)^2
-  mma16_rr(nx1, nt, x1);   // N N^2
-  mma16_rr(x1tnt, x1, nt); // (N^T)^2 N^T
-  f32x4 p1, p1t;           // P1 = (I - N)(I + N^2) and its transpose
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    p1[e] = id[e] - n[e] + x1[e] - nx1[e];
-    p1t[e] = id[e] - nt[e] + x1t[e] - x1tnt[e];
-  }
-  f32x4 x2 = zero4(), x2t = zero4(), p1x2 = zero4(), x2tp1t = zero4();
-  mma16_rr(x2, x1t, x1);      // N^4
-  mma16_rr(x2t, x1, x1t);     // (N^T)^4
-  mma16_rr(p1x2, p1t, x2);    // P1 N^4
-  mma16_rr(x2tp1t, x2, p1t);  // (N^T)^4 P1^T
-  f32x4 p2, p2t;              // P2 = P1 (I + N^4) and its transpose
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    p2[e] = p1[e] + p1x2[e];
-    p2t[e] = p1t[e] + x2tp1t[e];
-  }
-  f32x4 x3 = zero4(), p2x3 = zero4();
-  mma16_rr(x3, x2t, x2);      // N^8
-  mma16_rr(p2x3, p2t, x3);    // P2 N^8
-  f32x4 t;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) t[e] = p2[e] + p2x3[e];
-  return t;
-}
-
 // Column order of the bf16 [*][C] tiles of the WY kernel (P, Tb, Tv, W^T):
 // within each full 32-column block, column s = 32 u + 16 h + 4 q + e is
 // stored at 32 u + 8 q + 4 h + e, so that a k-tile-order operand unit (see
@@ -633,24 +585,21 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     }
     __syncthreads();
 
-    // T = (I + A)^-1.  Diagonal 16x16 blocks first: bf16 inputs take the
-    // product form on MFMA (one block per wave, waves 0 .. NB-1), fp32
-    // inputs forward substitution on wave 0 (one lane per column); then the
-    // blocks below the diagonal,
+    // T = (I + A)^-1.  Diagonal 16x16 blocks by forward substitution, one
+    // lane per column; then the blocks below the diagonal,
     //   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj   (fp32 MFMA, block column j
     // on wave j).
-    // Meanwhile the other waves (W0 ..) write K~^T [dk][r] = K^T[dk][r] rk_r
+    // Meanwhile waves 1.. write K~^T [dk][r] = K^T[dk][r] rk_r
     // e^(gamma_last - gamma_r), in k-tile order per 16-row tile of d_k
     // (contraction over r): one operand unit (16 d_k rows x 32 tokens for
     // bf16) per wave and step, read transposed from the K rows and stored as
     // one contiguous block.
-    constexpr int W0 = sizeof(TI) == 2 ? NB : 1;  // first K~^T wave
-    if (wave >= W0) {
+    if (wave > 0) {
       using KC = KTile<TI, C>;
       constexpr int TPU = KC::TPU;
       TI* kt_g = (TI*)p.im.kt + blk * DK * C;
       const int q = lane >> 4;
-      for (int w = wave - W0; w < (DK / 16) * KC::NU; w += NT / 64 - W0) {
+      for (int w = wave - 1; w < (DK / 16) * KC::NU; w += NT / 64 - 1) {
         const int dt = w / KC::NU, u = w % KC::NU;
         const int k0 = 16 * TPU * u + 4 * q;  // first contraction index of the lane
         TI* dst = kt_g + dt * 16 * C + KC::pos(lane & 15, k0);
@@ -676,20 +625,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
         }
       }
     }
-    if constexpr (sizeof(TI) == 2) {
-      if (wave < NB) {
-        const int b = wave, n = lane & 15, q = lane >> 4;
-        const float* Ab = sA + (16 * b) * LF + 16 * b;  // zero on and above the diagonal
-        f32x4 nd, ndt;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) nd[e] = Ab[(4 * q + e) * LF + n];
-        ndt = *(const f32x4*)(Ab + n * LF + 4 * q);
-        const f32x4 t = unit_lower_inverse16(nd, ndt, lane);
-        float* Tb = sT + (16 * b) * LF + 16 * b;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Tb[(4 * q + e) * LF + n] = t[e];
-      }
-    } else if (wave == 0) {
+    if (wave == 0) {
       const int b = lane >> 4, col = lane & 15;
       if (b < NB) {
         float x[16];
