@@ -205,7 +205,7 @@ __device__ __forceinline__ void row_inv_norms(const TI* src, int lds, int R,
 // ---------------------------------------------------------------------------
 // WY kernel
 
-// Column order of the bf16 [*][C] tiles of the WY kernel (P, Tb, Tv, W^T):
+// Column order of the bf16 [*][C] tiles of the WY kernel (P, Tb, Tv):
 // within each full 32-column block, column s = 32 u + 16 h + 4 q + e is
 // stored at 32 u + 8 q + 4 h + e, so that a k-tile-order operand unit (see
 // KTile: elements 32 u + 4 q + {0..3} and 32 u + 16 + 4 q + {0..3} for
@@ -285,7 +285,7 @@ constexpr int kWyThreads = 512;  // 8 waves, one workgroup per CU
 // reused as their contents die:
 //   kv  K rows [C][dk]                                       whole item
 //   v   V rows [C][128]                                      per value head
-//   t   T (f32) -> W^T [dk][C]
+//   t   T (f32)
 //   x   Q rows [C][dk] -> P [C][C] beside A (f32) -> P beside Tb, Tv
 template <typename TI, int C, int DK>
 struct WyLayout {
@@ -305,7 +305,7 @@ struct WyLayout {
   static constexpr int r_kv = 0;
   static constexpr int r_v = r_kv + C * LK * S;
   static constexpr int r_t = r_v + C * LV * S;
-  static constexpr int sz_t = cmax(C * LF * 4, DK * LC * S);
+  static constexpr int sz_t = C * LF * 4;
   static constexpr int r_x = r_t + sz_t;
   static constexpr int sz_p = C * LC * S;  // one [C][C] tile set (P, Tb or Tv)
   static constexpr int sz_x = cmax(cmax(C * LK * S, sz_p + C * LF * 4), 3 * sz_p);
@@ -388,7 +388,6 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   TI* sKV = (TI*)(smem + L::r_kv);   // K rows | V^T
   TI* sVr = (TI*)(smem + L::r_v);    // V rows
   float* sT = (float*)(smem + L::r_t);
-  TI* sWt = (TI*)(smem + L::r_t);    // W^T
   TI* sQ = (TI*)(smem + L::r_x);     // Q rows
   TI* sP = (TI*)(smem + L::r_x);
   float* sA = (float*)(smem + L::r_x + L::sz_p);
@@ -758,70 +757,81 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       for (int jr = 0; jr < NB; ++jr) store_acc_tile<TI>(ol_g + (j * NB + jr) * 256, ol[jr], lane);
     }
 
-    // W^T tiles (rows d_k, columns r): W[r][dk] = sum_s Tb[r][s] K[s][dk].
-    // W in k-tile order to global memory, W^T [dk][r] over the dead T.
-    constexpr int KPW = 1;  // d_k tiles per wave
+    // W[r][dk] = sum_s Tb[r][s] K[s][dk] for d_k tile `wave`, twice from the
+    // same operand registers: as W^T tiles (rows d_k, columns r), stored to
+    // global memory in k-tile order, and as W tiles (rows r, columns d_k),
+    // whose accumulators are the k-tile-order operand of
+    //   Q'^T = scale (diag(e^gamma rq) Q)^T - W^T P^T
+    // (contraction over the chunk, P's rows read in the same order), so W
+    // never goes through LDS.  A K^T operand unit (rows d_k, contraction over
+    // the chunk) holds the same registers as a K operand unit (columns d_k).
     const int i0 = wave;
     if (i0 < NKT) {
+      using KT = KTile<TI, C>;
+      constexpr int NUF = KT::HALF_TAIL ? KT::NU - 1 : KT::NU;  // full units
       TI* w_g = (TI*)p.im.w + blk * C * DK;
-      f32x4 acc[KPW][NB];
+      TI* qp_g = (TI*)p.im.qp + blk * C * DK;
+      const int rr = lane & 15;
+      f32x4 wt[NB], wr[NB];
 #pragma unroll
-      for (int i = 0; i < KPW; ++i)
+      for (int j = 0; j < NB; ++j) wt[j] = wr[j] = zero4();
 #pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = zero4();
-      // A = K^T (K rows read transposed), B = Tb rows, in k-tile order
-      {
-        using KT = KTile<TI, C>;
-        constexpr int NUF = KT::HALF_TAIL ? KT::NU - 1 : KT::NU;
-        const int rr = lane & 15;
+      for (int u = 0; u < NUF; ++u) {
+        const auto ka = col_unit<TI, false, SWK>(sKV, LK, 16 * i0, u, lane);
 #pragma unroll
-        for (int u = 0; u < NUF; ++u) {
-          const auto ka = col_unit<TI, false, SWK>(sKV, LK, 16 * i0, u, lane);
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-            mma_unit<false>(acc[0][j], ka, row_unit<TI, false, SWC>(sTb, LC, 16 * j + rr, u, lane));
-        }
-        if constexpr (KT::HALF_TAIL) {
-          constexpr int u = KT::NU - 1;
-          const auto ka = col_unit<TI, true, SWK>(sKV, LK, 16 * i0, u, lane);
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-            mma_unit<true>(acc[0][j], ka, row_unit<TI, true, SWC>(sTb, LC, 16 * j + rr, u, lane));
+        for (int j = 0; j < NB; ++j) {
+          const auto tb = row_unit<TI, false, SWC>(sTb, LC, 16 * j + rr, u, lane);
+          mma_unit<false>(wt[j], ka, tb);
+          mma_unit<false>(wr[j], tb, ka);
         }
       }
-#pragma unroll
-      for (int i = 0; i < KPW; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const int r = 16 * j + (lane & 15), dk0 = 16 * (i0 + i) + (lane >> 4) * 4;
-          store4<TI>(w_g + j * 16 * DK + KTile<TI, DK>::pos(lane & 15, dk0), acc[i][j][0], acc[i][j][1],
-                     acc[i][j][2], acc[i][j][3]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sWt[(dk0 + e) * LC + swz<TI, SWC>(dk0 + e, kperm<TI, C>(r))] = from_float<TI>(acc[i][j][e]);
-        }
-    }
-    __syncthreads();
-
-    // Q' = scale diag(e^gamma rq) Q - P W (Q'^T tiles, k-tile order).
-    if (i0 < NKT) {
-      TI* qp_g = (TI*)p.im.qp + blk * C * DK;
-      f32x4 acc[KPW][NB];
-#pragma unroll
-      for (int i = 0; i < KPW; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = zero4();
-      mma_block_sw<KPW, NB, C, SWC, SWC>(acc, sWt, LC, 16 * i0, sP, LC, 0, lane);
-#pragma unroll
-      for (int i = 0; i < KPW; ++i)
+      if constexpr (KT::HALF_TAIL) {
+        constexpr int u = KT::NU - 1;
+        const auto ka = col_unit<TI, true, SWK>(sKV, LK, 16 * i0, u, lane);
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          const int r = 16 * j + (lane & 15), dk0 = 16 * (i0 + i) + (lane >> 4) * 4;
-          const float qs = p.scale * sEg[r] * sRq[r];
-          const f32x4 qv = raw4_to_f32<TI>(qraw[j]);
-          store4<TI>(qp_g + j * 16 * DK + KTile<TI, DK>::pos(lane & 15, dk0), qs * qv[0] - acc[i][j][0],
-                     qs * qv[1] - acc[i][j][1], qs * qv[2] - acc[i][j][2], qs * qv[3] - acc[i][j][3]);
+          const auto tb = row_unit<TI, true, SWC>(sTb, LC, 16 * j + rr, u, lane);
+          mma_unit<true>(wt[j], ka, tb);
+          mma_unit<true>(wr[j], tb, ka);
         }
+      }
+      const int dk0 = 16 * i0 + (lane >> 4) * 4;
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        store4<TI>(w_g + j * 16 * DK + KTile<TI, DK>::pos(rr, dk0), wt[j][0], wt[j][1], wt[j][2],
+                   wt[j][3]);
+      typename Unit<TI>::type wu[KT::NU];
+#pragma unroll
+      for (int u = 0; u < NUF; ++u) {
+        constexpr int T1 = KT::TPU == 2 ? 1 : 0;
+        wu[u] = acc_unit<false>(wr[KT::TPU * u], wr[KT::TPU * u + T1], TI());
+      }
+      if constexpr (KT::HALF_TAIL) {
+        constexpr int u = KT::NU - 1;
+        wu[u] = acc_unit<true>(wr[KT::TPU * u], wr[KT::TPU * u], TI());
+      }
+      f32x4 pw[NB];
+#pragma unroll
+      for (int jr = 0; jr < NB; ++jr) pw[jr] = zero4();
+#pragma unroll
+      for (int u = 0; u < NUF; ++u)
+#pragma unroll
+        for (int jr = 0; jr < NB; ++jr)
+          mma_unit<false>(pw[jr], wu[u], row_unit<TI, false, SWC>(sP, LC, 16 * jr + rr, u, lane));
+      if constexpr (KT::HALF_TAIL) {
+        constexpr int u = KT::NU - 1;
+#pragma unroll
+        for (int jr = 0; jr < NB; ++jr)
+          mma_unit<true>(pw[jr], wu[u], row_unit<TI, true, SWC>(sP, LC, 16 * jr + rr, u, lane));
+      }
+#pragma unroll
+      for (int jr = 0; jr < NB; ++jr) {
+        const int r = 16 * jr + rr;
+        const float qs = p.scale * sEg[r] * sRq[r];
+        const f32x4 qv = raw4_to_f32<TI>(qraw[jr]);
+        store4<TI>(qp_g + jr * 16 * DK + KTile<TI, DK>::pos(rr, dk0), qs * qv[0] - pw[jr][0],
+                   qs * qv[1] - pw[jr][1], qs * qv[2] - pw[jr][2], qs * qv[3] - pw[jr][3]);
+      }
     }
     if (tid == 0) p.im.decay[blk] = sEg[C - 1];
     __syncthreads();
