@@ -276,6 +276,12 @@ __device__ __forceinline__ typename Unit<TI>::type col_unit(const TI* m, int ld,
   }
 }
 
+// A compile-time flag passed as a value (selects a branch-free product pass).
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 constexpr int kWyThreads = 512;  // 8 waves, one workgroup per CU
 
 // LDS plan of the WY kernel (bytes).  bf16 tiles are stored unpadded with
@@ -428,9 +434,14 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   // v rows and gates of value head h (heads after the first of a group go
   // through registers, one head ahead)
   auto load_head = [&](int h) {
+    // thread indices re-read here, so the addresses are formed at the call
+    // and not kept live across the value-head loop
+    int tid_l;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid_l) : "v"(tid));
+    const int lane = tid_l & 63;
 #pragma unroll
     for (int i = 0; i < NVG; ++i) {
-      const int idx = tid + i * NT;
+      const int idx = tid_l + i * NT;
       const int r = idx / GPRV, gc = idx % GPRV;
       vreg[i] = make_uint4(0, 0, 0, 0);
       if (idx < C * GPRV && r < n) vreg[i] = ld16(vg + (int64_t)(t0 + r) * p.v_st + h * p.v_sh + gc * GR);
@@ -704,134 +715,128 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     }
     __syncthreads();
 
-    // U~ = Tv V (all chunk row tiles x d_v tile `wave`), its accumulator
-    // tiles to global memory; then O_loc = P U~ as O_loc^T tiles (d_v tile
-    // `wave`, chunk tile jr) = sum_s U~^T[dv][s] P[r][s], with U~^T taken
-    // straight from the accumulators as operand units (contraction in
-    // k-tile order) and P's rows read in the same order.
-    TI* ut_g = (TI*)p.im.ut + blk * DV * C;
-    TI* ol_g = (TI*)p.im.oloc + blk * C * DV;
-    if (wave < NVT) {
+    // Per wave, from the LDS tiles Tv, Tb, V, K and P:
+    //  - U~ = Tv V for d_v tile `wave`: accumulator tiles to global memory,
+    //    and kept as operand units of U~^T (contraction over the chunk);
+    //  - W[r][dk] = sum_s Tb[r][s] K[s][dk] for d_k tile `wave`, twice from
+    //    the same operand registers: W^T tiles (rows d_k, columns r) to
+    //    global memory in k-tile order, and W tiles (rows r, columns d_k)
+    //    kept as operand units of W^T (a K^T operand unit, rows d_k, holds
+    //    the same registers as a K operand unit, columns d_k);
+    //  - one pass over P's rows (in the same contraction order) feeding
+    //    O_loc^T = U~^T P^T and Q'^T = scale (diag(e^gamma rq) Q)^T - W^T P^T.
+    // Neither U~ nor W goes through LDS.
+    {
       using KT = KTile<TI, C>;
+      using UT = typename Unit<TI>::type;
       constexpr int NUF = KT::HALF_TAIL ? KT::NU - 1 : KT::NU;  // full units
-      const int j = wave, rr = lane & 15;
-      f32x4 acc[NB][1];
-#pragma unroll
-      for (int i = 0; i < NB; ++i) acc[i][0] = zero4();
-      // B = V read transposed from its rows, A = Tv rows, both in k-tile order
-#pragma unroll
-      for (int u = 0; u < NUF; ++u) {
-        const auto vb = col_unit<TI, false, SWV>(sVr, LV, 16 * j, u, lane);
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-          mma_unit<false>(acc[i][0], row_unit<TI, false, SWC>(sTv, LC, 16 * i + rr, u, lane), vb);
-      }
-      if constexpr (KT::HALF_TAIL) {
-        constexpr int u = KT::NU - 1;
-        const auto vb = col_unit<TI, true, SWV>(sVr, LV, 16 * j, u, lane);
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-          mma_unit<true>(acc[i][0], row_unit<TI, true, SWC>(sTv, LC, 16 * i + rr, u, lane), vb);
-      }
-#pragma unroll
-      for (int i = 0; i < NB; ++i) store_acc_tile<TI>(ut_g + (j * NB + i) * 256, acc[i][0], lane);
-      f32x4 ol[NB];
-#pragma unroll
-      for (int jr = 0; jr < NB; ++jr) ol[jr] = zero4();
-#pragma unroll
-      for (int u = 0; u < NUF; ++u) {
-        constexpr int T1 = KT::TPU == 2 ? 1 : 0;
-        const auto ua = acc_unit<false>(acc[KT::TPU * u][0], acc[KT::TPU * u + T1][0], TI());
-#pragma unroll
-        for (int jr = 0; jr < NB; ++jr)
-          mma_unit<false>(ol[jr], ua, row_unit<TI, false, SWC>(sP, LC, 16 * jr + rr, u, lane));
-      }
-      if constexpr (KT::HALF_TAIL) {
-        constexpr int u = KT::NU - 1;
-        const auto ua = acc_unit<true>(acc[KT::TPU * u][0], acc[KT::TPU * u][0], TI());
-#pragma unroll
-        for (int jr = 0; jr < NB; ++jr)
-          mma_unit<true>(ol[jr], ua, row_unit<TI, true, SWC>(sP, LC, 16 * jr + rr, u, lane));
-      }
-#pragma unroll
-      for (int jr = 0; jr < NB; ++jr) store_acc_tile<TI>(ol_g + (j * NB + jr) * 256, ol[jr], lane);
-    }
-
-    // W[r][dk] = sum_s Tb[r][s] K[s][dk] for d_k tile `wave`, twice from the
-    // same operand registers: as W^T tiles (rows d_k, columns r), stored to
-    // global memory in k-tile order, and as W tiles (rows r, columns d_k),
-    // whose accumulators are the k-tile-order operand of
-    //   Q'^T = scale (diag(e^gamma rq) Q)^T - W^T P^T
-    // (contraction over the chunk, P's rows read in the same order), so W
-    // never goes through LDS.  A K^T operand unit (rows d_k, contraction over
-    // the chunk) holds the same registers as a K operand unit (columns d_k).
-    const int i0 = wave;
-    if (i0 < NKT) {
-      using KT = KTile<TI, C>;
-      constexpr int NUF = KT::HALF_TAIL ? KT::NU - 1 : KT::NU;  // full units
-      TI* w_g = (TI*)p.im.w + blk * C * DK;
-      TI* qp_g = (TI*)p.im.qp + blk * C * DK;
+      constexpr int T1 = KT::TPU == 2 ? 1 : 0;
       const int rr = lane & 15;
-      f32x4 wt[NB], wr[NB];
+      const bool uv = wave < NVT, wq = wave < NKT;
+      UT ua[KT::NU], wu[KT::NU];
+      if (uv) {
+        TI* ut_g = (TI*)p.im.ut + blk * DV * C;
+        f32x4 acc[NB];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) wt[j] = wr[j] = zero4();
+        for (int i = 0; i < NB; ++i) acc[i] = zero4();
 #pragma unroll
-      for (int u = 0; u < NUF; ++u) {
-        const auto ka = col_unit<TI, false, SWK>(sKV, LK, 16 * i0, u, lane);
+        for (int u = 0; u < NUF; ++u) {
+          const auto vb = col_unit<TI, false, SWV>(sVr, LV, 16 * wave, u, lane);
+#pragma unroll
+          for (int i = 0; i < NB; ++i)
+            mma_unit<false>(acc[i], row_unit<TI, false, SWC>(sTv, LC, 16 * i + rr, u, lane), vb);
+        }
+        if constexpr (KT::HALF_TAIL) {
+          constexpr int u = KT::NU - 1;
+          const auto vb = col_unit<TI, true, SWV>(sVr, LV, 16 * wave, u, lane);
+#pragma unroll
+          for (int i = 0; i < NB; ++i)
+            mma_unit<true>(acc[i], row_unit<TI, true, SWC>(sTv, LC, 16 * i + rr, u, lane), vb);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) store_acc_tile<TI>(ut_g + (wave * NB + i) * 256, acc[i], lane);
+#pragma unroll
+        for (int u = 0; u < NUF; ++u) ua[u] = acc_unit<false>(acc[KT::TPU * u], acc[KT::TPU * u + T1], TI());
+        if constexpr (KT::HALF_TAIL)
+          ua[KT::NU - 1] = acc_unit<true>(acc[KT::TPU * (KT::NU - 1)], acc[KT::TPU * (KT::NU - 1)], TI());
+      }
+      const int dk0 = 16 * wave + (lane >> 4) * 4;
+      if (wq) {
+        TI* w_g = (TI*)p.im.w + blk * C * DK;
+        // K operand units for every chunk unit, then one row tile of W and
+        // W^T at a time (each W^T tile is stored as soon as it is complete)
+        typename Unit<TI>::type ka[KT::NU];
+#pragma unroll
+        for (int u = 0; u < NUF; ++u) ka[u] = col_unit<TI, false, SWK>(sKV, LK, 16 * wave, u, lane);
+        if constexpr (KT::HALF_TAIL)
+          ka[KT::NU - 1] = col_unit<TI, true, SWK>(sKV, LK, 16 * wave, KT::NU - 1, lane);
+        f32x4 wr[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          const auto tb = row_unit<TI, false, SWC>(sTb, LC, 16 * j + rr, u, lane);
-          mma_unit<false>(wt[j], ka, tb);
-          mma_unit<false>(wr[j], tb, ka);
+          f32x4 wt = zero4();
+          wr[j] = zero4();
+#pragma unroll
+          for (int u = 0; u < NUF; ++u) {
+            const auto tb = row_unit<TI, false, SWC>(sTb, LC, 16 * j + rr, u, lane);
+            mma_unit<false>(wt, ka[u], tb);
+            mma_unit<false>(wr[j], tb, ka[u]);
+          }
+          if constexpr (KT::HALF_TAIL) {
+            constexpr int u = KT::NU - 1;
+            const auto tb = row_unit<TI, true, SWC>(sTb, LC, 16 * j + rr, u, lane);
+            mma_unit<true>(wt, ka[u], tb);
+            mma_unit<true>(wr[j], tb, ka[u]);
+          }
+          store4<TI>(w_g + j * 16 * DK + KTile<TI, DK>::pos(rr, dk0), wt[0], wt[1], wt[2], wt[3]);
         }
-      }
-      if constexpr (KT::HALF_TAIL) {
-        constexpr int u = KT::NU - 1;
-        const auto ka = col_unit<TI, true, SWK>(sKV, LK, 16 * i0, u, lane);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const auto tb = row_unit<TI, true, SWC>(sTb, LC, 16 * j + rr, u, lane);
-          mma_unit<true>(wt[j], ka, tb);
-          mma_unit<true>(wr[j], tb, ka);
+        for (int u = 0; u < NUF; ++u) wu[u] = acc_unit<false>(wr[KT::TPU * u], wr[KT::TPU * u + T1], TI());
+        if constexpr (KT::HALF_TAIL)
+          wu[KT::NU - 1] = acc_unit<true>(wr[KT::TPU * (KT::NU - 1)], wr[KT::TPU * (KT::NU - 1)], TI());
+      }
+      // The pass over P (branch-free in the common case of both products).
+      auto p_pass = [&](auto do_o, auto do_q) {
+        constexpr bool DO = decltype(do_o)::value, DQ = decltype(do_q)::value;
+        f32x4 ol[NB], pw[NB];
+#pragma unroll
+        for (int jr = 0; jr < NB; ++jr) ol[jr] = pw[jr] = zero4();
+#pragma unroll
+        for (int u = 0; u < NUF; ++u)
+#pragma unroll
+          for (int jr = 0; jr < NB; ++jr) {
+            const auto pu = row_unit<TI, false, SWC>(sP, LC, 16 * jr + rr, u, lane);
+            if constexpr (DO) mma_unit<false>(ol[jr], ua[u], pu);
+            if constexpr (DQ) mma_unit<false>(pw[jr], wu[u], pu);
+          }
+        if constexpr (KT::HALF_TAIL) {
+          constexpr int u = KT::NU - 1;
+#pragma unroll
+          for (int jr = 0; jr < NB; ++jr) {
+            const auto pu = row_unit<TI, true, SWC>(sP, LC, 16 * jr + rr, u, lane);
+            if constexpr (DO) mma_unit<true>(ol[jr], ua[u], pu);
+            if constexpr (DQ) mma_unit<true>(pw[jr], wu[u], pu);
+          }
         }
-      }
-      const int dk0 = 16 * i0 + (lane >> 4) * 4;
+        if constexpr (DO) {
+          TI* ol_g = (TI*)p.im.oloc + blk * C * DV;
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        store4<TI>(w_g + j * 16 * DK + KTile<TI, DK>::pos(rr, dk0), wt[j][0], wt[j][1], wt[j][2],
-                   wt[j][3]);
-      typename Unit<TI>::type wu[KT::NU];
+          for (int jr = 0; jr < NB; ++jr) store_acc_tile<TI>(ol_g + (wave * NB + jr) * 256, ol[jr], lane);
+        }
+        if constexpr (DQ) {
+          TI* qp_g = (TI*)p.im.qp + blk * C * DK;
 #pragma unroll
-      for (int u = 0; u < NUF; ++u) {
-        constexpr int T1 = KT::TPU == 2 ? 1 : 0;
-        wu[u] = acc_unit<false>(wr[KT::TPU * u], wr[KT::TPU * u + T1], TI());
-      }
-      if constexpr (KT::HALF_TAIL) {
-        constexpr int u = KT::NU - 1;
-        wu[u] = acc_unit<true>(wr[KT::TPU * u], wr[KT::TPU * u], TI());
-      }
-      f32x4 pw[NB];
-#pragma unroll
-      for (int jr = 0; jr < NB; ++jr) pw[jr] = zero4();
-#pragma unroll
-      for (int u = 0; u < NUF; ++u)
-#pragma unroll
-        for (int jr = 0; jr < NB; ++jr)
-          mma_unit<false>(pw[jr], wu[u], row_unit<TI, false, SWC>(sP, LC, 16 * jr + rr, u, lane));
-      if constexpr (KT::HALF_TAIL) {
-        constexpr int u = KT::NU - 1;
-#pragma unroll
-        for (int jr = 0; jr < NB; ++jr)
-          mma_unit<true>(pw[jr], wu[u], row_unit<TI, true, SWC>(sP, LC, 16 * jr + rr, u, lane));
-      }
-#pragma unroll
-      for (int jr = 0; jr < NB; ++jr) {
-        const int r = 16 * jr + rr;
-        const float qs = p.scale * sEg[r] * sRq[r];
-        const f32x4 qv = raw4_to_f32<TI>(qraw[jr]);
-        store4<TI>(qp_g + jr * 16 * DK + KTile<TI, DK>::pos(rr, dk0), qs * qv[0] - pw[jr][0],
-                   qs * qv[1] - pw[jr][1], qs * qv[2] - pw[jr][2], qs * qv[3] - pw[jr][3]);
-      }
+          for (int jr = 0; jr < NB; ++jr) {
+            const int r = 16 * jr + rr;
+            const float qs = p.scale * sEg[r] * sRq[r];
+            const f32x4 qv = raw4_to_f32<TI>(qraw[jr]);
+            store4<TI>(qp_g + jr * 16 * DK + KTile<TI, DK>::pos(rr, dk0), qs * qv[0] - pw[jr][0],
+                       qs * qv[1] - pw[jr][1], qs * qv[2] - pw[jr][2], qs * qv[3] - pw[jr][3]);
+          }
+        }
+      };
+      if (uv && wq) p_pass(BoolC<true>{}, BoolC<true>{});
+      else if (uv) p_pass(BoolC<true>{}, BoolC<false>{});
+      else if (wq) p_pass(BoolC<false>{}, BoolC<true>{});
     }
     if (tid == 0) p.im.decay[blk] = sEg[C - 1];
     __syncthreads();
