@@ -384,8 +384,10 @@ __device__ __forceinline__ int swz(int row, int col) {
 }
 
 // mma_block on swizzled operands: acc[i][j] += A_i * Bt_j^T, A rows start
-// at row a0 of A, Bt rows at row b0 of Bt.
-template <int MT, int NT, int K, int SWA, int SWB>
+// at row a0 of A, Bt rows at row b0 of Bt.  Only the tiles I0 <= i < I1,
+// J0 <= j < J1 are computed (and only their fragments read); the others are
+// left as they are.
+template <int MT, int NT, int K, int SWA, int SWB, int I0 = 0, int I1 = MT, int J0 = 0, int J1 = NT>
 __device__ __forceinline__ void mma_block_sw(f32x4 (&acc)[MT][NT], const bf16* A, int lda, int a0,
                                              const bf16* Bt, int ldb, int b0, int lane) {
   const int r = lane & 15, q = lane >> 4;
@@ -393,43 +395,44 @@ __device__ __forceinline__ void mma_block_sw(f32x4 (&acc)[MT][NT], const bf16* A
   for (int k0 = 0; k0 + 32 <= K; k0 += 32) {
     bf16x8 a[MT], b[NT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
+    for (int i = I0; i < I1; ++i) {
       const int row = a0 + 16 * i + r;
       a[i] = *(const bf16x8*)(A + row * lda + swz<bf16, SWA>(row, k0 + q * 8));
     }
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
+    for (int j = J0; j < J1; ++j) {
       const int row = b0 + 16 * j + r;
       b[j] = *(const bf16x8*)(Bt + row * ldb + swz<bf16, SWB>(row, k0 + q * 8));
     }
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int i = I0; i < I1; ++i)
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
+      for (int j = J0; j < J1; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   }
   if constexpr (K % 32 == 16) {
     constexpr int k0 = K - 16;
     bf16x4 a[MT], b[NT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
+    for (int i = I0; i < I1; ++i) {
       const int row = a0 + 16 * i + r;
       a[i] = *(const bf16x4*)(A + row * lda + swz<bf16, SWA>(row, k0 + q * 4));
     }
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
+    for (int j = J0; j < J1; ++j) {
       const int row = b0 + 16 * j + r;
       b[j] = *(const bf16x4*)(Bt + row * ldb + swz<bf16, SWB>(row, k0 + q * 4));
     }
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int i = I0; i < I1; ++i)
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
+      for (int j = J0; j < J1; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[i], b[j], acc[i][j], 0, 0, 0);
   }
 }
 
-template <int MT, int NT, int K, int SWA, int SWB>
+// fp32 operands: every tile is computed (the range only says which are needed).
+template <int MT, int NT, int K, int SWA, int SWB, int I0 = 0, int I1 = MT, int J0 = 0, int J1 = NT>
 __device__ __forceinline__ void mma_block_sw(f32x4 (&acc)[MT][NT], const float* A, int lda, int a0,
                                              const float* Bt, int ldb, int b0, int lane) {
   static_assert(SWA == 0 && SWB == 0, "fp32 operands use padded rows");

@@ -276,6 +276,20 @@ __device__ __forceinline__ typename Unit<TI>::type col_unit(const TI* m, int ld,
   }
 }
 
+// A compile-time integer passed as a value, and a dispatch of a runtime
+// value in [I, N) to f(IntC<value>) (f is not called for values outside).
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+template <int I, int N, typename F>
+__device__ __forceinline__ void dispatch_int(int v, F& f) {
+  if constexpr (I < N) {
+    if (v == I) f(IntC<I>{});
+    else dispatch_int<I + 1, N>(v, f);
+  }
+}
+
 // A compile-time flag passed as a value (selects a branch-free product pass).
 template <bool B>
 struct BoolC {
@@ -459,28 +473,34 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   row_inv_norms<TI, DK, NT>(sQ, LK, C, p.eps, sRq, tid);   // swizzle only permutes a row
 
   // Raw K K^T (waves 0..NB-1) and Q K^T (waves 4..4+NB-1), one row tile
-  // against every column tile.  The tiles stay in registers for all value
-  // heads of the group; norms and gates are applied when A and P are built.
+  // against the column tiles that A (strictly lower) and P (lower with the
+  // diagonal) use; the other tiles stay zero.  The tiles stay in registers
+  // for all value heads of the group; norms and gates are applied when A
+  // and P are built.
   const bool g_wave = wave < NB;
   const bool s_wave = wave >= 4 && wave - 4 < NB;
   const int rt = g_wave ? wave : wave - 4;
   f32x4 acc_gs[1][NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc_gs[0][j] = zero4();
-  if (g_wave) {
-    // K K^T row tile rt against every column tile
-    mma_block_sw<1, NB, DK, SWK, SWK>(acc_gs, sKV, LK, 16 * rt, sKV, LK, 0, lane);
-  } else if (s_wave) {
-    // (Q K^T)^T = K Q^T: column tile rt of Q K^T, as the row tiles of its
-    // transpose, so that each lane later holds four consecutive keys of
-    // one query row
-    f32x4 acc_t[NB][1];
+  auto gram_tiles = [&](auto rtc) {
+    constexpr int RT = decltype(rtc)::value;
+    if (g_wave) {
+      // K K^T row tile RT against column tiles RT.. (read transposed later)
+      mma_block_sw<1, NB, DK, SWK, SWK, 0, 1, RT, NB>(acc_gs, sKV, LK, 16 * RT, sKV, LK, 0, lane);
+    } else if (s_wave) {
+      // (Q K^T)^T = K Q^T: column tile RT of Q K^T, as the row tiles 0..RT of
+      // its transpose, so that each lane later holds four consecutive keys
+      // of one query row
+      f32x4 acc_t[NB][1];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc_t[j][0] = zero4();
-    mma_block_sw<NB, 1, DK, SWK, SWK>(acc_t, sKV, LK, 0, sQ, LK, 16 * rt, lane);
+      for (int j = 0; j < NB; ++j) acc_t[j][0] = zero4();
+      mma_block_sw<NB, 1, DK, SWK, SWK, 0, RT + 1, 0, 1>(acc_t, sKV, LK, 0, sQ, LK, 16 * RT, lane);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc_gs[0][j] = acc_t[j][0];
-  }
+      for (int j = 0; j < NB; ++j) acc_gs[0][j] = acc_t[j][0];
+    }
+  };
+  dispatch_int<0, NB>(rt, gram_tiles);
   if (g_wave || s_wave) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) settle(acc_gs[0][j]);
