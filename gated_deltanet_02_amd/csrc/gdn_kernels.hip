@@ -370,8 +370,6 @@ __device__ __forceinline__ void wy_fetch(char* buf, const WyParams& p, int kh, i
                                      p.k_st, DK, n, wave, lane);
   dma_rows<TI, C, L::LK, L::SWK, NW>(buf + L::r_x, (const TI*)p.q + (int64_t)t0 * p.q_st + kh * p.q_sh,
                                      p.q_st, DK, n, wave, lane);
-  dma_rows<TI, C, L::LV, L::SWV, NW>(buf + L::r_v, (const TI*)p.v + (int64_t)t0 * p.v_st + h * p.v_sh,
-                                     p.v_st, p.dv, n, wave, lane);
   if (wave == NW - 1 && lane < n) {
     __builtin_amdgcn_global_load_lds((const void*)(p.g + (int64_t)(t0 + lane) * p.g_st + h * p.g_sh),
                                      (__attribute__((address_space(3))) void*)(buf + L::r_gate), 4, 0, 0);
@@ -380,7 +378,6 @@ __device__ __forceinline__ void wy_fetch(char* buf, const WyParams& p, int kh, i
                                      4, 0, 0);
   }
 }
-
 // One workgroup per (chunk, key head) item, under 128 VGPRs and 80 KiB of
 // LDS so that two workgroups share a compute unit and hide each other's
 // barriers and latencies.
@@ -435,7 +432,6 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       sKV[n * LK + idx] = from_float<TI>(0.f);
       sQ[n * LK + idx] = from_float<TI>(0.f);
     }
-    for (int idx = tid; idx < (C - n) * LV; idx += NT) sVr[n * LV + idx] = from_float<TI>(0.f);
     if (tid < C - n) {
       ((float*)sGate)[n + tid] = 0.f;
       ((float*)sGate)[C + n + tid] = 0.f;
@@ -447,7 +443,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   float gv = 0.f, bv = 0.f;
   // v rows and gates of value head h (heads after the first of a group go
   // through registers, one head ahead)
-  auto load_head = [&](int h) {
+  auto load_head = [&](int h, bool gates) {
     // thread indices re-read here, so the addresses are formed at the call
     // and not kept live across the value-head loop
     int tid_l;
@@ -460,6 +456,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       vreg[i] = make_uint4(0, 0, 0, 0);
       if (idx < C * GPRV && r < n) vreg[i] = ld16(vg + (int64_t)(t0 + r) * p.v_st + h * p.v_sh + gc * GR);
     }
+    if (!gates) return;
     if (wave == 0 && lane < n) {
       gv = p.g[(int64_t)(t0 + lane) * p.g_st + h * p.g_sh];
       bv = p.beta[(int64_t)(t0 + lane) * p.b_st + h * p.b_sh];
@@ -468,6 +465,24 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       bv = 0.f;
     }
   };
+  // V rows from the registers load_head filled (rows past the chunk's end
+  // are zero) into the V region
+  auto store_v = [&]() {
+    int tid_s;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid_s) : "v"(tid));
+#pragma unroll
+    for (int i = 0; i < NVG; ++i) {
+      const int idx = tid_s + i * NT;
+      if (idx < C * GPRV) {
+        const int r = idx / GPRV, gc = idx % GPRV;
+        st16(sVr + r * LV + swz<TI, SWV>(r, gc * GR), vreg[i]);
+      }
+    }
+  };
+  // The first value head's V rows go to registers (its gates came with the
+  // q, k rows): they arrive while the Gram products, A, P and T are formed.
+  // (LDS-direct copies would not do: every LDS read would wait for them.)
+  load_head(kh * grp, false);
 
   row_inv_norms<TI, DK, NT>(sKV, LK, C, p.eps, sRk, tid);  // sums are order-free: the
   row_inv_norms<TI, DK, NT>(sQ, LK, C, p.eps, sRq, tid);   // swizzle only permutes a row
@@ -555,18 +570,10 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     // there already) and the gate scan.  Then the next value head's inputs
     // are requested.
     if (gi > 0) {
-#pragma unroll
-      for (int i = 0; i < NVG; ++i) {
-        const int idx = tid + i * NT;
-        if (idx < C * GPRV) {
-          const int r = idx / GPRV, gc = idx % GPRV;
-          st16(sVr + r * LV + swz<TI, SWV>(r, gc * GR), vreg[i]);
-        }
-      }
+      store_v();
       if (wave == 0) gate_scan();
+      __syncthreads();
     }
-    if (gi + 1 < grp) load_head(h + 1);
-    if (gi > 0) __syncthreads();
 
     // A from the K K^T tiles:
     // A_rs = beta_r exp(gamma_r - gamma_s) rk_r rk_s (k_r . k_s), s < r
@@ -733,6 +740,11 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
         *(f32x4*)(sTv + r * LC + s0 + 4) = __builtin_shufflevector(tv, tv, 4, 5, 6, 7);
       }
     }
+    // this value head's V rows into LDS for U~ = Tv V (the first head's
+    // arrive in registers here; later heads' were stored at the loop top),
+    // then the next value head's inputs are requested
+    if (gi == 0) store_v();
+    if (gi + 1 < grp) load_head(h + 1, true);
     __syncthreads();
 
     // Per wave, from the LDS tiles Tv, Tb, V, K and P:
