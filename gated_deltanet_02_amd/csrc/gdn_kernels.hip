@@ -276,6 +276,29 @@ __device__ __forceinline__ typename Unit<TI>::type col_unit(const TI* m, int ld,
   }
 }
 
+// The Gram tiles (kind 0: K_rt K_j^T, j >= rt, the blocks A reads) and
+// the (Q K^T)^T tiles (kind 1: K_j Q_rt^T, j <= rt, the blocks P reads)
+// held by wave w of the WY kernel, slot t (kind -1: none).  With four row
+// tiles the ten tiles of each kind go three, three, two, two to waves 0..3
+// (Gram) and 4..7 (Q K^T); with fewer, wave w (w - 4) takes every tile of
+// row (column) tile w (w - 4).
+struct WyTile {
+  int kind, rt, j;
+};
+__host__ __device__ constexpr WyTile wy_tile(int nb, int w, int t) {
+  if (nb == 4) {
+    constexpr int tb[8][3][2] = {{{0, 0}, {0, 1}, {0, 2}}, {{1, 1}, {1, 2}, {1, 3}},
+                                 {{2, 2}, {2, 3}, {-1, -1}}, {{3, 3}, {0, 3}, {-1, -1}},
+                                 {{0, 0}, {3, 0}, {-1, -1}}, {{1, 0}, {1, 1}, {-1, -1}},
+                                 {{2, 0}, {2, 1}, {2, 2}}, {{3, 1}, {3, 2}, {3, 3}}};
+    if (w < 0 || w > 7 || t < 0 || t > 2 || tb[w][t][0] < 0) return WyTile{-1, 0, 0};
+    return WyTile{w < 4 ? 0 : 1, tb[w][t][0], tb[w][t][1]};
+  }
+  if (w >= 0 && w < nb) return w + t < nb ? WyTile{0, w, w + t} : WyTile{-1, 0, 0};
+  if (w >= 4 && w - 4 < nb) return t <= w - 4 ? WyTile{1, w - 4, t} : WyTile{-1, 0, 0};
+  return WyTile{-1, 0, 0};
+}
+
 // A compile-time integer passed as a value, and a dispatch of a runtime
 // value in [I, N) to f(IntC<value>) (f is not called for values outside).
 template <int V>
@@ -487,39 +510,30 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   row_inv_norms<TI, DK, NT>(sKV, LK, C, p.eps, sRk, tid);  // sums are order-free: the
   row_inv_norms<TI, DK, NT>(sQ, LK, C, p.eps, sRq, tid);   // swizzle only permutes a row
 
-  // Raw K K^T (waves 0..NB-1) and Q K^T (waves 4..4+NB-1), one row tile
-  // against the column tiles that A (strictly lower) and P (lower with the
-  // diagonal) use; the other tiles stay zero.  The tiles stay in registers
-  // for all value heads of the group; norms and gates are applied when A
-  // and P are built.
-  const bool g_wave = wave < NB;
-  const bool s_wave = wave >= 4 && wave - 4 < NB;
-  const int rt = g_wave ? wave : wave - 4;
-  f32x4 acc_gs[1][NB];
+  // Raw K K^T and Q K^T tiles (the wave's slots, see wy_tile).  They stay
+  // in registers for all value heads of the group; norms and gates are
+  // applied when A and P are built.
+  constexpr int NSLOT = NB == 4 ? 3 : NB;
+  f32x4 acc_gs[NSLOT];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) acc_gs[0][j] = zero4();
-  auto gram_tiles = [&](auto rtc) {
-    constexpr int RT = decltype(rtc)::value;
-    if (g_wave) {
-      // K K^T row tile RT against column tiles RT.. (read transposed later)
-      mma_block_sw<1, NB, DK, SWK, SWK, 0, 1, RT, NB>(acc_gs, sKV, LK, 16 * RT, sKV, LK, 0, lane);
-    } else if (s_wave) {
-      // (Q K^T)^T = K Q^T: column tile RT of Q K^T, as the row tiles 0..RT of
-      // its transpose, so that each lane later holds four consecutive keys
-      // of one query row
-      f32x4 acc_t[NB][1];
+  for (int t = 0; t < NSLOT; ++t) acc_gs[t] = zero4();
+  auto gram_tiles = [&](auto wc) {
+    constexpr int W = decltype(wc)::value;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) acc_t[j][0] = zero4();
-      mma_block_sw<NB, 1, DK, SWK, SWK, 0, RT + 1, 0, 1>(acc_t, sKV, LK, 0, sQ, LK, 16 * RT, lane);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) acc_gs[0][j] = acc_t[j][0];
+    for (int t = 0; t < NSLOT; ++t) {
+      const WyTile T = wy_tile(NB, W, t);
+      if (T.kind < 0) continue;
+      f32x4 acc1[1][1] = {{zero4()}};
+      if (T.kind == 0)  // K_rt K_j^T: lane holds column 16 j + lane % 16
+        mma_block_sw<1, 1, DK, SWK, SWK>(acc1, sKV, LK, 16 * T.rt, sKV, LK, 16 * T.j, lane);
+      else  // K_j Q_rt^T: lane holds query 16 rt + lane % 16, four consecutive keys
+        mma_block_sw<1, 1, DK, SWK, SWK>(acc1, sKV, LK, 16 * T.j, sQ, LK, 16 * T.rt, lane);
+      acc_gs[t] = acc1[0][0];
     }
-  };
-  dispatch_int<0, NB>(rt, gram_tiles);
-  if (g_wave || s_wave) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) settle(acc_gs[0][j]);
-  }
+    for (int t = 0; t < NSLOT; ++t) settle(acc_gs[t]);
+  };
+  dispatch_int<0, kWyThreads / 64>(wave, gram_tiles);
   // The gate cumulative sum gamma, beta (sigmoid of a logit for a real
   // token; padded rows stay 0) and e^gamma of the value head whose g and
   // beta are in gv, bv (wave 0).
@@ -577,48 +591,58 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
 
     // A from the K K^T tiles:
     // A_rs = beta_r exp(gamma_r - gamma_s) rk_r rk_s (k_r . k_s), s < r
-    // (only the strictly lower part is ever read).
-    if (g_wave) {
-      // The Gram tile (rt, j) read transposed (K K^T is symmetric): lane
-      // holds rows r = 16 j + lane % 16 (tiles j >= rt) and the four
-      // consecutive columns c = 16 rt + 4 (lane / 16) + e.
-      const int c0 = 16 * rt + (lane >> 4) * 4;
-      const f32x4 gc = *(const f32x4*)(sGam + c0), rkc = *(const f32x4*)(sRk + c0);
+    // (only the strictly lower part is ever read), and
+    // P = scale D o (Q^K^T) from the (Q K^T)^T tiles, from each wave's slots.
+    auto build_ap = [&](auto wc) {
+      constexpr int W = decltype(wc)::value;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        if (j < rt) continue;
-        const int r = 16 * j + (lane & 15);
-        const float br = sBeta[r] * sRk[r], gr = sGam[r];
-        f32x4 a;
+      for (int t = 0; t < NSLOT; ++t) {
+        const WyTile T = wy_tile(NB, W, t);
+        if (T.kind == 0) {
+          // the Gram tile (rt, j) read transposed (K K^T is symmetric): lane
+          // holds row r = 16 j + lane % 16 and the four consecutive columns
+          // c = 16 rt + 4 (lane / 16) + e
+          const int c0 = 16 * T.rt + (lane >> 4) * 4;
+          const f32x4 gc = *(const f32x4*)(sGam + c0), rkc = *(const f32x4*)(sRk + c0);
+          const int r = 16 * T.j + (lane & 15);
+          const float br = sBeta[r] * sRk[r], gr = sGam[r];
+          f32x4 a;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          a[e] = (c0 + e < r) ? br * rkc[e] * fast_exp(gr - gc[e]) * acc_gs[0][j][e] : 0.f;
-        *(f32x4*)(sA + r * LF + c0) = a;
+          for (int e = 0; e < 4; ++e)
+            a[e] = (c0 + e < r) ? br * rkc[e] * fast_exp(gr - gc[e]) * acc_gs[t][e] : 0.f;
+          *(f32x4*)(sA + r * LF + c0) = a;
+        } else if (T.kind == 1) {
+          // lane holds query row r = 16 rt + lane % 16 and the four
+          // consecutive keys s = 16 j + 4 (lane / 16) + e
+          const int r = 16 * T.rt + (lane & 15);
+          const float qr = p.scale * sRq[r], gr = sGam[r];
+          const int s0 = 16 * T.j + (lane >> 4) * 4;
+          const f32x4 gs = *(const f32x4*)(sGam + s0), rks = *(const f32x4*)(sRk + s0);
+          f32x4 pv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pv[e] = (s0 + e <= r) ? qr * rks[e] * fast_exp(gr - gs[e]) * acc_gs[t][e] : 0.f;
+          store4<TI>(sP + r * LC + swz<TI, SWC>(r, kperm<TI, C>(s0)), pv[0], pv[1], pv[2], pv[3]);
+        }
       }
-      if (wave == NB - 1 && lane < C) {
-        // the K~ row scale rk_r e^(gamma_last - gamma_r) and Tb's column
-        // scale beta_s e^gamma_s rk_s
-        const float rk = sRk[lane];
-        sKs[lane] = rk * fast_exp(sGam[C - 1] - sGam[lane]);
-        sCb[lane] = sBeta[lane] * sEg[lane] * rk;
-      }
-    } else if (s_wave) {
-      // P = scale D o (Q^K^T) from the (Q K^T)^T tiles: lane holds query row
-      // r = 16 rt + lane % 16 and the four consecutive keys
-      // s = 16 j + 4 (lane / 16) + e.
-      const int r = 16 * rt + (lane & 15);
-      const float qr = p.scale * sRq[r], gr = sGam[r];
+      constexpr WyTile T0 = wy_tile(NB, W, 0);
+      if constexpr (T0.kind == 1) {
+        // P is zero right of the diagonal tile of the wave's first row tile
+        const int r = 16 * T0.rt + (lane & 15);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int s0 = 16 * j + (lane >> 4) * 4;
-        const f32x4 gs = *(const f32x4*)(sGam + s0), rks = *(const f32x4*)(sRk + s0);
-        f32x4 pv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pv[e] = (s0 + e <= r) ? qr * rks[e] * fast_exp(gr - gs[e]) * acc_gs[0][j][e] : 0.f;
-        const int ps = kperm<TI, C>(s0);
-        store4<TI>(sP + r * LC + swz<TI, SWC>(r, ps), pv[0], pv[1], pv[2], pv[3]);
+        for (int j = T0.rt + 1; j < NB; ++j) {
+          const int s0 = 16 * j + (lane >> 4) * 4;
+          store4<TI>(sP + r * LC + swz<TI, SWC>(r, kperm<TI, C>(s0)), 0.f, 0.f, 0.f, 0.f);
+        }
       }
+    };
+    dispatch_int<0, kWyThreads / 64>(wave, build_ap);
+    if (wave == NB - 1 && lane < C) {
+      // the K~ row scale rk_r e^(gamma_last - gamma_r) and Tb's column
+      // scale beta_s e^gamma_s rk_s
+      const float rk = sRk[lane];
+      sKs[lane] = rk * fast_exp(sGam[C - 1] - sGam[lane]);
+      sCb[lane] = sBeta[lane] * sEg[lane] * rk;
     }
     __syncthreads();
 
