@@ -439,6 +439,14 @@ __device__ __forceinline__ void mma_block_sw(f32x4 (&acc)[MT][NT], const float* 
   mma_block<MT, NT, K>(acc, A + a0 * lda, lda, Bt + b0 * ldb, ldb, lane);
 }
 
+// acc += A_blk * B with both 16 x 16 fp32 operands in registers: a holds
+// row lane % 16, columns 4 (lane / 16) + 0..3 of A_blk (as read by
+// mma16_f32_acc_b), b a tile in accumulator layout.
+__device__ __forceinline__ void mma16_f32_ab(f32x4& acc, const f32x4& a, const f32x4& b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc, 0, 0, 0);
+}
+
 // acc += A_blk * B where B is a 16 x 16 fp32 tile held in accumulator
 // layout by this wave (lane (q, r) holds B[4q + e][r]); with the contraction
 // order of instruction e taken as k = 4q + e this is exactly the operand

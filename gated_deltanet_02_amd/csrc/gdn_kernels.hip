@@ -693,13 +693,28 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) x[i] = (i == col) ? 1.f : 0.f;
         const float* Ab = sA + (16 * b) * LF + 16 * b;
+        // row r + 1's entries (16-byte reads; the block is zero on and above
+        // its diagonal) are requested while row r's sums run
+        f32x4 cur[4], nxt[4];
+        cur[0] = *(const f32x4*)(Ab + LF);
 #pragma unroll
         for (int r = 1; r < 16; ++r) {
-          float acc = x[r];
+          if (r + 1 < 16) {
 #pragma unroll
-          for (int s2 = 0; s2 < r; ++s2) acc -= Ab[r * LF + s2] * x[s2];
-          x[r] = acc;
-          // one row's operands at a time: keeps the register footprint small
+            for (int v = 0; v < 4; ++v)
+              if (4 * v < r + 1) nxt[v] = *(const f32x4*)(Ab + (r + 1) * LF + 4 * v);
+          }
+          float a0 = x[r], a1 = 0.f;  // two independent partial sums
+#pragma unroll
+          for (int s2 = 0; s2 < r; ++s2) {
+            if (s2 & 1) a1 -= cur[s2 >> 2][s2 & 3] * x[s2];
+            else a0 -= cur[s2 >> 2][s2 & 3] * x[s2];
+          }
+          x[r] = a0 + a1;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) cur[v] = nxt[v];
+          // one row's operands in flight at a time: keeps the register
+          // footprint small
           __builtin_amdgcn_sched_barrier(0);
         }
         float* Tb = sT + (16 * b) * LF + 16 * b;
@@ -712,33 +727,45 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     // is one it made itself, kept in registers in the accumulator layout
     // (lane (r, q) holds rows 4 q + e of column r), which is the second
     // operand's layout for the next product, so the column needs no
-    // exchange and no barrier between block rows.
-    if (wave < NB - 1) {
-      const int bj = wave, r = lane & 15, q = lane >> 4;
-      f32x4 tcol[NB];  // T_(bj+d, bj), d = 0..
+    // exchange and no barrier between block rows.  All A blocks and
+    // diagonal T blocks of the column are read first, and each term
+    // A_ik T_kj enters its sum as soon as T_kj is known (in k order), so
+    // the chain of dependent products holds only one term per block.
+    auto off_diag = [&](auto bjc) {
+      constexpr int BJ = decltype(bjc)::value;
+      constexpr int ND = NB - BJ;  // blocks of the column, the diagonal one included
+      const int r = lane & 15, q = lane >> 4;
+      f32x4 ab[ND][ND], td[ND], tcol[ND], m[ND];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tcol[0][e] = sT[(16 * bj + 4 * q + e) * LF + 16 * bj + r];
+      for (int di = 1; di < ND; ++di) {
+        const int bi = BJ + di;
+        td[di] = *(const f32x4*)(sT + (16 * bi + r) * LF + 16 * bi + 4 * q);
 #pragma unroll
-      for (int di = 1; di < NB; ++di) {
-        const int bi = bj + di;
-        if (bi < NB) {
-          f32x4 m = zero4();
+        for (int dk = 0; dk < di; ++dk)
+          ab[di][dk] = *(const f32x4*)(sA + (16 * bi + r) * LF + 16 * (BJ + dk) + 4 * q);
+        m[di] = zero4();
+      }
 #pragma unroll
-          for (int dk = 0; dk < di; ++dk)
-            mma16_f32_acc_b(m, sA + (16 * bi) * LF + 16 * (bj + dk), LF, tcol[dk], lane);
-          settle(m);
-          f32x4 t = zero4();
-          mma16_f32_acc_b(t, sT + (16 * bi) * LF + 16 * bi, LF, m, lane);
-          settle(t);
-          float* dst = sT + (16 * bi) * LF + 16 * bj;
+      for (int e = 0; e < 4; ++e) tcol[0][e] = sT[(16 * BJ + 4 * q + e) * LF + 16 * BJ + r];
+      // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            tcol[di][e] = -t[e];
-            dst[(4 * q + e) * LF + r] = -t[e];
-          }
+      for (int dk = 0; dk + 1 < ND; ++dk) {
+#pragma unroll
+        for (int di = dk + 1; di < ND; ++di) mma16_f32_ab(m[di], ab[di][dk], tcol[dk]);
+        const int di = dk + 1, bi = BJ + di;
+        settle(m[di]);
+        f32x4 t = zero4();
+        mma16_f32_ab(t, td[di], m[di]);
+        settle(t);
+        float* dst = sT + (16 * bi) * LF + 16 * BJ;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          tcol[di][e] = -t[e];
+          dst[(4 * q + e) * LF + r] = -t[e];
         }
       }
-    }
+    };
+    dispatch_int<0, NB - 1>(wave, off_diag);
     __syncthreads();
 
     // Tb = T diag(beta e^gamma rk), Tv = T diag(beta), 8 stored positions
