@@ -772,14 +772,25 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     // (kperm order) per item.
     for (int idx = tid; idx < C * (C / 8); idx += NT) {
       const int r = idx / (C / 8), s0 = (idx % (C / 8)) * 8;
+      // the 8 stored positions s0 .. s0 + 7 are the columns c_lo + 0..3 and
+      // c_hi + 0..3 (kperm within a full 32-column block, else natural)
+      int c_lo = s0, c_hi = s0 + 4;
+      if (sizeof(TI) == 2 && s0 < C / 32 * 32) {
+        c_lo = (s0 & ~31) + 4 * ((s0 >> 3) & 3);
+        c_hi = c_lo + 16;
+      }
+      const f32x4 tl = *(const f32x4*)(sT + r * LF + c_lo), th = *(const f32x4*)(sT + r * LF + c_hi);
+      const f32x4 bl = *(const f32x4*)(sCb + c_lo), bh = *(const f32x4*)(sCb + c_hi);
+      const f32x4 vl = *(const f32x4*)(sBeta + c_lo), vh = *(const f32x4*)(sBeta + c_hi);
       typedef TI vec8 __attribute__((ext_vector_type(8)));
       vec8 tb, tv;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int sc = kinv<TI, C>(s0 + j);
-        const float t = (sc <= r) ? sT[r * LF + sc] : 0.f;
-        tb[j] = from_float<TI>(t * sCb[sc]);
-        tv[j] = from_float<TI>(t * sBeta[sc]);
+      for (int e = 0; e < 4; ++e) {
+        const float t0 = (c_lo + e <= r) ? tl[e] : 0.f, t1 = (c_hi + e <= r) ? th[e] : 0.f;
+        tb[e] = from_float<TI>(t0 * bl[e]);
+        tv[e] = from_float<TI>(t0 * vl[e]);
+        tb[4 + e] = from_float<TI>(t1 * bh[e]);
+        tv[4 + e] = from_float<TI>(t1 * vh[e]);
       }
       if constexpr (sizeof(TI) == 2) {
         *(vec8*)(sTb + r * LC + swz<TI, SWC>(r, s0)) = tb;
