@@ -167,37 +167,36 @@ __global__ __launch_bounds__(1024) void table_kernel(TableParams p) {
 
 // out[r] = 1 / sqrt(sum_d src[r][d]^2 + eps); four lanes per row, each
 // reading its quarter of the row in 16-byte pieces.
-template <typename TI, int D, int NT = kThreads>
-__device__ __forceinline__ void row_inv_norms(const TI* src, int lds, int R,
-                                              float eps, float* out, int tid) {
+template <typename TI, int D, int R, int NT = kThreads>
+__device__ __forceinline__ void row_inv_norms(const TI* src, int lds, float eps, float* out,
+                                              int tid) {
   constexpr int GR = Gran<TI>::n;
-  for (int base = 0; base < R * 4; base += NT) {
+  constexpr int NG = D / GR;  // 16-byte granules per row (D is a multiple of GR)
+  static_assert(D % GR == 0, "rows of whole granules");
+  // adjacent lanes share a row, PARTS of them (a power of two)
+  constexpr int PARTS = NT / R < NG ? NT / R : NG;
+  static_assert((PARTS & (PARTS - 1)) == 0 && PARTS <= 64, "lanes per row");
+  for (int base = 0; base < R * PARTS; base += NT) {
     const int idx = base + tid;
-    const int r = idx >> 2, part = idx & 3;
-    float s = 0.f;
+    const int r = idx / PARTS, part = idx % PARTS;
+    float s0 = 0.f, s1 = 0.f;
     if (r < R) {
-      const TI* row = src + r * lds + part * (D / 4);
-      if constexpr ((D / 4) % GR == 0) {
+      const TI* row = src + r * lds;
 #pragma unroll
-        for (int g = 0; g < D / 4 / GR; ++g) {
-          const uint4 v = ld16(row + g * GR);
-          const TI* e = (const TI*)&v;
+      for (int g = part; g < NG; g += PARTS) {
+        const uint4 v = ld16(row + g * GR);
+        const TI* e = (const TI*)&v;
 #pragma unroll
-          for (int j = 0; j < GR; ++j) {
-            const float x = to_float(e[j]);
-            s += x * x;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int d = 0; d < D / 4; ++d) {
-          const float x = to_float(row[d]);
-          s += x * x;
+        for (int j = 0; j < GR; j += 2) {
+          const float x0 = to_float(e[j]), x1 = to_float(e[j + 1]);
+          s0 += x0 * x0;
+          s1 += x1 * x1;
         }
       }
     }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
+    float s = s0 + s1;
+#pragma unroll
+    for (int o = 1; o < PARTS; o <<= 1) s += __shfl_xor(s, o);
     if (r < R && part == 0) out[r] = 1.0f / sqrtf(s + eps);
   }
 }
@@ -507,8 +506,9 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   // (LDS-direct copies would not do: every LDS read would wait for them.)
   load_head(kh * grp, false);
 
-  row_inv_norms<TI, DK, NT>(sKV, LK, C, p.eps, sRk, tid);  // sums are order-free: the
-  row_inv_norms<TI, DK, NT>(sQ, LK, C, p.eps, sRq, tid);   // swizzle only permutes a row
+  // q's inverse row norms (the swizzle only permutes a row's granules); k's
+  // come from the diagonal of the Gram tiles below
+  row_inv_norms<TI, DK, C, NT>(sQ, LK, p.eps, sRq, tid);
 
   // Raw K K^T and Q K^T tiles (the wave's slots, see wy_tile).  They stay
   // in registers for all value heads of the group; norms and gates are
@@ -532,6 +532,20 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     }
 #pragma unroll
     for (int t = 0; t < NSLOT; ++t) settle(acc_gs[t]);
+    // slot 0 of a Gram wave is its diagonal tile (rt, rt): lane m + 16 (m / 4)
+    // holds |k_(16 rt + m)|^2 as element m % 4
+    constexpr WyTile T0 = wy_tile(NB, W, 0);
+    if constexpr (T0.kind == 0) {
+      static_assert(T0.rt == T0.j, "slot 0 of a Gram wave is diagonal");
+      const int m = lane & 15;
+      if ((m >> 2) == (lane >> 4)) {
+        float d = acc_gs[0][0];
+        if ((m & 3) == 1) d = acc_gs[0][1];
+        if ((m & 3) == 2) d = acc_gs[0][2];
+        if ((m & 3) == 3) d = acc_gs[0][3];
+        sRk[16 * T0.rt + m] = 1.0f / sqrtf(d + p.eps);
+      }
+    }
   };
   dispatch_int<0, kWyThreads / 64>(wave, gram_tiles);
   // The gate cumulative sum gamma, beta (sigmoid of a logit for a real
