@@ -46,7 +46,7 @@ class GdnOptions(ctypes.Structure):
 class GdnWorkspaceLayout(ctypes.Structure):
     _fields_ = [("total_bytes", ctypes.c_size_t), ("max_chunks", ctypes.c_int64)] + [
         (n, ctypes.c_size_t) for n in ("chunk_table", "chunk_offsets", "seq_starts",
-                                       "decay", "w", "qp", "kt", "ut", "oloc")] + [
+                                       "decay", "w", "qp", "ut", "oloc")] + [
         ("split_chunks", ctypes.c_int32)] + [
         (n, ctypes.c_size_t) for n in ("split_y", "split_hmid", "split_hmid_t", "split_psi",
                                        "split_phi")]

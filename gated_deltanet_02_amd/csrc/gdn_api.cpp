@@ -128,7 +128,7 @@ struct Problem {
 
 struct Layout {
   size_t table = 0, chunk_off = 0, seq_start = 0, decay = 0;
-  size_t w = 0, qp = 0, kt = 0, ut = 0, oloc = 0;
+  size_t w = 0, qp = 0, ut = 0, oloc = 0;
   size_t y = 0, hmid = 0, hmid_t = 0, psi = 0, phi = 0, total = 0;
 };
 
@@ -148,7 +148,6 @@ Layout make_layout(const Problem& P) {
   L.decay = take(blocks * 4);
   L.w = take(blocks * P.chunk * P.dk * es);
   L.qp = take(blocks * P.chunk * P.dk * es);
-  L.kt = take(blocks * P.chunk * P.dk * es);
   L.ut = take(blocks * P.chunk * P.dv * es);
   L.oloc = take(blocks * P.chunk * P.dv * es);
   if (P.split > 0) {
@@ -408,7 +407,6 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
   gdn::Intermediates im{};
   im.w = base + L.w;
   im.qp = base + L.qp;
-  im.kt = base + L.kt;
   im.ut = base + L.ut;
   im.oloc = base + L.oloc;
   im.decay = (float*)(base + L.decay);
@@ -458,6 +456,10 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
     sp.o_sh = P.o.sh;
     sp.init = init ? (const float*)init->data : nullptr;
     sp.final_state = fin ? (float*)fin->data : nullptr;
+    sp.k = k->data;
+    sp.k_st = P.k.st;
+    sp.k_sh = P.k.sh;
+    sp.grp = P.hv / P.hk;
     sp.hv = P.hv;
     sp.dv = P.dv;
     sp.map = map;
@@ -543,7 +545,6 @@ int gdn_get_workspace_layout(const gdn_tensor* q, const gdn_tensor* k, const gdn
   layout->decay = L.decay;
   layout->w = L.w;
   layout->qp = L.qp;
-  layout->kt = L.kt;
   layout->ut = L.ut;
   layout->oloc = L.oloc;
   layout->split_chunks = P.split;

@@ -33,11 +33,12 @@ struct TableParams {
 };
 
 // Per-(chunk, value head) intermediates, all in the input element type.
+// W and U~ are stored with row r scaled by s_r = e^(gamma_last - gamma_r)
+// / |k_r|, so that the state update takes k's own rows: K~^T U = K^T diag(s) U.
 struct Intermediates {
-  void* w;       // [C][dk]
+  void* w;       // [C][dk]  diag(s) W
   void* qp;      // [C][dk]
-  void* kt;      // [dk][C]
-  void* ut;      // [dv][C]
+  void* ut;      // [dv][C]  diag(s) U~
   void* oloc;    // [C][dv]
   float* decay;  // [chunk][Hv]
 };
@@ -61,6 +62,9 @@ struct WyParams {
 struct ScanParams {
   void* out;             // [T, Hv, dv] strides o_st, o_sh
   int64_t o_st, o_sh;
+  const void* k;         // [T, Hk, dk] strides k_st, k_sh: the state update's K rows
+  int64_t k_st, k_sh;
+  int32_t grp;           // value heads per key head
   const float* init;     // [N, Hv, dk, dv] or null
   float* final_state;    // [N, Hv, dk, dv] or null
   int32_t hv, dv;

@@ -12,9 +12,13 @@
 //   W   = T diag(beta e^gamma) K^,   U~ = T diag(beta) V
 //   P   = scale * D o (Q^ K^T)                    (causal, diagonal included)
 //   Q'  = scale diag(e^gamma) Q^ - P W,   O_loc = P U~
-//   K~_r = e^(gamma_last - gamma_r) k^_r
+//   K~_r = e^(gamma_last - gamma_r) k^_r = s_r k_r,
+//   s_r = e^(gamma_last - gamma_r) / sqrt(|k_r|^2 + eps)   (k_r as passed)
 // and, carried from chunk to chunk with state H (d_k x d_v, fp32):
 //   U = U~ - W H,   O = Q' H + O_loc,   H <- e^gamma_last H + K~^T U.
+// The state update is taken as K^T U' with U' = diag(s) U~ - diag(s) W H:
+// the WY kernel stores diag(s) W and diag(s) U~, and the scan reads the
+// chunk's key rows as passed, so no K~ is ever written.
 //
 // Kernels, launched in this order on the caller's stream:
 //   table_kernel  packed batches only: sanitised sequence starts, the
@@ -28,13 +32,15 @@
 //   scan_kernel   one workgroup per (sequence, value head, one or two
 //                 16-column slices of d_v): the only sequential part.  Per
 //                 slice one wave runs the recurrence with the state slice in
-//                 its MFMA accumulators; W, Q' and K~^T are stored by the WY
+//                 its MFMA accumulators; W and Q' are stored by the WY
 //                 kernel in k-tile order (the contraction index follows the
-//                 accumulator layout), so the state and the U rows feed the
+//                 accumulator layout) and the key rows are read transposed
+//                 in the same order, so the state and the U rows feed the
 //                 MFMAs from the registers they were accumulated in, with no
 //                 exchange through LDS; a second wave forms the slice's
-//                 output.  Two more waves stream the chunks' operands into
-//                 an LDS ring with LDS-direct loads, two chunks ahead.
+//                 output.  Two more waves stream the chunks' operands (W,
+//                 Q' and the key rows) into an LDS ring with LDS-direct
+//                 loads, two chunks ahead.
 //   scan_split_kernel, scan_fix_kernel
 //                 the two-level form of the scan, on request (both halves of
 //                 each sequence at once, then the second half's correction).
@@ -652,8 +658,8 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     };
     dispatch_int<0, kWyThreads / 64>(wave, build_ap);
     if (wave == NB - 1 && lane < C) {
-      // the K~ row scale rk_r e^(gamma_last - gamma_r) and Tb's column
-      // scale beta_s e^gamma_s rk_s
+      // the row scale s_r = rk_r e^(gamma_last - gamma_r) of the stored W
+      // and U~, and Tb's column scale beta_s e^gamma_s rk_s
       const float rk = sRk[lane];
       sKs[lane] = rk * fast_exp(sGam[C - 1] - sGam[lane]);
       sCb[lane] = sBeta[lane] * sEg[lane] * rk;
@@ -664,42 +670,6 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     // lane per column; then the blocks below the diagonal,
     //   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj   (fp32 MFMA, block column j
     // on wave j).
-    // Meanwhile waves 1.. write K~^T [dk][r] = K^T[dk][r] rk_r
-    // e^(gamma_last - gamma_r), in k-tile order per 16-row tile of d_k
-    // (contraction over r): one operand unit (16 d_k rows x 32 tokens for
-    // bf16) per wave and step, read transposed from the K rows and stored as
-    // one contiguous block.
-    if (wave > 0) {
-      using KC = KTile<TI, C>;
-      constexpr int TPU = KC::TPU;
-      TI* kt_g = (TI*)p.im.kt + blk * DK * C;
-      const int q = lane >> 4;
-      for (int w = wave - 1; w < (DK / 16) * KC::NU; w += NT / 64 - 1) {
-        const int dt = w / KC::NU, u = w % KC::NU;
-        const int k0 = 16 * TPU * u + 4 * q;  // first contraction index of the lane
-        TI* dst = kt_g + dt * 16 * C + KC::pos(lane & 15, k0);
-        const f32x4 sa = *(const f32x4*)(sKs + k0);
-        if (KC::HALF_TAIL && u == KC::NU - 1) {
-          const auto kv = col_unit<TI, true, SWK>(sKV, LK, 16 * dt, u, lane);
-          store4<TI>(dst, (float)kv[0] * sa[0], (float)kv[1] * sa[1], (float)kv[2] * sa[2],
-                     (float)kv[3] * sa[3]);
-        } else if constexpr (TPU == 2) {
-          const auto kv = col_unit<TI, false, SWK>(sKV, LK, 16 * dt, u, lane);
-          const f32x4 sb = *(const f32x4*)(sKs + k0 + 16);
-          bf16x8 o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[e] = from_float<TI>((float)kv[e] * sa[e]);
-            o[4 + e] = from_float<TI>((float)kv[4 + e] * sb[e]);
-          }
-          *(bf16x8*)dst = o;
-        } else {
-          const auto kv = col_unit<TI, false, SWK>(sKV, LK, 16 * dt, u, lane);
-          store4<TI>(dst, (float)kv[0] * sa[0], (float)kv[1] * sa[1], (float)kv[2] * sa[2],
-                     (float)kv[3] * sa[3]);
-        }
-      }
-    }
     if (wave == 0) {
       const int b = lane >> 4, col = lane & 15;
       if (b < NB) {
@@ -824,11 +794,12 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     __syncthreads();
 
     // Per wave, from the LDS tiles Tv, Tb, V, K and P:
-    //  - U~ = Tv V for d_v tile `wave`: accumulator tiles to global memory,
-    //    and kept as operand units of U~^T (contraction over the chunk);
+    //  - U~ = Tv V for d_v tile `wave`: accumulator tiles to global memory
+    //    (rows scaled by s_r), and kept as operand units of U~^T
+    //    (contraction over the chunk);
     //  - W[r][dk] = sum_s Tb[r][s] K[s][dk] for d_k tile `wave`, twice from
-    //    the same operand registers: W^T tiles (rows d_k, columns r) to
-    //    global memory in k-tile order, and W tiles (rows r, columns d_k)
+    //    the same operand registers: W^T tiles (rows d_k, columns r, scaled
+    //    by s_r) to global memory in k-tile order, and W tiles (rows r, columns d_k)
     //    kept as operand units of W^T (a K^T operand unit, rows d_k, holds
     //    the same registers as a K operand unit, columns d_k);
     //  - one pass over P's rows (in the same contraction order) feeding
@@ -861,8 +832,13 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
           for (int i = 0; i < NB; ++i)
             mma_unit<true>(acc[i], row_unit<TI, true, SWC>(sTv, LC, 16 * i + rr, u, lane), vb);
         }
+        // stored with row r scaled by s_r (lane holds rows 16 i + 4 (lane / 16) + e)
 #pragma unroll
-        for (int i = 0; i < NB; ++i) store_acc_tile<TI>(ut_g + (wave * NB + i) * 256, acc[i], lane);
+        for (int i = 0; i < NB; ++i) {
+          const f32x4 sr = *(const f32x4*)(sKs + 16 * i + (lane >> 4) * 4);
+          store4<TI>(ut_g + (wave * NB + i) * 256 + lane * 4, acc[i][0] * sr[0], acc[i][1] * sr[1],
+                     acc[i][2] * sr[2], acc[i][3] * sr[3]);
+        }
 #pragma unroll
         for (int u = 0; u < NUF; ++u) ua[u] = acc_unit<false>(acc[KT::TPU * u], acc[KT::TPU * u + T1], TI());
         if constexpr (KT::HALF_TAIL)
@@ -895,7 +871,10 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
             mma_unit<true>(wt, ka[u], tb);
             mma_unit<true>(wr[j], tb, ka[u]);
           }
-          store4<TI>(w_g + j * 16 * DK + KTile<TI, DK>::pos(rr, dk0), wt[0], wt[1], wt[2], wt[3]);
+          // stored with row r = 16 j + lane % 16 scaled by s_r
+          const float sr = sKs[16 * j + rr];
+          store4<TI>(w_g + j * 16 * DK + KTile<TI, DK>::pos(rr, dk0), wt[0] * sr, wt[1] * sr,
+                     wt[2] * sr, wt[3] * sr);
         }
 #pragma unroll
         for (int u = 0; u < NUF; ++u) wu[u] = acc_unit<false>(wr[KT::TPU * u], wr[KT::TPU * u + T1], TI());
@@ -963,7 +942,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
 //   wave NSL + s       the output of slice s, one chunk behind:
 //                      O = Q' H + O_loc from Q' held in registers since the
 //                      previous chunk, off the recurrence's critical path;
-//   the last two waves copy each chunk's W, Q' and K~^T (one slice: also its
+//   the last two waves copy each chunk's W, Q' and key rows (one slice: also its
 //                      U~ tiles and the decay) from global memory into a ring
 //                      of LDS stages with LDS-direct loads (no registers),
 //                      `lead` chunks ahead.
@@ -972,7 +951,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
 // registers, two chunks ahead.
 //
 // A wave reads LDS at about half of what its SIMD's LDS port delivers, and
-// the recurrence of one slice reads 32 KiB of W and K~^T per chunk, so its
+// the recurrence of one slice reads 32 KiB of W and key rows per chunk, so its
 // chunk step is bound by that wave's reads, not by its MFMAs.  Slices of one
 // workgroup share the ring's copies and run on separate SIMDs: two slices
 // cost the compute unit about what one does.
@@ -981,11 +960,15 @@ constexpr int kScanCopyWaves = 2;
 
 template <typename TI, int C, int DK, int NSL>
 struct ScanRing {
+  using Elem = TI;
+  static constexpr int D = DK;
   static constexpr int S = sizeof(TI);
-  static constexpr int BIG = C * DK * S;            // W, Q', K~^T of one chunk
+  static constexpr int BIG = C * DK * S;            // W, Q', K rows of one chunk
   static constexpr int SMALL = C * 16 * S;          // U~ tiles of one slice
   static constexpr bool UTR = NSL == 1;             // U~ and the decay staged too
-  static constexpr int w = 0, qp = BIG, kt = 2 * BIG, ut = 3 * BIG;
+  static constexpr int w = 0, qp = BIG, kr = 2 * BIG, ut = 3 * BIG;
+  // the key rows [C][DK] are row-swizzled (bf16) for the transposed reads
+  static constexpr int SWK = S == 2 ? DK / 8 - 1 : 0;
   static constexpr int dec = ut + SMALL;            // e^gamma_last (4 bytes)
   static constexpr int stage = UTR ? dec + 16 : 3 * BIG;
   static constexpr int HB = KTile<TI, DK>::NU * 1024;  // -H of one slice as operand units
@@ -1025,12 +1008,21 @@ __host__ __device__ constexpr int lgkmcnt0_imm() { return 15 | (3 << 14) | (7 <<
 // loads per stage.  All piece indices are compile-time constants.
 template <typename R, int C, int CW>
 __device__ __forceinline__ void ring_copy(char* stage, const ScanParams& p, int cc, int h,
-                                          int ctile, int lane) {
+                                          int ctile, int t0, int t_end, int lane) {
   constexpr int NB = C / 16;
+  constexpr int GE = 16 / R::S;  // elements per 16-byte granule
   const int64_t blk = (int64_t)cc * p.hv + h;
   const int64_t big = blk * R::BIG, small = (blk * C * p.dv + (int64_t)ctile * NB * 256) * R::S;
-  const char* bases[4] = {(const char*)p.im.w + big, (const char*)p.im.qp + big,
-                          (const char*)p.im.kt + big, (const char*)p.im.ut + small};
+  const char* bases[4] = {(const char*)p.im.w + big, (const char*)p.im.qp + big, nullptr,
+                          (const char*)p.im.ut + small};
+  // the chunk's key rows (of key head h / grp), row-swizzled like the WY
+  // kernel's K rows; rows past the chunk's end repeat its last row (finite,
+  // and the rows of U they meet are zero), so every copy issues the same
+  // number of loads
+  const int n = min(C, t_end - t0);
+  using TI = typename R::Elem;
+  constexpr int DK = R::D;
+  const TI* krow = (const TI*)p.k + (int64_t)(h / p.grp) * p.k_sh;
 #pragma unroll
   for (int j = 0; j < R::per_wave; ++j) {
     const int i = min(CW + kScanCopyWaves * j, R::pieces - 1);
@@ -1046,10 +1038,20 @@ __device__ __forceinline__ void ring_copy(char* stage, const ScanParams& p, int 
     const int bytes = r < 3 ? R::BIG : R::SMALL;
     const int lds_off = r * R::BIG + k * 1024;
     const bool half = (bytes % 1024) != 0 && k == (bytes - 1) / 1024;
-    if (!half || lane < 32)
-      __builtin_amdgcn_global_load_lds((const void*)(bases[r] + k * 1024 + lane * 16),
-                                       (__attribute__((address_space(3))) void*)(stage + lds_off),
-                                       16, 0, 0);
+    if (half && lane >= 32) continue;
+    const char* src;
+    if (r == 2) {
+      const int o = k * 1024 + lane * 16;          // byte offset in the [C][DK] rows
+      const int row = o / (DK * R::S), slot = (o % (DK * R::S)) / 16;
+      const int gcol = (slot ^ (row & R::SWK)) * GE;
+      const int trow = t0 + (row < n ? row : n - 1);
+      src = (const char*)(krow + (int64_t)trow * p.k_st + gcol);
+    } else {
+      src = bases[r] + k * 1024 + lane * 16;
+    }
+    __builtin_amdgcn_global_load_lds((const void*)src,
+                                     (__attribute__((address_space(3))) void*)(stage + lds_off),
+                                     16, 0, 0);
   }
 }
 
@@ -1058,16 +1060,19 @@ __device__ __forceinline__ void ring_copy(char* stage, const ScanParams& p, int 
 // need next has landed.  Loads past the last chunk re-read it.
 template <typename R, int C, int CW>
 __device__ __forceinline__ void ring_producer(char* smem, const ScanParams& p, int c_begin,
-                                              int c_end, int h, int ctile, int lane) {
+                                              int c_end, int h, int ctile, int tok0, int tok_end,
+                                              int lane) {
   const int last = c_end - 1;
+  auto copy = [&](char* stage, int cc) {
+    ring_copy<R, C, CW>(stage, p, cc, h, ctile, tok0 + (cc - c_begin) * C, tok_end, lane);
+  };
 #pragma unroll
-  for (int k = 0; k < R::lead; ++k)
-    ring_copy<R, C, CW>(smem + k * R::stage, p, min(c_begin + k, last), h, ctile, lane);
+  for (int k = 0; k < R::lead; ++k) copy(smem + k * R::stage, min(c_begin + k, last));
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::per_wave * (R::lead - 1)));
   ring_barrier();
   int slot = R::lead;
   for (int cc = c_begin; cc < c_end; ++cc) {
-    ring_copy<R, C, CW>(smem + slot * R::stage, p, min(cc + R::lead, last), h, ctile, lane);
+    copy(smem + slot * R::stage, min(cc + R::lead, last));
     slot = slot + 1 == R::slots ? 0 : slot + 1;
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::per_wave * (R::lead - 1)));
     ring_barrier();
@@ -1274,16 +1279,17 @@ __device__ __forceinline__ void scan_recurrence(char* smem, const ScanParams& p,
         ub[q] = (KC::HALF_TAIL && q == KC::NU - 1)
                     ? acc_unit<true>(au[KC::TPU * q], au[KC::TPU * q], TI{})
                     : acc_unit<false>(au[KC::TPU * q], au[KC::TPU * q + KC::TPU - 1], TI{});
-      // H <- e^gamma_last H + K~^T U.
+      // H <- e^gamma_last H + K^T U' (U' = diag(s) U, the key rows read
+      // transposed: K~^T U with K~_r = s_r k_r).
+      const TI* kr = (const TI*)(st + R::kr);
 #pragma unroll
       for (int q = 0; q < KC::NU; ++q)
 #pragma unroll
         for (int t = 0; t < NKT; ++t) {
-          const char* ku = st + R::kt + t * 16 * C * S + q * KC::UNIT * S;
           if (KC::HALF_TAIL && q == KC::NU - 1)
-            mma_unit<true>(hacc[t], lds_unit<TI, true>(ku, lane), ub[q]);
+            mma_unit<true>(hacc[t], col_unit<TI, true, R::SWK>(kr, DK, 16 * t, q, lane), ub[q]);
           else
-            mma_unit<false>(hacc[t], lds_unit<TI, false>(ku, lane), ub[q]);
+            mma_unit<false>(hacc[t], col_unit<TI, false, R::SWK>(kr, DK, 16 * t, q, lane), ub[q]);
         }
 #pragma unroll
       for (int t = 0; t < NKT; ++t) settle(hacc[t]);
@@ -1395,8 +1401,8 @@ __global__ __launch_bounds__(scan_threads<NSL>()) void scan_kernel(ScanParams p)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int NS = p.n_slices;
   // XCD-aware: the slice groups of one (sequence, head) share blockIdx % 8
-  // and so land on the same XCD, where they share W, Q' and K~^T through its
-  // L2.
+  // and so land on the same XCD, where they share W, Q' and the key rows
+  // through its L2.
   const int b = blockIdx.x;
   const int u = (b / (8 * NS)) * 8 + (b % 8);
   const int sl = (b / 8) % NS;
@@ -1408,8 +1414,8 @@ __global__ __launch_bounds__(scan_threads<NSL>()) void scan_kernel(ScanParams p)
 
   if (wave >= 2 * NSL) {
     if (nch <= 0) return;
-    if (wave == 2 * NSL) ring_producer<R, C, 0>(smem, p, c_begin, c_end, h, NSL * sl, lane);
-    else ring_producer<R, C, 1>(smem, p, c_begin, c_end, h, NSL * sl, lane);
+    if (wave == 2 * NSL) ring_producer<R, C, 0>(smem, p, c_begin, c_end, h, NSL * sl, tok0, tok_end, lane);
+    else ring_producer<R, C, 1>(smem, p, c_begin, c_end, h, NSL * sl, tok0, tok_end, lane);
     return;
   }
   if (wave >= NSL) {
@@ -1473,8 +1479,8 @@ __global__ __launch_bounds__(scan_threads<2>()) void scan_split_kernel(ScanParam
   if (ce <= cb) return;
 
   if (wave >= 4) {
-    if (wave == 4) ring_producer<R, C, 0>(smem, p, cb, ce, h, 0, lane);
-    else ring_producer<R, C, 1>(smem, p, cb, ce, h, 0, lane);
+    if (wave == 4) ring_producer<R, C, 0>(smem, p, cb, ce, h, 0, tb, te, lane);
+    else ring_producer<R, C, 1>(smem, p, cb, ce, h, 0, tb, te, lane);
     return;
   }
   const int s = wave & 1;

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 /* Status codes. */
 #define GDN_OK 0
@@ -86,7 +86,7 @@ typedef struct gdn_tensor {
  * caller-owned workspace keeps the intermediates between partial calls so a
  * caller may run (and time) the stages one at a time, in order. */
 #define GDN_STAGE_TABLE 1u /* chunk table from cu_seqlens                   */
-#define GDN_STAGE_WY 2u    /* L2 norms, gate cumsum, (I+A)^-1, W, U~, Q', K~ */
+#define GDN_STAGE_WY 2u    /* L2 norms, gate cumsum, (I+A)^-1, W, U~, Q', O_loc */
 #define GDN_STAGE_SCAN 4u  /* sequential state scan fused with the output   */
 #define GDN_STAGE_ALL 7u
 
@@ -178,12 +178,15 @@ int gdn_prefill_ex(const gdn_tensor* q, const gdn_tensor* k,
 
 /* Byte offsets of the intermediates inside the workspace (for inspection and
  * tests).  Per (chunk c, value head h) block, all in the input dtype:
- *   w     W  = T diag(beta e^gamma) K^             C x dk, k-tile order
- *   qp    Q' = scale diag(e^gamma) Q^ - P W        C x dk, k-tile order
- *   kt    K~^T, K~_r = e^(gamma_last - gamma_r) k^_r   dk x C, k-tile order
- *   ut    U~ = T diag(beta) V                      C x dv, accumulator tiles
- *   oloc  O_loc = P U~                             C x dv, transposed tiles
- * and f32 decay[c][h] = e^(gamma_last).  A block starts at
+ *   w     diag(s) W,  W = T diag(beta e^gamma) K^     C x dk, k-tile order
+ *   qp    Q' = scale diag(e^gamma) Q^ - P W             C x dk, k-tile order
+ *   ut    diag(s) U~, U~ = T diag(beta) V              C x dv, accumulator tiles
+ *   oloc  O_loc = P U~                                  C x dv, transposed tiles
+ * with the row scale s_r = e^(gamma_last - gamma_r) / sqrt(|k_r|^2 + eps)
+ * (k_r the key row as passed), and f32 decay[c][h] = e^(gamma_last).  With
+ * U' = diag(s) U~ - diag(s) W H the state update is H' = e^(gamma_last) H +
+ * K^T U' with K the chunk's key rows as passed, equal to K~^T U for
+ * K~_r = e^(gamma_last - gamma_r) k^_r.  A block starts at
  * offset + (c * Hv + h) * (its element count) * element_size.
  * "k-tile order": 16-row tiles one after another; inside a tile, for the
  * 16-wide k-tile t of the second index, lane l = m + 16 ((k % 16) / 4)
@@ -200,7 +203,7 @@ int gdn_prefill_ex(const gdn_tensor* q, const gdn_tensor* k,
 typedef struct gdn_workspace_layout {
   size_t total_bytes;
   int64_t max_chunks;
-  size_t chunk_table, chunk_offsets, seq_starts, decay, w, qp, kt, ut, oloc;
+  size_t chunk_table, chunk_offsets, seq_starts, decay, w, qp, ut, oloc;
   /* two-level scan (split_chunks > 0: chunks in the first segment), else 0:
    *   split_y      bf16 [chunk][Hv][C][dk]  Q' x M-product, second segment
    *   split_hmid   f32 [N][Hv][dk][dv]      state at the split

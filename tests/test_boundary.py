@@ -140,14 +140,14 @@ def test_state_and_cu_validation(lib):
 def test_workspace_size_formula(lib):
     q = torch.empty(4096, 16, 128, dtype=torch.bfloat16)
     v = torch.empty(4096, 16, 128, dtype=torch.bfloat16)
-    # one pass: 64 chunks x 16 heads x (3 C*dk + 2 C*dv) bf16 + decay, 256-byte aligned
+    # one pass: 64 chunks x 16 heads x (2 C*dk + 2 C*dv) bf16 + decay, 256-byte aligned
     one = G.options(scan_split=G.SCAN_ONE_PASS)
     n = G.gdn_workspace_size(q, q, v, opts=one)
-    per = 64 * 16 * (5 * 64 * 128) * 2
+    per = 64 * 16 * (4 * 64 * 128) * 2
     assert per <= n <= per + 64 * 16 * 4 + 6 * 256
     lay = G.gdn_get_workspace_layout(q, q, v, opts=one)
     assert lay.max_chunks == 64 and lay.total_bytes == n and lay.split_chunks == 0
-    offs = [lay.decay, lay.w, lay.qp, lay.kt, lay.ut, lay.oloc]
+    offs = [lay.decay, lay.w, lay.qp, lay.ut, lay.oloc]
     assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
     assert lay.split_y == lay.split_phi == 0
     assert G.gdn_workspace_size(q, q, v) == n  # the default is one pass

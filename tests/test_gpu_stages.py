@@ -101,7 +101,6 @@ def test_wy_intermediates(label, name, kw, tol):
     two = dt == torch.bfloat16
     Wb = unfrag(_blocks(ws, lay.w, mc * hv, (C, dk), dt), C, dk, two)
     Qp = unfrag(_blocks(ws, lay.qp, mc * hv, (C, dk), dt), C, dk, two)
-    Kt = unfrag(_blocks(ws, lay.kt, mc * hv, (dk, C), dt), dk, C, two)
     Ut = np.swapaxes(unacc(_blocks(ws, lay.ut, mc * hv, (C, dv), dt), C, dv, False), 1, 2)
     Ol = unacc(_blocks(ws, lay.oloc, mc * hv, (C, dv), dt), C, dv, True)
     dec = _blocks(ws, lay.decay, mc * hv, (1,), torch.float32)[:, 0]
@@ -125,13 +124,21 @@ def test_wy_intermediates(label, name, kw, tol):
         if w.n_seqs > 1:
             assert table[c, 0] == it["seq"] and table[c, 1] == it["t0"] and table[c, 2] == n
             assert it["t0"] == starts[it["seq"]] + it["chunk"] * C
-        for what, got, ref in (("W", Wb[blk, :n], it["W"]), ("Qprime", Qp[blk, :n], it["Qprime"]),
-                               ("Ktilde^T", Kt[blk][:, :n], it["Ktilde"].T),
-                               ("Utilde^T", Ut[blk][:, :n], it["Utilde"].T),
+        # W and U~ are stored with row r scaled by s_r = e^(gamma_last - gamma_r)
+        # / sqrt(|k_r|^2 + eps) (k_r the key row as passed), so that the scan's
+        # state update can take the key rows as they are
+        kh_ = it["head"] // (hv // w.q.shape[1])
+        kr = w.k[it["t0"]:it["t0"] + n, kh_].double().numpy()
+        s = np.exp(it["gamma"][-1] - it["gamma"]) / np.sqrt((kr * kr).sum(-1) + 1e-6)
+        for what, got, ref in (("W", Wb[blk, :n], s[:, None] * it["W"]),
+                               ("Qprime", Qp[blk, :n], it["Qprime"]),
+                               ("Utilde^T", Ut[blk][:, :n], (s[:, None] * it["Utilde"]).T),
                                ("Oloc", Ol[blk, :n], it["Oloc"])):
             worst[what] = max(worst.get(what, 0.0), close(got, ref, what))
+        # the scaled rows are the key rows the state update meets: K~ = diag(s) K
+        assert np.allclose(s[:, None] * kr, it["Ktilde"], rtol=1e-6, atol=1e-9)
         # rows past the chunk's end are zero
-        assert not Wb[blk, n:].any() and not Qp[blk, n:].any() and not Kt[blk][:, n:].any()
+        assert not Wb[blk, n:].any() and not Qp[blk, n:].any()
         assert not Ut[blk][:, n:].any() and not Ol[blk, n:].any()
         assert abs(dec[blk] - np.exp(it["gamma"][-1])) <= 1e-5 * max(1.0, np.exp(it["gamma"][-1]))
     U.say(f"  {label}: worst relative errors {worst}")
