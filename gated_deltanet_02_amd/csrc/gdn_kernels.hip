@@ -813,7 +813,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       const int rr = lane & 15;
       const bool uv = wave < NVT, wq = wave < NKT;
       UT ua[KT::NU], wu[KT::NU];
-      if (uv) {
+      auto u_part = [&]() {
         TI* ut_g = (TI*)p.im.ut + blk * DV * C;
         f32x4 acc[NB];
 #pragma unroll
@@ -843,9 +843,9 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
         for (int u = 0; u < NUF; ++u) ua[u] = acc_unit<false>(acc[KT::TPU * u], acc[KT::TPU * u + T1], TI());
         if constexpr (KT::HALF_TAIL)
           ua[KT::NU - 1] = acc_unit<true>(acc[KT::TPU * (KT::NU - 1)], acc[KT::TPU * (KT::NU - 1)], TI());
-      }
+      };
       const int dk0 = 16 * wave + (lane >> 4) * 4;
-      if (wq) {
+      auto w_part = [&]() {
         TI* w_g = (TI*)p.im.w + blk * C * DK;
         // K operand units for every chunk unit, then one row tile of W and
         // W^T at a time (each W^T tile is stored as soon as it is complete)
@@ -880,7 +880,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
         for (int u = 0; u < NUF; ++u) wu[u] = acc_unit<false>(wr[KT::TPU * u], wr[KT::TPU * u + T1], TI());
         if constexpr (KT::HALF_TAIL)
           wu[KT::NU - 1] = acc_unit<true>(wr[KT::TPU * (KT::NU - 1)], wr[KT::TPU * (KT::NU - 1)], TI());
-      }
+      };
       // The pass over P (branch-free in the common case of both products).
       auto p_pass = [&](auto do_o, auto do_q) {
         constexpr bool DO = decltype(do_o)::value, DQ = decltype(do_q)::value;
@@ -921,9 +921,19 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
           }
         }
       };
-      if (uv && wq) p_pass(BoolC<true>{}, BoolC<true>{});
-      else if (uv) p_pass(BoolC<true>{}, BoolC<false>{});
-      else if (wq) p_pass(BoolC<false>{}, BoolC<true>{});
+      // both parts in one straight-line block where a wave has both (every
+      // wave when d_k = d_v = 128), so their reads and products interleave
+      if (uv && wq) {
+        u_part();
+        w_part();
+        p_pass(BoolC<true>{}, BoolC<true>{});
+      } else if (uv) {
+        u_part();
+        p_pass(BoolC<true>{}, BoolC<false>{});
+      } else if (wq) {
+        w_part();
+        p_pass(BoolC<false>{}, BoolC<true>{});
+      }
     }
     if (tid == 0) p.im.decay[blk] = sEg[C - 1];
     __syncthreads();
