@@ -968,6 +968,18 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
 
 constexpr int kScanCopyWaves = 2;
 
+// The value head of the r-th (sequence, head) unit of a sequence.  Units
+// land on XCD r % 8 (blockIdx % 8).  With key heads shared by grp > 1 value
+// heads and a multiple of 8 key heads, the value heads of one key head are
+// placed on one XCD, where they share its key rows through the L2:
+// r = 8 y + x takes key head x + 8 (y / grp) and value head grp (x + 8 (y /
+// grp)) + y % grp (a permutation of 0 .. hv - 1).  Otherwise r itself.
+__device__ __forceinline__ int scan_head(int r, int grp, int hv) {
+  if (grp <= 1 || (hv / grp) % 8 != 0) return r;
+  const int x = r % 8, y = r / 8;
+  return grp * (x + 8 * (y / grp)) + y % grp;
+}
+
 template <typename TI, int C, int DK, int NSL>
 struct ScanRing {
   using Elem = TI;
@@ -1417,7 +1429,7 @@ __global__ __launch_bounds__(scan_threads<NSL>()) void scan_kernel(ScanParams p)
   const int u = (b / (8 * NS)) * 8 + (b % 8);
   const int sl = (b / 8) % NS;
   if (u >= p.map.n_seq * p.hv) return;
-  const int seq = u / p.hv, h = u % p.hv;
+  const int seq = u / p.hv, h = scan_head(u % p.hv, p.grp, p.hv);
   int c_begin, c_end, tok0, tok_end;
   seq_range(p.map, seq, C, c_begin, c_end, tok0, tok_end);
   const int nch = c_end - c_begin;
@@ -1473,7 +1485,7 @@ __global__ __launch_bounds__(scan_threads<2>()) void scan_split_kernel(ScanParam
   const int u = (b / (8 * NW)) * 8 + (b % 8);
   const int wg = (b / 8) % NW;
   if (u >= p.map.n_seq * p.hv) return;
-  const int seq = u / p.hv, h = u % p.hv;
+  const int seq = u / p.hv, h = scan_head(u % p.hv, p.grp, p.hv);
   int c_begin, c_end, tok0, tok_end;
   seq_range(p.map, seq, C, c_begin, c_end, tok0, tok_end);
   const int NV = p.dv / 16;  // value column tiles = first-segment workgroups
