@@ -36,6 +36,9 @@ REDUCED = [
     ("prompt_4k", dict(lengths=[257], hk=1, hv=2, dk=32, dv=128)),
     ("prompt_4k", dict(lengths=[77], hk=1, hv=1, dk=16, dv=16, chunk=16)),
     ("prompt_4k", dict(lengths=[190], hk=2, hv=4, dk=128, dv=64, chunk=32)),
+    # 8 key heads with 2 value heads each: the one-slice scan places the
+    # value heads of a key head on one XCD (a permuted head order)
+    ("long_16k_gqa", dict(lengths=[260], hk=8, hv=16)),
 ]
 
 

@@ -35,6 +35,7 @@ CASES = [
     ("prompt_4k", dict(lengths=[190], hk=2, hv=4, dk=128, dv=64, chunk=32)),
     ("prompt_4k", dict(lengths=[100], hk=1, hv=2)),                       # 2 chunks: split 1 + 1
     ("edge_mix", dict(lengths=[1000], hk=2, hv=2)),                       # strong decay, g = 0 rows
+    ("long_16k_gqa", dict(lengths=[400], hk=8, hv=16)),                   # 8 key heads: permuted head order
     # weak decay: the state at the split reaches every later chunk, so the
     # transition product (not only its first, identity, factor) decides the
     # second half
