@@ -427,7 +427,8 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const TI* vg = (const TI*)p.v;
   const int DV = p.dv;
-  const int GPRV = DV / GR;
+  const int GPRV = DV / GR;  // granules per v row: a power of two (d_v is 16 .. 128)
+  const int LGV = __builtin_ctz(GPRV);
   const int NVT = DV / 16;
   const int grp = p.hv / p.hk;
   TI* sKV = (TI*)(smem + L::r_kv);   // K rows | V^T
@@ -480,7 +481,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
 #pragma unroll
     for (int i = 0; i < NVG; ++i) {
       const int idx = tid_l + i * NT;
-      const int r = idx / GPRV, gc = idx % GPRV;
+      const int r = idx >> LGV, gc = idx & (GPRV - 1);
       vreg[i] = make_uint4(0, 0, 0, 0);
       if (idx < C * GPRV && r < n) vreg[i] = ld16(vg + (int64_t)(t0 + r) * p.v_st + h * p.v_sh + gc * GR);
     }
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     for (int i = 0; i < NVG; ++i) {
       const int idx = tid_s + i * NT;
       if (idx < C * GPRV) {
-        const int r = idx / GPRV, gc = idx % GPRV;
+        const int r = idx >> LGV, gc = idx & (GPRV - 1);
         st16(sVr + r * LV + swz<TI, SWV>(r, gc * GR), vreg[i]);
       }
     }
