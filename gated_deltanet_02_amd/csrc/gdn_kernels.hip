@@ -755,7 +755,10 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
 
     // Tb = T diag(beta e^gamma rk), Tv = T diag(beta), 8 stored positions
     // (kperm order) per item.
-    for (int idx = tid; idx < C * (C / 8); idx += NT) {
+#pragma unroll
+    for (int it = 0; it < (C * (C / 8) + NT - 1) / NT; ++it) {
+      const int idx = tid + it * NT;
+      if (C * (C / 8) % NT != 0 && idx >= C * (C / 8)) break;
       const int r = idx / (C / 8), s0 = (idx % (C / 8)) * 8;
       // the 8 stored positions s0 .. s0 + 7 are the columns c_lo + 0..3 and
       // c_hi + 0..3 (kperm within a full 32-column block, else natural)
