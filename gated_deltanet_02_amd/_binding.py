@@ -154,6 +154,13 @@ def _stream_handle(stream, ref: torch.Tensor) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _torch_stream(stream, device) -> torch.cuda.Stream:
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.ExternalStream(handle, device=device)
+
+
 def gdn_abi_version() -> int:
     return lib().gdn_abi_version()
 
@@ -225,15 +232,21 @@ def gdn_prefill_ex(q, k, v, g, beta, cu_seqlens=None, init_state=None,
     torch if None).  Returns (out, final_state)."""
     if out is None:
         out = torch.empty_like(v)
-    if workspace is None:
+    own_ws = workspace is None
+    if own_ws:
         workspace = alloc_workspace(q, k, v, cu_seqlens, opts)
     if workspace.device.type != "cuda":
         raise ValueError("workspace must be a GPU tensor")
     ds = _descs(q, k, v, g, beta, cu_seqlens, init_state, out, final_state)
+    handle = _stream_handle(stream, v)
     _check(lib().gdn_prefill_ex(*[_ref(d) for d in ds],
                                 ctypes.byref(opts) if opts else None,
-                                workspace.data_ptr(), workspace.numel(),
-                                _stream_handle(stream, v)))
+                                workspace.data_ptr(), workspace.numel(), handle))
+    if own_ws and stream is not None:
+        # the temporary workspace came from the current stream's pool while
+        # the kernels run on ``stream``: keep the block from being handed out
+        # again before that stream has finished with it
+        workspace.record_stream(_torch_stream(stream, v.device))
     return out, final_state
 
 

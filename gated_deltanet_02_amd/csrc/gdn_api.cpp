@@ -255,8 +255,10 @@ int validate(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
     if (P->q.B != 1) return fail(GDN_ERR_SHAPE, "with cu_seqlens the batch dimension must be 1");
     if (cu->shape[0] - 1 >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "too many sequences");
     P->n_seq = (int)(cu->shape[0] - 1);
-    P->packed = P->n_seq > 1;
-    P->seq_len = (int)P->T;  // used only when not packed (a single sequence)
+    // the sequence bounds are read on the device from cu_seqlens, also for
+    // one sequence (cu = [0, L] with L < T covers L tokens only)
+    P->packed = true;
+    P->seq_len = 0;
   } else {
     P->n_seq = (int)P->q.B;
     P->packed = false;

@@ -1,9 +1,14 @@
 // gfx950 (CDNA4) kernels of the chunked Gated DeltaNet prefill.
 //
-// The operation is the gated delta rule (Gated Delta Networks, Yang, Kautz,
-// Hatamizadeh, ICLR 2025, section 3), evaluated chunk by chunk in its WY
-// form (Parallelizing Linear Transformers with the Delta Rule over Sequence
-// Length, Yang et al., NeurIPS 2024, section 3).  For a chunk of n <= C
+// The operation is the chunked Gated DeltaNet prefill that the serving pages
+// run in their native backend and test against float64 references ("Cua-S1
+// 4B 0.2 native text worker"; "Open-Jev-27B-v1.1 native text worker",
+// section "Validation and optimization scope").  The pages print no formula;
+// the recurrence taken here (state H, d_k x d_v) is
+//   H_t = exp(g_t) (I - beta_t k^_t k^_t^T) H_{t-1} + beta_t k^_t v_t^T,
+//   o_t = scale H_t^T q^_t,  q^, k^ the L2-normalised rows,
+// evaluated chunk by chunk in its WY (compact product) form, which follows
+// from summing the recurrence over a chunk.  For a chunk of n <= C
 // tokens with chunk-local cumulative gate gamma_r = g_0 + ... + g_r and
 // D_rs = exp(gamma_r - gamma_s) (s <= r):
 //

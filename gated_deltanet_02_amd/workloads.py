@@ -22,6 +22,17 @@ beta -> init, numpy PCG64 seeded with ``seed``):
   edge mix one of three classes per (token, head): sigmoid(-12), sigmoid(12),
   sigmoid(N(0, 3)), each drawn with probability 1/3;
 * init: zeros (passed as NULL) or N(0, init_std) float32.
+
+The q and k rows may instead be left un-normalised, so that the library's
+own L2 normalisation is what makes them unit rows (``qk_rows``):
+
+* "unit" (default): as above;
+* "raw": the same Gaussian rows, not divided by their length (norm about
+  sqrt(d));
+* "scaled": the unit rows, then (drawn after init, so the other draws are
+  unchanged) each (token, key head) row of q and of k multiplied by a factor
+  of one class: 0 (a zero row, 4 %), 1e-3 (squared norm 1e-6, the size of
+  the default eps, 8 %), 1e3 (4 %), else log-uniform in [0.05, 20].
 """
 from __future__ import annotations
 
@@ -77,6 +88,11 @@ SPECS = {
                        init_std=0.5, g_zero_frac=0.0, token_offset=0),
 }
 
+# Row factor classes of qk_rows="scaled": (probability, factor); None is
+# the log-uniform class.
+SCALED_ROW_CLASSES = ((0.04, 0.0), (0.08, 1e-3), (0.04, 1e3), (0.84, None))
+SCALED_ROW_RANGE = (0.05, 20.0)
+
 
 @dataclasses.dataclass
 class Workload:
@@ -125,6 +141,25 @@ def _unit_rows(rng, shape) -> np.ndarray:
     return (x / n).astype(np.float32)
 
 
+def _gauss_rows(rng, shape) -> np.ndarray:
+    """The same draws as ``_unit_rows``, left un-normalised."""
+    return rng.standard_normal(shape, dtype=np.float32)
+
+
+def _row_factors(rng, shape) -> np.ndarray:
+    """One factor per row from SCALED_ROW_CLASSES (float32)."""
+    u = rng.random(shape)
+    lo, hi = SCALED_ROW_RANGE
+    f = np.exp(rng.uniform(np.log(lo), np.log(hi), size=shape))
+    edge = 0.0
+    for p, val in SCALED_ROW_CLASSES:
+        if val is None:
+            continue
+        f = np.where((u >= edge) & (u < edge + p), val, f)
+        edge += p
+    return f.astype(np.float32)
+
+
 def _store(x: np.ndarray, dtype: str) -> torch.Tensor:
     t = torch.from_numpy(np.ascontiguousarray(x))
     if dtype == "bf16":
@@ -150,8 +185,12 @@ def make_workload(name: str, seed: int = 0, **overrides) -> Workload:
     hk, hv, dk, dv = spec["hk"], spec["hv"], spec["dk"], spec["dv"]
     if hv % hk:
         raise ValueError("hv must be a multiple of hk")
-    q = _unit_rows(rng, (T, hk, dk))
-    k = _unit_rows(rng, (T, hk, dk))
+    qk_rows = spec.get("qk_rows", "unit")
+    if qk_rows not in ("unit", "raw", "scaled"):
+        raise ValueError(qk_rows)
+    rows = _gauss_rows if qk_rows == "raw" else _unit_rows
+    q = rows(rng, (T, hk, dk))
+    k = rows(rng, (T, hk, dk))
     v = rng.standard_normal((T, hv, dv), dtype=np.float32)
     g = rng.uniform(spec["g_low"], 0.0, size=(T, hv)).astype(np.float32)
     if spec["g_zero_frac"] > 0:
@@ -177,6 +216,9 @@ def make_workload(name: str, seed: int = 0, **overrides) -> Workload:
         init = torch.from_numpy(
             (spec["init_std"] * rng.standard_normal(
                 (len(lengths), hv, dk, dv), dtype=np.float32)).astype(np.float32))
+    if qk_rows == "scaled":
+        q = q * _row_factors(rng, (T, hk))[..., None]
+        k = k * _row_factors(rng, (T, hk))[..., None]
     dt = spec["dtype"]
     return Workload(name=name, q=_store(q, dt), k=_store(k, dt),
                     v=_store(v, dt), g=torch.from_numpy(g),

@@ -9,14 +9,14 @@
  *     H  = exp(g_t) (I - beta_t k^ k^T) H + beta_t k^ v_t^T
  *     out[t, h] = scale * H^T q^
  *
- * and final_state[i, h] = H after the sequence's last token.  This is the
- * gated delta rule ("Gated Delta Networks: Improving Mamba2 with Delta
- * Rule", Yang, Kautz, Hatamizadeh, ICLR 2025, section 3) with the state
- * stored as d_k x d_v.  The serving pages name the operation as the
- * "chunked Gated DeltaNet prefill" of their native Qwen3.5 backend ("Cua-S1
- * 4B 0.2 native text worker"; "Open-Jev-27B-v1.1 native text worker",
- * section "Validation and optimization scope") and test it against float64
- * references, as this library's tests do.
+ * and final_state[i, h] = H after the sequence's last token: the gated
+ * delta rule, with the state stored as d_k x d_v.  The serving pages name
+ * the operation as the chunked Gated DeltaNet prefill of their native
+ * Qwen3.5 backend ("Cua-S1 4B 0.2 native text worker"; "Open-Jev-27B-v1.1
+ * native text worker", section "Validation and optimization scope") and
+ * test it against float64 references, as this library's tests do; they
+ * print no formula, so the recurrence above is the definition this library
+ * takes.
  *
  * The library evaluates it chunk by chunk (chunk C in {16, 32, 64}, default
  * 64) on the caller's HIP stream with three kernels: a chunk table, a fused
@@ -102,7 +102,7 @@ typedef struct gdn_options {
 /*
  * GDN_FLAG_BETA_LOGITS: `beta` holds the write gate's raw projection b, and
  * the kernels use beta = sigmoid(b) = 1 / (1 + e^-b), computed in fp32 as the
- * gate is loaded ("Gated Delta Networks": beta in (0, 1) from a sigmoid), so
+ * gate is loaded (beta in (0, 1) is a sigmoid of a projection), so
  * no separate activation pass over [T, Hv] runs before the prefill or the
  * decode step.  b = +-inf give beta = 1 / 0.
  */
@@ -110,8 +110,8 @@ typedef struct gdn_options {
 
 /*
  * The state scan's schedule.  Each chunk maps its incoming state affinely
- * (the gated delta rule of "Gated Delta Networks", section 3, summed over a
- * chunk): H' = M H + B with M = e^{gamma_last} I - K~^T W and B = K~^T U~.
+ * (the recurrence above summed over a chunk): H' = M H + B with
+ * M = e^{gamma_last} I - K~^T W and B = K~^T U~.
  * GDN_SCAN_TWO_LEVEL splits every sequence (at 5/8 of its chunks) and scans
  * both halves at once: the second from zero, beside the product of its M
  * (d_k more state columns), then adds M-product x (state at the split) to
@@ -147,7 +147,8 @@ void gdn_default_options(gdn_options* opts);
  *   cu_seqlens  int32 [N+1] device array of sequence starts, or NULL: one
  *               sequence of T tokens (3-D inputs) or B sequences of T/B
  *               tokens each (4-D inputs).  With cu_seqlens, 4-D inputs need
- *               B == 1.
+ *               B == 1, and the bounds are read from it also for N = 1:
+ *               rows at or after cu[N] are not written.
  *   init_state  f32 [N, Hv, dk, dv] contiguous, or NULL for zeros
  *   final_state f32 [N, Hv, dk, dv] contiguous, or NULL (not written); it
  *               may be the same memory as init_state.
@@ -226,7 +227,7 @@ int gdn_get_workspace_layout(const gdn_tensor* q, const gdn_tensor* k,
 
 /*
  * gdn_decode -- one recurrent step per sequence: the single-token form of
- * the same gated delta rule ("Gated Delta Networks", section 3), as a
+ * the same gated delta rule, as a
  * generator runs it after the prefill, on the state the prefill returned.
  * For every sequence i and value head h (key head h / (Hv/Hk)):
  *     H = state[i, h];  H <- exp(g) (I - beta k^ k^T) H + beta k^ v^T;

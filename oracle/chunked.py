@@ -6,12 +6,13 @@ recurrence in ``gdn_oracle.c``, written in numpy, and it exposes the
 per-chunk intermediates that the GPU stages produce so that each stage can be
 checked on its own.
 
-The chunk algebra is the WY (compact Householder) form of the delta rule
-("Parallelizing Linear Transformers with the Delta Rule over Sequence
-Length", Yang et al., NeurIPS 2024, section 3) with the gate folded in as in
-"Gated Delta Networks" (Yang, Kautz, Hatamizadeh; ICLR 2025, section 3.3).
-For one chunk of n tokens entering with state H (d_k x d_v), with
-r, s = 0..n-1 and s <= r meaning "not after":
+The chunk algebra is the WY (compact product) form of the gated delta
+rule: the product over a chunk of the per-token maps
+H -> alpha_t (I - beta_t k^ k^T) H + beta_t k^ v^T, written with one
+triangular inverse per chunk (derived here from the recurrence in
+``gdn_oracle.c``; the pages print no chunk algebra).  For one chunk of n
+tokens entering with state H (d_k x d_v), with r, s = 0..n-1 and s <= r
+meaning "not after":
 
     gamma_r = g_0 + ... + g_r                       (chunk-local cumulative gate)
     D_rs    = exp(gamma_r - gamma_s) if s <= r else 0
@@ -32,7 +33,8 @@ sequence may be shorter than ``chunk``.  With chunk = 1 the evaluator is the
 token recurrence itself.  Every exponent above is <= 0 when g <= 0.
 
 Equality with the token recurrence for many chunk sizes is a pin
-(tests/test_oracle_chunked.py).
+(``test_chunk_size_invariance`` and ``test_chunk_invariance_strong_decay``
+in tests/test_oracle_invariants.py).
 """
 from __future__ import annotations
 

@@ -6,10 +6,9 @@
  * It shares no code with the HIP library.
  *
  * What it computes (the plain definition, one token at a time):
- *   The gated delta rule of "Gated Delta Networks: Improving Mamba2 with
- *   Delta Rule" (Yang, Kautz, Hatamizadeh; ICLR 2025), section 2-3, eq. for
- *   the gated delta rule, written for a state H of shape d_k x d_v (the
- *   transpose of that paper's S):
+ *   The gated delta rule, written for a state H of shape d_k x d_v (the
+ *   transpose of the d_v x d_k form S_t = alpha_t S_{t-1} (I - b k k^T) +
+ *   b v k^T, o_t = S_t q):
  *
  *       q^ = q / sqrt(sum q^2 + eps),   k^ = k / sqrt(sum k^2 + eps)
  *       alpha = exp(g),                  b = beta (already in [0, 1])

@@ -2,8 +2,11 @@
 delta rule, each computed WITHOUT calling the oracle's own token loop, so
 that a wrong term, sign, index or operand in the oracle fails at least one.
 
-The recurrence (Gated Delta Networks, Yang, Kautz, Hatamizadeh, ICLR 2025,
-section 3, state written as d_k x d_v):
+The recurrence (the gated delta rule of the chunked Gated DeltaNet prefill
+that "Open-Jev-27B-v1.1 native text worker", section "Validation and
+optimization scope", tests against float64 references; the pages print no
+formula, so this is the definition the library takes, with the state
+written as d_k x d_v):
     H_t = alpha_t (I - b_t k^_t k^_t^T) H_{t-1} + b_t k^_t v_t^T,
     o_t = scale * H_t^T q^_t,   x^ = x / sqrt(|x|^2 + eps),  alpha = exp(g).
 

@@ -62,6 +62,26 @@ def test_single_token_and_cu_with_one_sequence():
     U.check_bf16(o1, f1, ro, rf, label="one token")
 
 
+def test_cu_with_one_sequence_shorter_than_t():
+    """cu_seqlens = [0, L] with L < T: only the first L tokens form the
+    sequence; the rows after it are not written."""
+    L = 150
+    w = W.make_workload("long_16k_gqa", lengths=[200], hk=1, hv=3)
+    d = W.to_device(w)
+    d["out"].fill_(7.0)
+    cu = torch.tensor([0, L], dtype=torch.int32, device=d["q"].device)
+    G.gdn_prefill_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, d["init_state"],
+                     d["out"], d["final_state"])
+    torch.cuda.synchronize()
+    out = d["out"].float().cpu().numpy()
+    fin = d["final_state"].cpu().numpy()
+    assert np.all(out[L:] == 7.0)
+    a = W.make_workload("long_16k_gqa", lengths=[200], hk=1, hv=3)
+    a.q, a.k, a.v, a.g, a.beta, a.lengths = a.q[:L], a.k[:L], a.v[:L], a.g[:L], a.beta[:L], [L]
+    ro, rf = oracle.reference_workload(a)
+    U.check_bf16(out[:L], fin, ro, rf, label="cu [0, 150] of 200 tokens")
+
+
 def test_split_continuation():
     """[0, t) then [t, T) with the final state passed as the next initial state."""
     w = W.make_workload("long_16k_gqa", lengths=[333], hk=1, hv=3)
