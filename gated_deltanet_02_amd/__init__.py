@@ -11,6 +11,7 @@ from ._binding import (GdnError, GdnOptions, GdnTensor, GdnWorkspaceLayout,  # n
                        alloc_workspace, describe, gdn_abi_version,
                        gdn_default_options, gdn_get_workspace_layout,
                        gdn_decode, gdn_last_error, gdn_prefill, gdn_prefill_ex,
+                       gdn_prefill_noalloc, NOALLOC_SCRATCH_BYTES,
                        gdn_status_string, gdn_workspace_size, library_path,
                        options)
 from ._binding import GraphCache, PreparedPrefill  # noqa: F401,E402

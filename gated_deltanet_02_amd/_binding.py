@@ -23,7 +23,7 @@ STAGE_TABLE, STAGE_WY, STAGE_SCAN, STAGE_ALL = 1, 2, 4, 7
 SCAN_AUTO, SCAN_ONE_PASS, SCAN_TWO_LEVEL = 0, 1, 2
 FLAG_BETA_LOGITS = 1
 EXPORTED = ("gdn_abi_version", "gdn_default_options", "gdn_prefill",
-            "gdn_prefill_ex", "gdn_workspace_size", "gdn_get_workspace_layout",
+            "gdn_prefill_ex", "gdn_prefill_noalloc", "gdn_workspace_size", "gdn_get_workspace_layout",
             "gdn_decode", "gdn_graph_cache_create", "gdn_graph_cache_destroy",
             "gdn_graph_cache_clear", "gdn_graph_cache_stats", "gdn_prefill_graph",
             "gdn_status_string", "gdn_last_error")
@@ -88,6 +88,8 @@ def lib():
         L.gdn_prefill_ex.argtypes = [T] * 9 + [P(GdnOptions), ctypes.c_void_p,
                                                ctypes.c_size_t, ctypes.c_void_p]
         L.gdn_prefill_ex.restype = ctypes.c_int
+        L.gdn_prefill_noalloc.argtypes = [T] * 9 + [P(GdnOptions), ctypes.c_void_p]
+        L.gdn_prefill_noalloc.restype = ctypes.c_int
         L.gdn_workspace_size.argtypes = [T, T, T, T, P(GdnOptions), P(ctypes.c_size_t)]
         L.gdn_workspace_size.restype = ctypes.c_int
         L.gdn_get_workspace_layout.argtypes = [T, T, T, T, P(GdnOptions), P(GdnWorkspaceLayout)]
@@ -247,6 +249,24 @@ def gdn_prefill_ex(q, k, v, g, beta, cu_seqlens=None, init_state=None,
         # the kernels run on ``stream``: keep the block from being handed out
         # again before that stream has finished with it
         workspace.record_stream(_torch_stream(stream, v.device))
+    return out, final_state
+
+
+NOALLOC_SCRATCH_BYTES = 96 << 20
+
+
+def gdn_prefill_noalloc(q, k, v, g, beta, cu_seqlens=None, init_state=None,
+                        out=None, final_state=None, opts: Optional[GdnOptions] = None,
+                        stream=None):
+    """gdn_prefill_ex on the library's static device scratch: no allocation
+    by the library (``out`` must be given).  Calls that overlap on one GPU
+    share the scratch and must be serialised.  Returns (out, final_state)."""
+    if out is None:
+        raise ValueError("out is required (this entry point allocates nothing)")
+    ds = _descs(q, k, v, g, beta, cu_seqlens, init_state, out, final_state)
+    _check(lib().gdn_prefill_noalloc(*[_ref(d) for d in ds],
+                                     ctypes.byref(opts) if opts else None,
+                                     _stream_handle(stream, v)))
     return out, final_state
 
 

@@ -597,6 +597,29 @@ int gdn_prefill(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
   return rc;
 }
 
+int gdn_prefill_noalloc(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
+                        const gdn_tensor* g, const gdn_tensor* beta,
+                        const gdn_tensor* cu_seqlens, const gdn_tensor* init_state,
+                        gdn_tensor* out, gdn_tensor* final_state, const gdn_options* opts,
+                        void* stream) {
+  static_assert(gdn::kScratchBytes == GDN_NOALLOC_SCRATCH_BYTES, "scratch size in gdn.h");
+  Problem P;
+  int rc = validate(q, k, v, g, beta, cu_seqlens, init_state, out, final_state, opts, true, &P);
+  if (rc) return rc;
+  const size_t need = make_layout(P).total;
+  if (need > gdn::kScratchBytes)
+    return fail(GDN_ERR_WORKSPACE,
+                "these sizes need a workspace of %zu bytes; the no-allocation prefill's scratch "
+                "holds %zu (use gdn_prefill_ex with a larger workspace)",
+                need, gdn::kScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = gdn::scratch_region(&ws);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "scratch lookup: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return run(P, q, k, v, g, beta, cu_seqlens, init_state, out, final_state, ws,
+             (hipStream_t)stream);
+}
+
 int gdn_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
                const gdn_tensor* g, const gdn_tensor* beta, gdn_tensor* state,
                gdn_tensor* out, const gdn_options* opts, void* stream) {

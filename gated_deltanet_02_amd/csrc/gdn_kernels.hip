@@ -58,6 +58,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -1907,6 +1908,39 @@ static hipError_t launch_decode_dv(const DecodeParams& p, hipStream_t s) {
 #undef GDN_DECODE
   }
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation prefill: the workspace as a file-scope device
+// array, one copy per GPU, held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol); the device address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and is what the launches receive.
+
+}  // namespace gdn
+
+static __device__ __align__(256) char scratch[gdn::kScratchBytes];
+
+namespace gdn {
+
+hipError_t scratch_region(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(bool bf16, int dk, const DecodeParams& p, hipStream_t s) {

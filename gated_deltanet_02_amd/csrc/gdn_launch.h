@@ -28,4 +28,12 @@ hipError_t launch_scan_two_level(int chunk, int dk, const ScanParams& p, hipStre
 
 hipError_t launch_decode(bool bf16, int dk, const DecodeParams& p, hipStream_t s);
 
+// Size of the device scratch that serves as the workspace of
+// gdn_prefill_noalloc (include/gdn.h: GDN_NOALLOC_SCRATCH_BYTES).
+constexpr size_t kScratchBytes = (size_t)96 << 20;
+
+// Device address of the current device's scratch (looked up on the first
+// call per device; no allocation).
+hipError_t scratch_region(void** ptr);
+
 }  // namespace gdn

@@ -177,6 +177,30 @@ int gdn_prefill_ex(const gdn_tensor* q, const gdn_tensor* k,
                    gdn_tensor* final_state, const gdn_options* opts,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * gdn_prefill_noalloc -- gdn_prefill_ex without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Its workspace is a static device array of
+ * GDN_NOALLOC_SCRATCH_BYTES held by the library on every GPU it runs on
+ * until the process ends (looked up on the first call on each device).  The
+ * caller still passes every input and output; `opts` may be NULL.  Sizes
+ * whose workspace (gdn_workspace_size) exceeds the scratch are rejected with
+ * GDN_ERR_WORKSPACE before anything is enqueued (96 MiB covers, e.g., 4096
+ * tokens x 16 heads at d = 128 in bf16, which needs 64 MiB).  No part of the
+ * scratch has to start at zero: each call writes everything it reads.  All
+ * calls on one GPU share its scratch, which keeps the last call's contents:
+ * calls that overlap on one GPU (different streams or threads) race, and
+ * must be serialised by the caller.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+int gdn_prefill_noalloc(const gdn_tensor* q, const gdn_tensor* k,
+                        const gdn_tensor* v, const gdn_tensor* g,
+                        const gdn_tensor* beta, const gdn_tensor* cu_seqlens,
+                        const gdn_tensor* init_state, gdn_tensor* out,
+                        gdn_tensor* final_state, const gdn_options* opts,
+                        void* stream);
+
 /* Byte offsets of the intermediates inside the workspace (for inspection and
  * tests).  Per (chunk c, value head h) block, all in the input dtype:
  *   w     diag(s) W,  W = T diag(beta e^gamma) K^     C x dk, k-tile order

@@ -269,3 +269,24 @@ def test_graph_cache_host_side(lib):
                                  None, None, r(a["out"]), None, None, None, 0, None) == -1
     lib.gdn_graph_cache_clear(cache)
     lib.gdn_graph_cache_destroy(cache)
+
+
+def test_noalloc_validation_on_host(lib):
+    """gdn_prefill_noalloc validates like gdn_prefill_ex and rejects sizes
+    whose workspace exceeds its static scratch, before any HIP call."""
+    r = lambda x: ctypes.byref(x) if x is not None else None  # noqa: E731
+    a = base()
+    rc = lib.gdn_prefill_noalloc(None, r(a["k"]), r(a["v"]), r(a["g"]), r(a["b"]), None, None,
+                                 r(a["out"]), None, None, None)
+    assert rc == -1
+    big = base(T=7000, hk=16, hv=16, dk=128, dv=128)
+    need = ctypes.c_size_t(0)
+    assert lib.gdn_workspace_size(r(big["q"]), r(big["k"]), r(big["v"]), None, None,
+                                  ctypes.byref(need)) == 0
+    assert need.value > G.NOALLOC_SCRATCH_BYTES
+    rc = lib.gdn_prefill_noalloc(r(big["q"]), r(big["k"]), r(big["v"]), r(big["g"]), r(big["b"]),
+                                 None, None, r(big["out"]), None, None, None)
+    assert rc == -6 and "scratch" in G.gdn_last_error()
+    src = open(HEADER).read()
+    m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert int(m.group(1)) << int(m.group(2)) == G.NOALLOC_SCRATCH_BYTES
