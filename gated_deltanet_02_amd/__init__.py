@@ -8,6 +8,7 @@ raises if it was not built.
 from ._binding import (GdnError, GdnOptions, GdnTensor, GdnWorkspaceLayout,  # noqa: F401
                        STAGE_ALL, STAGE_SCAN, STAGE_TABLE, STAGE_WY, EXPORTED,
                        SCAN_AUTO, SCAN_ONE_PASS, SCAN_TWO_LEVEL, FLAG_BETA_LOGITS,
+                       FLAG_DECAY_PROJ, FLAG_OUTPUT_GATE, gdn_output_gate,
                        alloc_workspace, describe, gdn_abi_version,
                        gdn_default_options, gdn_get_workspace_layout,
                        gdn_decode, gdn_last_error, gdn_prefill, gdn_prefill_ex,

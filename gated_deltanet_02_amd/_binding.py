@@ -21,10 +21,10 @@ STATUS_NAMES = {0: "GDN_OK", -1: "GDN_ERR_NULL_ARG", -2: "GDN_ERR_DTYPE",
                 -7: "GDN_ERR_HIP"}
 STAGE_TABLE, STAGE_WY, STAGE_SCAN, STAGE_ALL = 1, 2, 4, 7
 SCAN_AUTO, SCAN_ONE_PASS, SCAN_TWO_LEVEL = 0, 1, 2
-FLAG_BETA_LOGITS = 1
+FLAG_BETA_LOGITS, FLAG_DECAY_PROJ, FLAG_OUTPUT_GATE = 1, 2, 4
 EXPORTED = ("gdn_abi_version", "gdn_default_options", "gdn_prefill",
             "gdn_prefill_ex", "gdn_prefill_noalloc", "gdn_workspace_size", "gdn_get_workspace_layout",
-            "gdn_decode", "gdn_graph_cache_create", "gdn_graph_cache_destroy",
+            "gdn_decode", "gdn_output_gate", "gdn_graph_cache_create", "gdn_graph_cache_destroy",
             "gdn_graph_cache_clear", "gdn_graph_cache_stats", "gdn_prefill_graph",
             "gdn_status_string", "gdn_last_error")
 
@@ -40,7 +40,10 @@ class GdnTensor(ctypes.Structure):
 class GdnOptions(ctypes.Structure):
     _fields_ = [("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("l2_eps", ctypes.c_float), ("stages", ctypes.c_uint32),
-                ("scan_split", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("scan_split", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("decay_a_log", ctypes.c_void_p), ("decay_bias", ctypes.c_void_p),
+                ("gate_z", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float)]
 
 
 class GdnWorkspaceLayout(ctypes.Structure):
@@ -96,6 +99,8 @@ def lib():
         L.gdn_get_workspace_layout.restype = ctypes.c_int
         L.gdn_decode.argtypes = [T] * 7 + [P(GdnOptions), ctypes.c_void_p]
         L.gdn_decode.restype = ctypes.c_int
+        L.gdn_output_gate.argtypes = [T, T, ctypes.c_void_p, ctypes.c_float, T, ctypes.c_void_p]
+        L.gdn_output_gate.restype = ctypes.c_int
         L.gdn_graph_cache_create.argtypes = [ctypes.c_int, P(ctypes.c_void_p)]
         L.gdn_graph_cache_create.restype = ctypes.c_int
         L.gdn_graph_cache_destroy.argtypes = [ctypes.c_void_p]
@@ -135,13 +140,41 @@ def _ref(d):
     return ctypes.byref(d) if d is not None else None
 
 
+def _dev_ptr(t: Optional[torch.Tensor], name: str, dtype=torch.float32):
+    if t is None:
+        return None
+    if t.device.type != "cuda" or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor")
+    return t.data_ptr()
+
+
 def options(chunk: int = 0, scale: float = 1.0, l2_eps: float = 1e-6,
-            stages: int = STAGE_ALL, scan_split: int = 0, beta_logits: bool = False) -> GdnOptions:
+            stages: int = STAGE_ALL, scan_split: int = 0, beta_logits: bool = False,
+            decay_proj: bool = False, decay_a_log: Optional[torch.Tensor] = None,
+            decay_bias: Optional[torch.Tensor] = None,
+            gate_z: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
+            norm_eps: float = 1e-6) -> GdnOptions:
     """scan_split: SCAN_AUTO (0), SCAN_ONE_PASS (1) or SCAN_TWO_LEVEL (2);
-    beta_logits: beta holds raw projections b and the kernels use sigmoid(b)."""
+    beta_logits: beta holds raw projections b and the kernels use sigmoid(b);
+    decay_proj: g holds the decay gate's raw projection a, with per value head
+    f32 tensors decay_a_log and decay_bias (None: zeros);
+    gate_z: the output gate's projection, laid out exactly as ``out`` (sets
+    the output-gate flag), with the f32 [dv] norm_weight (None: ones).  The
+    options hold raw device pointers: the tensors are kept referenced by the
+    returned object and must stay alive while calls using it may run."""
     o = GdnOptions()
     o.chunk, o.scale, o.l2_eps, o.stages, o.scan_split = chunk, scale, l2_eps, stages, scan_split
-    o.flags = FLAG_BETA_LOGITS if beta_logits else 0
+    o.flags = (FLAG_BETA_LOGITS if beta_logits else 0) | (FLAG_DECAY_PROJ if decay_proj else 0)
+    o.decay_a_log = _dev_ptr(decay_a_log, "decay_a_log")
+    o.decay_bias = _dev_ptr(decay_bias, "decay_bias")
+    o.norm_weight = _dev_ptr(norm_weight, "norm_weight")
+    o.norm_eps = norm_eps
+    if gate_z is not None:
+        if gate_z.device.type != "cuda":
+            raise ValueError("gate_z must be a GPU tensor")
+        o.gate_z = gate_z.data_ptr()
+        o.flags |= FLAG_OUTPUT_GATE
+    o._keep = (decay_a_log, decay_bias, gate_z, norm_weight)
     return o
 
 
@@ -268,6 +301,21 @@ def gdn_prefill_noalloc(q, k, v, g, beta, cu_seqlens=None, init_state=None,
                                      ctypes.byref(opts) if opts else None,
                                      _stream_handle(stream, v)))
     return out, final_state
+
+
+def gdn_output_gate(x, z, weight=None, eps: float = 1e-6, out=None, stream=None):
+    """out = x / sqrt(mean(x^2) + eps) * weight * silu(z) over the last axis
+    (x, z, out [R, dv] or [T, H, dv], one dtype; out may be x).  Returns out."""
+    if out is None:
+        out = torch.empty_like(x)
+    for name, t in (("x", x), ("z", z), ("out", out)):
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    w = _dev_ptr(weight, "weight")
+    ds = [describe(t) for t in (x, z, out)]
+    _check(lib().gdn_output_gate(_ref(ds[0]), _ref(ds[1]), w, ctypes.c_float(eps), _ref(ds[2]),
+                                 _stream_handle(stream, x)))
+    return out
 
 
 def gdn_decode(q, k, v, g, beta, state, out=None, opts: Optional[GdnOptions] = None,

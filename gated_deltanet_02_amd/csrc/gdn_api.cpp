@@ -123,8 +123,26 @@ struct Problem {
   uint32_t stages = GDN_STAGE_ALL;
   int scan_split = GDN_SCAN_AUTO;
   bool beta_logits = false;
+  bool decay_proj = false;   // GDN_FLAG_DECAY_PROJ
+  bool out_gate = false;     // GDN_FLAG_OUTPUT_GATE
+  const float* a_log = nullptr;
+  const float* a_bias = nullptr;
+  const void* gate_z = nullptr;
+  const float* norm_w = nullptr;
+  float norm_eps = 1e-6f;
   int split = 0;  // two-level scan: chunks in the first segment (0: one pass)
 };
+
+constexpr uint32_t kKnownFlags = GDN_FLAG_BETA_LOGITS | GDN_FLAG_DECAY_PROJ | GDN_FLAG_OUTPUT_GATE;
+
+// Checks of the gate fields of gdn_options that need no shapes.
+int check_gate_options(const gdn_options& o) {
+  if (o.flags & ~kKnownFlags) return fail(GDN_ERR_SHAPE, "unknown flag bits 0x%x", o.flags);
+  if (!(o.norm_eps >= 0.f)) return fail(GDN_ERR_SHAPE, "norm_eps must be >= 0");
+  if ((uintptr_t)o.decay_a_log % 4 || (uintptr_t)o.decay_bias % 4 || (uintptr_t)o.norm_weight % 4)
+    return fail(GDN_ERR_LAYOUT, "decay_a_log, decay_bias and norm_weight must be 4-byte aligned");
+  return GDN_OK;
+}
 
 struct Layout {
   size_t table = 0, chunk_off = 0, seq_start = 0, decay = 0;
@@ -174,13 +192,21 @@ int resolve_options(const gdn_options* opts, bool bf16, Problem* P) {
   if ((o.stages & ~GDN_STAGE_ALL) != 0) return fail(GDN_ERR_SHAPE, "unknown stage bits 0x%x", o.stages);
   if (o.scan_split < GDN_SCAN_AUTO || o.scan_split > GDN_SCAN_TWO_LEVEL)
     return fail(GDN_ERR_SHAPE, "unknown scan_split %d", o.scan_split);
-  if (o.flags & ~GDN_FLAG_BETA_LOGITS) return fail(GDN_ERR_SHAPE, "unknown flag bits 0x%x", o.flags);
+  int rc;
+  if ((rc = check_gate_options(o))) return rc;
   P->chunk = chunk;
   P->scale = o.scale;
   P->eps = o.l2_eps;
   P->stages = o.stages;
   P->scan_split = o.scan_split;
   P->beta_logits = (o.flags & GDN_FLAG_BETA_LOGITS) != 0;
+  P->decay_proj = (o.flags & GDN_FLAG_DECAY_PROJ) != 0;
+  P->out_gate = (o.flags & GDN_FLAG_OUTPUT_GATE) != 0;
+  P->a_log = P->decay_proj ? o.decay_a_log : nullptr;
+  P->a_bias = P->decay_proj ? o.decay_bias : nullptr;
+  P->gate_z = P->out_gate ? o.gate_z : nullptr;
+  P->norm_w = P->out_gate ? o.norm_weight : nullptr;
+  P->norm_eps = o.norm_eps;
   return GDN_OK;
 }
 
@@ -297,6 +323,10 @@ int validate(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
       return fail(GDN_ERR_LAYOUT, "%s: token/head strides must be multiples of %d elements", x.n, gr);
   }
   if (P->T > 0 && (!g->data || !beta->data)) return fail(GDN_ERR_NULL_ARG, "g/beta data is NULL");
+  if (P->out_gate && P->T > 0) {
+    if (!P->gate_z) return fail(GDN_ERR_NULL_ARG, "GDN_FLAG_OUTPUT_GATE needs gate_z");
+    if ((uintptr_t)P->gate_z % 16) return fail(GDN_ERR_LAYOUT, "gate_z must be 16-byte aligned");
+  }
   if (P->T > 0 && ((uintptr_t)g->data % 4 || (uintptr_t)beta->data % 4))
     return fail(GDN_ERR_LAYOUT, "g/beta must be 4-byte aligned");
   const gdn_tensor* states[2] = {init, fin};
@@ -375,7 +405,17 @@ int validate_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* 
   gdn_default_options(&o);
   if (opts) o = *opts;
   if (!(o.l2_eps >= 0.f)) return fail(GDN_ERR_SHAPE, "l2_eps must be >= 0");
-  if (o.flags & ~GDN_FLAG_BETA_LOGITS) return fail(GDN_ERR_SHAPE, "unknown flag bits 0x%x", o.flags);
+  int rc;
+  if ((rc = check_gate_options(o))) return rc;
+  if ((o.flags & GDN_FLAG_OUTPUT_GATE) && N > 0) {
+    // the gate moves 16-byte granules of out and z (z laid out as out)
+    const int64_t epg = q->dtype == GDN_DTYPE_BF16 ? 8 : 4;
+    if (!o.gate_z) return fail(GDN_ERR_NULL_ARG, "GDN_FLAG_OUTPUT_GATE needs gate_z");
+    if ((uintptr_t)o.gate_z % 16 || (uintptr_t)out->data % 16 || out->stride[0] % epg ||
+        out->stride[1] % epg)
+      return fail(GDN_ERR_LAYOUT, "with GDN_FLAG_OUTPUT_GATE, out and gate_z rows must start on "
+                  "16-byte boundaries");
+  }
   d->q = q->data; d->k = k->data; d->v = v->data; d->out = out->data;
   d->g = (const float*)g->data; d->beta = (const float*)beta->data; d->state = (float*)state->data;
   d->q_st = q->stride[0]; d->q_sh = q->stride[1];
@@ -387,6 +427,9 @@ int validate_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* 
   d->n = (int32_t)N; d->hk = (int32_t)hk; d->hv = (int32_t)hv; d->dv = (int32_t)dv;
   d->scale = o.scale; d->eps = o.l2_eps;
   d->beta_logits = (o.flags & GDN_FLAG_BETA_LOGITS) ? 1 : 0;
+  d->decay_proj = (o.flags & GDN_FLAG_DECAY_PROJ) ? 1 : 0;
+  d->a_log = d->decay_proj ? o.decay_a_log : nullptr;
+  d->a_bias = d->decay_proj ? o.decay_bias : nullptr;
   *bf16 = q->dtype == GDN_DTYPE_BF16;
   *dk = (int)dkk;
   return GDN_OK;
@@ -448,6 +491,9 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
     wp.im = im;
     wp.n_items = (int32_t)(P.max_chunks * P.hk);
     wp.beta_logits = P.beta_logits ? 1 : 0;
+    wp.decay_proj = P.decay_proj ? 1 : 0;
+    wp.a_log = P.a_log;
+    wp.a_bias = P.a_bias;
     if ((e = gdn::launch_wy(P.bf16, P.chunk, P.dk, wp, s)) != hipSuccess)
       return fail(GDN_ERR_HIP, "WY launch: %s", hipGetErrorString(e));
   }
@@ -485,6 +531,22 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
       if ((e = gdn::launch_scan(P.bf16, P.chunk, P.dk, sp, (int)blocks, s)) != hipSuccess)
         return fail(GDN_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
     }
+    if (P.out_gate && P.T > 0) {
+      // the gated output norm over the stored rows (packed: up to cu[N])
+      gdn::GateParams gp{};
+      gp.x = out->data;
+      gp.z = P.gate_z;
+      gp.out = out->data;
+      gp.w = P.norm_w;
+      gp.t_end = P.packed ? (const int32_t*)cu->data + P.n_seq : nullptr;
+      gp.rows = P.T * P.hv;
+      gp.inner = P.hv;
+      gp.x_st = gp.z_st = gp.o_st = P.o.st;
+      gp.x_sh = gp.z_sh = gp.o_sh = P.o.sh;
+      gp.eps = P.norm_eps;
+      if ((e = gdn::launch_output_gate(P.bf16, P.dv, gp, s)) != hipSuccess)
+        return fail(GDN_ERR_HIP, "output gate launch: %s", hipGetErrorString(e));
+    }
   }
   return GDN_OK;
 }
@@ -503,6 +565,11 @@ void gdn_default_options(gdn_options* opts) {
   opts->stages = GDN_STAGE_ALL;
   opts->scan_split = GDN_SCAN_AUTO;
   opts->flags = 0;
+  opts->decay_a_log = nullptr;
+  opts->decay_bias = nullptr;
+  opts->gate_z = nullptr;
+  opts->norm_weight = nullptr;
+  opts->norm_eps = 1e-6f;
 }
 
 const char* gdn_status_string(int status) {
@@ -630,8 +697,78 @@ int gdn_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
   if (rc) return rc;
   g_last_error.clear();
   if (d.n == 0) return GDN_OK;
-  const hipError_t e = gdn::launch_decode(bf16, dk, d, (hipStream_t)stream);
+  hipError_t e = gdn::launch_decode(bf16, dk, d, (hipStream_t)stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  if (opts && (opts->flags & GDN_FLAG_OUTPUT_GATE)) {
+    gdn::GateParams gp{};
+    gp.x = out->data;
+    gp.z = opts->gate_z;
+    gp.out = out->data;
+    gp.w = opts->norm_weight;
+    gp.rows = (int64_t)d.n * d.hv;
+    gp.inner = d.hv;
+    gp.x_st = gp.z_st = gp.o_st = out->stride[0];
+    gp.x_sh = gp.z_sh = gp.o_sh = out->stride[1];
+    gp.eps = opts->norm_eps;
+    if ((e = gdn::launch_output_gate(bf16, d.dv, gp, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDN_ERR_HIP, "output gate launch: %s", hipGetErrorString(e));
+  }
+  return GDN_OK;
+}
+
+int gdn_output_gate(const gdn_tensor* x, const gdn_tensor* z, const float* weight, float eps,
+                    gdn_tensor* out, void* stream) {
+  if (!x || !z || !out) return fail(GDN_ERR_NULL_ARG, "x, z and out are required");
+  if (x->dtype != GDN_DTYPE_BF16 && x->dtype != GDN_DTYPE_F32) return fail(GDN_ERR_DTYPE, "x must be bf16 or f32");
+  if (z->dtype != x->dtype || out->dtype != x->dtype) return fail(GDN_ERR_DTYPE, "x, z and out must share one dtype");
+  if (x->ndim != 2 && x->ndim != 3) return fail(GDN_ERR_SHAPE, "x must be [R, dv] or [T, H, dv]");
+  if (z->ndim != x->ndim || out->ndim != x->ndim) return fail(GDN_ERR_SHAPE, "x, z and out must have one rank");
+  for (int i = 0; i < x->ndim; ++i) {
+    if (x->shape[i] < 0) return fail(GDN_ERR_SHAPE, "negative size");
+    if (z->shape[i] != x->shape[i] || out->shape[i] != x->shape[i])
+      return fail(GDN_ERR_SHAPE, "x, z and out shapes differ");
+  }
+  const int64_t dv = x->shape[x->ndim - 1];
+  if (!supported_head_dim(dv)) return fail(GDN_ERR_UNSUPPORTED, "dv must be 16, 32, 64 or 128");
+  if (!(eps >= 0.f)) return fail(GDN_ERR_SHAPE, "eps must be >= 0");
+  if ((uintptr_t)weight % 4) return fail(GDN_ERR_LAYOUT, "weight must be 4-byte aligned");
+  const bool three = x->ndim == 3;
+  const int64_t outer = x->shape[0], inner = three ? x->shape[1] : 1;
+  const int64_t rows = outer * inner;
+  if (rows == 0) {
+    g_last_error.clear();
+    return GDN_OK;
+  }
+  const int64_t epg = x->dtype == GDN_DTYPE_BF16 ? 8 : 4;
+  const gdn_tensor* ts[3] = {x, z, out};
+  const char* names[3] = {"x", "z", "out"};
+  for (int i = 0; i < 3; ++i) {
+    const gdn_tensor* t = ts[i];
+    if (!t->data) return fail(GDN_ERR_NULL_ARG, "%s data is NULL", names[i]);
+    if ((uintptr_t)t->data % 16) return fail(GDN_ERR_LAYOUT, "%s must be 16-byte aligned", names[i]);
+    if (t->stride[t->ndim - 1] != 1) return fail(GDN_ERR_LAYOUT, "%s: last dimension must have unit stride", names[i]);
+    for (int d = 0; d + 1 < t->ndim; ++d)
+      if (t->stride[d] < 0 || t->stride[d] % epg)
+        return fail(GDN_ERR_LAYOUT, "%s: strides must be non-negative multiples of %lld elements", names[i],
+                    (long long)epg);
+  }
+  gdn::GateParams gp{};
+  gp.x = x->data;
+  gp.z = z->data;
+  gp.out = out->data;
+  gp.w = weight;
+  gp.rows = rows;
+  gp.inner = inner;
+  gp.x_st = x->stride[0];
+  gp.z_st = z->stride[0];
+  gp.o_st = out->stride[0];
+  gp.x_sh = three ? x->stride[1] : 0;
+  gp.z_sh = three ? z->stride[1] : 0;
+  gp.o_sh = three ? out->stride[1] : 0;
+  gp.eps = eps;
+  g_last_error.clear();
+  const hipError_t e = gdn::launch_output_gate(x->dtype == GDN_DTYPE_BF16, (int)dv, gp, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "output gate launch: %s", hipGetErrorString(e));
   return GDN_OK;
 }
 
@@ -743,7 +880,18 @@ int gdn_prefill_graph(gdn_graph_cache* cache, const gdn_tensor* q, const gdn_ten
   gdn_options o;
   gdn_default_options(&o);
   if (opts) o = *opts;
-  append(key, &o, sizeof o);
+  // field by field (the struct's padding carries no value)
+  append(key, &o.chunk, sizeof o.chunk);
+  append(key, &o.scale, sizeof o.scale);
+  append(key, &o.l2_eps, sizeof o.l2_eps);
+  append(key, &o.stages, sizeof o.stages);
+  append(key, &o.scan_split, sizeof o.scan_split);
+  append(key, &o.flags, sizeof o.flags);
+  append(key, &o.decay_a_log, sizeof o.decay_a_log);
+  append(key, &o.decay_bias, sizeof o.decay_bias);
+  append(key, &o.gate_z, sizeof o.gate_z);
+  append(key, &o.norm_weight, sizeof o.norm_weight);
+  append(key, &o.norm_eps, sizeof o.norm_eps);
   append(key, &workspace, sizeof workspace);
   append(key, &workspace_bytes, sizeof workspace_bytes);
 

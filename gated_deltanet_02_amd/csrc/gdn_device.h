@@ -367,6 +367,17 @@ __device__ __forceinline__ void mma_block(f32x4 (&acc)[MT][NT], const float* A, 
 // values below 5e-5 whose absolute error is then negligible).
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+// The decay gate from its raw projection a for value head h (the reading
+// documented at GDN_FLAG_DECAY_PROJ): g = -exp(A[h]) * softplus(a + bias[h]),
+// softplus(x) = log(1 + e^x), in fp32.  For x > 20, e^-x is below half an
+// fp32 ulp of x and softplus(x) rounds to x; otherwise log1p(e^x).  Null
+// parameter arrays read as zeros.
+__device__ __forceinline__ float decay_gate(float a, const float* a_log, const float* a_bias, int h) {
+  const float x = a + (a_bias ? a_bias[h] : 0.f);
+  const float sp = x > 20.f ? x : log1pf(expf(x));
+  return -expf(a_log ? a_log[h] : 0.f) * sp;
+}
+
 }  // namespace gdn
 
 namespace gdn {

@@ -54,6 +54,9 @@ struct WyParams {
   int32_t hk, hv, dv;
   int32_t n_items;    // (chunk, key head) work items: max_chunks * hk
   int32_t beta_logits;  // 1: beta holds logits b, the kernel takes sigmoid(b)
+  int32_t decay_proj;   // 1: g holds the projection a, the kernel takes decay_gate(a)
+  const float* a_log;   // [Hv] or null (zeros), with decay_proj
+  const float* a_bias;  // [Hv] or null (zeros), with decay_proj
   float scale, eps;
   ChunkMap map;
   Intermediates im;
@@ -95,7 +98,23 @@ struct DecodeParams {
   int64_t g_st, g_sh, b_st, b_sh;
   int32_t n, hk, hv, dv;
   int32_t beta_logits;   // 1: beta holds logits b, the kernel takes sigmoid(b)
+  int32_t decay_proj;    // 1: g holds the projection a, the kernel takes decay_gate(a)
+  const float* a_log;    // [Hv] or null (zeros), with decay_proj
+  const float* a_bias;   // [Hv] or null (zeros), with decay_proj
   float scale, eps;
+};
+
+// The gated output norm over rows of dv elements: row r is (r / inner,
+// r % inner) of a [outer, inner, dv] view with the given strides.
+struct GateParams {
+  const void* x;
+  const void* z;
+  void* out;
+  const float* w;        // [dv] or null (ones)
+  const int32_t* t_end;  // rows of tokens at or after *t_end are left alone (null: none)
+  int64_t rows, inner;
+  int64_t x_st, x_sh, z_st, z_sh, o_st, o_sh;
+  float eps;
 };
 
 }  // namespace gdn

@@ -564,8 +564,9 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   // The gate cumulative sum gamma, beta (sigmoid of a logit for a real
   // token; padded rows stay 0) and e^gamma of the value head whose g and
   // beta are in gv, bv (wave 0).
-  auto gate_scan = [&]() {
+  auto gate_scan = [&](int h) {
     float x = gv;  // inclusive scan over the chunk
+    if (p.decay_proj && lane < n) x = decay_gate(x, p.a_log, p.a_bias, h);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(x, off);
@@ -582,7 +583,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     gv = sGate[lane < C ? lane : 0];
     bv = sGate[C + (lane < C ? lane : 0)];
     if (lane >= C) gv = bv = 0.f;
-    gate_scan();  // the first value head's, beside the Gram products
+    gate_scan(kh * grp);  // the first value head's, beside the Gram products
   }
   // The q elements this wave needs for Q' (d_k tile `wave`, rows
   // 16 j + lane % 16, four columns from 4 (lane / 16)) for every value head
@@ -612,7 +613,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     // are requested.
     if (gi > 0) {
       store_v();
-      if (wave == 0) gate_scan();
+      if (wave == 0) gate_scan(h);
       __syncthreads();
     }
 
@@ -1684,7 +1685,8 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(Decod
       if (l == 0) snorm[sel] = 1.0f / sqrtf(s2 + p.eps);
     }
   }
-  const float g = p.g[(int64_t)i * p.g_st + (int64_t)h * p.g_sh];
+  float g = p.g[(int64_t)i * p.g_st + (int64_t)h * p.g_sh];
+  if (p.decay_proj) g = decay_gate(g, p.a_log, p.a_bias, h);
   float beta = p.beta[(int64_t)i * p.b_st + (int64_t)h * p.b_sh];
   if (p.beta_logits) beta = 1.f / (1.f + __expf(-beta));
   const float alpha = expf(g);
@@ -1908,6 +1910,81 @@ static hipError_t launch_decode_dv(const DecodeParams& p, hipStream_t s) {
 #undef GDN_DECODE
   }
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// The gated output norm: y = x / sqrt(mean(x^2) + eps) * w * silu(z) over
+// rows of DV elements (the reading at GDN_FLAG_OUTPUT_GATE in gdn.h).  A
+// bandwidth-bound pass: each lane moves one 16-byte granule of x, z and y;
+// DV / (granule elements) lanes hold a row and reduce its sum of squares
+// with butterfly shuffles inside their lane group, so a wave covers several
+// rows and every access is a full 16-byte vector access.
+
+constexpr int kGateThreads = 256;
+
+template <typename TI, int DV>
+__global__ __launch_bounds__(kGateThreads) void output_gate_kernel(GateParams p) {
+  constexpr int EPL = 16 / (int)sizeof(TI);  // elements per lane
+  constexpr int LPR = DV / EPL;              // lanes per row (a power of two, <= 64)
+  static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "row width");
+  constexpr int RPB = kGateThreads / LPR;    // rows per workgroup
+  const int sub = threadIdx.x % LPR;
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  bool live = r < p.rows;
+  const int64_t t = live ? r / p.inner : 0, h = live ? r % p.inner : 0;
+  if (live && p.t_end) live = t < (int64_t)*p.t_end;  // rows past the packed batch's end
+  float x[EPL], z[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) x[e] = z[e] = 0.f;
+  if (live) {
+    const uint4 xv = ld16((const TI*)p.x + t * p.x_st + h * p.x_sh + sub * EPL);
+    const uint4 zv = ld16((const TI*)p.z + t * p.z_st + h * p.z_sh + sub * EPL);
+    const TI* xe = (const TI*)&xv;
+    const TI* ze = (const TI*)&zv;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      x[e] = to_float(xe[e]);
+      z[e] = to_float(ze[e]);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  const float rn = 1.0f / sqrtf(ss / (float)DV + p.eps);
+  if (!live) return;
+  uint4 yv;
+  TI* ye = (TI*)&yv;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const float w = p.w ? p.w[sub * EPL + e] : 1.f;
+    const float silu = z[e] / (1.f + expf(-z[e]));
+    ye[e] = from_float<TI>(x[e] * rn * w * silu);
+  }
+  st16((TI*)p.out + t * p.o_st + h * p.o_sh + sub * EPL, yv);
+}
+
+template <typename TI>
+static hipError_t launch_output_gate_t(int dv, const GateParams& p, hipStream_t s) {
+  constexpr int EPL = 16 / (int)sizeof(TI);
+  const int64_t rpb = kGateThreads / (dv / EPL);
+  const int64_t blocks = (p.rows + rpb - 1) / rpb;
+  if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  switch (dv) {
+#define GDN_GATE(V)                                                                                 \
+    case V:                                                                                         \
+      hipLaunchKernelGGL((output_gate_kernel<TI, V>), dim3((unsigned)blocks), dim3(kGateThreads), 0, s, p); \
+      return hipGetLastError();
+    GDN_GATE(16) GDN_GATE(32) GDN_GATE(64) GDN_GATE(128)
+#undef GDN_GATE
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_output_gate(bool bf16, int dv, const GateParams& p, hipStream_t s) {
+  if (p.rows <= 0) return hipSuccess;
+  return bf16 ? launch_output_gate_t<gdn::bf16>(dv, p, s) : launch_output_gate_t<float>(dv, p, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -28,6 +28,9 @@ hipError_t launch_scan_two_level(int chunk, int dk, const ScanParams& p, hipStre
 
 hipError_t launch_decode(bool bf16, int dk, const DecodeParams& p, hipStream_t s);
 
+// The gated output norm (dv in {16, 32, 64, 128}).
+hipError_t launch_output_gate(bool bf16, int dv, const GateParams& p, hipStream_t s);
+
 // Size of the device scratch that serves as the workspace of
 // gdn_prefill_noalloc (include/gdn.h: GDN_NOALLOC_SCRATCH_BYTES).
 constexpr size_t kScratchBytes = (size_t)96 << 20;

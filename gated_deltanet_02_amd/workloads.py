@@ -33,6 +33,16 @@ own L2 normalisation is what makes them unit rows (``qk_rows``):
   unchanged) each (token, key head) row of q and of k multiplied by a factor
   of one class: 0 (a zero row, 4 %), 1e-3 (squared norm 1e-6, the size of
   the default eps, 8 %), 1e3 (4 %), else log-uniform in [0.05, 20].
+
+The gates on either side of the prefill (``make_gate_inputs``, drawn from
+their own seeded stream so the workload above is unchanged): the decay
+gate's raw projection a ~ N(0, 1) float32 per (token, value head); per value
+head A = log U(1, 16) and bias ~ U(-6.9, -2.3) (so softplus(a + bias) spans
+about 1e-4 .. 1 and the decay rate e^A 1 .. 16); the output gate's projection
+z ~ N(0, 1) rounded to v's dtype; the norm weight 1 + 0.1 N(0, 1) float32.
+``make_gate_rows`` draws standalone rows for the output gate alone: rows of
+N(0, 1) times a per-row factor (0, 1e-3, 1e3 or log-uniform in [0.05, 20],
+as "scaled" above), z ~ N(0, 2) with a few entries at +-30.
 """
 from __future__ import annotations
 
@@ -45,6 +55,9 @@ import torch
 __all__ = [
     "SPECS",
     "Workload",
+    "GateInputs",
+    "make_gate_inputs",
+    "make_gate_rows",
     "make_workload",
     "permute_sequences",
     "select_sequences",
@@ -287,3 +300,40 @@ def to_device(w: Workload, device="cuda"):
                         dtype=torch.float32, device=device)
     return dict(q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu,
                 init_state=init, out=out, final_state=final)
+
+
+@dataclasses.dataclass
+class GateInputs:
+    a: torch.Tensor        # [T, Hv] fp32: the decay gate's raw projection
+    a_log: torch.Tensor    # [Hv] fp32: log of the per-head decay rate
+    bias: torch.Tensor     # [Hv] fp32: per-head shift of the projection
+    z: torch.Tensor        # [T, Hv, dv] in v's dtype: the output gate's projection
+    norm_w: torch.Tensor   # [dv] fp32: the output norm's weight
+
+
+def make_gate_inputs(w: Workload, seed: int = 1) -> GateInputs:
+    """Seeded gate inputs shaped for workload ``w`` (recipe in the module
+    docstring; fixed draw order a -> A -> bias -> z -> weight)."""
+    rng = np.random.default_rng([seed, 0x6A7E])
+    T, hv, dv = w.v.shape
+    a = rng.standard_normal((T, hv), dtype=np.float32)
+    a_log = np.log(rng.uniform(1.0, 16.0, size=hv)).astype(np.float32)
+    bias = rng.uniform(-6.9, -2.3, size=hv).astype(np.float32)
+    z = rng.standard_normal((T, hv, dv), dtype=np.float32)
+    nw = (1.0 + 0.1 * rng.standard_normal(dv)).astype(np.float32)
+    dt = "bf16" if w.v.dtype == torch.bfloat16 else "fp32"
+    return GateInputs(a=torch.from_numpy(a), a_log=torch.from_numpy(a_log),
+                      bias=torch.from_numpy(bias), z=_store(z, dt), norm_w=torch.from_numpy(nw))
+
+
+def make_gate_rows(rows: int, heads: int, dv: int, dtype: str = "bf16", seed: int = 2):
+    """Standalone rows for the output gate: x, z [rows, heads, dv] in
+    ``dtype``, weight [dv] fp32 (recipe in the module docstring)."""
+    rng = np.random.default_rng([seed, 0x6A7F])
+    x = rng.standard_normal((rows, heads, dv), dtype=np.float32)
+    x *= _row_factors(rng, (rows, heads))[..., None]
+    z = 2.0 * rng.standard_normal((rows, heads, dv), dtype=np.float32)
+    hot = rng.random((rows, heads, dv)) < 0.01
+    z = np.where(hot, np.where(rng.random((rows, heads, dv)) < 0.5, 30.0, -30.0), z).astype(np.float32)
+    nw = (1.0 + 0.1 * rng.standard_normal(dv)).astype(np.float32)
+    return _store(x, dtype), _store(z, dtype), torch.from_numpy(nw)

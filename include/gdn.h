@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 /* Status codes. */
 #define GDN_OK 0
@@ -97,6 +97,16 @@ typedef struct gdn_options {
   uint32_t stages;    /* GDN_STAGE_* mask (default GDN_STAGE_ALL)            */
   int32_t scan_split; /* GDN_SCAN_* (default GDN_SCAN_AUTO)                  */
   uint32_t flags;     /* GDN_FLAG_* (default 0)                              */
+  /* GDN_FLAG_DECAY_PROJ: per value head f32 [Hv] device arrays A and bias
+   * (NULL reads as zeros; default NULL)                                     */
+  const float* decay_a_log;
+  const float* decay_bias;
+  /* GDN_FLAG_OUTPUT_GATE: the gate projection z, device memory laid out
+   * exactly as `out` (same shape, dtype and strides); the weight, f32 [dv]
+   * device array (NULL reads as ones); the epsilon inside the root (1e-6) */
+  const void* gate_z;
+  const float* norm_weight;
+  float norm_eps;
 } gdn_options;
 
 /*
@@ -107,6 +117,33 @@ typedef struct gdn_options {
  * decode step.  b = +-inf give beta = 1 / 0.
  */
 #define GDN_FLAG_BETA_LOGITS 1u
+
+/*
+ * The gates on either side of the prefill.  The serving pages run "fused
+ * norm, activation" operations around the chunked Gated DeltaNet and keep
+ * the bf16 rounding points of the unfused sequence when they fuse a gate
+ * into an epilogue ("Open-Jev-27B-v1.1 native text worker", section
+ * "Validation and optimization scope"); they print no formula for either,
+ * so the two below are this library's reading.
+ *
+ * GDN_FLAG_DECAY_PROJ: `g` holds the decay gate's raw projection a, and the
+ * kernels take
+ *     g = -exp(A[h]) * softplus(a + bias[h]),   softplus(x) = log(1 + e^x)
+ * in fp32 as they load it (A = decay_a_log, bias = decay_bias, per value
+ * head), so every g is <= 0 for any a and no activation pass over [T, Hv]
+ * runs first.  (A = bias = 0 with -a in place of a gives log sigmoid(a).)
+ *
+ * GDN_FLAG_OUTPUT_GATE: after the outputs are stored (rounded to the output
+ * type, as an unfused norm would read them), each (token, value head) row o
+ * of d_v outputs is replaced, in one pass, by
+ *     y = o / sqrt(mean(o^2) + norm_eps) * w * silu(z),  silu(z) = z / (1 + e^-z)
+ * computed in fp32 from the stored o and rounded once.  The norm spans the
+ * whole row, which the state scan writes in 16-column slices from separate
+ * workgroups, so it runs as its own bandwidth-bound kernel at the end of the
+ * call (the same kernel as gdn_output_gate).  z is read with out's strides.
+ */
+#define GDN_FLAG_DECAY_PROJ 2u
+#define GDN_FLAG_OUTPUT_GATE 4u
 
 /*
  * The state scan's schedule.  Each chunk maps its incoming state affinely
@@ -143,7 +180,8 @@ void gdn_default_options(gdn_options* opts);
  *   g, beta     [T, Hv] (or [B, T/B, Hv]) f32: g is the log-decay (<= 0,
  *               alpha = exp(g)), beta the write strength in [0, 1] (already
  *               passed through the sigmoid).  These ranges are
- *               preconditions, not checked.
+ *               preconditions, not checked (see GDN_FLAG_DECAY_PROJ and
+ *               GDN_FLAG_BETA_LOGITS for raw projections).
  *   cu_seqlens  int32 [N+1] device array of sequence starts, or NULL: one
  *               sequence of T tokens (3-D inputs) or B sequences of T/B
  *               tokens each (4-D inputs).  With cu_seqlens, 4-D inputs need
@@ -263,7 +301,8 @@ int gdn_get_workspace_layout(const gdn_tensor* q, const gdn_tensor* k,
  *   state    f32 [N, Hv, dk, dv] contiguous and 16-byte aligned, read and
  *            written in place; v and out rows start on 4-element
  *            boundaries (address and strides)
- *   opts     NULL or options; only scale, l2_eps and flags are used
+ *   opts     NULL or options; scale, l2_eps, flags and the gate fields are
+ *            used (with GDN_FLAG_OUTPUT_GATE, gate_z is laid out as out)
  * dk, dv in {16, 32, 64, 128}.  N = 0 enqueues nothing.  Allocates nothing.
  * Returns a GDN_* status; validation errors enqueue nothing.
  */
@@ -304,6 +343,24 @@ int gdn_prefill_graph(gdn_graph_cache* cache, const gdn_tensor* q,
                       gdn_tensor* out, gdn_tensor* final_state,
                       const gdn_options* opts, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_output_gate -- the gated output norm of GDN_FLAG_OUTPUT_GATE on its
+ * own, for outputs already in memory:
+ *     out[r] = x[r] / sqrt(mean(x[r]^2) + eps) * w * silu(z[r])
+ * for every row r of d_v elements, computed in fp32, rounded once.
+ *   x, z, out  [R, dv] or [T, H, dv]; one dtype, bf16 or f32; unit stride
+ *              in the last dimension; other strides multiples of 8 (bf16)
+ *              or 4 (f32) elements; 16-byte aligned data.  out may be x
+ *              (in place).
+ *   weight     f32 [dv] device array (4-byte aligned), or NULL for ones
+ *   eps        >= 0
+ * dv in {16, 32, 64, 128}.  No rows enqueues nothing.  Allocates nothing.
+ * The reading and its citation are at GDN_FLAG_OUTPUT_GATE.  Returns a
+ * GDN_* status; validation errors enqueue nothing.
+ */
+int gdn_output_gate(const gdn_tensor* x, const gdn_tensor* z, const float* weight,
+                    float eps, gdn_tensor* out, void* stream);
 
 /* Short description of a status code (static storage). */
 const char* gdn_status_string(int status);

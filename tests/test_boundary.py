@@ -168,7 +168,7 @@ def test_flags_option(lib):
     """Unknown flag bits are rejected by the prefill and the decode step."""
     a = base()
     o = B.options()
-    o.flags = 2
+    o.flags = 8
     assert call(lib, a["q"], a["k"], a["v"], a["g"], a["b"], out=a["out"], opts=o) == -3
     o.flags = B.FLAG_BETA_LOGITS
     N, hk, hv, dk, dv = 2, 1, 1, 16, 16
@@ -178,6 +178,57 @@ def test_flags_option(lib):
     bad = B.options()
     bad.flags = 0x10
     assert lib.gdn_decode(r(q), r(q), r(v), r(g), r(g), r(st), r(v), r(bad), None) == -3
+
+
+def test_gate_options(lib):
+    """The gate fields of gdn_options: the output gate needs a 16-byte aligned
+    gate_z, norm_eps >= 0, and the f32 parameter arrays 4-byte alignment;
+    the prefill and the decode step check them before any HIP call."""
+    a = base()
+
+    def opts(**kw):
+        o = B.options()
+        for key, val in kw.items():
+            setattr(o, key, val)
+        return o
+    pre = lambda o: call(lib, a["q"], a["k"], a["v"], a["g"], a["b"], out=a["out"], opts=o)  # noqa: E731
+    assert pre(opts(flags=B.FLAG_OUTPUT_GATE)) == -1                      # no gate_z
+    assert pre(opts(flags=B.FLAG_OUTPUT_GATE, gate_z=0x20008)) == -4      # misaligned z
+    assert pre(opts(norm_eps=-1.0)) == -3
+    assert pre(opts(flags=B.FLAG_DECAY_PROJ, decay_a_log=0x20002)) == -4
+    assert pre(opts(flags=B.FLAG_DECAY_PROJ, decay_bias=0x20001)) == -4
+    assert pre(opts(norm_weight=0x20003)) == -4
+    N, hk, hv, dk, dv = 2, 1, 1, 16, 16
+    r = ctypes.byref
+    q, v = fake((N, hk, dk), torch.bfloat16), fake((N, hv, dv), torch.bfloat16)
+    g, st = fake((N, hv), torch.float32), fake((N, hv, dk, dv), torch.float32)
+    dec = lambda o, out=v: lib.gdn_decode(r(q), r(q), r(v), r(g), r(g), r(st), r(out), r(o), None)  # noqa: E731
+    assert dec(opts(flags=B.FLAG_OUTPUT_GATE)) == -1
+    assert dec(opts(flags=B.FLAG_OUTPUT_GATE, gate_z=0x20000),
+               out=fake((N, hv, dv), torch.bfloat16, addr=0x10008)) == -4  # out rows not 16-byte aligned
+    assert dec(opts(norm_eps=float("nan"))) == -3
+
+
+def test_output_gate_validation(lib):
+    """gdn_output_gate: shapes, dtypes, head sizes, strides and alignment are
+    checked on the host; no rows enqueues nothing."""
+    r = lambda x: ctypes.byref(x) if x is not None else None  # noqa: E731
+    bf = torch.bfloat16
+
+    def gate(x, z, out, w=None, eps=1e-6):
+        return lib.gdn_output_gate(r(x), r(z), w, ctypes.c_float(eps), r(out), None)
+    x = fake((10, 4, 64), bf)
+    assert gate(None, x, x) == -1
+    assert gate(x, fake((10, 4, 64), torch.float32), x) == -2
+    assert gate(x, fake((10, 4, 32), bf), x) == -3
+    assert gate(fake((10, 4, 48), bf), fake((10, 4, 48), bf), fake((10, 4, 48), bf)) == -5
+    assert gate(x, x, x, eps=-1.0) == -3
+    assert gate(x, x, x, w=0x20002) == -4
+    assert gate(fake((10, 4, 64), bf, addr=0x10008), x, x) == -4
+    assert gate(fake((10, 4, 64), bf, strides=(260, 65, 1)), x, x) == -4
+    assert gate(fake((10, 64), bf, strides=(64, 2)), fake((10, 64), bf), fake((10, 64), bf)) == -4
+    assert gate(fake((10, 64), bf), fake((10, 64), bf), fake((10, 4, 64), bf)) == -3
+    assert gate(fake((0, 4, 64), bf), fake((0, 4, 64), bf), fake((0, 4, 64), bf)) == 0
 
 
 def test_scan_split_option(lib):
