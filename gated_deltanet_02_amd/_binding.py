@@ -18,13 +18,13 @@ GDN_OK = 0
 STATUS_NAMES = {0: "GDN_OK", -1: "GDN_ERR_NULL_ARG", -2: "GDN_ERR_DTYPE",
                 -3: "GDN_ERR_SHAPE", -4: "GDN_ERR_LAYOUT",
                 -5: "GDN_ERR_UNSUPPORTED", -6: "GDN_ERR_WORKSPACE",
-                -7: "GDN_ERR_HIP"}
+                -7: "GDN_ERR_HIP", -8: "GDN_ERR_INPUT"}
 STAGE_TABLE, STAGE_WY, STAGE_SCAN, STAGE_ALL = 1, 2, 4, 7
 SCAN_AUTO, SCAN_ONE_PASS, SCAN_TWO_LEVEL = 0, 1, 2
 FLAG_BETA_LOGITS, FLAG_DECAY_PROJ, FLAG_OUTPUT_GATE = 1, 2, 4
 EXPORTED = ("gdn_abi_version", "gdn_default_options", "gdn_prefill",
             "gdn_prefill_ex", "gdn_prefill_noalloc", "gdn_workspace_size", "gdn_get_workspace_layout",
-            "gdn_decode", "gdn_output_gate", "gdn_graph_cache_create", "gdn_graph_cache_destroy",
+            "gdn_decode", "gdn_output_gate", "gdn_check_cu_seqlens", "gdn_graph_cache_create", "gdn_graph_cache_destroy",
             "gdn_graph_cache_clear", "gdn_graph_cache_stats", "gdn_prefill_graph",
             "gdn_status_string", "gdn_last_error")
 
@@ -101,6 +101,8 @@ def lib():
         L.gdn_decode.restype = ctypes.c_int
         L.gdn_output_gate.argtypes = [T, T, ctypes.c_void_p, ctypes.c_float, T, ctypes.c_void_p]
         L.gdn_output_gate.restype = ctypes.c_int
+        L.gdn_check_cu_seqlens.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64]
+        L.gdn_check_cu_seqlens.restype = ctypes.c_int
         L.gdn_graph_cache_create.argtypes = [ctypes.c_int, P(ctypes.c_void_p)]
         L.gdn_graph_cache_create.restype = ctypes.c_int
         L.gdn_graph_cache_destroy.argtypes = [ctypes.c_void_p]
@@ -316,6 +318,17 @@ def gdn_output_gate(x, z, weight=None, eps: float = 1e-6, out=None, stream=None)
     _check(lib().gdn_output_gate(_ref(ds[0]), _ref(ds[1]), w, ctypes.c_float(eps), _ref(ds[2]),
                                  _stream_handle(stream, x)))
     return out
+
+
+def gdn_check_cu_seqlens(cu, t_total: int) -> None:
+    """Checks a host copy of cu_seqlens (int32, N + 1 entries) against the
+    prefill's preconditions; raises GdnError (GDN_ERR_INPUT) naming the
+    first bad entry."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(cu.cpu() if hasattr(cu, "cpu") else cu, dtype=np.int32))
+    if a.ndim != 1:
+        raise ValueError("cu_seqlens must be 1-D")
+    _check(lib().gdn_check_cu_seqlens(a.ctypes.data if a.size else None, a.size - 1, int(t_total)))
 
 
 def gdn_decode(q, k, v, g, beta, state, out=None, opts: Optional[GdnOptions] = None,

@@ -9,6 +9,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <algorithm>
 #include <list>
@@ -16,6 +17,7 @@
 #include <string>
 
 #include "gdn.h"
+#include "gdn_cu_check.h"
 #include "gdn_internal.h"
 #include "gdn_launch.h"
 
@@ -435,6 +437,36 @@ int validate_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* 
   return GDN_OK;
 }
 
+// Names the fault bits of a cu_seqlens table.
+const char* cu_fault_text(int32_t f) {
+  if (f & gdn::kCuFirstNonzero) return "cu[0] != 0";
+  if (f & gdn::kCuDecreasing) return "entries decrease";
+  if (f & gdn::kCuPastEnd) return "cu[N] > T";
+  return "malformed";
+}
+
+bool debug_check_enabled() {
+  const char* e = getenv("GDN_DEBUG_CHECK");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+// GDN_DEBUG_CHECK=1: the device table is checked before anything else is
+// enqueued (skipped while the stream is being captured).
+int debug_check_cu(const Problem& P, const gdn_tensor* cu, hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) return fail(GDN_ERR_HIP, "hipStreamIsCapturing failed");
+  if (cs != hipStreamCaptureStatusNone) return GDN_OK;
+  int32_t* word = nullptr;
+  hipError_t e = gdn::debug_word_region(&word);
+  if (e == hipSuccess) e = gdn::launch_check_cu((const int32_t*)cu->data, P.n_seq, P.T, word, s);
+  int32_t faults = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&faults, word, sizeof faults, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "cu_seqlens check: %s", hipGetErrorString(e));
+  if (faults) return fail(GDN_ERR_INPUT, "cu_seqlens is malformed (%s; GDN_DEBUG_CHECK)", cu_fault_text(faults));
+  return GDN_OK;
+}
+
 int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
         const gdn_tensor* v, const gdn_tensor* g, const gdn_tensor* beta,
         const gdn_tensor* cu, const gdn_tensor* init, gdn_tensor* out,
@@ -457,6 +489,10 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
   im.decay = (float*)(base + L.decay);
 
   hipError_t e;
+  if (P.packed && (P.stages & GDN_STAGE_TABLE) && debug_check_enabled()) {
+    const int rc = debug_check_cu(P, cu, s);
+    if (rc) return rc;
+  }
   if (P.packed && (P.stages & GDN_STAGE_TABLE)) {
     gdn::TableParams tp{};
     tp.cu = (const int32_t*)cu->data;
@@ -582,6 +618,7 @@ const char* gdn_status_string(int status) {
     case GDN_ERR_UNSUPPORTED: return "unsupported configuration";
     case GDN_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case GDN_ERR_HIP: return "HIP error";
+    case GDN_ERR_INPUT: return "malformed input values";
   }
   return "unknown status";
 }
@@ -713,6 +750,17 @@ int gdn_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
     if ((e = gdn::launch_output_gate(bf16, d.dv, gp, (hipStream_t)stream)) != hipSuccess)
       return fail(GDN_ERR_HIP, "output gate launch: %s", hipGetErrorString(e));
   }
+  return GDN_OK;
+}
+
+int gdn_check_cu_seqlens(const int32_t* cu_host, int64_t n_seq, int64_t t_total) {
+  if (!cu_host) return fail(GDN_ERR_NULL_ARG, "cu_host is NULL");
+  if (n_seq < 1 || t_total < 0) return fail(GDN_ERR_SHAPE, "n_seq must be >= 1 and t_total >= 0");
+  for (int64_t i = 0; i <= n_seq; ++i) {
+    const int32_t f = gdn::cu_entry_faults(cu_host, i, n_seq, t_total);
+    if (f) return fail(GDN_ERR_INPUT, "cu_seqlens[%lld] = %d: %s", (long long)i, cu_host[i], cu_fault_text(f));
+  }
+  g_last_error.clear();
   return GDN_OK;
 }
 

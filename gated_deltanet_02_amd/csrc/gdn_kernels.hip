@@ -62,6 +62,7 @@
 
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_cu_check.h"
 #include "gdn_launch.h"
 
 namespace gdn {
@@ -1844,6 +1845,25 @@ int scan_slices_per_group(bool bf16, int chunk, int dk, int dv, int64_t seq_head
   return seq_heads * (dv / 16) > device_cus() ? 2 : 1;
 }
 
+// GDN_DEBUG_CHECK: one workgroup checks every entry of cu_seqlens.
+__global__ __launch_bounds__(256) void check_cu_kernel(const int32_t* cu, int64_t n_seq,
+                                                      int64_t t_total, int32_t* faults) {
+  __shared__ int32_t s_f;
+  if (threadIdx.x == 0) s_f = 0;
+  __syncthreads();
+  int32_t f = 0;
+  for (int64_t i = threadIdx.x; i <= n_seq; i += blockDim.x) f |= cu_entry_faults(cu, i, n_seq, t_total);
+  if (f) atomicOr(&s_f, f);
+  __syncthreads();
+  if (threadIdx.x == 0) *faults = s_f;
+}
+
+hipError_t launch_check_cu(const int32_t* cu, int64_t n_seq, int64_t t_total, int32_t* faults,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(check_cu_kernel, dim3(1), dim3(256), 0, s, cu, n_seq, t_total, faults);
+  return hipGetLastError();
+}
+
 hipError_t launch_table(const TableParams& p, hipStream_t s) {
   hipLaunchKernelGGL(table_kernel, dim3(1), dim3(1024), 0, s, p);
   return hipGetLastError();
@@ -1997,6 +2017,7 @@ hipError_t launch_output_gate(bool bf16, int dv, const GateParams& p, hipStream_
 }  // namespace gdn
 
 static __device__ __align__(256) char scratch[gdn::kScratchBytes];
+static __device__ int32_t debug_word;
 
 namespace gdn {
 
@@ -2015,6 +2036,26 @@ hipError_t scratch_region(void** ptr) {
     if (e != hipSuccess) return e;
     if (!p) return hipErrorInvalidSymbol;
     addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t debug_word_region(int32_t** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int32_t* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(debug_word));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = (int32_t*)p;
   }
   *ptr = addr[dev];
   return hipSuccess;

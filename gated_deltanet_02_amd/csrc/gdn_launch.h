@@ -28,6 +28,15 @@ hipError_t launch_scan_two_level(int chunk, int dk, const ScanParams& p, hipStre
 
 hipError_t launch_decode(bool bf16, int dk, const DecodeParams& p, hipStream_t s);
 
+// GDN_DEBUG_CHECK: ORs the fault bits (gdn_cu_check.h) of cu[0 .. n_seq]
+// into one word and stores it at *faults (one workgroup).
+hipError_t launch_check_cu(const int32_t* cu, int64_t n_seq, int64_t t_total, int32_t* faults,
+                           hipStream_t s);
+
+// Device address of the current device's fault word for launch_check_cu
+// (a static device variable, looked up once per device).
+hipError_t debug_word_region(int32_t** ptr);
+
 // The gated output norm (dv in {16, 32, 64, 128}).
 hipError_t launch_output_gate(bool bf16, int dv, const GateParams& p, hipStream_t s);
 

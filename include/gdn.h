@@ -37,12 +37,19 @@
  * before any HIP call; a failed validation returns a negative status and
  * enqueues nothing.  No exception crosses the ABI.  gdn_last_error() gives a
  * message for the calling thread's last failure.  The contents of
- * cu_seqlens are a precondition (cu[0] = 0, non-decreasing, cu[N] = T); the
- * library never reads device memory on the host, so it cannot check them,
- * but the kernels clamp them so that a bad table cannot make them access
- * memory outside the tensors.  Faults of enqueued work surface at the
- * caller's next synchronisation of the stream.  No call synchronises the
- * device.
+ * cu_seqlens are a precondition (cu[0] = 0, non-decreasing, cu[N] <= T);
+ * by default the library does not read device memory on the host, so it
+ * does not check them, but the kernels clamp them so that a bad table
+ * cannot make them access memory outside the tensors.  gdn_check_cu_seqlens
+ * checks a host copy.  With the environment variable GDN_DEBUG_CHECK=1, a
+ * packed prefill first checks the device table in a one-workgroup kernel,
+ * waits for it (a stream synchronisation) and, if the table is malformed,
+ * returns GDN_ERR_INPUT with nothing else enqueued (the pages reject bad
+ * input before any work starts: "Open-Jev-27B-v1.1 native text worker",
+ * section "Prepare the checkpoint").  The check is skipped while the stream
+ * is being captured into a graph (a capture cannot wait).  Faults of
+ * enqueued work surface at the caller's next synchronisation of the
+ * stream.  Apart from GDN_DEBUG_CHECK, no call synchronises the device.
  */
 #ifndef GDN_H_
 #define GDN_H_
@@ -65,6 +72,7 @@ extern "C" {
 #define GDN_ERR_UNSUPPORTED (-5) /* valid but not built: head size, chunk ... */
 #define GDN_ERR_WORKSPACE (-6)   /* workspace missing, too small or misaligned */
 #define GDN_ERR_HIP (-7)         /* a HIP call or kernel launch failed        */
+#define GDN_ERR_INPUT (-8)       /* malformed input values (cu_seqlens)       */
 
 /* Element types. */
 #define GDN_DTYPE_BF16 1
@@ -361,6 +369,16 @@ int gdn_prefill_graph(gdn_graph_cache* cache, const gdn_tensor* q,
  */
 int gdn_output_gate(const gdn_tensor* x, const gdn_tensor* z, const float* weight,
                     float eps, gdn_tensor* out, void* stream);
+
+/*
+ * gdn_check_cu_seqlens -- checks a host copy of a cu_seqlens table of
+ * n_seq + 1 entries for t_total tokens against the preconditions above
+ * (cu[0] = 0, non-decreasing, cu[n_seq] <= t_total) with the predicate the
+ * GDN_DEBUG_CHECK device check uses.  cu_host is host memory.  Returns
+ * GDN_OK, GDN_ERR_INPUT (the message names the first bad entry), or
+ * GDN_ERR_NULL_ARG / GDN_ERR_SHAPE for a NULL table or n_seq < 1.
+ */
+int gdn_check_cu_seqlens(const int32_t* cu_host, int64_t n_seq, int64_t t_total);
 
 /* Short description of a status code (static storage). */
 const char* gdn_status_string(int status);

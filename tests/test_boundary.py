@@ -47,7 +47,7 @@ def test_abi_version_and_defaults(lib):
     o = G.gdn_default_options()
     assert (o.chunk, o.scale, o.stages, o.scan_split, o.flags) == (0, 1.0, 7, 0, 0)
     assert abs(o.l2_eps - 1e-6) < 1e-12
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         assert G.gdn_status_string(s) != "unknown status"
     assert G.gdn_status_string(5) == "unknown status"
 
@@ -341,3 +341,31 @@ def test_noalloc_validation_on_host(lib):
     src = open(HEADER).read()
     m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
     assert int(m.group(1)) << int(m.group(2)) == G.NOALLOC_SCRATCH_BYTES
+
+
+CU_CASES = {
+    "first_nonzero": ([1, 5, 9], 9, "cu_seqlens[0] = 1: cu[0] != 0"),
+    "decreasing": ([0, 5, 4, 9], 9, "cu_seqlens[2] = 4: entries decrease"),
+    "negative": ([0, -3, 9], 9, "cu_seqlens[1] = -3: entries decrease"),
+    "past_end": ([0, 5, 10], 9, "cu_seqlens[2] = 10: cu[N] > T"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CU_CASES))
+def test_check_cu_seqlens_rejects(lib, case):
+    """The host validator (the predicate GDN_DEBUG_CHECK runs on the device)
+    names the first bad entry of a malformed table."""
+    cu, T, msg = CU_CASES[case]
+    with pytest.raises(G.GdnError) as ei:
+        G.gdn_check_cu_seqlens(cu, T)
+    assert ei.value.status == -8
+    assert msg in str(ei.value)
+
+
+def test_check_cu_seqlens_accepts(lib):
+    for cu, T in (([0, 9], 9), ([0, 0, 0], 5), ([0, 3, 3, 7], 7), ([0, 4], 9)):
+        G.gdn_check_cu_seqlens(cu, T)
+    with pytest.raises(G.GdnError) as ei:
+        G.gdn_check_cu_seqlens([0], 0)
+    assert ei.value.status == -3
+    assert lib.gdn_check_cu_seqlens(None, 1, 1) == -1
