@@ -72,6 +72,34 @@ def algorithmic_flops(w) -> int:
     return int(T * hv * per)
 
 
+def read_sclk_mhz():
+    """The shader clock rocm-smi reports for GPU 0 (MHz), or None."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    m = re.search(r"sclk[^\n]*?\((\d+)\s*Mhz\)", r.stdout, flags=re.IGNORECASE)
+    return int(m.group(1)) if m else None
+
+
+def sclk_under_load(step, torch, seconds: float = 5.0):
+    """rocm-smi's shader clock read while the GPU keeps running `step` (the
+    read takes a fraction of a second; the GPU is kept busy meanwhile)."""
+    import threading
+    box = {}
+    th = threading.Thread(target=lambda: box.update(v=read_sclk_mhz()), daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while th.is_alive() and time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            step()
+        torch.cuda.synchronize()
+    th.join(timeout=1.0)
+    return box.get("v")
+
+
 def load_traffic(workload: str, kernel: str):
     """HBM bytes per launch measured with rocprofv3 counters, if the record
     matches the current kernel sources (else None)."""
@@ -307,7 +335,20 @@ def main():
                           "algorithmic_flops": nflops},
         "kernel_ms": {k: round(v, 5) for k, v in kernels.items()},
         "gpu_event_ms_per_step": t_gpu,
+        "sclk_mhz_under_load": sclk_under_load(full, torch),
     }
+    # Warm single calls: HIP events around each call alone (inputs and
+    # workspace left in the caches by the previous call).
+    reps = 30
+    wev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for i in range(reps):
+        wev[i][0].record()
+        full()
+        wev[i][1].record()
+    torch.cuda.synchronize()
+    warm = sorted(e[0].elapsed_time(e[1]) for e in wev)
+    pickw = lambda f: warm[min(len(warm) - 1, int(f * len(warm)))]  # noqa: E731
+    result["warm"] = {"ms_median": pickw(0.5), "ms_p10": pickw(0.1), "ms_p90": pickw(0.9), "reps": reps}
     # Cold calls: before each, a 512 MiB device copy (256 MiB read, 256 MiB
     # written) evicts the 256 MB Infinity Cache and the L2s, so the call
     # reads its inputs from HBM; HIP events around the call only.
