@@ -1448,8 +1448,10 @@ __global__ __launch_bounds__(scan_threads<NSL>()) void scan_kernel(ScanParams p)
 
   if (wave >= 2 * NSL) {
     if (nch <= 0) return;
-    if (wave == 2 * NSL) ring_producer<R, C, 0>(smem, p, c_begin, c_end, h, NSL * sl, tok0, tok_end, lane);
-    else ring_producer<R, C, 1>(smem, p, c_begin, c_end, h, NSL * sl, tok0, tok_end, lane);
+    auto produce = [&](auto cw) {
+      ring_producer<R, C, decltype(cw)::value>(smem, p, c_begin, c_end, h, NSL * sl, tok0, tok_end, lane);
+    };
+    dispatch_int<0, kScanCopyWaves>(wave - 2 * NSL, produce);
     return;
   }
   if (wave >= NSL) {
@@ -1513,8 +1515,10 @@ __global__ __launch_bounds__(scan_threads<2>()) void scan_split_kernel(ScanParam
   if (ce <= cb) return;
 
   if (wave >= 4) {
-    if (wave == 4) ring_producer<R, C, 0>(smem, p, cb, ce, h, 0, tb, te, lane);
-    else ring_producer<R, C, 1>(smem, p, cb, ce, h, 0, tb, te, lane);
+    auto produce = [&](auto cw) {
+      ring_producer<R, C, decltype(cw)::value>(smem, p, cb, ce, h, 0, tb, te, lane);
+    };
+    dispatch_int<0, kScanCopyWaves>(wave - 4, produce);
     return;
   }
   const int s = wave & 1;
