@@ -176,45 +176,6 @@ __global__ __launch_bounds__(1024) void table_kernel(TableParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS helpers (whole workgroup)
-
-// out[r] = 1 / sqrt(sum_d src[r][d]^2 + eps); four lanes per row, each
-// reading its quarter of the row in 16-byte pieces.
-template <typename TI, int D, int R, int NT = kThreads>
-__device__ __forceinline__ void row_inv_norms(const TI* src, int lds, float eps, float* out,
-                                              int tid) {
-  constexpr int GR = Gran<TI>::n;
-  constexpr int NG = D / GR;  // 16-byte granules per row (D is a multiple of GR)
-  static_assert(D % GR == 0, "rows of whole granules");
-  // adjacent lanes share a row, PARTS of them (a power of two)
-  constexpr int PARTS = NT / R < NG ? NT / R : NG;
-  static_assert((PARTS & (PARTS - 1)) == 0 && PARTS <= 64, "lanes per row");
-  for (int base = 0; base < R * PARTS; base += NT) {
-    const int idx = base + tid;
-    const int r = idx / PARTS, part = idx % PARTS;
-    float s0 = 0.f, s1 = 0.f;
-    if (r < R) {
-      const TI* row = src + r * lds;
-#pragma unroll
-      for (int g = part; g < NG; g += PARTS) {
-        const uint4 v = ld16(row + g * GR);
-        const TI* e = (const TI*)&v;
-#pragma unroll
-        for (int j = 0; j < GR; j += 2) {
-          const float x0 = to_float(e[j]), x1 = to_float(e[j + 1]);
-          s0 += x0 * x0;
-          s1 += x1 * x1;
-        }
-      }
-    }
-    float s = s0 + s1;
-#pragma unroll
-    for (int o = 1; o < PARTS; o <<= 1) s += __shfl_xor(s, o);
-    if (r < R && part == 0) out[r] = 1.0f / sqrtf(s + eps);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // WY kernel
 
 // Column order of the bf16 [*][C] tiles of the WY kernel (P, Tb, Tv):
@@ -288,17 +249,21 @@ __device__ __forceinline__ typename Unit<TI>::type col_unit(const TI* m, int ld,
   }
 }
 
-// The Gram tiles (kind 0: K_rt K_j^T, j >= rt, the blocks A reads) and
-// the (Q K^T)^T tiles (kind 1: K_j Q_rt^T, j <= rt, the blocks P reads)
-// held by wave w of the WY kernel, slot t (kind -1: none).  With four row
-// tiles the ten tiles of each kind go three, three, two, two to waves 0..3
-// (Gram) and 4..7 (Q K^T); with fewer, wave w (w - 4) takes every tile of
-// row (column) tile w (w - 4).
+// The Gram tiles (kind 0: K_rt K_j^T, j >= rt, the blocks A reads), the
+// (Q K^T)^T tiles (kind 1: K_j Q_rt^T, j <= rt, the blocks P reads) and the
+// diagonal Q Q^T tiles (kind 2: Q_rt Q_rt^T, whose diagonal gives q's row
+// norms) held by wave w of the WY kernel, slot t (kind -1: none).  With four
+// row tiles the ten tiles of each of the first two kinds go three, three,
+// two, two to waves 0..3 (Gram) and 4..7 (Q K^T), and the four Q Q^T tiles
+// fill the third slots of waves 2..5; with fewer (one or two), wave w
+// (w - 4) takes every tile of row (column) tile w (w - 4) and wave nb + rt
+// the Q Q^T tile rt.
 struct WyTile {
   int kind, rt, j;
 };
 __host__ __device__ constexpr WyTile wy_tile(int nb, int w, int t) {
   if (nb == 4) {
+    if (t == 2 && w >= 2 && w <= 5) return WyTile{2, w - 2, w - 2};
     constexpr int tb[8][3][2] = {{{0, 0}, {0, 1}, {0, 2}}, {{1, 1}, {1, 2}, {1, 3}},
                                  {{2, 2}, {2, 3}, {-1, -1}}, {{3, 3}, {0, 3}, {-1, -1}},
                                  {{0, 0}, {3, 0}, {-1, -1}}, {{1, 0}, {1, 1}, {-1, -1}},
@@ -308,8 +273,24 @@ __host__ __device__ constexpr WyTile wy_tile(int nb, int w, int t) {
   }
   if (w >= 0 && w < nb) return w + t < nb ? WyTile{0, w, w + t} : WyTile{-1, 0, 0};
   if (w >= 4 && w - 4 < nb) return t <= w - 4 ? WyTile{1, w - 4, t} : WyTile{-1, 0, 0};
+  if (nb <= 2 && w >= nb && w < 2 * nb) return t == 0 ? WyTile{2, w - nb, w - nb} : WyTile{-1, 0, 0};
   return WyTile{-1, 0, 0};
 }
+// Each row tile's Gram diagonal and Q Q^T tile is held exactly once.
+__host__ __device__ constexpr bool wy_tiles_cover(int nb) {
+  for (int rt = 0; rt < nb; ++rt) {
+    int kdiag = 0, qdiag = 0;
+    for (int w = 0; w < 8; ++w)
+      for (int t = 0; t < 3; ++t) {
+        const WyTile T = wy_tile(nb, w, t);
+        if (T.kind == 0 && T.rt == rt && T.j == rt) ++kdiag;
+        if (T.kind == 2 && T.rt == rt) ++qdiag;
+      }
+    if (kdiag != 1 || qdiag != 1) return false;
+  }
+  return true;
+}
+static_assert(wy_tiles_cover(1) && wy_tiles_cover(2) && wy_tiles_cover(4), "diagonal tiles");
 
 // A compile-time integer passed as a value, and a dispatch of a runtime
 // value in [I, N) to f(IntC<value>) (f is not called for values outside).
@@ -520,13 +501,10 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   // (LDS-direct copies would not do: every LDS read would wait for them.)
   load_head(kh * grp, false);
 
-  // q's inverse row norms (the swizzle only permutes a row's granules); k's
-  // come from the diagonal of the Gram tiles below
-  row_inv_norms<TI, DK, C, NT>(sQ, LK, p.eps, sRq, tid);
-
   // Raw K K^T and Q K^T tiles (the wave's slots, see wy_tile).  They stay
   // in registers for all value heads of the group; norms and gates are
-  // applied when A and P are built.
+  // applied when A and P are built.  The inverse row norms of k and q come
+  // from the diagonals of the Gram and Q Q^T tiles.
   constexpr int NSLOT = NB == 4 ? 3 : NB;
   f32x4 acc_gs[NSLOT];
 #pragma unroll
@@ -540,26 +518,33 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       f32x4 acc1[1][1] = {{zero4()}};
       if (T.kind == 0)  // K_rt K_j^T: lane holds column 16 j + lane % 16
         mma_block_sw<1, 1, DK, SWK, SWK>(acc1, sKV, LK, 16 * T.rt, sKV, LK, 16 * T.j, lane);
-      else  // K_j Q_rt^T: lane holds query 16 rt + lane % 16, four consecutive keys
+      else if (T.kind == 1)  // K_j Q_rt^T: lane holds query 16 rt + lane % 16, four consecutive keys
         mma_block_sw<1, 1, DK, SWK, SWK>(acc1, sKV, LK, 16 * T.j, sQ, LK, 16 * T.rt, lane);
+      else  // Q_rt Q_rt^T
+        mma_block_sw<1, 1, DK, SWK, SWK>(acc1, sQ, LK, 16 * T.rt, sQ, LK, 16 * T.rt, lane);
       acc_gs[t] = acc1[0][0];
     }
 #pragma unroll
     for (int t = 0; t < NSLOT; ++t) settle(acc_gs[t]);
-    // slot 0 of a Gram wave is its diagonal tile (rt, rt): lane m + 16 (m / 4)
-    // holds |k_(16 rt + m)|^2 as element m % 4
-    constexpr WyTile T0 = wy_tile(NB, W, 0);
-    if constexpr (T0.kind == 0) {
-      static_assert(T0.rt == T0.j, "slot 0 of a Gram wave is diagonal");
-      const int m = lane & 15;
-      if ((m >> 2) == (lane >> 4)) {
-        float d = acc_gs[0][0];
-        if ((m & 3) == 1) d = acc_gs[0][1];
-        if ((m & 3) == 2) d = acc_gs[0][2];
-        if ((m & 3) == 3) d = acc_gs[0][3];
-        sRk[16 * T0.rt + m] = 1.0f / sqrtf(d + p.eps);
+    // a diagonal tile (rt, rt): lane m + 16 (m / 4) holds the squared norm of
+    // row 16 rt + m as element m % 4
+    auto diag_norms = [&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      constexpr WyTile T = wy_tile(NB, W, t);
+      if constexpr ((T.kind == 0 && T.rt == T.j) || T.kind == 2) {
+        const int m = lane & 15;
+        if ((m >> 2) == (lane >> 4)) {
+          float d = acc_gs[t][0];
+          if ((m & 3) == 1) d = acc_gs[t][1];
+          if ((m & 3) == 2) d = acc_gs[t][2];
+          if ((m & 3) == 3) d = acc_gs[t][3];
+          (T.kind == 0 ? sRk : sRq)[16 * T.rt + m] = 1.0f / sqrtf(d + p.eps);
+        }
       }
-    }
+    };
+    diag_norms(IntC<0>{});
+    if constexpr (NSLOT > 1) diag_norms(IntC<1>{});
+    if constexpr (NSLOT > 2) diag_norms(IntC<2>{});
   };
   dispatch_int<0, kWyThreads / 64>(wave, gram_tiles);
   // The gate cumulative sum gamma, beta (sigmoid of a logit for a real
