@@ -436,7 +436,10 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   float* sCb = sKs + C;     // beta_s e^gamma_s rk_s  (column scale of Tb)
   const float* sGate = (const float*)(smem + L::r_gate);
 
-  const int c = it / p.hk, kh = it % p.hk;
+  // Chunks are taken last first: the scan reads the first chunks first, and
+  // those, written last, are the likeliest to be still in the memory-side
+  // cache when the intermediates do not all fit there.
+  const int c = p.n_items / p.hk - 1 - it / p.hk, kh = it % p.hk;
   int seq, t0, n;
   if (!chunk_info(p.map, c, C, seq, t0, n)) return;
   (void)seq;
