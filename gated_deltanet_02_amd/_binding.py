@@ -43,7 +43,7 @@ class GdnOptions(ctypes.Structure):
                 ("scan_split", ctypes.c_int32), ("flags", ctypes.c_uint32),
                 ("decay_a_log", ctypes.c_void_p), ("decay_bias", ctypes.c_void_p),
                 ("gate_z", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
-                ("norm_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("segment_chunks", ctypes.c_int32)]
 
 
 class GdnWorkspaceLayout(ctypes.Structure):
@@ -52,7 +52,8 @@ class GdnWorkspaceLayout(ctypes.Structure):
                                        "decay", "w", "qp", "ut", "oloc")] + [
         ("split_chunks", ctypes.c_int32)] + [
         (n, ctypes.c_size_t) for n in ("split_y", "split_hmid", "split_hmid_t", "split_psi",
-                                       "split_phi")]
+                                       "split_phi")] + [
+        ("segment_chunks", ctypes.c_int32), ("segment_state", ctypes.c_size_t)]
 
 
 class GdnError(RuntimeError):
@@ -155,8 +156,9 @@ def options(chunk: int = 0, scale: float = 1.0, l2_eps: float = 1e-6,
             decay_proj: bool = False, decay_a_log: Optional[torch.Tensor] = None,
             decay_bias: Optional[torch.Tensor] = None,
             gate_z: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
-            norm_eps: float = 1e-6) -> GdnOptions:
+            norm_eps: float = 1e-6, segment_chunks: int = 0) -> GdnOptions:
     """scan_split: SCAN_AUTO (0), SCAN_ONE_PASS (1) or SCAN_TWO_LEVEL (2);
+    segment_chunks: 0 automatic, -1 never, n > 0 segments of n chunks;
     beta_logits: beta holds raw projections b and the kernels use sigmoid(b);
     decay_proj: g holds the decay gate's raw projection a, with per value head
     f32 tensors decay_a_log and decay_bias (None: zeros);
@@ -171,6 +173,7 @@ def options(chunk: int = 0, scale: float = 1.0, l2_eps: float = 1e-6,
     o.decay_bias = _dev_ptr(decay_bias, "decay_bias")
     o.norm_weight = _dev_ptr(norm_weight, "norm_weight")
     o.norm_eps = norm_eps
+    o.segment_chunks = segment_chunks
     if gate_z is not None:
         if gate_z.device.type != "cuda":
             raise ValueError("gate_z must be a GPU tensor")

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <numeric>
 #include <cstring>
 #include <algorithm>
 #include <list>
@@ -133,6 +134,8 @@ struct Problem {
   const float* norm_w = nullptr;
   float norm_eps = 1e-6f;
   int split = 0;  // two-level scan: chunks in the first segment (0: one pass)
+  int seg_opt = 0;           // gdn_options.segment_chunks
+  int64_t seg_chunks = 0;    // chunks per segment (0: one pass over all chunks)
 };
 
 constexpr uint32_t kKnownFlags = GDN_FLAG_BETA_LOGITS | GDN_FLAG_DECAY_PROJ | GDN_FLAG_OUTPUT_GATE;
@@ -149,8 +152,15 @@ int check_gate_options(const gdn_options& o) {
 struct Layout {
   size_t table = 0, chunk_off = 0, seq_start = 0, decay = 0;
   size_t w = 0, qp = 0, ut = 0, oloc = 0;
-  size_t y = 0, hmid = 0, hmid_t = 0, psi = 0, phi = 0, total = 0;
+  size_t y = 0, hmid = 0, hmid_t = 0, psi = 0, phi = 0, carry = 0, total = 0;
 };
+
+// Bytes of the intermediates of one (chunk, value head): W, Q', U~, O_loc
+// and the decay.
+size_t block_bytes(const Problem& P) {
+  const size_t es = P.bf16 ? 2 : 4;
+  return (size_t)P.chunk * (2 * P.dk + 2 * P.dv) * es + 4;
+}
 
 Layout make_layout(const Problem& P) {
   Layout L;
@@ -178,6 +188,7 @@ Layout make_layout(const Problem& P) {
     L.psi = take(heads * P.dk * P.dv * 4);
     L.phi = take(heads * P.dk * P.dk * 4);
   }
+  if (P.seg_chunks > 0) L.carry = take((size_t)P.n_seq * P.hv * P.dk * P.dv * 4);
   L.total = off;
   return L;
 }
@@ -194,6 +205,7 @@ int resolve_options(const gdn_options* opts, bool bf16, Problem* P) {
   if ((o.stages & ~GDN_STAGE_ALL) != 0) return fail(GDN_ERR_SHAPE, "unknown stage bits 0x%x", o.stages);
   if (o.scan_split < GDN_SCAN_AUTO || o.scan_split > GDN_SCAN_TWO_LEVEL)
     return fail(GDN_ERR_SHAPE, "unknown scan_split %d", o.scan_split);
+  if (o.segment_chunks < -1) return fail(GDN_ERR_SHAPE, "segment_chunks must be >= -1 (got %d)", o.segment_chunks);
   int rc;
   if ((rc = check_gate_options(o))) return rc;
   P->chunk = chunk;
@@ -209,7 +221,48 @@ int resolve_options(const gdn_options* opts, bool bf16, Problem* P) {
   P->gate_z = P->out_gate ? o.gate_z : nullptr;
   P->norm_w = P->out_gate ? o.norm_weight : nullptr;
   P->norm_eps = o.norm_eps;
+  P->seg_opt = o.segment_chunks;
   return GDN_OK;
+}
+
+// Intermediates the automatic choice keeps per segment (W, Q', U~ and O_loc
+// of every sequence and value head; the decays are not counted): half of the 256 MiB
+// memory-side cache, the rest left to the inputs and outputs the two
+// launches touch.  Measured on MI355X (whole calls): a 16384-token prompt
+// with 16 heads (256 MiB of intermediates) takes 323 us in one pass, 281 us
+// in segments of 128 chunks (the automatic choice), 278 us in segments of
+// 64 and 307 us in segments of 32; with 16 key and 48 value heads 586 us in
+// one pass, 554 us in segments of 32 chunks (the automatic choice), 586 us
+// in segments of 64 and 689 us in segments of 16.
+constexpr size_t kSegmentBytes = (size_t)128 << 20;
+constexpr int64_t kMinAutoSegment = 8;
+// WY workgroups resident at once on MI355X: 256 compute units, two each.
+constexpr int64_t kWySlots = 512;
+
+// Chunks per segment (gdn_options.segment_chunks), 0 for one pass.
+void choose_segments(Problem* P) {
+  P->seg_chunks = 0;
+  if (P->packed || P->split > 0 || P->stages != GDN_STAGE_ALL || P->seg_opt < 0 ||
+      P->chunks_per_seq < 2)
+    return;
+  int64_t seg = P->seg_opt;
+  if (seg == 0) {
+    const size_t per_chunk = (size_t)P->n_seq * P->hv * (block_bytes(*P) - 4);
+    if ((size_t)P->chunks_per_seq * per_chunk <= kSegmentBytes) return;
+    const int64_t most = (int64_t)(kSegmentBytes / per_chunk);
+    if (most < kMinAutoSegment) return;
+    // the longest segment within the budget whose WY work items fill whole
+    // rounds of the workgroup slots; else the fewest segments of equal length
+    const int64_t items = (int64_t)P->n_seq * P->hk;  // WY work items per chunk position
+    const int64_t round = kWySlots / std::gcd(kWySlots, items);
+    if (round <= most) {
+      seg = most / round * round;
+    } else {
+      const int64_t n = (P->chunks_per_seq + most - 1) / most;
+      seg = (P->chunks_per_seq + n - 1) / n;
+    }
+  }
+  if (seg < P->chunks_per_seq) P->seg_chunks = seg;
 }
 
 // The two-level scan's split point (see GDN_SCAN_TWO_LEVEL), 0 for one pass.
@@ -304,6 +357,7 @@ int validate(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
   const int64_t scan_blocks = ((int64_t)P->n_seq * P->hv + 7) / 8 * 8 * n_slices;
   if (scan_blocks >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "too many (sequence, head) pairs");
   if ((rc = choose_split(P))) return rc;
+  choose_segments(P);
   if (!full) return GDN_OK;
 
   // The remaining tensors.
@@ -477,6 +531,7 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
   map.packed = P.packed ? 1 : 0;
   map.n_seq = P.n_seq;
   map.seq_len = P.seq_len;
+  map.seq_stride = P.seq_len;
   map.chunks_per_seq = P.chunks_per_seq;
   map.table = (const int32_t*)(base + L.table);
   map.chunk_off = (const int32_t*)(base + L.chunk_off);
@@ -506,13 +561,20 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
     if ((e = gdn::launch_table(tp, s)) != hipSuccess)
       return fail(GDN_ERR_HIP, "chunk table launch: %s", hipGetErrorString(e));
   }
-  if ((P.stages & GDN_STAGE_WY) && P.max_chunks > 0) {
+  // Byte offsets of token t0 in the token-indexed tensors (a segment's
+  // views: its first token, the same strides).
+  const size_t es = P.bf16 ? 2 : 4;
+  auto at = [](const void* base, int64_t t0, int64_t st, size_t bytes) {
+    return (const char*)base + t0 * st * (int64_t)bytes;
+  };
+  // The WY transform of the chunks `m` maps, inputs from token t0 on.
+  auto wy = [&](const gdn::ChunkMap& m, int64_t n_chunks, int64_t t0) -> int {
     gdn::WyParams wp{};
-    wp.q = q->data;
-    wp.k = k->data;
-    wp.v = v->data;
-    wp.g = (const float*)g->data;
-    wp.beta = (const float*)beta->data;
+    wp.q = at(q->data, t0, P.q.st, es);
+    wp.k = at(k->data, t0, P.k.st, es);
+    wp.v = at(v->data, t0, P.v.st, es);
+    wp.g = (const float*)at(g->data, t0, P.g.st, 4);
+    wp.beta = (const float*)at(beta->data, t0, P.b.st, 4);
     wp.q_st = P.q.st; wp.q_sh = P.q.sh;
     wp.k_st = P.k.st; wp.k_sh = P.k.sh;
     wp.v_st = P.v.st; wp.v_sh = P.v.sh;
@@ -523,32 +585,36 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
     wp.dv = P.dv;
     wp.scale = P.scale;
     wp.eps = P.eps;
-    wp.map = map;
+    wp.map = m;
     wp.im = im;
-    wp.n_items = (int32_t)(P.max_chunks * P.hk);
+    wp.n_items = (int32_t)(n_chunks * P.hk);
     wp.beta_logits = P.beta_logits ? 1 : 0;
     wp.decay_proj = P.decay_proj ? 1 : 0;
     wp.a_log = P.a_log;
     wp.a_bias = P.a_bias;
-    if ((e = gdn::launch_wy(P.bf16, P.chunk, P.dk, wp, s)) != hipSuccess)
-      return fail(GDN_ERR_HIP, "WY launch: %s", hipGetErrorString(e));
-  }
-  if (P.stages & GDN_STAGE_SCAN) {
+    const hipError_t e = gdn::launch_wy(P.bf16, P.chunk, P.dk, wp, s);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "WY launch: %s", hipGetErrorString(e));
+    return GDN_OK;
+  };
+  // The scan of the chunks `m` maps from state `h0` (null: zeros) to `h1`
+  // (null: not stored), outputs from token t0 on.
+  auto scan = [&](const gdn::ChunkMap& m, int64_t t0, const float* h0, float* h1) -> int {
     gdn::ScanParams sp{};
-    sp.out = out->data;
+    sp.out = (void*)at(out->data, t0, P.o.st, es);
     sp.o_st = P.o.st;
     sp.o_sh = P.o.sh;
-    sp.init = init ? (const float*)init->data : nullptr;
-    sp.final_state = fin ? (float*)fin->data : nullptr;
-    sp.k = k->data;
+    sp.init = h0;
+    sp.final_state = h1;
+    sp.k = at(k->data, t0, P.k.st, es);
     sp.k_st = P.k.st;
     sp.k_sh = P.k.sh;
     sp.grp = P.hv / P.hk;
     sp.hv = P.hv;
     sp.dv = P.dv;
-    sp.map = map;
+    sp.map = m;
     sp.im = im;
     const int64_t heads8 = ((int64_t)P.n_seq * P.hv + 7) / 8 * 8;
+    hipError_t e;
     if (P.split > 0) {
       sp.split = P.split;
       sp.sp_y = base + L.y;
@@ -567,6 +633,31 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
       if ((e = gdn::launch_scan(P.bf16, P.chunk, P.dk, sp, (int)blocks, s)) != hipSuccess)
         return fail(GDN_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
     }
+    return GDN_OK;
+  };
+  const float* h_init = init ? (const float*)init->data : nullptr;
+  float* h_fin = fin ? (float*)fin->data : nullptr;
+  int rc;
+  if (P.seg_chunks > 0) {
+    // Segments of whole chunks of every sequence: tokens [t0, t0 + len) of
+    // each, the state carried in f32 through the workspace (read and
+    // written in place, each element by the lane that owns it).
+    float* carry = (float*)(base + L.carry);
+    for (int64_t c0 = 0; c0 < P.chunks_per_seq; c0 += P.seg_chunks) {
+      const int64_t nc = std::min<int64_t>(P.seg_chunks, P.chunks_per_seq - c0);
+      const int64_t t0 = c0 * P.chunk;
+      const bool last = c0 + nc >= P.chunks_per_seq;
+      gdn::ChunkMap m = map;
+      m.seq_len = (int32_t)std::min<int64_t>(P.seq_len - t0, nc * P.chunk);
+      m.chunks_per_seq = (int32_t)nc;
+      if ((rc = wy(m, (int64_t)P.n_seq * nc, t0))) return rc;
+      if ((rc = scan(m, t0, c0 == 0 ? h_init : carry, last ? h_fin : carry))) return rc;
+    }
+  } else {
+    if ((P.stages & GDN_STAGE_WY) && P.max_chunks > 0 && (rc = wy(map, P.max_chunks, 0))) return rc;
+    if ((P.stages & GDN_STAGE_SCAN) && (rc = scan(map, 0, h_init, h_fin))) return rc;
+  }
+  if (P.stages & GDN_STAGE_SCAN) {
     if (P.out_gate && P.T > 0) {
       // the gated output norm over the stored rows (packed: up to cu[N])
       gdn::GateParams gp{};
@@ -606,6 +697,7 @@ void gdn_default_options(gdn_options* opts) {
   opts->gate_z = nullptr;
   opts->norm_weight = nullptr;
   opts->norm_eps = 1e-6f;
+  opts->segment_chunks = 0;
 }
 
 const char* gdn_status_string(int status) {
@@ -659,6 +751,8 @@ int gdn_get_workspace_layout(const gdn_tensor* q, const gdn_tensor* k, const gdn
   layout->split_hmid_t = L.hmid_t;
   layout->split_psi = L.psi;
   layout->split_phi = L.phi;
+  layout->segment_chunks = (int32_t)P.seg_chunks;
+  layout->segment_state = L.carry;
   return GDN_OK;
 }
 
@@ -940,6 +1034,7 @@ int gdn_prefill_graph(gdn_graph_cache* cache, const gdn_tensor* q, const gdn_ten
   append(key, &o.gate_z, sizeof o.gate_z);
   append(key, &o.norm_weight, sizeof o.norm_weight);
   append(key, &o.norm_eps, sizeof o.norm_eps);
+  append(key, &o.segment_chunks, sizeof o.segment_chunks);
   append(key, &workspace, sizeof workspace);
   append(key, &workspace_bytes, sizeof workspace_bytes);
 

@@ -8,13 +8,15 @@
 namespace gdn {
 
 // How a global chunk id maps to (sequence, first token, length).
-//   uniform: n_seq sequences of seq_len tokens each, chunk ids in sequence
-//            order (covers the single-sequence case); no table is read.
+//   uniform: n_seq sequences of seq_len tokens each, seq_stride tokens
+//            apart (seq_len, or more for a segment of longer sequences),
+//            chunk ids in sequence order; no table is read.
 //   packed:  the chunk table built on the device from cu_seqlens.
 struct ChunkMap {
   int32_t packed;        // 0 = uniform, 1 = packed
   int32_t n_seq;
-  int32_t seq_len;       // uniform mode
+  int32_t seq_len;       // uniform mode: tokens per sequence
+  int32_t seq_stride;    // uniform mode: tokens from one sequence's first token to the next's
   int32_t chunks_per_seq;// uniform mode
   const int32_t* table;      // packed: int32[max_chunks][4]
   const int32_t* chunk_off;  // packed: int32[n_seq + 1]

@@ -79,7 +79,7 @@ __device__ __forceinline__ bool chunk_info(const ChunkMap& m, int c, int C,
     if (c >= m.n_seq * m.chunks_per_seq) return false;
     seq = c / m.chunks_per_seq;
     const int j = c - seq * m.chunks_per_seq;
-    t0 = seq * m.seq_len + j * C;
+    t0 = seq * m.seq_stride + j * C;
     n = min(C, m.seq_len - j * C);
     return true;
   }
@@ -97,7 +97,7 @@ __device__ __forceinline__ void seq_range(const ChunkMap& m, int seq, int C,
   if (!m.packed) {
     c_begin = seq * m.chunks_per_seq;
     c_end = c_begin + m.chunks_per_seq;
-    tok0 = seq * m.seq_len;
+    tok0 = seq * m.seq_stride;
     tok_end = tok0 + m.seq_len;
     return;
   }
@@ -1554,8 +1554,8 @@ __global__ __launch_bounds__(kFixThreads) void scan_fix_kernel(ScanParams p) {
       const int i1 = gi * kFixChunks + jb / (C / 16), rt = jb % (C / 16);
       if (i1 >= L1) break;
       const int cc = seq * p.map.chunks_per_seq + p.split + i1;
-      const int tok = seq * p.map.seq_len + (p.split + i1) * C;
-      const int n = min(C, (seq + 1) * p.map.seq_len - tok);
+      const int tok = seq * p.map.seq_stride + (p.split + i1) * C;
+      const int n = min(C, seq * p.map.seq_stride + p.map.seq_len - tok);
       const int r = 16 * rt + (lane & 15);
       const bf16* yrow = (const bf16*)p.sp_y + (((int64_t)cc * p.hv + h) * C + r) * DK + (lane >> 4) * 8;
       bf16x8 yb[DK / 32];

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 /* Status codes. */
 #define GDN_OK 0
@@ -115,6 +115,19 @@ typedef struct gdn_options {
   const void* gate_z;
   const float* norm_weight;
   float norm_eps;
+  /* Segments (uniform sequences, all stages, one-pass scan; ignored
+   * otherwise): the sequences run as consecutive segments of whole chunks,
+   * each the WY transform and then the scan from the previous segment's
+   * state (carried in f32 in the workspace), so that a segment's
+   * intermediates stay in the GPU's 256 MiB memory-side cache between the
+   * two launches.  The results are bit-identical to one pass.  0 (default):
+   * automatic, when the intermediates of the whole call (W, Q', U~ and
+   * O_loc over all sequences and value heads) exceed 128 MiB: segments
+   * within 128 MiB each, at least 8 chunks long, the longest whose WY work
+   * items (sequences x key heads x chunks) fill whole rounds of the 512
+   * WY workgroups an MI355X holds at once, else the fewest of equal
+   * length; -1: never; n > 0: segments of n chunks.                      */
+  int32_t segment_chunks;
 } gdn_options;
 
 /*
@@ -283,6 +296,10 @@ typedef struct gdn_workspace_layout {
    *   split_phi    f32 [N][Hv][dk][dk]      second segment's M-product   */
   int32_t split_chunks;
   size_t split_y, split_hmid, split_hmid_t, split_psi, split_phi;
+  /* segments (gdn_options.segment_chunks): chunks per segment, 0 for one
+   * pass, and the state carried between segments, f32 [N][Hv][dk][dv]    */
+  int32_t segment_chunks;
+  size_t segment_state;
 } gdn_workspace_layout;
 
 /* Computes the workspace size / layout for the given tensors and options

@@ -164,6 +164,60 @@ def test_workspace_size_formula(lib):
     assert G.gdn_workspace_size(q, q, v, opts=two) == lay2.total_bytes
 
 
+def test_segment_option(lib):
+    """gdn_options.segment_chunks: validation, the automatic choice (when
+    the whole call's intermediates exceed 128 MiB: segments within 128 MiB,
+    at least 8 chunks, preferring lengths whose WY items fill whole rounds
+    of 512 workgroups), the explicit count, the cases it does not apply to,
+    and the carried state's region (f32 N x Hv x dk x dv)."""
+    o = G.gdn_default_options()
+    assert o.segment_chunks == 0
+    q = torch.empty(4096, 16, 128, dtype=torch.bfloat16)
+    with pytest.raises(G.GdnError) as e:
+        G.gdn_workspace_size(q, q, q, opts=G.options(segment_chunks=-2))
+    assert e.value.status == -3  # GDN_ERR_SHAPE
+    # 64 chunks x 16 heads x 64 KiB = 64 MiB of intermediates: one pass
+    lay = G.gdn_get_workspace_layout(q, q, q)
+    assert lay.segment_chunks == 0 and lay.segment_state == 0
+    # explicit: segments of 16 chunks and a 1 MiB state region at the end
+    lay16 = G.gdn_get_workspace_layout(q, q, q, opts=G.options(segment_chunks=16))
+    assert lay16.segment_chunks == 16 and lay16.segment_state >= lay.oloc
+    assert lay16.segment_state % 256 == 0
+    assert lay16.total_bytes == lay16.segment_state + 16 * 128 * 128 * 4
+    assert G.gdn_workspace_size(q, q, q, opts=G.options(segment_chunks=16)) == lay16.total_bytes
+    # a segment as long as the sequence is one pass
+    assert G.gdn_get_workspace_layout(q, q, q, opts=G.options(segment_chunks=64)).segment_chunks == 0
+    # 16384 tokens x 16 heads: 256 MiB of intermediates, segments of 128 chunks
+    q16 = torch.empty(16384, 16, 128, dtype=torch.bfloat16)
+    assert G.gdn_get_workspace_layout(q16, q16, q16).segment_chunks == 128
+    assert G.gdn_get_workspace_layout(q16, q16, q16, opts=G.options(segment_chunks=-1)).segment_chunks == 0
+    # 48 value heads: 3 MiB of intermediates per chunk, at most 42 chunks per
+    # segment; 16 key heads make 16 WY items per chunk, so segments of 32
+    # chunks fill one round of 512 WY workgroups
+    v48 = torch.empty(16384, 48, 128, dtype=torch.bfloat16)
+    assert G.gdn_get_workspace_layout(q16, q16, v48).segment_chunks == 32
+    # 4 key heads: 4 items per chunk; 8 value heads x 64 KiB: at most 256
+    # chunks per segment, rounds of 128 chunks -> 256
+    q4h = torch.empty(65536, 4, 128, dtype=torch.bfloat16)
+    v8h = torch.empty(65536, 8, 128, dtype=torch.bfloat16)
+    assert G.gdn_get_workspace_layout(q4h, q4h, v8h).segment_chunks == 256
+    # fewer than 8 chunks fit: one pass
+    q512 = torch.empty(16384, 64, 128, dtype=torch.bfloat16)
+    v512 = torch.empty(16384, 512, 128, dtype=torch.bfloat16)
+    assert G.gdn_get_workspace_layout(q512, q512, v512).segment_chunks == 0
+    # not for packed sequences, partial stages or the two-level scan
+    cu = torch.tensor([0, 8000, 16384], dtype=torch.int32)
+    assert G.gdn_get_workspace_layout(q16, q16, q16, cu, G.options(segment_chunks=16)).segment_chunks == 0
+    assert G.gdn_get_workspace_layout(q16, q16, q16, opts=G.options(
+        segment_chunks=16, stages=G.STAGE_WY)).segment_chunks == 0
+    assert G.gdn_get_workspace_layout(q16, q16, q16, opts=G.options(
+        segment_chunks=16, scan_split=G.SCAN_TWO_LEVEL)).segment_chunks == 0
+    # a uniform batch: the budget covers every sequence (4 x 8192 tokens x 16
+    # heads: 32 chunks per segment)
+    q4 = torch.empty(4, 8192, 16, 128, dtype=torch.bfloat16)
+    assert G.gdn_get_workspace_layout(q4, q4, q4).segment_chunks == 32
+
+
 def test_flags_option(lib):
     """Unknown flag bits are rejected by the prefill and the decode step."""
     a = base()
