@@ -270,20 +270,38 @@ def main():
     ms_step = wall * 1e3 / K
 
     # Per-kernel times for the roofline, from a second run of K steps with HIP
-    # events on the launching stream around each stage.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    for i in range(K):
-        ev[i][0].record()
-        pre()
-        ev[i][1].record()
-        scan()
-        ev[i][2].record()
-    torch.cuda.synchronize()
-    t_pre = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    t_scan = sum(e[1].elapsed_time(e[2]) for e in ev) / K
-    t_gpu = sum(e[0].elapsed_time(e[2]) for e in ev) / K
-    kernels = {"gdn_wy_kernel(+table)": t_pre, "gdn_scan_kernel": t_scan}
-    dom = max(kernels, key=kernels.get)
+    # events on the launching stream around each stage.  A segmented call
+    # (long uniform sequences) alternates the two kernels once per segment:
+    # there the events bracket whole calls, and each kernel's counted traffic
+    # per call is its per-launch figure times the segments.
+    n_seg = 1
+    if lay.segment_chunks > 0:
+        cps = -(-(w.t_total // w.n_seqs) // w.chunk)
+        n_seg = -(-cps // lay.segment_chunks)
+    if n_seg == 1:
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        for i in range(K):
+            ev[i][0].record()
+            pre()
+            ev[i][1].record()
+            scan()
+            ev[i][2].record()
+        torch.cuda.synchronize()
+        t_pre = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+        t_scan = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+        t_gpu = sum(e[0].elapsed_time(e[2]) for e in ev) / K
+        kernels = {"gdn_wy_kernel(+table)": t_pre, "gdn_scan_kernel": t_scan}
+        dom = max(kernels, key=kernels.get)
+    else:
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            ev[i][0].record()
+            full()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        t_gpu = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+        kernels = {"gdn_wy_kernel(+table)": None, "gdn_scan_kernel": None}
+        dom = None
     nbytes = algorithmic_bytes(w)
     nflops = algorithmic_flops(w)
     # The roofline object covers the hot path's launches as one unit: the
@@ -296,10 +314,13 @@ def main():
     counted = []
     for k, t in kernels.items():
         tb = load_traffic(args.workload, k)
+        if tb is not None:
+            tb *= n_seg
         counted.append(tb)
-        per_kernel[k] = {"ms": round(t, 5), "counted_bytes": tb,
-                         "counted_GBs": None if tb is None else tb / (t * 1e-3) / 1e9,
-                         "counted_frac": None if tb is None else tb / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        timed = t is not None and tb is not None
+        per_kernel[k] = {"ms": None if t is None else round(t, 5), "counted_bytes": tb,
+                         "counted_GBs": tb / (t * 1e-3) / 1e9 if timed else None,
+                         "counted_frac": tb / (t * 1e-3) / 1e9 / HBM_PEAK_GBS if timed else None}
     traffic = None if any(x is None for x in counted) else int(sum(counted))
     bf16 = w.q.dtype == torch.bfloat16
     mfma_peak = BF16_MFMA_PEAK_TFLOPS if bf16 else F32_MFMA_PEAK_TFLOPS
@@ -321,7 +342,8 @@ def main():
                    "dk": int(w.q.shape[2]), "dv": int(w.v.shape[2]), "chunk": w.chunk,
                    "seed": 0, "parallelism": "single GPU",
                    "scan": (f"two-level (split at chunk {lay.split_chunks})" if lay.split_chunks
-                            else "one pass")},
+                            else "one pass"),
+                   "segments": n_seg},
         "roofline": {"bound": "hbm", "kernel": "prefill (wy_kernel + scan_kernel launches)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
@@ -333,7 +355,7 @@ def main():
                           "mfma_TFLOPs": nflops / (ms_step * 1e-3) / 1e12,
                           "mfma_frac": nflops / (ms_step * 1e-3) / 1e12 / mfma_peak,
                           "algorithmic_flops": nflops},
-        "kernel_ms": {k: round(v, 5) for k, v in kernels.items()},
+        "kernel_ms": {k: (None if v is None else round(v, 5)) for k, v in kernels.items()},
         "gpu_event_ms_per_step": t_gpu,
         "sclk_mhz_under_load": sclk_under_load(full, torch),
     }
