@@ -21,7 +21,7 @@ STATUS_NAMES = {0: "GDN_OK", -1: "GDN_ERR_NULL_ARG", -2: "GDN_ERR_DTYPE",
                 -7: "GDN_ERR_HIP", -8: "GDN_ERR_INPUT"}
 STAGE_TABLE, STAGE_WY, STAGE_SCAN, STAGE_ALL = 1, 2, 4, 7
 SCAN_AUTO, SCAN_ONE_PASS, SCAN_TWO_LEVEL = 0, 1, 2
-FLAG_BETA_LOGITS, FLAG_DECAY_PROJ, FLAG_OUTPUT_GATE = 1, 2, 4
+FLAG_BETA_LOGITS, FLAG_DECAY_PROJ, FLAG_OUTPUT_GATE, FLAG_QKV_SILU = 1, 2, 4, 8
 EXPORTED = ("gdn_abi_version", "gdn_default_options", "gdn_prefill",
             "gdn_prefill_ex", "gdn_prefill_noalloc", "gdn_workspace_size", "gdn_get_workspace_layout",
             "gdn_decode", "gdn_output_gate", "gdn_check_cu_seqlens", "gdn_graph_cache_create", "gdn_graph_cache_destroy",
@@ -53,7 +53,8 @@ class GdnWorkspaceLayout(ctypes.Structure):
         ("split_chunks", ctypes.c_int32)] + [
         (n, ctypes.c_size_t) for n in ("split_y", "split_hmid", "split_hmid_t", "split_psi",
                                        "split_phi")] + [
-        ("segment_chunks", ctypes.c_int32), ("segment_state", ctypes.c_size_t)]
+        ("segment_chunks", ctypes.c_int32), ("segment_state", ctypes.c_size_t),
+        ("k_act", ctypes.c_size_t)]
 
 
 class GdnError(RuntimeError):
@@ -156,9 +157,11 @@ def options(chunk: int = 0, scale: float = 1.0, l2_eps: float = 1e-6,
             decay_proj: bool = False, decay_a_log: Optional[torch.Tensor] = None,
             decay_bias: Optional[torch.Tensor] = None,
             gate_z: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
-            norm_eps: float = 1e-6, segment_chunks: int = 0) -> GdnOptions:
+            norm_eps: float = 1e-6, segment_chunks: int = 0,
+            qkv_silu: bool = False) -> GdnOptions:
     """scan_split: SCAN_AUTO (0), SCAN_ONE_PASS (1) or SCAN_TWO_LEVEL (2);
     segment_chunks: 0 automatic, -1 never, n > 0 segments of n chunks;
+    qkv_silu: q, k, v hold pre-activation values and the kernels take silu;
     beta_logits: beta holds raw projections b and the kernels use sigmoid(b);
     decay_proj: g holds the decay gate's raw projection a, with per value head
     f32 tensors decay_a_log and decay_bias (None: zeros);
@@ -168,7 +171,8 @@ def options(chunk: int = 0, scale: float = 1.0, l2_eps: float = 1e-6,
     returned object and must stay alive while calls using it may run."""
     o = GdnOptions()
     o.chunk, o.scale, o.l2_eps, o.stages, o.scan_split = chunk, scale, l2_eps, stages, scan_split
-    o.flags = (FLAG_BETA_LOGITS if beta_logits else 0) | (FLAG_DECAY_PROJ if decay_proj else 0)
+    o.flags = ((FLAG_BETA_LOGITS if beta_logits else 0) | (FLAG_DECAY_PROJ if decay_proj else 0)
+               | (FLAG_QKV_SILU if qkv_silu else 0))
     o.decay_a_log = _dev_ptr(decay_a_log, "decay_a_log")
     o.decay_bias = _dev_ptr(decay_bias, "decay_bias")
     o.norm_weight = _dev_ptr(norm_weight, "norm_weight")

@@ -128,6 +128,7 @@ struct Problem {
   bool beta_logits = false;
   bool decay_proj = false;   // GDN_FLAG_DECAY_PROJ
   bool out_gate = false;     // GDN_FLAG_OUTPUT_GATE
+  bool qkv_silu = false;     // GDN_FLAG_QKV_SILU
   const float* a_log = nullptr;
   const float* a_bias = nullptr;
   const void* gate_z = nullptr;
@@ -138,7 +139,8 @@ struct Problem {
   int64_t seg_chunks = 0;    // chunks per segment (0: one pass over all chunks)
 };
 
-constexpr uint32_t kKnownFlags = GDN_FLAG_BETA_LOGITS | GDN_FLAG_DECAY_PROJ | GDN_FLAG_OUTPUT_GATE;
+constexpr uint32_t kKnownFlags =
+    GDN_FLAG_BETA_LOGITS | GDN_FLAG_DECAY_PROJ | GDN_FLAG_OUTPUT_GATE | GDN_FLAG_QKV_SILU;
 
 // Checks of the gate fields of gdn_options that need no shapes.
 int check_gate_options(const gdn_options& o) {
@@ -152,7 +154,7 @@ int check_gate_options(const gdn_options& o) {
 struct Layout {
   size_t table = 0, chunk_off = 0, seq_start = 0, decay = 0;
   size_t w = 0, qp = 0, ut = 0, oloc = 0;
-  size_t y = 0, hmid = 0, hmid_t = 0, psi = 0, phi = 0, carry = 0, total = 0;
+  size_t y = 0, hmid = 0, hmid_t = 0, psi = 0, phi = 0, carry = 0, kact = 0, total = 0;
 };
 
 // Bytes of the intermediates of one (chunk, value head): W, Q', U~, O_loc
@@ -189,6 +191,7 @@ Layout make_layout(const Problem& P) {
     L.phi = take(heads * P.dk * P.dk * 4);
   }
   if (P.seg_chunks > 0) L.carry = take((size_t)P.n_seq * P.hv * P.dk * P.dv * 4);
+  if (P.qkv_silu) L.kact = take((size_t)P.T * P.hk * P.dk * es);
   L.total = off;
   return L;
 }
@@ -216,6 +219,7 @@ int resolve_options(const gdn_options* opts, bool bf16, Problem* P) {
   P->beta_logits = (o.flags & GDN_FLAG_BETA_LOGITS) != 0;
   P->decay_proj = (o.flags & GDN_FLAG_DECAY_PROJ) != 0;
   P->out_gate = (o.flags & GDN_FLAG_OUTPUT_GATE) != 0;
+  P->qkv_silu = (o.flags & GDN_FLAG_QKV_SILU) != 0;
   P->a_log = P->decay_proj ? o.decay_a_log : nullptr;
   P->a_bias = P->decay_proj ? o.decay_bias : nullptr;
   P->gate_z = P->out_gate ? o.gate_z : nullptr;
@@ -484,6 +488,7 @@ int validate_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* 
   d->scale = o.scale; d->eps = o.l2_eps;
   d->beta_logits = (o.flags & GDN_FLAG_BETA_LOGITS) ? 1 : 0;
   d->decay_proj = (o.flags & GDN_FLAG_DECAY_PROJ) ? 1 : 0;
+  d->qkv_silu = (o.flags & GDN_FLAG_QKV_SILU) ? 1 : 0;
   d->a_log = d->decay_proj ? o.decay_a_log : nullptr;
   d->a_bias = d->decay_proj ? o.decay_bias : nullptr;
   *bf16 = q->dtype == GDN_DTYPE_BF16;
@@ -592,6 +597,8 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
     wp.decay_proj = P.decay_proj ? 1 : 0;
     wp.a_log = P.a_log;
     wp.a_bias = P.a_bias;
+    wp.qkv_silu = P.qkv_silu ? 1 : 0;
+    wp.k_act = P.qkv_silu ? base + L.kact + t0 * P.hk * P.dk * (int64_t)es : nullptr;
     const hipError_t e = gdn::launch_wy(P.bf16, P.chunk, P.dk, wp, s);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "WY launch: %s", hipGetErrorString(e));
     return GDN_OK;
@@ -605,9 +612,15 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
     sp.o_sh = P.o.sh;
     sp.init = h0;
     sp.final_state = h1;
-    sp.k = at(k->data, t0, P.k.st, es);
-    sp.k_st = P.k.st;
-    sp.k_sh = P.k.sh;
+    if (P.qkv_silu) {  // the WY kernel's activated key rows, [T][Hk][dk] contiguous
+      sp.k = base + L.kact + t0 * P.hk * P.dk * (int64_t)es;
+      sp.k_st = (int64_t)P.hk * P.dk;
+      sp.k_sh = P.dk;
+    } else {
+      sp.k = at(k->data, t0, P.k.st, es);
+      sp.k_st = P.k.st;
+      sp.k_sh = P.k.sh;
+    }
     sp.grp = P.hv / P.hk;
     sp.hv = P.hv;
     sp.dv = P.dv;
@@ -753,6 +766,7 @@ int gdn_get_workspace_layout(const gdn_tensor* q, const gdn_tensor* k, const gdn
   layout->split_phi = L.phi;
   layout->segment_chunks = (int32_t)P.seg_chunks;
   layout->segment_state = L.carry;
+  layout->k_act = L.kact;
   return GDN_OK;
 }
 

@@ -378,6 +378,14 @@ __device__ __forceinline__ float decay_gate(float a, const float* a_log, const f
   return -expf(a_log ? a_log[h] : 0.f) * sp;
 }
 
+// The activation before the prefill (GDN_FLAG_QKV_SILU): silu(x) = x / (1 +
+// e^-x) in fp32, rounded to the input type TI as a separate activation pass
+// would store it.
+template <typename TI>
+__device__ __forceinline__ float qkv_act(float x) {
+  return to_float(from_float<TI>(x / (1.f + expf(-x))));
+}
+
 }  // namespace gdn
 
 namespace gdn {

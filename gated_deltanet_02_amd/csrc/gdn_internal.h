@@ -59,6 +59,8 @@ struct WyParams {
   int32_t decay_proj;   // 1: g holds the projection a, the kernel takes decay_gate(a)
   const float* a_log;   // [Hv] or null (zeros), with decay_proj
   const float* a_bias;  // [Hv] or null (zeros), with decay_proj
+  int32_t qkv_silu;     // 1: q, k, v hold pre-activation values, the kernel takes silu
+  void* k_act;          // with qkv_silu: activated key rows out, [T][Hk][dk] contiguous
   float scale, eps;
   ChunkMap map;
   Intermediates im;
@@ -103,6 +105,7 @@ struct DecodeParams {
   int32_t decay_proj;    // 1: g holds the projection a, the kernel takes decay_gate(a)
   const float* a_log;    // [Hv] or null (zeros), with decay_proj
   const float* a_bias;   // [Hv] or null (zeros), with decay_proj
+  int32_t qkv_silu;      // 1: q, k, v hold pre-activation values, the kernel takes silu
   float scale, eps;
 };
 

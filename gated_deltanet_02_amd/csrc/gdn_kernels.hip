@@ -458,6 +458,31 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     }
     __syncthreads();
   }
+  if (p.qkv_silu) {
+    // the activation on the q and k rows in place (elementwise, so the
+    // granule swizzle does not matter; silu(0) = 0 keeps padded rows zero),
+    // then the chunk's activated key rows out for the scan, unswizzled, in
+    // the token layout of a contiguous [T][Hk][dk] tensor
+    constexpr int GE = 16 / (int)sizeof(TI), GPR = DK / GE;
+    for (int idx = tid; idx < 2 * C * GPR; idx += NT) {
+      const int m = idx / (C * GPR), r = (idx / GPR) % C, g = idx % GPR;
+      TI* e = (m ? sKV : sQ) + r * LK + g * GE;
+      const uint4 raw = ld16(e);
+      TI x[GE];
+      __builtin_memcpy(x, &raw, 16);
+#pragma unroll
+      for (int j = 0; j < GE; ++j) x[j] = from_float<TI>(qkv_act<TI>(to_float(x[j])));
+      uint4 out;
+      __builtin_memcpy(&out, x, 16);
+      st16(e, out);
+    }
+    __syncthreads();
+    TI* ka = (TI*)p.k_act + ((int64_t)t0 * p.hk + kh) * DK;
+    for (int idx = tid; idx < n * GPR; idx += NT) {
+      const int r = idx / GPR, g = idx % GPR;
+      st16(ka + (int64_t)r * p.hk * DK + ((g ^ (r & SWK)) * GE), ld16(sKV + r * LK + g * GE));
+    }
+  }
 
   uint4 vreg[NVG];
   float gv = 0.f, bv = 0.f;
@@ -495,7 +520,15 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       const int idx = tid_s + i * NT;
       if (idx < C * GPRV) {
         const int r = idx >> LGV, gc = idx & (GPRV - 1);
-        st16(sVr + r * LV + swz<TI, SWV>(r, gc * GR), vreg[i]);
+        uint4 vv = vreg[i];
+        if (p.qkv_silu) {
+          TI x[GR];
+          __builtin_memcpy(x, &vv, 16);
+#pragma unroll
+          for (int j = 0; j < GR; ++j) x[j] = from_float<TI>(qkv_act<TI>(to_float(x[j])));
+          __builtin_memcpy(&vv, x, 16);
+        }
+        st16(sVr + r * LV + swz<TI, SWV>(r, gc * GR), vv);
       }
     }
   };
@@ -1663,6 +1696,10 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(Decod
   for (int d = tid; d < DK; d += NT) {
     sq[d] = to_float(qr[d]);
     sk[d] = to_float(kr[d]);
+    if (p.qkv_silu) {
+      sq[d] = qkv_act<TI>(sq[d]);
+      sk[d] = qkv_act<TI>(sk[d]);
+    }
   }
   __syncthreads();
   if (tid < 64 * (NT >= 128 ? 2 : 1)) {
@@ -1683,7 +1720,11 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(Decod
   float beta = p.beta[(int64_t)i * p.b_st + (int64_t)h * p.b_sh];
   if (p.beta_logits) beta = 1.f / (1.f + __expf(-beta));
   const float alpha = expf(g);
-  const f32x4 vj = load4<TI>((const TI*)p.v + (int64_t)i * p.v_st + (int64_t)h * p.v_sh + c0);
+  f32x4 vj = load4<TI>((const TI*)p.v + (int64_t)i * p.v_st + (int64_t)h * p.v_sh + c0);
+  if (p.qkv_silu) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vj[e] = qkv_act<TI>(vj[e]);
+  }
 
   // (k^T H)_j over this band, with the raw k (the norm is applied below)
   f32x4 part = zero4();

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 /* Status codes. */
 #define GDN_OK 0
@@ -165,6 +165,23 @@ typedef struct gdn_options {
  */
 #define GDN_FLAG_DECAY_PROJ 2u
 #define GDN_FLAG_OUTPUT_GATE 4u
+
+/*
+ * GDN_FLAG_QKV_SILU: q, k and v hold the values before the activation that
+ * precedes the layer, and the kernels (prefill and decode) take
+ *     silu(x) = x / (1 + e^-x)
+ * elementwise in fp32 as they load them, each result rounded to the input
+ * dtype as a separate activation pass would store it (so the L2 norms of q
+ * and k are taken of the activated rows).  The same reading as the gates
+ * above: the pages run "fused norm, activation" operations around the
+ * chunked Gated DeltaNet and name SiLU as the activation they check
+ * ("Open-Jev-27B-v1.1 native text worker", section "Validation and
+ * optimization scope"); they name no convolution, so none is applied.  In
+ * the prefill the WY kernel writes the activated key rows to the workspace
+ * (the `k_act` region, laid out as a contiguous [T][Hk][dk] tensor of the
+ * input dtype) for the scan.
+ */
+#define GDN_FLAG_QKV_SILU 8u
 
 /*
  * The state scan's schedule.  Each chunk maps its incoming state affinely
@@ -300,6 +317,9 @@ typedef struct gdn_workspace_layout {
    * pass, and the state carried between segments, f32 [N][Hv][dk][dv]    */
   int32_t segment_chunks;
   size_t segment_state;
+  /* GDN_FLAG_QKV_SILU: the activated key rows, a contiguous [T][Hk][dk]
+   * tensor of the input dtype (0 without the flag)                       */
+  size_t k_act;
 } gdn_workspace_layout;
 
 /* Computes the workspace size / layout for the given tensors and options

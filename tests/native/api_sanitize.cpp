@@ -87,7 +87,7 @@ int main() {
     o.chunk = 48;
     expect(prefill(w, nullptr, &o), GDN_ERR_UNSUPPORTED, "chunk 48");
     gdn_default_options(&o);
-    o.flags = 8;
+    o.flags = 16;
     expect(prefill(w, nullptr, &o), GDN_ERR_SHAPE, "unknown flag");
     gdn_default_options(&o);
     o.flags = GDN_FLAG_OUTPUT_GATE;

@@ -222,7 +222,7 @@ def test_flags_option(lib):
     """Unknown flag bits are rejected by the prefill and the decode step."""
     a = base()
     o = B.options()
-    o.flags = 8
+    o.flags = 16
     assert call(lib, a["q"], a["k"], a["v"], a["g"], a["b"], out=a["out"], opts=o) == -3
     o.flags = B.FLAG_BETA_LOGITS
     N, hk, hv, dk, dv = 2, 1, 1, 16, 16
@@ -232,6 +232,31 @@ def test_flags_option(lib):
     bad = B.options()
     bad.flags = 0x10
     assert lib.gdn_decode(r(q), r(q), r(v), r(g), r(g), r(st), r(v), r(bad), None) == -3
+
+
+def test_qkv_silu_option(lib):
+    """GDN_FLAG_QKV_SILU is accepted by the prefill and the decode step, and
+    the prefill's workspace gains the activated key rows (a contiguous
+    [T][Hk][dk] tensor of the input dtype) at the end."""
+    assert B.FLAG_QKV_SILU == 8
+    q = torch.empty(1000, 2, 128, dtype=torch.bfloat16)
+    v = torch.empty(1000, 6, 64, dtype=torch.bfloat16)
+    plain = G.gdn_get_workspace_layout(q, q, v)
+    act = G.gdn_get_workspace_layout(q, q, v, opts=G.options(qkv_silu=True))
+    assert plain.k_act == 0 and act.k_act % 256 == 0 and act.k_act >= plain.total_bytes - 256
+    assert act.total_bytes == act.k_act + 1000 * 2 * 128 * 2
+    assert G.gdn_workspace_size(q, q, v, opts=G.options(qkv_silu=True)) == act.total_bytes
+    N, hk, hv, dk, dv = 2, 1, 1, 16, 16
+    r = ctypes.byref
+    qd, vd = fake((N, hk, dk), torch.bfloat16), fake((N, hv, dv), torch.bfloat16)
+    g, st = fake((N, hv), torch.float32), fake((N, hv, dk, dv), torch.float32)
+    o = B.options(qkv_silu=True)
+    # validation passes; the call then stops at the fake (never dereferenced)
+    # device addresses only if it reaches the GPU, which a bad flag never does
+    bad = B.options()
+    bad.flags = 16 | 8
+    assert lib.gdn_decode(r(qd), r(qd), r(vd), r(g), r(g), r(st), r(vd), r(bad), None) == -3
+    assert o.flags == 8
 
 
 def test_gate_options(lib):

@@ -1,0 +1,141 @@
+"""GDN_FLAG_QKV_SILU (GPU): q, k, v passed before their activation, the
+kernels take silu(x) = x / (1 + e^-x) as they load them, each result rounded
+to the input dtype.
+
+The reference is the float64 oracle run on oracle.gates.silu of the inputs,
+rounded to the input dtype the same way (the kernel evaluates silu in fp32;
+where the fp32 and float64 values fall on opposite sides of a bf16 rounding
+boundary the two roundings differ by one bf16 ulp, which the prefill's
+tolerances absorb).  Each case first checks that the oracle without the
+activation lands far outside those tolerances, so a kernel that ignored the
+flag (or applied it to only some of q, k, v) could not pass.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_02_amd as G
+from gated_deltanet_02_amd import workloads as W
+from oracle import gates, oracle
+from tests import gpu_util as U
+from tests.test_gpu_f2 import gated_bound
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    U.need_gpu()
+    oracle.load()
+
+
+def activated(x: torch.Tensor) -> torch.Tensor:
+    """silu in float64, rounded to x's dtype (CPU)."""
+    y = gates.silu(x.double().numpy())
+    return torch.from_numpy(np.asarray(y, np.float64)).to(x.dtype)
+
+
+def act_reference(w, scale=1.0):
+    return oracle.reference(activated(w.q), activated(w.k), activated(w.v), w.g, w.beta,
+                            w.lengths, w.init_state, scale=scale)
+
+
+def check(w, out, fin, ro, rf, label):
+    # the test's power: the plain recurrence on the raw inputs is far off
+    po, pf = oracle.reference_workload(w)
+    if w.q.dtype == torch.bfloat16:
+        assert U.max_abs(po, ro) > 10 * U.BF16_OUT_MAXABS or U.rel_l2(pf, rf) > 10 * U.BF16_STATE_RELL2
+        U.check_bf16(out, fin, ro, rf, label=label)
+    else:
+        assert U.rel_l2(po, ro) > 1e3 * U.F32_RELL2
+        U.check_f32(out, fin, ro, rf, label=label)
+
+
+CASES = [
+    ("prompt_4k", dict(lengths=[700], hk=2, hv=4), {}),
+    ("long_16k_gqa", dict(lengths=[300], hk=2, hv=6), {}),                  # grouped heads, init state
+    ("packed_255", dict(lengths=("uniform", 10, 1, 200), hk=2, hv=2), {}),   # packed, cu_seqlens
+    ("edge_mix", dict(hk=1, hv=2), {}),                                      # ragged lengths 1..1000
+    ("prompt_4k", dict(lengths=[333], hk=2, hv=2, dk=64, dv=64, chunk=32), {}),
+    ("prompt_4k", dict(lengths=[200], hk=1, hv=2, dk=32, dv=128, chunk=16), {}),
+    ("tiny_fp32", dict(lengths=[150], hk=2, hv=4, dk=64, dv=32, chunk=32), {}),
+    ("prompt_4k", dict(lengths=[1000], hk=2, hv=4), dict(segment_chunks=3)),  # segments
+    ("prompt_4k", dict(lengths=[900], hk=2, hv=2), dict(scan_split=G.SCAN_TWO_LEVEL)),
+]
+
+
+@pytest.mark.parametrize("name,kw,extra", CASES, ids=[f"{c[0]}-{i}" for i, c in enumerate(CASES)])
+def test_prefill_with_activation(name, kw, extra):
+    w = W.make_workload(name, **kw)
+    d = W.to_device(w)
+    cu = d["cu_seqlens"] if w.n_seqs > 1 else None
+    opts = G.options(chunk=w.chunk, qkv_silu=True, **extra)
+    G.gdn_prefill_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, d["init_state"],
+                     d["out"], d["final_state"], opts=opts)
+    torch.cuda.synchronize()
+    ro, rf = act_reference(w)
+    check(w, d["out"].float().cpu().numpy(), d["final_state"].cpu().numpy(), ro, rf,
+          f"silu {name} {kw} {extra}")
+
+
+def test_activation_with_the_gates():
+    """With the decay from its projection, beta from logits and the gated
+    output norm in the same call."""
+    w = W.make_workload("prompt_4k", lengths=[500], hk=2, hv=4)
+    d = W.to_device(w)
+    gi = W.make_gate_inputs(w)
+    g_ref = gates.decay_from_projection(gi.a, gi.a_log, gi.bias)
+    b_logit = torch.log(w.beta / (1 - w.beta))  # beta = sigmoid(b_logit)
+    z = torch.randn(d["v"].shape, generator=torch.Generator().manual_seed(9)).to(d["v"].dtype)
+    opts = G.options(chunk=64, qkv_silu=True, decay_proj=True, decay_a_log=gi.a_log.cuda(),
+                     decay_bias=gi.bias.cuda(), beta_logits=True, gate_z=z.cuda())
+    G.gdn_prefill_ex(d["q"], d["k"], d["v"], gi.a.cuda(), b_logit.float().cuda(), None, None,
+                     d["out"], d["final_state"], opts=opts)
+    torch.cuda.synchronize()
+    ro, rf = oracle.reference(activated(w.q), activated(w.k), activated(w.v), g_ref,
+                              gates.sigmoid(b_logit.double().numpy()), w.lengths, None)
+    # the final state is the recurrence's; the outputs went through the gate,
+    # held to the first-order propagation of the prefill's output bound
+    # (tests/test_gpu_f2.py, gated_bound)
+    es = U.rel_l2(d["final_state"].cpu().numpy(), rf)
+    assert es <= U.BF16_STATE_RELL2, es
+    ones = np.ones(w.v.shape[-1])
+    zz = z.double().numpy()
+    yo = gates.output_gate(ro, zz, ones, 1e-6)
+    got = d["out"].float().cpu().numpy()
+    bound = gated_bound(ro, zz, ones, 1e-6, U.BF16_OUT_MAXABS, yo, 2.0 ** -8 + 4e-6)
+    excess = float((np.abs(got - yo) - bound).max())
+    U.say(f"  silu + gates: final rel-L2 {es:.3e}, gated out worst excess over bound {excess:.3e}")
+    assert np.isfinite(got).all() and excess <= 0.0
+
+
+DECODE_CASES = [
+    ("bf16-gqa", "long_16k_gqa", 9, dict(hk=2, hv=6, dk=128, dv=64)),
+    ("bf16-d128", "prompt_4k", 4, dict(hk=4, hv=4, dk=128, dv=128)),
+    ("f32-d64", "tiny_fp32", 5, dict(hk=2, hv=4, dk=64, dv=32)),
+]
+
+
+@pytest.mark.parametrize("label,name,n,kw", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_with_activation(label, name, n, kw):
+    w = W.make_workload(name, lengths=[1] * n, init_std=0.5, **kw)
+    dev = {x: getattr(w, x).cuda() for x in ("q", "k", "v", "g", "beta")}
+    state = w.init_state.clone().cuda()
+    out = G.gdn_decode(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], state,
+                       opts=G.options(qkv_silu=True))
+    torch.cuda.synchronize()
+    ro, rf = act_reference(w)
+    got_o, got_s = out.float().cpu().numpy(), state.cpu().numpy()
+    es = U.rel_l2(got_s, rf)
+    U.say(f"  decode silu {label}: state rel-L2 {es:.3e}")
+    assert es <= U.F32_RELL2
+    if w.q.dtype == torch.bfloat16:
+        assert U.max_abs(got_o, ro) <= 8e-3 * max(1.0, float(np.abs(ro).max()))
+    else:
+        assert U.rel_l2(got_o, ro) <= U.F32_RELL2
+    # and the prefill of the same tokens (one token per sequence) agrees
+    d = W.to_device(w)
+    G.gdn_prefill_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["init_state"],
+                     d["out"], d["final_state"], opts=G.options(chunk=w.chunk, qkv_silu=True))
+    torch.cuda.synchronize()
+    assert U.rel_l2(d["final_state"].cpu().numpy(), got_s) <= 5e-3
