@@ -139,3 +139,26 @@ def test_decode_with_activation(label, name, n, kw):
                      d["out"], d["final_state"], opts=G.options(chunk=w.chunk, qkv_silu=True))
     torch.cuda.synchronize()
     assert U.rel_l2(d["final_state"].cpu().numpy(), got_s) <= 5e-3
+
+
+def test_activation_in_graph_replays():
+    """Captured calls with the activation replay bit for bit the eager call."""
+    w = W.make_workload("long_16k_gqa", lengths=[300], hk=2, hv=4)
+    d = W.to_device(w)
+    opts = G.options(chunk=64, qkv_silu=True)
+    eo, ef = torch.empty_like(d["out"]), torch.empty_like(d["final_state"])
+    G.gdn_prefill_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], None, d["init_state"], eo, ef,
+                     opts=opts)
+    torch.cuda.synchronize()
+    ws = G.alloc_workspace(d["q"], d["k"], d["v"], None, opts)
+    cache = G.GraphCache(capacity=2)
+    for it in range(3):
+        d["out"].fill_(7.0)
+        d["final_state"].fill_(7.0)
+        cache.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], None, d["init_state"],
+                      d["out"], d["final_state"], opts=opts, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(d["out"], eo) and torch.equal(d["final_state"], ef), f"replay {it}"
+    st = cache.stats()
+    assert st["misses"] == 1 and st["hits"] == 2 and st["fallbacks"] == 0
+    cache.close()
