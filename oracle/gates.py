@@ -30,9 +30,21 @@ plainest one the rest supports:
   The library applies it to the outputs as the prefill stores them (rounded
   to the output type) and rounds y once.
 
+* The short convolution before the activation.  Each channel of q, k and v
+  (one column of the [T, H * d] token rows) passes through a causal
+  depthwise convolution of width W along the tokens of its own sequence:
+
+      y[t, c] = sum_{j=0}^{W-1} w[c, j] * e[t + j, c],
+
+  where e is the sequence's W - 1 history rows (the raw rows before its
+  first token; zeros for a fresh sequence) followed by its own rows, so the
+  last tap w[c, W-1] multiplies the current token.  The state a later call
+  continues from is the last W - 1 rows of e (raw values, not convolved).
+
 Pins: ``tests/test_oracle_gates.py`` (closed forms, hand-derived values in
-``tests/golden/gates_hand.json``, invariants) and planted mutations of this
-file that each break at least one of them.
+``tests/golden/gates_hand.json``, invariants, numpy's convolution for the
+short convolution) and planted mutations of this file that each break at
+least one of them.
 """
 from __future__ import annotations
 
@@ -76,3 +88,27 @@ def output_gate(o, z, w, eps):
     w = _f64(w)
     ms = np.mean(o * o, axis=-1, keepdims=True)
     return o / np.sqrt(ms + eps) * w * silu(z)
+
+
+def short_conv(x, w, lengths, state=None):
+    """Causal depthwise convolution along the tokens of each sequence.
+
+    x [T, D]: the rows of the sequences back to back, lengths[n] rows each;
+    w [D, W]; state [N, W - 1, D]: the raw rows before each sequence (None:
+    zeros).  Returns (y [T, D], final [N, W - 1, D]).
+    """
+    x = _f64(x)
+    w = _f64(w)
+    D, W = w.shape
+    y = np.zeros(x.shape)
+    final = np.zeros((len(lengths), W - 1, D))
+    b = 0
+    for n, L in enumerate(lengths):
+        hist = np.zeros((W - 1, D)) if state is None else _f64(state[n])
+        e = np.concatenate([hist, x[b:b + L]], axis=0)
+        for t in range(L):
+            for j in range(W):
+                y[b + t] += w[:, j] * e[t + j]
+        final[n] = e[L:L + W - 1]
+        b += L
+    return y, final

@@ -7,9 +7,15 @@ What pins them, besides the functions themselves:
   limits; a one-hot row's norm sqrt(d_v);
 * invariants: g <= 0; the per-head parameters follow the head axis; a row's
   norm ignores the other rows and is unchanged by scaling the row (eps = 0);
-  the output is odd in o.
+  the output is odd in o;
+* the short convolution: numpy's own convolution of each channel's history
+  and rows; one-hot taps (the current row, a shift by W - 1 rows into the
+  history); a constant input's partial tap sums; a sequence run in two
+  calls, the state carried, equal to one call; packed sequences that do not
+  see each other.
 Each planted mutation of oracle/gates.py (a dropped factor, a wrong sign, a
-swapped axis, an activation exchanged) breaks at least one pin.
+swapped axis, an activation exchanged, taps reversed, history lost or taken
+from the previous sequence) breaks at least one pin.
 """
 import json
 import math
@@ -34,6 +40,11 @@ def pin_golden(m):
     for c in GOLDEN["output_gate"]:
         y = m.output_gate(c["o"], c["z"], c["w"], c["eps"])
         assert np.abs(y - np.asarray(c["y"])).max() <= tol, c["derivation"]
+    for c in GOLDEN["short_conv"]:
+        st = None if c["state"] is None else np.asarray(c["state"])
+        y, fin = m.short_conv(np.asarray(c["x"]), np.asarray(c["w"]), c["lengths"], st)
+        assert np.abs(y - np.asarray(c["y"])).max() <= tol, c["derivation"]
+        assert np.abs(fin - np.asarray(c["final"])).max() <= tol, c["derivation"]
 
 
 def pin_softplus(m):
@@ -102,7 +113,94 @@ def pin_output_gate(m):
     assert np.allclose(yo, 0.5 * 40.0, rtol=1e-12)
 
 
-PINS = [pin_golden, pin_softplus, pin_decay, pin_silu, pin_output_gate]
+def _conv_case(rng, lengths, D, W, with_state=True):
+    x = rng.normal(0, 1, (sum(lengths), D))
+    w = rng.normal(0, 1, (D, W))
+    st = rng.normal(0, 1, (len(lengths), W - 1, D)) if with_state else None
+    return x, w, st
+
+
+def pin_conv_numpy(m):
+    """Each channel against numpy's convolution of its history and rows
+    (np.convolve flips its second argument, so the taps go in reversed)."""
+    rng = np.random.default_rng(7)
+    for W in (1, 2, 3, 4):
+        lengths = [5, 0, 1, 2, 9, 3]
+        for with_state in (True, False):
+            x, w, st = _conv_case(rng, lengths, 3, W, with_state)
+            y, fin = m.short_conv(x, w, lengths, st)
+            assert y.shape == x.shape and fin.shape == (len(lengths), W - 1, 3)
+            b = 0
+            for n, L in enumerate(lengths):
+                hist = st[n] if with_state else np.zeros((W - 1, 3))
+                e = np.concatenate([hist, x[b:b + L]], axis=0)
+                for c in range(3 if L > 0 else 0):  # (np.convolve takes no empty input)
+                    want = np.convolve(e[:, c], w[c, ::-1], mode="valid")
+                    assert np.allclose(y[b:b + L, c], want, rtol=1e-13, atol=1e-13)
+                if W > 1:
+                    assert np.array_equal(fin[n], e[len(e) - (W - 1):])
+                b += L
+
+
+def pin_conv_taps(m):
+    """One-hot taps: the last tap passes the current row, the first one the
+    row W - 1 back (the history for the first W - 1 rows)."""
+    rng = np.random.default_rng(8)
+    lengths = [6, 2]
+    x, _, st = _conv_case(rng, lengths, 4, 4)
+    last = np.zeros((4, 4))
+    last[:, 3] = 1.0
+    y, _ = m.short_conv(x, last, lengths, st)
+    assert np.array_equal(y, x)
+    first = np.zeros((4, 4))
+    first[:, 0] = 1.0
+    y, fin = m.short_conv(x, first, lengths, st)
+    assert np.array_equal(y[3:6], x[0:3]) and np.array_equal(y[0:3], st[0])
+    assert np.array_equal(y[6:8], st[1][0:2])
+    assert np.array_equal(fin[0], x[3:6]) and np.array_equal(fin[1], np.concatenate([st[1][2:], x[6:8]]))
+    # per-channel taps: channel c keeps only its own weights
+    mixed = np.zeros((4, 4))
+    for c in range(4):
+        mixed[c, c] = 1.0
+    y, _ = m.short_conv(x, mixed, [6], None)
+    for c in range(4):
+        shift = 3 - c
+        assert np.array_equal(y[shift:6, c], x[0:6 - shift, c])
+        assert np.all(y[:shift, c] == 0.0)
+
+
+def pin_conv_constant(m):
+    """A constant row after zero history: y[t] = sum_{j >= W-1-t} w[:, j]."""
+    w = np.array([[0.25, -2.0, 3.0, 0.5], [1.0, 2.0, 4.0, 8.0]])
+    y, _ = m.short_conv(np.ones((7, 2)), w, [7], None)
+    for t in range(7):
+        want = w[:, max(0, 3 - t):].sum(axis=1)
+        assert np.allclose(y[t], want, rtol=0, atol=1e-15)
+
+
+def pin_conv_split_and_packing(m):
+    """A sequence in two calls (the first call's final state carried) equals
+    one call; packed sequences do not see each other."""
+    rng = np.random.default_rng(9)
+    x, w, st = _conv_case(rng, [11], 5, 4)
+    y, fin = m.short_conv(x, w, [11], st)
+    for cut in (0, 1, 2, 3, 7, 11):
+        y1, f1 = m.short_conv(x[:cut], w, [cut], st)
+        y2, f2 = m.short_conv(x[cut:], w, [11 - cut], f1)
+        assert np.allclose(np.concatenate([y1, y2]), y, rtol=0, atol=1e-13)
+        assert np.array_equal(f2, fin)
+    lengths = [4, 6, 3]
+    x, w, st = _conv_case(rng, lengths, 2, 3)
+    y, fin = m.short_conv(x, w, lengths, st)
+    x2 = x.copy()
+    x2[:4] = rng.normal(0, 1, (4, 2))  # sequence 0 changed
+    y2, fin2 = m.short_conv(x2, w, lengths, st)
+    assert np.array_equal(y2[4:], y[4:]) and np.array_equal(fin2[1:], fin[1:])
+    assert not np.allclose(y2[:4], y[:4])
+
+
+PINS = [pin_golden, pin_softplus, pin_decay, pin_silu, pin_output_gate, pin_conv_numpy,
+        pin_conv_taps, pin_conv_constant, pin_conv_split_and_packing]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -133,6 +231,15 @@ MUTATIONS = {
                        "return o / np.sqrt(ms + eps) * w * silu(o)"),
     "rms_of_absolute": ("ms = np.mean(o * o, axis=-1, keepdims=True)",
                         "ms = np.mean(np.abs(o), axis=-1, keepdims=True) ** 2"),
+    "conv_taps_reversed": ("y[b + t] += w[:, j] * e[t + j]", "y[b + t] += w[:, W - 1 - j] * e[t + j]"),
+    "conv_one_channel_weights": ("y[b + t] += w[:, j] * e[t + j]", "y[b + t] += w[0, j] * e[t + j]"),
+    "conv_current_row_dropped": ("for j in range(W):", "for j in range(W - 1):"),
+    "conv_history_ignored": ("hist = np.zeros((W - 1, D)) if state is None else _f64(state[n])",
+                             "hist = np.zeros((W - 1, D))"),
+    "conv_history_from_previous_sequence": (
+        "e = np.concatenate([hist, x[b:b + L]], axis=0)",
+        "e = np.concatenate([x[b - (W - 1):b] if b >= W - 1 else hist, x[b:b + L]], axis=0)"),
+    "conv_final_one_row_early": ("final[n] = e[L:L + W - 1]", "final[n] = e[max(L - 1, 0):max(L - 1, 0) + W - 1]"),
 }
 
 
@@ -148,6 +255,6 @@ def test_gate_mutation_is_caught(name):
         try:
             with np.errstate(all="ignore"):
                 pin(mod)
-        except AssertionError:
+        except Exception:  # a failed check, or a mutant that no longer runs
             failed.append(pin.__name__)
     assert failed, f"mutation {name} passed every pin"
