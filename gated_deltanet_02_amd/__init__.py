@@ -8,7 +8,7 @@ raises if it was not built.
 from ._binding import (GdnError, GdnOptions, GdnTensor, GdnWorkspaceLayout,  # noqa: F401
                        STAGE_ALL, STAGE_SCAN, STAGE_TABLE, STAGE_WY, EXPORTED,
                        SCAN_AUTO, SCAN_ONE_PASS, SCAN_TWO_LEVEL, FLAG_BETA_LOGITS,
-                       FLAG_DECAY_PROJ, FLAG_OUTPUT_GATE, FLAG_QKV_SILU, gdn_output_gate,
+                       FLAG_DECAY_PROJ, FLAG_OUTPUT_GATE, FLAG_QKV_SILU, FLAG_QKV_CONV, gdn_output_gate,
                        gdn_check_cu_seqlens,
                        alloc_workspace, describe, gdn_abi_version,
                        gdn_default_options, gdn_get_workspace_layout,

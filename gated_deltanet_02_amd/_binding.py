@@ -21,7 +21,7 @@ STATUS_NAMES = {0: "GDN_OK", -1: "GDN_ERR_NULL_ARG", -2: "GDN_ERR_DTYPE",
                 -7: "GDN_ERR_HIP", -8: "GDN_ERR_INPUT"}
 STAGE_TABLE, STAGE_WY, STAGE_SCAN, STAGE_ALL = 1, 2, 4, 7
 SCAN_AUTO, SCAN_ONE_PASS, SCAN_TWO_LEVEL = 0, 1, 2
-FLAG_BETA_LOGITS, FLAG_DECAY_PROJ, FLAG_OUTPUT_GATE, FLAG_QKV_SILU = 1, 2, 4, 8
+FLAG_BETA_LOGITS, FLAG_DECAY_PROJ, FLAG_OUTPUT_GATE, FLAG_QKV_SILU, FLAG_QKV_CONV = 1, 2, 4, 8, 16
 EXPORTED = ("gdn_abi_version", "gdn_default_options", "gdn_prefill",
             "gdn_prefill_ex", "gdn_prefill_noalloc", "gdn_workspace_size", "gdn_get_workspace_layout",
             "gdn_decode", "gdn_output_gate", "gdn_check_cu_seqlens", "gdn_graph_cache_create", "gdn_graph_cache_destroy",
@@ -43,7 +43,9 @@ class GdnOptions(ctypes.Structure):
                 ("scan_split", ctypes.c_int32), ("flags", ctypes.c_uint32),
                 ("decay_a_log", ctypes.c_void_p), ("decay_bias", ctypes.c_void_p),
                 ("gate_z", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
-                ("norm_eps", ctypes.c_float), ("segment_chunks", ctypes.c_int32)]
+                ("norm_eps", ctypes.c_float), ("segment_chunks", ctypes.c_int32),
+                ("conv_weight", ctypes.c_void_p), ("conv_width", ctypes.c_int32),
+                ("conv_state_in", ctypes.c_void_p), ("conv_state_out", ctypes.c_void_p)]
 
 
 class GdnWorkspaceLayout(ctypes.Structure):
@@ -158,10 +160,17 @@ def options(chunk: int = 0, scale: float = 1.0, l2_eps: float = 1e-6,
             decay_bias: Optional[torch.Tensor] = None,
             gate_z: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
             norm_eps: float = 1e-6, segment_chunks: int = 0,
-            qkv_silu: bool = False) -> GdnOptions:
+            qkv_silu: bool = False, conv_weight: Optional[torch.Tensor] = None,
+            conv_state_in: Optional[torch.Tensor] = None,
+            conv_state_out: Optional[torch.Tensor] = None) -> GdnOptions:
     """scan_split: SCAN_AUTO (0), SCAN_ONE_PASS (1) or SCAN_TWO_LEVEL (2);
     segment_chunks: 0 automatic, -1 never, n > 0 segments of n chunks;
     qkv_silu: q, k, v hold pre-activation values and the kernels take silu;
+    conv_weight: the short convolution's taps, a contiguous f32 GPU tensor
+    [2 Hk dk + Hv dv, W] (sets the convolution flag, W = its second size),
+    with the history rows conv_state_in and the new history conv_state_out,
+    contiguous [N, W - 1, 2 Hk dk + Hv dv] GPU tensors of the input dtype
+    (None: zeros / not written; they may be one tensor);
     beta_logits: beta holds raw projections b and the kernels use sigmoid(b);
     decay_proj: g holds the decay gate's raw projection a, with per value head
     f32 tensors decay_a_log and decay_bias (None: zeros);
@@ -178,12 +187,23 @@ def options(chunk: int = 0, scale: float = 1.0, l2_eps: float = 1e-6,
     o.norm_weight = _dev_ptr(norm_weight, "norm_weight")
     o.norm_eps = norm_eps
     o.segment_chunks = segment_chunks
+    o.conv_width = 4
+    if conv_weight is not None:
+        if conv_weight.dim() != 2:
+            raise ValueError("conv_weight must be [channels, width]")
+        o.conv_weight = _dev_ptr(conv_weight, "conv_weight")
+        o.conv_width = conv_weight.shape[1]
+        o.flags |= FLAG_QKV_CONV
+        for name, t in (("conv_state_in", conv_state_in), ("conv_state_out", conv_state_out)):
+            if t is not None:
+                setattr(o, name, _dev_ptr(t, name, t.dtype))
     if gate_z is not None:
         if gate_z.device.type != "cuda":
             raise ValueError("gate_z must be a GPU tensor")
         o.gate_z = gate_z.data_ptr()
         o.flags |= FLAG_OUTPUT_GATE
-    o._keep = (decay_a_log, decay_bias, gate_z, norm_weight)
+    o._keep = (decay_a_log, decay_bias, gate_z, norm_weight, conv_weight, conv_state_in,
+               conv_state_out)
     return o
 
 

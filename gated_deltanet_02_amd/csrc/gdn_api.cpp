@@ -129,6 +129,11 @@ struct Problem {
   bool decay_proj = false;   // GDN_FLAG_DECAY_PROJ
   bool out_gate = false;     // GDN_FLAG_OUTPUT_GATE
   bool qkv_silu = false;     // GDN_FLAG_QKV_SILU
+  bool qkv_conv = false;     // GDN_FLAG_QKV_CONV
+  const float* conv_w = nullptr;
+  int conv_width = 0;
+  const void* conv_in = nullptr;
+  void* conv_out = nullptr;
   const float* a_log = nullptr;
   const float* a_bias = nullptr;
   const void* gate_z = nullptr;
@@ -140,7 +145,8 @@ struct Problem {
 };
 
 constexpr uint32_t kKnownFlags =
-    GDN_FLAG_BETA_LOGITS | GDN_FLAG_DECAY_PROJ | GDN_FLAG_OUTPUT_GATE | GDN_FLAG_QKV_SILU;
+    GDN_FLAG_BETA_LOGITS | GDN_FLAG_DECAY_PROJ | GDN_FLAG_OUTPUT_GATE | GDN_FLAG_QKV_SILU |
+    GDN_FLAG_QKV_CONV;
 
 // Checks of the gate fields of gdn_options that need no shapes.
 int check_gate_options(const gdn_options& o) {
@@ -148,6 +154,13 @@ int check_gate_options(const gdn_options& o) {
   if (!(o.norm_eps >= 0.f)) return fail(GDN_ERR_SHAPE, "norm_eps must be >= 0");
   if ((uintptr_t)o.decay_a_log % 4 || (uintptr_t)o.decay_bias % 4 || (uintptr_t)o.norm_weight % 4)
     return fail(GDN_ERR_LAYOUT, "decay_a_log, decay_bias and norm_weight must be 4-byte aligned");
+  if (o.flags & GDN_FLAG_QKV_CONV) {
+    if (o.conv_width < 1 || o.conv_width > gdn::kConvMaxWidth)
+      return fail(GDN_ERR_SHAPE, "conv_width must be 1 .. %d (got %d)", gdn::kConvMaxWidth, o.conv_width);
+    if ((uintptr_t)o.conv_weight % 16 || (uintptr_t)o.conv_state_in % 16 ||
+        (uintptr_t)o.conv_state_out % 16)
+      return fail(GDN_ERR_LAYOUT, "conv_weight, conv_state_in and conv_state_out must be 16-byte aligned");
+  }
   return GDN_OK;
 }
 
@@ -191,7 +204,7 @@ Layout make_layout(const Problem& P) {
     L.phi = take(heads * P.dk * P.dk * 4);
   }
   if (P.seg_chunks > 0) L.carry = take((size_t)P.n_seq * P.hv * P.dk * P.dv * 4);
-  if (P.qkv_silu) L.kact = take((size_t)P.T * P.hk * P.dk * es);
+  if (P.qkv_silu || P.qkv_conv) L.kact = take((size_t)P.T * P.hk * P.dk * es);
   L.total = off;
   return L;
 }
@@ -220,6 +233,11 @@ int resolve_options(const gdn_options* opts, bool bf16, Problem* P) {
   P->decay_proj = (o.flags & GDN_FLAG_DECAY_PROJ) != 0;
   P->out_gate = (o.flags & GDN_FLAG_OUTPUT_GATE) != 0;
   P->qkv_silu = (o.flags & GDN_FLAG_QKV_SILU) != 0;
+  P->qkv_conv = (o.flags & GDN_FLAG_QKV_CONV) != 0;
+  P->conv_w = P->qkv_conv ? o.conv_weight : nullptr;
+  P->conv_width = P->qkv_conv ? o.conv_width : 0;
+  P->conv_in = P->qkv_conv ? o.conv_state_in : nullptr;
+  P->conv_out = P->qkv_conv ? o.conv_state_out : nullptr;
   P->a_log = P->decay_proj ? o.decay_a_log : nullptr;
   P->a_bias = P->decay_proj ? o.decay_bias : nullptr;
   P->gate_z = P->out_gate ? o.gate_z : nullptr;
@@ -383,6 +401,8 @@ int validate(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
       return fail(GDN_ERR_LAYOUT, "%s: token/head strides must be multiples of %d elements", x.n, gr);
   }
   if (P->T > 0 && (!g->data || !beta->data)) return fail(GDN_ERR_NULL_ARG, "g/beta data is NULL");
+  if (P->qkv_conv && P->T > 0 && !P->conv_w)
+    return fail(GDN_ERR_NULL_ARG, "GDN_FLAG_QKV_CONV needs conv_weight");
   if (P->out_gate && P->T > 0) {
     if (!P->gate_z) return fail(GDN_ERR_NULL_ARG, "GDN_FLAG_OUTPUT_GATE needs gate_z");
     if ((uintptr_t)P->gate_z % 16) return fail(GDN_ERR_LAYOUT, "gate_z must be 16-byte aligned");
@@ -489,6 +509,13 @@ int validate_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* 
   d->beta_logits = (o.flags & GDN_FLAG_BETA_LOGITS) ? 1 : 0;
   d->decay_proj = (o.flags & GDN_FLAG_DECAY_PROJ) ? 1 : 0;
   d->qkv_silu = (o.flags & GDN_FLAG_QKV_SILU) ? 1 : 0;
+  if (o.flags & GDN_FLAG_QKV_CONV) {
+    if (N > 0 && !o.conv_weight) return fail(GDN_ERR_NULL_ARG, "GDN_FLAG_QKV_CONV needs conv_weight");
+    d->conv_w = o.conv_weight;
+    d->conv_state = o.conv_state_in;
+    d->conv_width = o.conv_width;
+    d->conv_d = (int32_t)(2 * hk * dkk + hv * dv);
+  }
   d->a_log = d->decay_proj ? o.decay_a_log : nullptr;
   d->a_bias = d->decay_proj ? o.decay_bias : nullptr;
   *bf16 = q->dtype == GDN_DTYPE_BF16;
@@ -598,7 +625,14 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
     wp.a_log = P.a_log;
     wp.a_bias = P.a_bias;
     wp.qkv_silu = P.qkv_silu ? 1 : 0;
-    wp.k_act = P.qkv_silu ? base + L.kact + t0 * P.hk * P.dk * (int64_t)es : nullptr;
+    wp.k_act = L.kact ? base + L.kact + t0 * P.hk * P.dk * (int64_t)es : nullptr;
+    if (P.qkv_conv) {
+      wp.conv_w = P.conv_w;
+      wp.conv_state = P.conv_in;
+      wp.conv_width = P.conv_width;
+      wp.conv_d = 2 * P.hk * P.dk + P.hv * P.dv;
+      wp.conv_cont = t0 > 0 ? 1 : 0;  // a later segment continues its sequences
+    }
     const hipError_t e = gdn::launch_wy(P.bf16, P.chunk, P.dk, wp, s);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "WY launch: %s", hipGetErrorString(e));
     return GDN_OK;
@@ -612,7 +646,7 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
     sp.o_sh = P.o.sh;
     sp.init = h0;
     sp.final_state = h1;
-    if (P.qkv_silu) {  // the WY kernel's activated key rows, [T][Hk][dk] contiguous
+    if (L.kact) {  // the WY kernel's key rows as used, [T][Hk][dk] contiguous
       sp.k = base + L.kact + t0 * P.hk * P.dk * (int64_t)es;
       sp.k_st = (int64_t)P.hk * P.dk;
       sp.k_sh = P.dk;
@@ -670,6 +704,25 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
     if ((P.stages & GDN_STAGE_WY) && P.max_chunks > 0 && (rc = wy(map, P.max_chunks, 0))) return rc;
     if ((P.stages & GDN_STAGE_SCAN) && (rc = scan(map, 0, h_init, h_fin))) return rc;
   }
+  if (P.qkv_conv && P.conv_out && (P.stages & GDN_STAGE_WY)) {
+    // the short convolution's history for a later call: after every WY
+    // launch has read the old one (it may be the same memory)
+    gdn::ConvStateParams cp{};
+    cp.q = q->data; cp.k = k->data; cp.v = v->data;
+    cp.q_st = P.q.st; cp.q_sh = P.q.sh;
+    cp.k_st = P.k.st; cp.k_sh = P.k.sh;
+    cp.v_st = P.v.st; cp.v_sh = P.v.sh;
+    cp.state_in = P.conv_in;
+    cp.state_out = P.conv_out;
+    cp.seq_start = P.packed ? (const int32_t*)(base + L.seq_start) : nullptr;
+    cp.n_seq = P.n_seq;
+    cp.seq_len = P.seq_len;
+    cp.width = P.conv_width;
+    cp.d = 2 * P.hk * P.dk + P.hv * P.dv;
+    cp.hk = P.hk; cp.dk = P.dk; cp.dv = P.dv;
+    if ((e = gdn::launch_conv_state(P.bf16, cp, s)) != hipSuccess)
+      return fail(GDN_ERR_HIP, "convolution state launch: %s", hipGetErrorString(e));
+  }
   if (P.stages & GDN_STAGE_SCAN) {
     if (P.out_gate && P.T > 0) {
       // the gated output norm over the stored rows (packed: up to cu[N])
@@ -711,6 +764,10 @@ void gdn_default_options(gdn_options* opts) {
   opts->norm_weight = nullptr;
   opts->norm_eps = 1e-6f;
   opts->segment_chunks = 0;
+  opts->conv_weight = nullptr;
+  opts->conv_width = 4;
+  opts->conv_state_in = nullptr;
+  opts->conv_state_out = nullptr;
 }
 
 const char* gdn_status_string(int status) {
@@ -844,6 +901,23 @@ int gdn_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
   if (d.n == 0) return GDN_OK;
   hipError_t e = gdn::launch_decode(bf16, dk, d, (hipStream_t)stream);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  if (d.conv_w && opts->conv_state_out) {
+    // the step's raw rows shifted into the history, after the step read it
+    gdn::ConvStateParams cp{};
+    cp.q = q->data; cp.k = k->data; cp.v = v->data;
+    cp.q_st = q->stride[0]; cp.q_sh = q->stride[1];
+    cp.k_st = k->stride[0]; cp.k_sh = k->stride[1];
+    cp.v_st = v->stride[0]; cp.v_sh = v->stride[1];
+    cp.state_in = opts->conv_state_in;
+    cp.state_out = opts->conv_state_out;
+    cp.n_seq = d.n;
+    cp.seq_len = 1;
+    cp.width = d.conv_width;
+    cp.d = d.conv_d;
+    cp.hk = d.hk; cp.dk = dk; cp.dv = d.dv;
+    if ((e = gdn::launch_conv_state(bf16, cp, (hipStream_t)stream)) != hipSuccess)
+      return fail(GDN_ERR_HIP, "convolution state launch: %s", hipGetErrorString(e));
+  }
   if (opts && (opts->flags & GDN_FLAG_OUTPUT_GATE)) {
     gdn::GateParams gp{};
     gp.x = out->data;
@@ -1049,6 +1123,10 @@ int gdn_prefill_graph(gdn_graph_cache* cache, const gdn_tensor* q, const gdn_ten
   append(key, &o.norm_weight, sizeof o.norm_weight);
   append(key, &o.norm_eps, sizeof o.norm_eps);
   append(key, &o.segment_chunks, sizeof o.segment_chunks);
+  append(key, &o.conv_weight, sizeof o.conv_weight);
+  append(key, &o.conv_width, sizeof o.conv_width);
+  append(key, &o.conv_state_in, sizeof o.conv_state_in);
+  append(key, &o.conv_state_out, sizeof o.conv_state_out);
   append(key, &workspace, sizeof workspace);
   append(key, &workspace_bytes, sizeof workspace_bytes);
 

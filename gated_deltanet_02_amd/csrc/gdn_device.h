@@ -378,12 +378,25 @@ __device__ __forceinline__ float decay_gate(float a, const float* a_log, const f
   return -expf(a_log ? a_log[h] : 0.f) * sp;
 }
 
-// The activation before the prefill (GDN_FLAG_QKV_SILU): silu(x) = x / (1 +
-// e^-x) in fp32, rounded to the input type TI as a separate activation pass
-// would store it.
+// silu(x) = x / (1 + e^-x) in fp32 with the hardware exp2 and reciprocal
+// (each within about an ulp; for x below about -88 the reciprocal of the
+// overflowed 1 + e^-x is 0 and silu gives -0).
+__device__ __forceinline__ float silu_f32(float x) {
+  return x * __builtin_amdgcn_rcpf(1.f + fast_exp(-x));
+}
+
+// The activation before the prefill (GDN_FLAG_QKV_SILU): silu in fp32,
+// rounded to the input type TI as a separate activation pass would store it.
 template <typename TI>
 __device__ __forceinline__ float qkv_act(float x) {
-  return to_float(from_float<TI>(x / (1.f + expf(-x))));
+  return to_float(from_float<TI>(silu_f32(x)));
+}
+
+// The end of the short convolution (GDN_FLAG_QKV_CONV): its fp32 sum, through
+// silu when the activation is on, rounded once to the input type TI.
+template <typename TI>
+__device__ __forceinline__ TI conv_act(float y, int silu) {
+  return from_float<TI>(silu ? silu_f32(y) : y);
 }
 
 }  // namespace gdn

@@ -7,6 +7,9 @@
 
 namespace gdn {
 
+// Widest short convolution (GDN_FLAG_QKV_CONV) the kernels take.
+constexpr int kConvMaxWidth = 4;
+
 // How a global chunk id maps to (sequence, first token, length).
 //   uniform: n_seq sequences of seq_len tokens each, seq_stride tokens
 //            apart (seq_len, or more for a segment of longer sequences),
@@ -60,7 +63,14 @@ struct WyParams {
   const float* a_log;   // [Hv] or null (zeros), with decay_proj
   const float* a_bias;  // [Hv] or null (zeros), with decay_proj
   int32_t qkv_silu;     // 1: q, k, v hold pre-activation values, the kernel takes silu
-  void* k_act;          // with qkv_silu: activated key rows out, [T][Hk][dk] contiguous
+  void* k_act;          // with qkv_silu or the convolution: key rows as used, [T][Hk][dk] contiguous
+  // the short convolution before the activation (conv_w null: none)
+  const float* conv_w;      // taps [conv_d][conv_width] f32
+  const void* conv_state;   // raw rows before each sequence [N][conv_width - 1][conv_d], or null (zeros)
+  int32_t conv_width;       // 1 .. 4
+  int32_t conv_d;           // channels: 2 hk dk + hv dv (q | k | v)
+  int32_t conv_cont;        // 1: the first chunk of a sequence here continues it (a later
+                            // segment): its history rows are the input rows before it
   float scale, eps;
   ChunkMap map;
   Intermediates im;
@@ -106,7 +116,26 @@ struct DecodeParams {
   const float* a_log;    // [Hv] or null (zeros), with decay_proj
   const float* a_bias;   // [Hv] or null (zeros), with decay_proj
   int32_t qkv_silu;      // 1: q, k, v hold pre-activation values, the kernel takes silu
+  const float* conv_w;   // the short convolution's taps [conv_d][conv_width], or null (none)
+  const void* conv_state;// history rows [N][conv_width - 1][conv_d], or null (zeros)
+  int32_t conv_width, conv_d;
   float scale, eps;
+};
+
+// The short convolution's state after a call: for every sequence and
+// channel, the last width - 1 raw rows of its history followed by its rows.
+// Sequences as in ChunkMap (uniform: seq_len tokens seq_len apart; packed:
+// the sanitised starts).
+struct ConvStateParams {
+  const void* q;         // token rows, strides as the inputs'
+  const void* k;
+  const void* v;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh;
+  const void* state_in;  // [N][width - 1][D] or null (zeros)
+  void* state_out;       // [N][width - 1][D]; may be state_in
+  const int32_t* seq_start;  // packed: int32[n_seq + 1], else null
+  int32_t n_seq, seq_len, width, d;
+  int32_t hk, dk, dv;
 };
 
 // The gated output norm over rows of dv elements: row r is (r / inner,

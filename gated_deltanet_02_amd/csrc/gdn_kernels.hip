@@ -347,7 +347,22 @@ struct WyLayout {
   static constexpr int sz_x = cmax(cmax(C * LK * S, sz_p + C * LF * 4), 3 * sz_p);
   static constexpr int r_vec = r_x + sz_x;
   static constexpr int r_gate = r_vec + 7 * C * 4;  // g, beta of the first value head
-  static constexpr int total = r_gate + 2 * C * 4;
+  // The short convolution (GDN_FLAG_QKV_CONV): taps (f32, flat [d][W]) and
+  // up to KW - 1 history rows (unswizzled) of q and k, used before the Gram
+  // products, and of one value head's v, used as its V rows are stored.
+  // The q, k part sits in the V and T regions, which hold nothing until the
+  // first V rows are stored and T is formed, where they are large enough.
+  static constexpr int KW = kConvMaxWidth;
+  static constexpr int h_qk = (KW - 1) * DK * S;  // one history block of q or k
+  static constexpr int t_qk = DK * KW * 4;        // one tap block of q or k
+  static constexpr int qk_need = 2 * h_qk + 2 * t_qk;
+  static constexpr int h_v = (KW - 1) * DVM * S;
+  static constexpr int v_need = h_v + DVM * KW * 4;
+  static constexpr bool qk_in_vt = C * LV * S + sz_t >= qk_need;
+  static constexpr int plain = r_gate + 2 * C * 4;  // the kernel without the convolution
+  static constexpr int r_cv = plain;  // v history, then v taps
+  static constexpr int r_cqk = qk_in_vt ? r_v : r_cv + v_need;  // q, k history, then q, k taps
+  static constexpr int total = r_cv + v_need + (qk_in_vt ? 0 : qk_need);
 };
 
 // Issues LDS-direct copies of rows 0 .. R-1 of a row-major LDS region (row
@@ -373,12 +388,48 @@ __device__ __forceinline__ void dma_rows(char* region, const TI* src, int64_t st
   }
 }
 
+// Issues LDS-direct copies of `bytes` (a multiple of 16) contiguous bytes
+// from src to region, 1 KiB pieces spread over the NW waves.
+template <int NW>
+__device__ __forceinline__ void dma_flat(char* region, const char* src, int bytes, int wave,
+                                         int lane) {
+  for (int pc = wave; pc * 1024 < bytes; pc += NW) {
+    const int o = pc * 1024 + lane * 16;
+    if (o < bytes)
+      __builtin_amdgcn_global_load_lds((const void*)(src + o),
+                                       (__attribute__((address_space(3))) void*)(region + pc * 1024),
+                                       16, 0, 0);
+  }
+}
+
+// The short convolution's inputs beside one block of d channels: its taps
+// (flat [d][W] f32) and its W - 1 history rows, from the inputs' rows before
+// the chunk (src, row stride st) or, at a sequence's first chunk, from the
+// history array (null: left for the caller to zero).  ch: the block's first
+// channel among the D of q | k | v.
+template <typename TI, int LDR, int NW>
+__device__ __forceinline__ void conv_fetch(char* hist, char* taps, const WyParams& p, bool first,
+                                           int seq, const TI* src, int64_t st, int ch, int d,
+                                           int wave, int lane) {
+  const int W = p.conv_width;
+  dma_flat<NW>(taps, (const char*)(p.conv_w + (int64_t)ch * W), d * W * 4, wave, lane);
+  if (W < 2) return;
+  if (first) {
+    if (p.conv_state)
+      dma_rows<TI, 3, LDR, 0, NW>(hist, (const TI*)p.conv_state + (int64_t)seq * (W - 1) * p.conv_d + ch,
+                                  p.conv_d, d, W - 1, wave, lane);
+  } else {
+    dma_rows<TI, 3, LDR, 0, NW>(hist, src - (int64_t)(W - 1) * st, st, d, W - 1, wave, lane);
+  }
+}
+
 // The inputs of the chunk (first token t0, n tokens) for key head kh: q, k
 // rows and the first value head's v rows and gates, copied straight into
-// their LDS regions (no registers).
-template <typename TI, int C, int DK>
+// their LDS regions (no registers); with the short convolution also the
+// taps and history rows of q, k and that value head's v.
+template <typename TI, int C, int DK, bool CONV>
 __device__ __forceinline__ void wy_fetch(char* buf, const WyParams& p, int kh, int t0, int n,
-                                         int wave, int lane) {
+                                         bool first, int seq, int wave, int lane) {
   using L = WyLayout<TI, C, DK>;
   constexpr int NW = kWyThreads / 64;
   const int h = kh * (p.hv / p.hk);
@@ -393,11 +444,25 @@ __device__ __forceinline__ void wy_fetch(char* buf, const WyParams& p, int kh, i
                                      (__attribute__((address_space(3))) void*)(buf + L::r_gate + C * 4),
                                      4, 0, 0);
   }
+  if constexpr (CONV) {
+    static_assert(L::KW - 1 <= 3, "history rows fit the copies below");
+    char* qk = buf + L::r_cqk;
+    conv_fetch<TI, DK, NW>(qk, qk + 2 * L::h_qk, p, first, seq,
+                           (const TI*)p.q + (int64_t)t0 * p.q_st + kh * p.q_sh, p.q_st, kh * DK, DK,
+                           wave, lane);
+    conv_fetch<TI, DK, NW>(qk + L::h_qk, qk + 2 * L::h_qk + L::t_qk, p, first, seq,
+                           (const TI*)p.k + (int64_t)t0 * p.k_st + kh * p.k_sh, p.k_st,
+                           (p.hk + kh) * DK, DK, wave, lane);
+    conv_fetch<TI, L::DVM, NW>(buf + L::r_cv, buf + L::r_cv + L::h_v, p, first, seq,
+                               (const TI*)p.v + (int64_t)t0 * p.v_st + h * p.v_sh, p.v_st,
+                               2 * p.hk * DK + h * p.dv, p.dv, wave, lane);
+  }
 }
 // One workgroup per (chunk, key head) item, under 128 VGPRs and 80 KiB of
 // LDS so that two workgroups share a compute unit and hide each other's
-// barriers and latencies.
-template <typename TI, int C, int DK>
+// barriers and latencies.  CONV: the short convolution is on (a separate
+// build of the kernel, so that its code costs the plain kernel nothing).
+template <typename TI, int C, int DK, bool CONV>
 __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   using L = WyLayout<TI, C, DK>;
   constexpr int NT = kWyThreads;
@@ -407,7 +472,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   constexpr int NB = C / 16;    // 16-row tiles along the chunk
   constexpr int NKT = DK / 16;  // 16-row tiles along d_k
   constexpr int NVG = (C * (128 / GR) + NT - 1) / NT;  // v granules per thread (d_v <= 128)
-  __shared__ __attribute__((aligned(1024))) char smem[L::total];
+  __shared__ __attribute__((aligned(1024))) char smem[CONV ? L::total : L::plain];
 
   const int it = blockIdx.x;
   if (it >= p.n_items) return;
@@ -442,12 +507,19 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
   const int c = p.n_items / p.hk - 1 - it / p.hk, kh = it % p.hk;
   int seq, t0, n;
   if (!chunk_info(p.map, c, C, seq, t0, n)) return;
-  (void)seq;
-  wy_fetch<TI, C, DK>(smem, p, kh, t0, n, wave, lane);
+  // The short convolution: a sequence's first chunk takes its history rows
+  // from the history array, the others from the rows before them.
+  constexpr bool conv = CONV;
+  bool first = false;
+  if constexpr (conv)
+    first = p.map.packed ? t0 == p.map.seq_start[seq] : !p.conv_cont && t0 == seq * p.map.seq_stride;
+  const bool zero_hist = conv && first && !p.conv_state && p.conv_width > 1;
+  wy_fetch<TI, C, DK, CONV>(smem, p, kh, t0, n, first, seq, wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (n < C) {
-    // rows past the chunk's end are zero (the copies skipped them)
+  if (n < C || zero_hist) {
+    // rows past the chunk's end are zero (the copies skipped them), and so
+    // is a fresh sequence's history
     for (int idx = tid; idx < (C - n) * LK; idx += NT) {
       sKV[n * LK + idx] = from_float<TI>(0.f);
       sQ[n * LK + idx] = from_float<TI>(0.f);
@@ -456,13 +528,81 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       ((float*)sGate)[n + tid] = 0.f;
       ((float*)sGate)[C + n + tid] = 0.f;
     }
+    if (zero_hist) {
+      TI* hqk = (TI*)(smem + L::r_cqk);  // q and k history blocks, back to back
+      for (int idx = tid; idx < 2 * L::h_qk / (int)sizeof(TI); idx += NT) hqk[idx] = from_float<TI>(0.f);
+      TI* hv = (TI*)(smem + L::r_cv);
+      for (int idx = tid; idx < L::h_v / (int)sizeof(TI); idx += NT) hv[idx] = from_float<TI>(0.f);
+    }
     __syncthreads();
   }
-  if (p.qkv_silu) {
+  if constexpr (conv) {
+    // q and k rows through the convolution (and silu), in place: each
+    // thread takes RB consecutive rows of one 16-byte column of q or k,
+    // walks the rows from W - 1 before them once with the column's taps in
+    // registers, and stores its results after every thread has read its
+    // raw rows
+    auto qk_pass = [&](auto wc) {
+      constexpr int W = decltype(wc)::value;
+      constexpr int GE = 16 / (int)sizeof(TI), GPR = DK / GE;
+      constexpr int RB = 2 * C * GPR / NT < 1 ? 1 : 2 * C * GPR / NT;
+      constexpr int NBLK = C / RB;
+      static_assert(2 * GPR * NBLK <= NT && C % RB == 0, "one column block per thread");
+      const int m = tid / (GPR * NBLK), gc = (tid / NBLK) % GPR, r0 = (tid % NBLK) * RB;
+      const bool live = tid < 2 * GPR * NBLK && r0 < n;
+      uint4 res[RB];
+      if (live) {
+        const TI* rows = m ? sKV : sQ;
+        const TI* hist = (const TI*)(smem + L::r_cqk + m * L::h_qk) + gc * GE;
+        const float* tp = (const float*)(smem + L::r_cqk + 2 * L::h_qk + m * L::t_qk) + gc * GE * W;
+        float taps[GE][W], acc[RB][GE];
+#pragma unroll
+        for (int e = 0; e < GE; ++e)
+#pragma unroll
+          for (int j = 0; j < W; ++j) taps[e][j] = tp[e * W + j];
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+          for (int e = 0; e < GE; ++e) acc[i][e] = 0.f;
+        // window row t is row r0 - (W - 1) + t; it feeds output row i = t - j
+        // with tap j (so each output sums its taps in order)
+#pragma unroll
+        for (int t = 0; t < RB + W - 1; ++t) {
+          const int rr = r0 - (W - 1) + t;
+          const uint4 raw = ld16(rr >= 0 ? rows + rr * LK + ((gc ^ (rr & SWK)) * GE) : hist + (rr + W - 1) * DK);
+          TI x[GE];
+          __builtin_memcpy(x, &raw, 16);
+#pragma unroll
+          for (int j = 0; j < W; ++j) {
+            const int i = t - j;
+            if (i < 0 || i >= RB) continue;
+#pragma unroll
+            for (int e = 0; e < GE; ++e) acc[i][e] += taps[e][j] * to_float(x[e]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          TI y[GE];
+#pragma unroll
+          for (int e = 0; e < GE; ++e) y[e] = conv_act<TI>(acc[i][e], p.qkv_silu);
+          __builtin_memcpy(&res[i], y, 16);
+        }
+      }
+      __syncthreads();
+      if (live) {
+        TI* rows = m ? sKV : sQ;
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          const int r = r0 + i;
+          if (r < n) st16(rows + r * LK + ((gc ^ (r & SWK)) * GE), res[i]);  // padded rows stay zero
+        }
+      }
+      __syncthreads();
+    };
+    dispatch_int<1, L::KW + 1>(p.conv_width, qk_pass);
+  } else if (p.qkv_silu) {
     // the activation on the q and k rows in place (elementwise, so the
-    // granule swizzle does not matter; silu(0) = 0 keeps padded rows zero),
-    // then the chunk's activated key rows out for the scan, unswizzled, in
-    // the token layout of a contiguous [T][Hk][dk] tensor
+    // granule swizzle does not matter; silu(0) = 0 keeps padded rows zero)
     constexpr int GE = 16 / (int)sizeof(TI), GPR = DK / GE;
     for (int idx = tid; idx < 2 * C * GPR; idx += NT) {
       const int m = idx / (C * GPR), r = (idx / GPR) % C, g = idx % GPR;
@@ -477,6 +617,11 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       st16(e, out);
     }
     __syncthreads();
+  }
+  if (conv || p.qkv_silu) {
+    // the chunk's key rows as used out for the scan, unswizzled, in the
+    // token layout of a contiguous [T][Hk][dk] tensor
+    constexpr int GE = 16 / (int)sizeof(TI), GPR = DK / GE;
     TI* ka = (TI*)p.k_act + ((int64_t)t0 * p.hk + kh) * DK;
     for (int idx = tid; idx < n * GPR; idx += NT) {
       const int r = idx / GPR, g = idx % GPR;
@@ -510,9 +655,87 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       bv = 0.f;
     }
   };
+  // The short convolution of value head h's V rows, stored raw in the V
+  // region: its taps and history rows (the group's first head's came with
+  // the chunk's inputs), then every result from the raw rows, then stored.
+  auto conv_v = [&](int gi_, int h_, int tid_s) {
+    const int W = p.conv_width;
+    TI* hv = (TI*)(smem + L::r_cv);
+    float* tv = (float*)(smem + L::r_cv + L::h_v);
+    if (gi_ > 0) {
+      const int ch = 2 * p.hk * DK + h_ * DV;
+      for (int idx = tid_s; idx < DV * W / 4; idx += NT)
+        ((f32x4*)tv)[idx] = ((const f32x4*)(p.conv_w + (int64_t)ch * W))[idx];
+      for (int idx = tid_s; idx < (W - 1) * GPRV; idx += NT) {
+        const int r = idx >> LGV, gc = idx & (GPRV - 1);
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (!first)
+          x = ld16(vg + (int64_t)(t0 - (W - 1) + r) * p.v_st + h_ * p.v_sh + gc * GR);
+        else if (p.conv_state)
+          x = ld16((const TI*)p.conv_state + ((int64_t)seq * (W - 1) + r) * p.conv_d + ch + gc * GR);
+        st16(hv + r * L::DVM + gc * GR, x);
+      }
+    }
+    __syncthreads();
+    // as the q, k pass: RB consecutive rows of one 16-byte column per thread
+    auto v_pass = [&](auto wc) {
+      constexpr int WC = decltype(wc)::value;
+      constexpr int GMAX = L::DVM / GR;  // columns of the widest d_v
+      constexpr int RB = C * GMAX / NT < 1 ? 1 : C * GMAX / NT;
+      constexpr int NBLK = C / RB;
+      static_assert(GMAX * NBLK <= NT && C % RB == 0, "one column block per thread");
+      const int gc = tid_s / NBLK, r0 = (tid_s % NBLK) * RB;
+      const bool live = gc < GPRV && r0 < n;
+      uint4 res[RB];
+      if (live) {
+        const float* tp = tv + gc * GR * WC;
+        float taps[GR][WC], acc[RB][GR];
+#pragma unroll
+        for (int e = 0; e < GR; ++e)
+#pragma unroll
+          for (int j = 0; j < WC; ++j) taps[e][j] = tp[e * WC + j];
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+          for (int e = 0; e < GR; ++e) acc[i][e] = 0.f;
+#pragma unroll
+        for (int t = 0; t < RB + WC - 1; ++t) {
+          const int rr = r0 - (WC - 1) + t;
+          const uint4 raw = ld16(rr >= 0 ? sVr + rr * LV + swz<TI, SWV>(rr, gc * GR)
+                                         : hv + (rr + WC - 1) * L::DVM + gc * GR);
+          TI x[GR];
+          __builtin_memcpy(x, &raw, 16);
+#pragma unroll
+          for (int j = 0; j < WC; ++j) {
+            const int i = t - j;
+            if (i < 0 || i >= RB) continue;
+#pragma unroll
+            for (int e = 0; e < GR; ++e) acc[i][e] += taps[e][j] * to_float(x[e]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          TI y[GR];
+#pragma unroll
+          for (int e = 0; e < GR; ++e) y[e] = conv_act<TI>(acc[i][e], p.qkv_silu);
+          __builtin_memcpy(&res[i], y, 16);
+        }
+      }
+      __syncthreads();
+      if (live) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          const int r = r0 + i;
+          if (r < n) st16(sVr + r * LV + swz<TI, SWV>(r, gc * GR), res[i]);  // padded rows stay zero
+        }
+      }
+    };
+    dispatch_int<1, L::KW + 1>(W, v_pass);
+  };
   // V rows from the registers load_head filled (rows past the chunk's end
-  // are zero) into the V region
-  auto store_v = [&]() {
+  // are zero) into the V region (through the convolution when it is on;
+  // the caller's barrier follows)
+  auto store_v = [&](int gi_, int h_) {
     int tid_s;
     asm volatile("v_mov_b32 %0, %1" : "=v"(tid_s) : "v"(tid));
 #pragma unroll
@@ -521,7 +744,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
       if (idx < C * GPRV) {
         const int r = idx >> LGV, gc = idx & (GPRV - 1);
         uint4 vv = vreg[i];
-        if (p.qkv_silu) {
+        if (p.qkv_silu && !conv) {
           TI x[GR];
           __builtin_memcpy(x, &vv, 16);
 #pragma unroll
@@ -531,6 +754,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
         st16(sVr + r * LV + swz<TI, SWV>(r, gc * GR), vv);
       }
     }
+    if constexpr (conv) conv_v(gi_, h_, tid_s);
   };
   // The first value head's V rows go to registers (its gates came with the
   // q, k rows): they arrive while the Gram products, A, P and T are formed.
@@ -634,7 +858,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     // there already) and the gate scan.  Then the next value head's inputs
     // are requested.
     if (gi > 0) {
-      store_v();
+      store_v(gi, h);
       if (wave == 0) gate_scan(h);
       __syncthreads();
     }
@@ -822,7 +1046,7 @@ __global__ __launch_bounds__(kWyThreads, 4) void wy_kernel(WyParams p) {
     // this value head's V rows into LDS for U~ = Tv V (the first head's
     // arrive in registers here; later heads' were stored at the loop top),
     // then the next value head's inputs are requested
-    if (gi == 0) store_v();
+    if (gi == 0) store_v(gi, h);
     if (gi + 1 < grp) load_head(h + 1, true);
     __syncthreads();
 
@@ -1671,6 +1895,20 @@ struct DecodeShape {
   static constexpr int RPT = DK / RG;                                  // rows per thread
 };
 
+// Channel c of sequence i's token x through the short convolution: its
+// history rows, then x with the last tap; silu when on; rounded to TI.
+template <typename TI>
+__device__ __forceinline__ float decode_conv(const DecodeParams& p, int i, int c, float x) {
+  const int W = p.conv_width;
+  const float* w = p.conv_w + (int64_t)c * W;
+  const TI* hist = (const TI*)p.conv_state;
+  float acc = 0.f;
+  for (int j = 0; j + 1 < W; ++j)
+    acc += w[j] * (hist ? to_float(hist[((int64_t)i * (W - 1) + j) * p.conv_d + c]) : 0.f);
+  acc += w[W - 1] * x;
+  return to_float(conv_act<TI>(acc, p.qkv_silu));
+}
+
 template <typename TI, int DK, int DV>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(DecodeParams p) {
   using D = DecodeShape<DK, DV>;
@@ -1696,7 +1934,10 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(Decod
   for (int d = tid; d < DK; d += NT) {
     sq[d] = to_float(qr[d]);
     sk[d] = to_float(kr[d]);
-    if (p.qkv_silu) {
+    if (p.conv_w) {
+      sq[d] = decode_conv<TI>(p, i, kh * DK + d, sq[d]);
+      sk[d] = decode_conv<TI>(p, i, (p.hk + kh) * DK + d, sk[d]);
+    } else if (p.qkv_silu) {
       sq[d] = qkv_act<TI>(sq[d]);
       sk[d] = qkv_act<TI>(sk[d]);
     }
@@ -1721,7 +1962,10 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(Decod
   if (p.beta_logits) beta = 1.f / (1.f + __expf(-beta));
   const float alpha = expf(g);
   f32x4 vj = load4<TI>((const TI*)p.v + (int64_t)i * p.v_st + (int64_t)h * p.v_sh + c0);
-  if (p.qkv_silu) {
+  if (p.conv_w) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vj[e] = decode_conv<TI>(p, i, 2 * p.hk * DK + h * p.dv + c0 + e, vj[e]);
+  } else if (p.qkv_silu) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) vj[e] = qkv_act<TI>(vj[e]);
   }
@@ -1794,7 +2038,10 @@ static int launch_pair(int stage, const WyParams* wy, const ScanParams* sc,
                        dim3 grid, hipStream_t s) {
   if constexpr (fits<TI, C, DK>()) {
     if (stage == 0) {
-      hipLaunchKernelGGL((wy_kernel<TI, C, DK>), grid, dim3(kWyThreads), 0, s, *wy);
+      if (wy->conv_w)
+        hipLaunchKernelGGL((wy_kernel<TI, C, DK, true>), grid, dim3(kWyThreads), 0, s, *wy);
+      else
+        hipLaunchKernelGGL((wy_kernel<TI, C, DK, false>), grid, dim3(kWyThreads), 0, s, *wy);
     } else if (sc->nsl == 2) {
       if constexpr (fits_group<TI, C, DK>())
         hipLaunchKernelGGL((scan_kernel<TI, C, DK, 2>), grid, dim3(scan_threads<2>()), 0, s, *sc);
@@ -2038,6 +2285,72 @@ static hipError_t launch_output_gate_t(int dv, const GateParams& p, hipStream_t 
 hipError_t launch_output_gate(bool bf16, int dv, const GateParams& p, hipStream_t s) {
   if (p.rows <= 0) return hipSuccess;
   return bf16 ? launch_output_gate_t<gdn::bf16>(dv, p, s) : launch_output_gate_t<float>(dv, p, s);
+}
+
+// ---------------------------------------------------------------------------
+// The short convolution's state after a call (GDN_FLAG_QKV_CONV): for
+// sequence s (L rows) and channel c, row j of the new state is row L + j of
+// the old history followed by the sequence, i.e. input row L + j - (W - 1)
+// when that is >= 0, else history row L + j.  One thread per (sequence,
+// channel) reads all of its values before it writes any, so the new state
+// may overwrite the old.
+
+constexpr int kConvStateThreads = 256;
+
+template <typename TI>
+__global__ __launch_bounds__(kConvStateThreads) void conv_state_kernel(ConvStateParams p) {
+  const int64_t u = (int64_t)blockIdx.x * kConvStateThreads + threadIdx.x;
+  if (u >= (int64_t)p.n_seq * p.d) return;
+  const int seq = (int)(u / p.d), c = (int)(u % p.d);
+  const int W = p.width;
+  int64_t tok0;
+  int L;
+  if (p.seq_start) {
+    tok0 = p.seq_start[seq];
+    L = p.seq_start[seq + 1] - p.seq_start[seq];
+  } else {
+    tok0 = (int64_t)seq * p.seq_len;
+    L = p.seq_len;
+  }
+  // channel c of q | k | v: its column of the token rows
+  const int qk = p.hk * p.dk;
+  const TI* x;
+  int64_t st;
+  if (c < qk) {
+    x = (const TI*)p.q + (int64_t)(c / p.dk) * p.q_sh + c % p.dk;
+    st = p.q_st;
+  } else if (c < 2 * qk) {
+    x = (const TI*)p.k + (int64_t)((c - qk) / p.dk) * p.k_sh + (c - qk) % p.dk;
+    st = p.k_st;
+  } else {
+    x = (const TI*)p.v + (int64_t)((c - 2 * qk) / p.dv) * p.v_sh + (c - 2 * qk) % p.dv;
+    st = p.v_st;
+  }
+  const TI* hin = (const TI*)p.state_in;
+  TI vals[kConvMaxWidth - 1];
+#pragma unroll
+  for (int j = 0; j < kConvMaxWidth - 1; ++j) {
+    if (j >= W - 1) break;
+    const int r = L + j;
+    if (r >= W - 1) vals[j] = x[(tok0 + r - (W - 1)) * st];
+    else vals[j] = hin ? hin[((int64_t)seq * (W - 1) + r) * p.d + c] : from_float<TI>(0.f);
+  }
+  TI* hout = (TI*)p.state_out;
+#pragma unroll
+  for (int j = 0; j < kConvMaxWidth - 1; ++j)
+    if (j < W - 1) hout[((int64_t)seq * (W - 1) + j) * p.d + c] = vals[j];
+}
+
+hipError_t launch_conv_state(bool bf16, const ConvStateParams& p, hipStream_t s) {
+  const int64_t threads = (int64_t)p.n_seq * p.d;
+  if (threads <= 0 || p.width < 2) return hipSuccess;
+  const int64_t blocks = (threads + kConvStateThreads - 1) / kConvStateThreads;
+  if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (bf16)
+    hipLaunchKernelGGL((conv_state_kernel<gdn::bf16>), dim3((unsigned)blocks), dim3(kConvStateThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((conv_state_kernel<float>), dim3((unsigned)blocks), dim3(kConvStateThreads), 0, s, p);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -28,6 +28,10 @@ hipError_t launch_scan_two_level(int chunk, int dk, const ScanParams& p, hipStre
 
 hipError_t launch_decode(bool bf16, int dk, const DecodeParams& p, hipStream_t s);
 
+// The short convolution's state after a prefill or a decode step: the last
+// width - 1 raw rows of every sequence and channel.
+hipError_t launch_conv_state(bool bf16, const ConvStateParams& p, hipStream_t s);
+
 // GDN_DEBUG_CHECK: ORs the fault bits (gdn_cu_check.h) of cu[0 .. n_seq]
 // into one word and stores it at *faults (one workgroup).
 hipError_t launch_check_cu(const int32_t* cu, int64_t n_seq, int64_t t_total, int32_t* faults,

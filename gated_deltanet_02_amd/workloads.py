@@ -43,6 +43,12 @@ z ~ N(0, 1) rounded to v's dtype; the norm weight 1 + 0.1 N(0, 1) float32.
 ``make_gate_rows`` draws standalone rows for the output gate alone: rows of
 N(0, 1) times a per-row factor (0, 1e-3, 1e3 or log-uniform in [0.05, 20],
 as "scaled" above), z ~ N(0, 2) with a few entries at +-30.
+
+The short convolution before the activation (``make_conv_inputs``, its own
+seeded stream): taps N(0, 1/W) float32 over the D = 2 Hk dk + Hv dv
+channels (q | k | v), plus 1 on the last tap (so the current token keeps a
+share of about one); history rows [N, W - 1, D] drawn as the inputs are
+(unit q and k rows per key head, v N(0, 1)), rounded to the storage dtype.
 """
 from __future__ import annotations
 
@@ -58,6 +64,7 @@ __all__ = [
     "GateInputs",
     "make_gate_inputs",
     "make_gate_rows",
+    "make_conv_inputs",
     "make_workload",
     "permute_sequences",
     "select_sequences",
@@ -337,3 +344,22 @@ def make_gate_rows(rows: int, heads: int, dv: int, dtype: str = "bf16", seed: in
     z = np.where(hot, np.where(rng.random((rows, heads, dv)) < 0.5, 30.0, -30.0), z).astype(np.float32)
     nw = (1.0 + 0.1 * rng.standard_normal(dv)).astype(np.float32)
     return _store(x, dtype), _store(z, dtype), torch.from_numpy(nw)
+
+
+def make_conv_inputs(w: Workload, width: int = 4, seed: int = 3):
+    """Taps [D, W] fp32 and history rows [N, W - 1, D] in the workload's
+    dtype for the short convolution (recipe in the module docstring; draw
+    order taps -> q history -> k history -> v history)."""
+    rng = np.random.default_rng([seed, 0xC0DE])
+    T, hk, dk = w.q.shape
+    hv, dv = w.v.shape[1], w.v.shape[2]
+    D = 2 * hk * dk + hv * dv
+    taps = rng.standard_normal((D, width), dtype=np.float32) / np.float32(np.sqrt(width))
+    taps[:, width - 1] += 1.0
+    n, h = w.n_seqs, width - 1
+    hq = _unit_rows(rng, (n, h, hk, dk)).reshape(n, h, hk * dk)
+    hkk = _unit_rows(rng, (n, h, hk, dk)).reshape(n, h, hk * dk)
+    hvv = rng.standard_normal((n, h, hv * dv), dtype=np.float32)
+    dt = "bf16" if w.q.dtype == torch.bfloat16 else "fp32"
+    hist = np.concatenate([hq, hkk, hvv], axis=2).astype(np.float32)
+    return torch.from_numpy(taps.astype(np.float32)), _store(hist, dt)

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 7
+#define GDN_ABI_VERSION 8
 
 /* Status codes. */
 #define GDN_OK 0
@@ -128,6 +128,20 @@ typedef struct gdn_options {
    * WY workgroups an MI355X holds at once, else the fewest of equal
    * length; -1: never; n > 0: segments of n chunks.                      */
   int32_t segment_chunks;
+  /* GDN_FLAG_QKV_CONV: the short convolution's taps, an f32 device array
+   * [D][conv_width] (channel-major, the last tap multiplies the current
+   * token) over D = 2 Hk dk + Hv dv channels in the order q | k | v, each
+   * part in its tensor's [H][d] order, 16-byte aligned; its width, 1 .. 4
+   * (default 4); the raw rows before each sequence, a contiguous device
+   * array [N][conv_width - 1][D] of the input dtype, 16-byte aligned, or
+   * NULL for zeros (fresh sequences); and where the last conv_width - 1 raw
+   * rows of each sequence go, the same layout, or NULL (not written).
+   * conv_state_out may be conv_state_in.  Sizes are not checked: the arrays
+   * must hold what these shapes name.                                     */
+  const float* conv_weight;
+  int32_t conv_width;
+  const void* conv_state_in;
+  void* conv_state_out;
 } gdn_options;
 
 /*
@@ -176,12 +190,36 @@ typedef struct gdn_options {
  * above: the pages run "fused norm, activation" operations around the
  * chunked Gated DeltaNet and name SiLU as the activation they check
  * ("Open-Jev-27B-v1.1 native text worker", section "Validation and
- * optimization scope"); they name no convolution, so none is applied.  In
- * the prefill the WY kernel writes the activated key rows to the workspace
+ * optimization scope").  Alone it applies no convolution (see
+ * GDN_FLAG_QKV_CONV).  In the prefill the WY kernel writes the activated key rows to the workspace
  * (the `k_act` region, laid out as a contiguous [T][Hk][dk] tensor of the
  * input dtype) for the scan.
  */
 #define GDN_FLAG_QKV_SILU 8u
+
+/*
+ * GDN_FLAG_QKV_CONV: before the activation, every channel c of q, k and v
+ * passes through a causal depthwise convolution of width W = conv_width
+ * along the tokens of its own sequence:
+ *     y[t, c] = sum_{j=0}^{W-1} conv_weight[c][j] * e[t + j, c],
+ * e being the sequence's W - 1 history rows (conv_state_in, or zeros)
+ * followed by its raw rows.  y then goes through silu when
+ * GDN_FLAG_QKV_SILU is also set, and is rounded once to the input dtype;
+ * the L2 norms of q and k are taken of the result.  Computed in fp32 as the
+ * rows are loaded: the WY kernel reads W - 1 rows before each chunk (from
+ * the inputs, or from conv_state_in at a sequence's first chunk) and writes
+ * the chunk's key rows as used to the `k_act` workspace region for the
+ * scan.  With conv_state_out the last W - 1 raw rows of each sequence (the
+ * history a later call continues from; fewer rows than that shift in the
+ * tail of conv_state_in) are written after the WY stage.  The decode step
+ * does the same per token and shifts its row into conv_state_out.
+ * Reading: the pages name "fused norm, activation" operations around the
+ * chunked Gated DeltaNet ("Open-Jev-27B-v1.1 native text worker", section
+ * "Validation and optimization scope") and name no convolution; this is the
+ * short convolution a Gated DeltaNet layer runs on its q, k, v projections
+ * before the SiLU, for callers that fuse it here.
+ */
+#define GDN_FLAG_QKV_CONV 16u
 
 /*
  * The state scan's schedule.  Each chunk maps its incoming state affinely
@@ -317,8 +355,9 @@ typedef struct gdn_workspace_layout {
    * pass, and the state carried between segments, f32 [N][Hv][dk][dv]    */
   int32_t segment_chunks;
   size_t segment_state;
-  /* GDN_FLAG_QKV_SILU: the activated key rows, a contiguous [T][Hk][dk]
-   * tensor of the input dtype (0 without the flag)                       */
+  /* GDN_FLAG_QKV_SILU or GDN_FLAG_QKV_CONV: the key rows as the
+   * recurrence uses them (activated, convolved), a contiguous [T][Hk][dk]
+   * tensor of the input dtype (0 without either flag)                    */
   size_t k_act;
 } gdn_workspace_layout;
 
@@ -347,7 +386,11 @@ int gdn_get_workspace_layout(const gdn_tensor* q, const gdn_tensor* k,
  *            written in place; v and out rows start on 4-element
  *            boundaries (address and strides)
  *   opts     NULL or options; scale, l2_eps, flags and the gate fields are
- *            used (with GDN_FLAG_OUTPUT_GATE, gate_z is laid out as out)
+ *            used (with GDN_FLAG_OUTPUT_GATE, gate_z is laid out as out;
+ *            with GDN_FLAG_QKV_CONV the convolution fields, N sequences of
+ *            one token each: the history is read from conv_state_in and
+ *            the step's raw row shifted into conv_state_out, which may be
+ *            conv_state_in)
  * dk, dv in {16, 32, 64, 128}.  N = 0 enqueues nothing.  Allocates nothing.
  * Returns a GDN_* status; validation errors enqueue nothing.
  */

@@ -87,8 +87,17 @@ int main() {
     o.chunk = 48;
     expect(prefill(w, nullptr, &o), GDN_ERR_UNSUPPORTED, "chunk 48");
     gdn_default_options(&o);
-    o.flags = 16;
+    o.flags = 32;
     expect(prefill(w, nullptr, &o), GDN_ERR_SHAPE, "unknown flag");
+    gdn_default_options(&o);
+    o.flags = GDN_FLAG_QKV_CONV;
+    expect(prefill(w, nullptr, &o), GDN_ERR_NULL_ARG, "convolution without taps");
+    o.conv_weight = (const float*)0x200000;
+    o.conv_width = 5;
+    expect(prefill(w, nullptr, &o), GDN_ERR_SHAPE, "convolution width 5");
+    o.conv_width = 3;
+    o.conv_state_in = (const void*)0x200008;
+    expect(prefill(w, nullptr, &o), GDN_ERR_LAYOUT, "misaligned convolution history");
     gdn_default_options(&o);
     o.flags = GDN_FLAG_OUTPUT_GATE;
     expect(prefill(w, nullptr, &o), GDN_ERR_NULL_ARG, "gate without z");

@@ -20,6 +20,7 @@ hipError_t launch_scan(bool, int, int, const ScanParams&, int, hipStream_t) { re
 bool two_level_available(bool bf16, int chunk, int dk) { return bf16 && chunk >= 32 && dk >= 32; }
 hipError_t launch_scan_two_level(int, int, const ScanParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_decode(bool, int, const DecodeParams&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_conv_state(bool, const ConvStateParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_check_cu(const int32_t*, int64_t, int64_t, int32_t*, hipStream_t) { return hipErrorNoDevice; }
 hipError_t debug_word_region(int32_t**) { return hipErrorNoDevice; }
 hipError_t launch_output_gate(bool, int, const GateParams&, hipStream_t) { return hipErrorNoDevice; }

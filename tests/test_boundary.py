@@ -222,7 +222,7 @@ def test_flags_option(lib):
     """Unknown flag bits are rejected by the prefill and the decode step."""
     a = base()
     o = B.options()
-    o.flags = 16
+    o.flags = 32
     assert call(lib, a["q"], a["k"], a["v"], a["g"], a["b"], out=a["out"], opts=o) == -3
     o.flags = B.FLAG_BETA_LOGITS
     N, hk, hv, dk, dv = 2, 1, 1, 16, 16
@@ -230,7 +230,7 @@ def test_flags_option(lib):
     q, v = fake((N, hk, dk), torch.bfloat16), fake((N, hv, dv), torch.bfloat16)
     g, st = fake((N, hv), torch.float32), fake((N, hv, dk, dv), torch.float32)
     bad = B.options()
-    bad.flags = 0x10
+    bad.flags = 0x20
     assert lib.gdn_decode(r(q), r(q), r(v), r(g), r(g), r(st), r(v), r(bad), None) == -3
 
 
@@ -254,9 +254,51 @@ def test_qkv_silu_option(lib):
     # validation passes; the call then stops at the fake (never dereferenced)
     # device addresses only if it reaches the GPU, which a bad flag never does
     bad = B.options()
-    bad.flags = 16 | 8
+    bad.flags = 32 | 8
     assert lib.gdn_decode(r(qd), r(qd), r(vd), r(g), r(g), r(st), r(vd), r(bad), None) == -3
     assert o.flags == 8
+
+
+def test_qkv_conv_option(lib):
+    """GDN_FLAG_QKV_CONV: the width must be 1 .. 4, the taps given and the
+    taps and history arrays 16-byte aligned, in the prefill and the decode
+    step; the prefill's workspace gains the key rows as used (as with the
+    activation)."""
+    assert B.FLAG_QKV_CONV == 16
+    o = B.options()
+    assert o.conv_width == 4 and o.conv_weight is None
+    q = torch.empty(1000, 2, 128, dtype=torch.bfloat16)
+    v = torch.empty(1000, 6, 64, dtype=torch.bfloat16)
+    conv = B.options()
+    conv.flags = B.FLAG_QKV_CONV
+    conv.conv_weight = 0x300000
+    lay = G.gdn_get_workspace_layout(q, q, v, opts=conv)
+    assert lay.k_act > 0 and lay.total_bytes == lay.k_act + 1000 * 2 * 128 * 2
+    a = base()
+    args = (a["q"], a["k"], a["v"], a["g"], a["b"])
+    for width, want in ((0, -3), (5, -3), (-1, -3)):
+        bad = B.options()
+        bad.flags, bad.conv_weight, bad.conv_width = B.FLAG_QKV_CONV, 0x300000, width
+        assert call(lib, *args, out=a["out"], opts=bad) == want, width
+    bad = B.options()
+    bad.flags = B.FLAG_QKV_CONV
+    assert call(lib, *args, out=a["out"], opts=bad) == -1  # no taps
+    for field in ("conv_weight", "conv_state_in", "conv_state_out"):
+        bad = B.options()
+        bad.flags, bad.conv_weight = B.FLAG_QKV_CONV, 0x300000
+        setattr(bad, field, 0x300008)
+        assert call(lib, *args, out=a["out"], opts=bad) == -4, field
+    N, hk, hv, dk, dv = 2, 1, 1, 16, 16
+    r = ctypes.byref
+    qd, vd = fake((N, hk, dk), torch.bfloat16), fake((N, hv, dv), torch.bfloat16)
+    g, st = fake((N, hv), torch.float32), fake((N, hv, dk, dv), torch.float32)
+    bad = B.options()
+    bad.flags, bad.conv_weight, bad.conv_width = B.FLAG_QKV_CONV, 0x300000, 7
+    assert lib.gdn_decode(r(qd), r(qd), r(vd), r(g), r(g), r(st), r(vd), r(bad), None) == -3
+    bad.conv_width, bad.conv_weight = 4, None
+    assert lib.gdn_decode(r(qd), r(qd), r(vd), r(g), r(g), r(st), r(vd), r(bad), None) == -1
+    bad.conv_weight, bad.conv_state_in = 0x300000, 0x300004
+    assert lib.gdn_decode(r(qd), r(qd), r(vd), r(g), r(g), r(st), r(vd), r(bad), None) == -4
 
 
 def test_gate_options(lib):
