@@ -73,31 +73,41 @@ def algorithmic_flops(w) -> int:
 
 
 def read_sclk_mhz():
-    """The shader clock rocm-smi reports for GPU 0 (MHz), or None."""
+    """The shader clock (MHz) of the first GPU that exposes one in sysfs: the
+    level the driver marks current ('*') in pp_dpm_sclk, which is what
+    rocm-smi reports.  A file read: no program is started (a child program
+    would be an exec from a process that has initialised the GPU, and under
+    rocprofv3 every process does).  None if there is none."""
+    import glob
     import re
-    import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
-    except (OSError, subprocess.SubprocessError):
-        return None
-    m = re.search(r"sclk[^\n]*?\((\d+)\s*Mhz\)", r.stdout, flags=re.IGNORECASE)
-    return int(m.group(1)) if m else None
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                text = f.read()
+        except OSError:
+            continue
+        for line in text.splitlines():
+            if line.rstrip().endswith("*"):
+                m = re.search(r"(\d+)\s*mhz", line, flags=re.IGNORECASE)
+                if m:
+                    return int(m.group(1))
+    return None
 
 
-def sclk_under_load(step, torch, seconds: float = 5.0):
-    """rocm-smi's shader clock read while the GPU keeps running `step` (the
-    read takes a fraction of a second; the GPU is kept busy meanwhile)."""
-    import threading
-    box = {}
-    th = threading.Thread(target=lambda: box.update(v=read_sclk_mhz()), daemon=True)
+def sclk_under_load(step, torch, seconds: float = 1.0):
+    """The shader clock read while the GPU runs `step` back to back: after
+    `seconds` of that load, read with a few milliseconds of steps still
+    queued, so that the GPU is busy during the read."""
     t0 = time.perf_counter()
-    th.start()
-    while th.is_alive() and time.perf_counter() - t0 < seconds:
+    while time.perf_counter() - t0 < seconds:
         for _ in range(50):
             step()
         torch.cuda.synchronize()
-    th.join(timeout=1.0)
-    return box.get("v")
+    for _ in range(200):
+        step()
+    v = read_sclk_mhz()
+    torch.cuda.synchronize()
+    return v
 
 
 def load_traffic(workload: str, kernel: str):
