@@ -217,6 +217,9 @@ def main():
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--scan-split", choices=("auto", "one", "two"), default="auto",
                     help="the state scan's schedule: the library's choice, one pass, or two-level")
+    ap.add_argument("--fused", choices=("none", "silu", "conv"), default="none",
+                    help="steps fused into the loads of q, k, v: none, silu, or a width-4 short "
+                         "convolution (seeded taps and history) then silu")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -256,7 +259,13 @@ def main():
     d = W.to_device(w, dev)
     cu = d["cu_seqlens"] if w.n_seqs > 1 else None
     split = {"auto": G.SCAN_AUTO, "one": G.SCAN_ONE_PASS, "two": G.SCAN_TWO_LEVEL}[args.scan_split]
-    opts = G.options(chunk=w.chunk, scan_split=split)
+    fused = {}
+    if args.fused == "silu":
+        fused = dict(qkv_silu=True)
+    elif args.fused == "conv":
+        taps, hist = W.make_conv_inputs(w, 4)
+        fused = dict(qkv_silu=True, conv_weight=taps.to(dev), conv_state_in=hist.to(dev))
+    opts = G.options(chunk=w.chunk, scan_split=split, **fused)
     lay = G.gdn_get_workspace_layout(d["q"], d["k"], d["v"], cu, opts=opts)
     full = G.PreparedPrefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, d["init_state"],
                              d["out"], d["final_state"], opts=opts)
@@ -323,7 +332,8 @@ def main():
     per_kernel = {}
     counted = []
     for k, t in kernels.items():
-        tb = load_traffic(args.workload, k)
+        # the counted traffic on record is that of the kernels without fused steps
+        tb = load_traffic(args.workload, k) if args.fused == "none" else None
         if tb is not None:
             tb *= n_seg
         counted.append(tb)
@@ -353,7 +363,7 @@ def main():
                    "seed": 0, "parallelism": "single GPU",
                    "scan": (f"two-level (split at chunk {lay.split_chunks})" if lay.split_chunks
                             else "one pass"),
-                   "segments": n_seg},
+                   "segments": n_seg, "fused": args.fused},
         "roofline": {"bound": "hbm", "kernel": "prefill (wy_kernel + scan_kernel launches)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

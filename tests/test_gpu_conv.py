@@ -114,6 +114,22 @@ def test_prefill_with_conv(name, kw, width, silu, with_hist, extra):
         history_equal(h_out, rh, name)
 
 
+def test_prompt_4k_full_with_conv():
+    """The throughput workload at full size (4096 tokens, 16 heads, d = 128)
+    with the convolution and silu, compared in full."""
+    w = W.make_workload("prompt_4k")
+    taps, hist = W.make_conv_inputs(w, 4)
+    d = W.to_device(w)
+    h_out = torch.empty_like(hist).cuda()
+    G.gdn_prefill_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], None, None, d["out"], d["final_state"],
+                     opts=G.options(qkv_silu=True, conv_weight=taps.cuda(), conv_state_in=hist.cuda(),
+                                    conv_state_out=h_out))
+    torch.cuda.synchronize()
+    ro, rf, rh = conv_reference(w, taps, hist, True)
+    check(w, d["out"].float().cpu().numpy(), d["final_state"].cpu().numpy(), ro, rf, "conv prompt_4k full")
+    history_equal(h_out, rh, "prompt_4k full")
+
+
 def test_uniform_batch_and_in_place_history():
     """[B, T, H, d] inputs without cu_seqlens (sequences at the batch
     stride), the history read and rewritten in place."""
