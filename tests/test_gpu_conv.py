@@ -85,6 +85,7 @@ CASES = [
     ("prompt_4k", dict(lengths=[200], hk=1, hv=2, dk=32, dv=128, chunk=16), 4, True, True, {}),
     ("tiny_fp32", dict(lengths=[150], hk=2, hv=4, dk=64, dv=32, chunk=32), 4, True, True, {}),
     ("tiny_fp32", dict(lengths=[90, 1, 41], hk=1, hv=3, dk=32, dv=64, chunk=16), 3, True, True, {}),
+    ("edge_mix", dict(lengths=[0, 2, 1, 0, 130], hk=2, hv=2), 4, True, True, {}),  # empty, 1, 2 tokens
     ("prompt_4k", dict(lengths=[500], hk=2, hv=4), 4, False, True, {}),          # no silu
     ("prompt_4k", dict(lengths=[300], hk=2, hv=2), 1, True, False, {}),          # width 1
     ("prompt_4k", dict(lengths=[1000], hk=2, hv=4), 4, True, True, dict(segment_chunks=3)),
