@@ -74,7 +74,7 @@ def algorithmic_flops(w) -> int:
 
 def read_sclk_mhz():
     """The shader clock (MHz) of the first GPU that exposes one in sysfs: the
-    level the driver marks current ('*') in pp_dpm_sclk, which is what
+    level the amdgpu kernel driver marks current ('*') in pp_dpm_sclk, which is what
     rocm-smi reports.  A file read: no program is started (a child program
     would be an exec from a process that has initialised the GPU, and under
     rocprofv3 every process does).  None if there is none."""

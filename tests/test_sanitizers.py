@@ -9,7 +9,7 @@
   host-only stand-ins for the launchers and the HIP runtime
   (tests/native/api_stubs.cpp) and driven by tests/native/api_sanitize.cpp.
   No GPU code is built; the sanitizers apply to host code only.
-A sanitizer report makes the driver exit non-zero.
+A sanitizer report makes the test program exit non-zero.
 """
 import os
 import shutil
