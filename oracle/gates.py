@@ -30,7 +30,9 @@ plainest one the rest supports:
   The library applies it to the outputs as the prefill stores them (rounded
   to the output type) and rounds y once.
 
-* The short convolution before the activation.  Each channel of q, k and v
+* The short convolution before the activation (the pages name none; this
+  is the one a Gated DeltaNet layer runs on its q, k, v projections before
+  the SiLU, taken as this library's reading).  Each channel of q, k and v
   (one column of the [T, H * d] token rows) passes through a causal
   depthwise convolution of width W along the tokens of its own sequence:
 
