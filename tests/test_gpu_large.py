@@ -62,3 +62,30 @@ def test_offsets_past_2_pow_31():
             assert torch.count_nonzero(out[s]) == 0 and torch.count_nonzero(fin[s]) == 0, s
         del out
         torch.cuda.empty_cache()
+
+
+def test_decode_state_past_2_pow_31():
+    """Decode over 8500 sequences x 16 heads: the f32 state holds 2.2e9
+    elements (8.9 GB), the last sequence's past element 2^31; only it holds
+    seeded data."""
+    N = 8500
+    assert (N - 1) * H * D * D > 2 ** 31
+    w = W.make_workload("prompt_4k", lengths=[1], init_std=0.5)
+    ro, rf = oracle.reference_workload(w)
+    dev = torch.device("cuda")
+    q = torch.zeros(N, H, D, dtype=torch.bfloat16, device=dev)
+    k, v = torch.zeros_like(q), torch.zeros_like(q)
+    g = torch.zeros(N, H, dtype=torch.float32, device=dev)
+    beta = torch.zeros_like(g)
+    state = torch.zeros(N, H, D, D, dtype=torch.float32, device=dev)
+    for dst, src in ((q, w.q), (k, w.k), (v, w.v), (g, w.g), (beta, w.beta)):
+        dst[N - 1].copy_(src[0].to(dev))
+    state[N - 1].copy_(w.init_state[0].to(dev))
+    out = G.gdn_decode(q, k, v, g, beta, state)
+    torch.cuda.synchronize()
+    es = U.rel_l2(state[N - 1:].cpu().numpy(), rf)
+    eo = U.max_abs(out[N - 1:].float().cpu().numpy(), ro)
+    U.say(f"  decode {N} x {H} heads: last sequence state rel-L2 {es:.3e}, out max-abs {eo:.3e}")
+    assert es <= U.F32_RELL2 and eo <= 8e-3 * max(1.0, float(abs(ro).max()))
+    for s in (0, N // 2, N - 2):
+        assert torch.count_nonzero(out[s]) == 0 and torch.count_nonzero(state[s]) == 0, s
