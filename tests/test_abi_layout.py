@@ -3,7 +3,9 @@
 include/gdn.h is compiled as C99 by gcc (no C++ in a C header), and a small
 program prints the size of each struct the binding mirrors and the offset
 of every field; the ctypes structures must agree field by field, so that
-the options and layouts the binding passes are read as written.
+the options and layouts the binding passes are read as written.  The
+header's status, dtype, stage, flag and scan constants must equal the
+binding's.
 """
 import ctypes
 import os
@@ -52,3 +54,37 @@ def test_binding_structs_match_the_c_header(tmp_path):
         assert got[(name, "size")] == ctypes.sizeof(cls), name
         for field, _ in cls._fields_:
             assert got[(name, field)] == getattr(cls, field).offset, f"{name}.{field}"
+
+
+def test_binding_constants_match_the_c_header():
+    """Every status, dtype, stage, flag and scan constant the header
+    defines has the same value in the binding."""
+    import re
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    defs = {m.group(1): m.group(2) for m in re.finditer(r"^#define (GDN_\w+) (.+?)\s*(?:/\*.*)?$", src, re.M)}
+    ints = {}
+    for name, text in defs.items():
+        m = re.fullmatch(r"\(?(-?\d+)u?\)?", text.strip())
+        if m:
+            ints[name] = int(m.group(1))
+    expect = {
+        "GDN_DTYPE_BF16": B._DTYPES[B.torch.bfloat16], "GDN_DTYPE_F32": B._DTYPES[B.torch.float32],
+        "GDN_DTYPE_I32": B._DTYPES[B.torch.int32],
+        "GDN_STAGE_TABLE": B.STAGE_TABLE, "GDN_STAGE_WY": B.STAGE_WY, "GDN_STAGE_SCAN": B.STAGE_SCAN,
+        "GDN_STAGE_ALL": B.STAGE_ALL,
+        "GDN_SCAN_AUTO": B.SCAN_AUTO, "GDN_SCAN_ONE_PASS": B.SCAN_ONE_PASS,
+        "GDN_SCAN_TWO_LEVEL": B.SCAN_TWO_LEVEL,
+        "GDN_FLAG_BETA_LOGITS": B.FLAG_BETA_LOGITS, "GDN_FLAG_DECAY_PROJ": B.FLAG_DECAY_PROJ,
+        "GDN_FLAG_OUTPUT_GATE": B.FLAG_OUTPUT_GATE, "GDN_FLAG_QKV_SILU": B.FLAG_QKV_SILU,
+        "GDN_FLAG_QKV_CONV": B.FLAG_QKV_CONV,
+    }
+    for name, value in B.STATUS_NAMES.items():
+        expect[value] = name
+    for name, value in expect.items():
+        assert ints[name] == value, name
+    # every flag, stage and scan constant of the header is covered
+    for name in ints:
+        if name.startswith(("GDN_FLAG_", "GDN_STAGE_", "GDN_SCAN_", "GDN_ERR_", "GDN_DTYPE_")):
+            assert name in expect, f"{name} has no binding constant"
+    assert ints["GDN_OK"] == 0 and B.GDN_OK == 0
+    assert B.NOALLOC_SCRATCH_BYTES == 96 << 20 and "((size_t)96 << 20)" in defs["GDN_NOALLOC_SCRATCH_BYTES"]
