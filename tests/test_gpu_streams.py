@@ -7,6 +7,7 @@ stream (default priority) and must equal, bit for bit, the same call on the
 current stream; the temporary workspace case also allocates and overwrites
 memory on the current stream while the side stream's kernels run, which
 would corrupt the result if the block were handed out again too early.
+One graph cache is also shared by four threads with a stream each.
 """
 import pytest
 import torch
@@ -105,4 +106,49 @@ def test_graph_replays_on_a_side_stream():
         assert torch.equal(d["out"], ref_o) and torch.equal(d["final_state"], ref_f), f"replay {it}"
     st = cache.stats()
     assert st["misses"] == 1 and st["hits"] == 2 and st["fallbacks"] == 0
+    cache.close()
+
+
+def test_one_graph_cache_shared_by_threads():
+    """Four threads share one cache, each with its own buffers, workspace and
+    stream (calls into the cache are serialised by the library); every
+    result is bit-equal to the eager call."""
+    import threading
+    w, d = _inputs()
+    opts = G.options(chunk=64)
+    ref_o, ref_f = torch.empty_like(d["out"]), torch.empty_like(d["final_state"])
+    G.gdn_prefill_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], None, d["init_state"], ref_o, ref_f,
+                     opts=opts)
+    torch.cuda.synchronize()
+    cache = G.GraphCache(capacity=8)
+    errors = []
+
+    def worker(tid):
+        try:
+            side = torch.cuda.Stream()
+            with torch.cuda.stream(side):
+                o, f = torch.empty_like(ref_o), torch.empty_like(ref_f)
+                ws = G.alloc_workspace(d["q"], d["k"], d["v"], None, opts)
+            side.synchronize()
+            for it in range(5):
+                with torch.cuda.stream(side):
+                    o.fill_(7.0)
+                    f.fill_(7.0)
+                cache.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], None, d["init_state"], o, f,
+                              opts=opts, workspace=ws, stream=side)
+                side.synchronize()
+                if not (torch.equal(o, ref_o) and torch.equal(f, ref_f)):
+                    errors.append(f"thread {tid}, call {it}")
+        except Exception as e:  # reported below
+            errors.append(f"thread {tid}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a thread did not finish"
+    assert not errors, errors
+    st = cache.stats()
+    assert st["misses"] == 4 and st["hits"] == 16 and st["fallbacks"] == 0, st
     cache.close()
