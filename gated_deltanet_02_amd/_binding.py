@@ -15,6 +15,9 @@ from typing import Optional
 import torch
 
 GDN_OK = 0
+# The C ABI these structures and prototypes describe (GDN_ABI_VERSION of
+# include/gdn.h); a library built from other sources is refused at load.
+ABI_VERSION = 8
 STATUS_NAMES = {0: "GDN_OK", -1: "GDN_ERR_NULL_ARG", -2: "GDN_ERR_DTYPE",
                 -3: "GDN_ERR_SHAPE", -4: "GDN_ERR_LAYOUT",
                 -5: "GDN_ERR_UNSUPPORTED", -6: "GDN_ERR_WORKSPACE",
@@ -88,6 +91,11 @@ def lib():
         P = ctypes.POINTER
         T = P(GdnTensor)
         L.gdn_abi_version.restype = ctypes.c_int
+        built = L.gdn_abi_version()
+        if built != ABI_VERSION:
+            raise RuntimeError(
+                f"{path} implements ABI {built}, this binding ABI {ABI_VERSION}; rebuild it with "
+                "`python -m gated_deltanet_02_amd.build`")
         L.gdn_default_options.argtypes = [P(GdnOptions)]
         L.gdn_default_options.restype = None
         L.gdn_prefill.argtypes = [T] * 9 + [ctypes.c_void_p]

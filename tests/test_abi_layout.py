@@ -88,3 +88,36 @@ def test_binding_constants_match_the_c_header():
             assert name in expect, f"{name} has no binding constant"
     assert ints["GDN_OK"] == 0 and B.GDN_OK == 0
     assert B.NOALLOC_SCRATCH_BYTES == 96 << 20 and "((size_t)96 << 20)" in defs["GDN_NOALLOC_SCRATCH_BYTES"]
+
+
+def test_binding_abi_version_and_missing_library():
+    """The binding states the header's ABI version, and it refuses a missing
+    library with a clear error instead of running anything else."""
+    import re
+    import sys
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    assert B.ABI_VERSION == int(re.search(r"#define GDN_ABI_VERSION (\d+)", src).group(1))
+    code = ("import gated_deltanet_02_amd as G\n"
+            "try:\n    G.gdn_abi_version()\nexcept RuntimeError as e:\n    print('refused:', e)\n")
+    env = dict(os.environ, GDN_LIB="/nonexistent/libgdn.so")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT,
+                       timeout=120)
+    assert r.returncode == 0 and "refused: libgdn.so not found" in r.stdout, r.stdout + r.stderr
+
+
+def test_binding_refuses_another_abi(tmp_path):
+    """A library that reports another ABI version (a stand-in built here that
+    exports only gdn_abi_version) is refused at load."""
+    import sys
+    if not shutil.which("gcc"):
+        pytest.skip("gcc not found")
+    src = tmp_path / "old.c"
+    src.write_text(f"int gdn_abi_version(void) {{ return {B.ABI_VERSION - 1}; }}\n")
+    so = tmp_path / "libold.so"
+    subprocess.run(["gcc", "-shared", "-fPIC", str(src), "-o", str(so)], check=True)
+    code = ("import gated_deltanet_02_amd as G\n"
+            "try:\n    G.gdn_abi_version()\nexcept RuntimeError as e:\n    print('refused:', e)\n")
+    env = dict(os.environ, GDN_LIB=str(so))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT,
+                       timeout=120)
+    assert r.returncode == 0 and f"implements ABI {B.ABI_VERSION - 1}" in r.stdout, r.stdout + r.stderr
