@@ -31,7 +31,7 @@ EXPORTED = ("gdn_abi_version", "gdn_default_options", "gdn_prefill",
             "gdn_graph_cache_clear", "gdn_graph_cache_stats", "gdn_prefill_graph",
             "gdn_status_string", "gdn_last_error")
 
-_DTYPES = {torch.bfloat16: 1, torch.float32: 2, torch.int32: 3}
+_DTYPES = {torch.bfloat16: 1, torch.float32: 2, torch.int32: 3, torch.int64: 4}
 
 
 class GdnTensor(ctypes.Structure):

@@ -351,7 +351,8 @@ int validate(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
 
   // Sequences.
   if (cu) {
-    if (cu->dtype != GDN_DTYPE_I32) return fail(GDN_ERR_DTYPE, "cu_seqlens must be int32");
+    if (cu->dtype != GDN_DTYPE_I32 && cu->dtype != GDN_DTYPE_I64)
+      return fail(GDN_ERR_DTYPE, "cu_seqlens must be int32 or int64");
     if (cu->ndim != 1 || cu->shape[0] < 2) return fail(GDN_ERR_SHAPE, "cu_seqlens must be 1-D with N+1 >= 2 entries");
     if (cu->stride[0] != 1) return fail(GDN_ERR_LAYOUT, "cu_seqlens must be contiguous");
     if (!cu->data) return fail(GDN_ERR_NULL_ARG, "cu_seqlens data is NULL");
@@ -544,7 +545,8 @@ int debug_check_cu(const Problem& P, const gdn_tensor* cu, hipStream_t s) {
   if (cs != hipStreamCaptureStatusNone) return GDN_OK;
   int32_t* word = nullptr;
   hipError_t e = gdn::debug_word_region(&word);
-  if (e == hipSuccess) e = gdn::launch_check_cu((const int32_t*)cu->data, P.n_seq, P.T, word, s);
+  if (e == hipSuccess)
+    e = gdn::launch_check_cu(cu->data, cu->dtype == GDN_DTYPE_I64, P.n_seq, P.T, word, s);
   int32_t faults = 0;
   if (e == hipSuccess) e = hipMemcpyAsync(&faults, word, sizeof faults, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -582,7 +584,8 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
   }
   if (P.packed && (P.stages & GDN_STAGE_TABLE)) {
     gdn::TableParams tp{};
-    tp.cu = (const int32_t*)cu->data;
+    tp.cu = cu->data;
+    tp.cu_i64 = cu->dtype == GDN_DTYPE_I64 ? 1 : 0;
     tp.seq_start = (int32_t*)(base + L.seq_start);
     tp.chunk_off = (int32_t*)(base + L.chunk_off);
     tp.table = (int32_t*)(base + L.table);
@@ -731,7 +734,8 @@ int run(const Problem& P, const gdn_tensor* q, const gdn_tensor* k,
       gp.z = P.gate_z;
       gp.out = out->data;
       gp.w = P.norm_w;
-      gp.t_end = P.packed ? (const int32_t*)cu->data + P.n_seq : nullptr;
+      // (the sanitised end the chunk table kept: cu[N] clamped into [0, T])
+      gp.t_end = P.packed ? (const int32_t*)(base + L.seq_start) + P.n_seq : nullptr;
       gp.rows = P.T * P.hv;
       gp.inner = P.hv;
       gp.x_st = gp.z_st = gp.o_st = P.o.st;

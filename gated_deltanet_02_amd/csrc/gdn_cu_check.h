@@ -15,8 +15,10 @@ enum : int32_t {
   kCuPastEnd = 4,       // cu[N] > T
 };
 
-// Faults of entry i (0 .. n_seq) of cu[n_seq + 1] for t_total tokens.
-__host__ __device__ inline int32_t cu_entry_faults(const int32_t* cu, int64_t i, int64_t n_seq,
+// Faults of entry i (0 .. n_seq) of cu[n_seq + 1] (int32 or int64 entries)
+// for t_total tokens.
+template <typename I>
+__host__ __device__ inline int32_t cu_entry_faults(const I* cu, int64_t i, int64_t n_seq,
                                                    int64_t t_total) {
   int32_t f = 0;
   if (i == 0 && cu[0] != 0) f |= kCuFirstNonzero;

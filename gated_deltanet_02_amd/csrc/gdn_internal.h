@@ -27,7 +27,8 @@ struct ChunkMap {
 };
 
 struct TableParams {
-  const int32_t* cu;     // caller's cu_seqlens, int32[n_seq + 1]
+  const void* cu;        // caller's cu_seqlens, [n_seq + 1] int32 or int64 (cu_i64)
+  int32_t cu_i64;
   int32_t* seq_start;    // out: sanitised copy
   int32_t* chunk_off;    // out: exclusive prefix of chunk counts
   int32_t* table;        // out: per chunk (seq, t0, n, 0)

@@ -124,8 +124,9 @@ __global__ __launch_bounds__(1024) void table_kernel(TableParams p) {
   __syncthreads();
   for (int base = 0; base < p.n_seq; base += 1024) {
     const int i = base + tid;
-    int e = (i < p.n_seq) ? p.cu[i + 1] : 0;
-    e = min(max(e, 0), p.t_total);
+    int64_t e64 = 0;
+    if (i < p.n_seq) e64 = p.cu_i64 ? ((const int64_t*)p.cu)[i + 1] : ((const int32_t*)p.cu)[i + 1];
+    const int e = (int)min(max(e64, (int64_t)0), (int64_t)p.t_total);
     s_max[tid] = e;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
@@ -2126,7 +2127,8 @@ int scan_slices_per_group(bool bf16, int chunk, int dk, int dv, int64_t seq_head
 }
 
 // GDN_DEBUG_CHECK: one workgroup checks every entry of cu_seqlens.
-__global__ __launch_bounds__(256) void check_cu_kernel(const int32_t* cu, int64_t n_seq,
+template <typename I>
+__global__ __launch_bounds__(256) void check_cu_kernel(const I* cu, int64_t n_seq,
                                                       int64_t t_total, int32_t* faults) {
   __shared__ int32_t s_f;
   if (threadIdx.x == 0) s_f = 0;
@@ -2138,9 +2140,14 @@ __global__ __launch_bounds__(256) void check_cu_kernel(const int32_t* cu, int64_
   if (threadIdx.x == 0) *faults = s_f;
 }
 
-hipError_t launch_check_cu(const int32_t* cu, int64_t n_seq, int64_t t_total, int32_t* faults,
-                           hipStream_t s) {
-  hipLaunchKernelGGL(check_cu_kernel, dim3(1), dim3(256), 0, s, cu, n_seq, t_total, faults);
+hipError_t launch_check_cu(const void* cu, bool cu_i64, int64_t n_seq, int64_t t_total,
+                           int32_t* faults, hipStream_t s) {
+  if (cu_i64)
+    hipLaunchKernelGGL(check_cu_kernel<int64_t>, dim3(1), dim3(256), 0, s, (const int64_t*)cu, n_seq,
+                       t_total, faults);
+  else
+    hipLaunchKernelGGL(check_cu_kernel<int32_t>, dim3(1), dim3(256), 0, s, (const int32_t*)cu, n_seq,
+                       t_total, faults);
   return hipGetLastError();
 }
 

@@ -33,9 +33,10 @@ hipError_t launch_decode(bool bf16, int dk, const DecodeParams& p, hipStream_t s
 hipError_t launch_conv_state(bool bf16, const ConvStateParams& p, hipStream_t s);
 
 // GDN_DEBUG_CHECK: ORs the fault bits (gdn_cu_check.h) of cu[0 .. n_seq]
-// into one word and stores it at *faults (one workgroup).
-hipError_t launch_check_cu(const int32_t* cu, int64_t n_seq, int64_t t_total, int32_t* faults,
-                           hipStream_t s);
+// (int32 entries, or int64 with cu_i64) into one word and stores it at
+// *faults (one workgroup).
+hipError_t launch_check_cu(const void* cu, bool cu_i64, int64_t n_seq, int64_t t_total,
+                           int32_t* faults, hipStream_t s);
 
 // Device address of the current device's fault word for launch_check_cu
 // (a static device variable, looked up once per device).

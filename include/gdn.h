@@ -78,6 +78,7 @@ extern "C" {
 #define GDN_DTYPE_BF16 1
 #define GDN_DTYPE_F32 2
 #define GDN_DTYPE_I32 3
+#define GDN_DTYPE_I64 4
 
 /* A strided view of caller-owned memory (device memory for every tensor
  * argument).  shape/stride have ndim valid entries, outermost first; strides
@@ -258,7 +259,8 @@ void gdn_default_options(gdn_options* opts);
  *               passed through the sigmoid).  These ranges are
  *               preconditions, not checked (see GDN_FLAG_DECAY_PROJ and
  *               GDN_FLAG_BETA_LOGITS for raw projections).
- *   cu_seqlens  int32 [N+1] device array of sequence starts, or NULL: one
+ *   cu_seqlens  int32 or int64 [N+1] device array of sequence starts
+ *               (entries below 2^31), or NULL: one
  *               sequence of T tokens (3-D inputs) or B sequences of T/B
  *               tokens each (4-D inputs).  With cu_seqlens, 4-D inputs need
  *               B == 1, and the bounds are read from it also for N = 1:

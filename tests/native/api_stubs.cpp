@@ -21,7 +21,7 @@ bool two_level_available(bool bf16, int chunk, int dk) { return bf16 && chunk >=
 hipError_t launch_scan_two_level(int, int, const ScanParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_decode(bool, int, const DecodeParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_conv_state(bool, const ConvStateParams&, hipStream_t) { return hipErrorNoDevice; }
-hipError_t launch_check_cu(const int32_t*, int64_t, int64_t, int32_t*, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_check_cu(const void*, bool, int64_t, int64_t, int32_t*, hipStream_t) { return hipErrorNoDevice; }
 hipError_t debug_word_region(int32_t**) { return hipErrorNoDevice; }
 hipError_t launch_output_gate(bool, int, const GateParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t scratch_region(void**) { return hipErrorNoDevice; }

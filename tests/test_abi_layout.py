@@ -69,7 +69,7 @@ def test_binding_constants_match_the_c_header():
             ints[name] = int(m.group(1))
     expect = {
         "GDN_DTYPE_BF16": B._DTYPES[B.torch.bfloat16], "GDN_DTYPE_F32": B._DTYPES[B.torch.float32],
-        "GDN_DTYPE_I32": B._DTYPES[B.torch.int32],
+        "GDN_DTYPE_I32": B._DTYPES[B.torch.int32], "GDN_DTYPE_I64": B._DTYPES[B.torch.int64],
         "GDN_STAGE_TABLE": B.STAGE_TABLE, "GDN_STAGE_WY": B.STAGE_WY, "GDN_STAGE_SCAN": B.STAGE_SCAN,
         "GDN_STAGE_ALL": B.STAGE_ALL,
         "GDN_SCAN_AUTO": B.SCAN_AUTO, "GDN_SCAN_ONE_PASS": B.SCAN_ONE_PASS,

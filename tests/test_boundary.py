@@ -259,6 +259,23 @@ def test_qkv_silu_option(lib):
     assert o.flags == 8
 
 
+def test_cu_seqlens_dtypes(lib):
+    """cu_seqlens may be int32 or int64; other integer types are refused."""
+    q = torch.empty(300, 2, 64, dtype=torch.bfloat16)
+    v = torch.empty(300, 2, 64, dtype=torch.bfloat16)
+    sizes = [G.gdn_workspace_size(q, q, v, torch.zeros(4, dtype=dt)) for dt in (torch.int32, torch.int64)]
+    assert sizes[0] == sizes[1] > 0
+    t = torch.zeros(4, dtype=torch.float32)
+    for code in (1, 2, 9):  # bf16, f32, unknown
+        bad = B.GdnTensor()
+        bad.data, bad.dtype, bad.ndim = t.data_ptr(), code, 1
+        bad.shape[0], bad.stride[0] = 4, 1
+        qd, vd = B.describe(q), B.describe(v)
+        n = ctypes.c_size_t()
+        assert lib.gdn_workspace_size(ctypes.byref(qd), ctypes.byref(qd), ctypes.byref(vd),
+                                      ctypes.byref(bad), None, ctypes.byref(n)) == -2
+
+
 def test_qkv_conv_option(lib):
     """GDN_FLAG_QKV_CONV: the width must be 1 .. 4, the taps given and the
     taps and history arrays 16-byte aligned, in the prefill and the decode

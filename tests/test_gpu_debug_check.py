@@ -33,12 +33,13 @@ BAD = {
 }
 
 
+@pytest.mark.parametrize("dtype", [torch.int32, torch.int64], ids=["int32", "int64"])
 @pytest.mark.parametrize("case", sorted(BAD))
-def test_malformed_table_is_rejected(monkeypatch, case):
+def test_malformed_table_is_rejected(monkeypatch, case, dtype):
     monkeypatch.setenv("GDN_DEBUG_CHECK", "1")
     w = W.make_workload("packed_255", lengths=[50, 40, 30], hk=1, hv=2)
     d = W.to_device(w)
-    cu = torch.tensor(BAD[case], dtype=torch.int32, device="cuda")
+    cu = torch.tensor(BAD[case], dtype=dtype, device="cuda")
     out = torch.full_like(d["out"], 7.0)
     U.say(f"  debug check, {case}: cu = {BAD[case]}")
     with pytest.raises(G.GdnError) as ei:

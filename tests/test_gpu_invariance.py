@@ -185,3 +185,28 @@ def test_rejects_bad_arguments_before_launch():
     small = torch.zeros(16, dtype=torch.uint8, device="cuda")
     assert status_of(*args, workspace=small) == -6
     torch.cuda.synchronize()
+
+
+def test_int64_cu_seqlens_equal_int32():
+    """cu_seqlens as int64 (torch's default integer type) gives the same
+    bits as int32, with the output gate (whose row limit is the table's end)
+    and with a table ending before T."""
+    w = W.make_workload("packed_255", lengths=[130, 1, 0, 64, 63], hk=2, hv=2)
+    d = W.to_device(w)
+    gi = W.make_gate_inputs(w)
+    res = {}
+    for dt in (torch.int32, torch.int64):
+        cu = d["cu_seqlens"].to(dt)
+        for name, cu_t, opts in (("plain", cu, G.options()),
+                                 ("gated", cu, G.options(gate_z=gi.z.cuda(), norm_weight=gi.norm_w.cuda())),
+                                 ("short", torch.tensor([0, 100, 150], dtype=dt, device="cuda"), G.options())):
+            o = torch.full_like(d["out"], 7.0)
+            f = torch.full((cu_t.numel() - 1,) + tuple(d["final_state"].shape[1:]), 7.0, device="cuda")
+            G.gdn_prefill_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_t, None, o, f, opts=opts)
+            torch.cuda.synchronize()
+            res[(dt, name)] = (o, f)
+    for name in ("plain", "gated", "short"):
+        a, b = res[(torch.int32, name)], res[(torch.int64, name)]
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), name
+    # rows at or after the table's end are left alone, with and without the gate
+    assert torch.all(res[(torch.int64, "short")][0][150:] == 7.0)
