@@ -86,7 +86,7 @@ struct ScanParams {
   const float* init;     // [N, Hv, dk, dv] or null
   float* final_state;    // [N, Hv, dk, dv] or null
   int32_t hv, dv;
-  int32_t nsl;           // 16-column slices per workgroup (1 or 2)
+  int32_t nsl;           // 16-column slices per workgroup (1, 2 or 4)
   int32_t n_slices;      // workgroups per (sequence, head): dv / (16 nsl)
   ChunkMap map;
   Intermediates im;

@@ -2028,10 +2028,10 @@ static constexpr bool fits() {
          (sizeof(TI) == 2 || C <= 32);
 }
 
-// Workgroups of two slices are built for bf16 inputs.
-template <typename TI, int C, int DK>
+// Workgroups of two or four slices are built for bf16 inputs.
+template <typename TI, int C, int DK, int NSL = 2>
 static constexpr bool fits_group() {
-  return fits<TI, C, DK>() && sizeof(TI) == 2 && ScanRing<TI, C, DK, 2>::slots >= 2;
+  return fits<TI, C, DK>() && sizeof(TI) == 2 && ScanRing<TI, C, DK, NSL>::slots >= 2;
 }
 
 template <typename TI, int C, int DK>
@@ -2043,6 +2043,11 @@ static int launch_pair(int stage, const WyParams* wy, const ScanParams* sc,
         hipLaunchKernelGGL((wy_kernel<TI, C, DK, true>), grid, dim3(kWyThreads), 0, s, *wy);
       else
         hipLaunchKernelGGL((wy_kernel<TI, C, DK, false>), grid, dim3(kWyThreads), 0, s, *wy);
+    } else if (sc->nsl == 4) {
+      if constexpr (fits_group<TI, C, DK, 4>())
+        hipLaunchKernelGGL((scan_kernel<TI, C, DK, 4>), grid, dim3(scan_threads<4>()), 0, s, *sc);
+      else
+        return -1;
     } else if (sc->nsl == 2) {
       if constexpr (fits_group<TI, C, DK>())
         hipLaunchKernelGGL((scan_kernel<TI, C, DK, 2>), grid, dim3(scan_threads<2>()), 0, s, *sc);
@@ -2094,8 +2099,10 @@ bool kernels_available(bool bf16, int chunk, int dk) {
   return bf16 ? fits_any<gdn::bf16>(chunk, dk) : fits_any<float>(chunk, dk);
 }
 
-static bool group_available(int chunk, int dk) {
-#define GDN_FITS(CC, DD) if (chunk == CC && dk == DD) return fits_group<gdn::bf16, CC, DD>();
+static bool group_available(int chunk, int dk, int nsl) {
+#define GDN_FITS(CC, DD)                                                                \
+  if (chunk == CC && dk == DD)                                                          \
+    return nsl == 4 ? fits_group<gdn::bf16, CC, DD, 4>() : fits_group<gdn::bf16, CC, DD, 2>();
   GDN_FITS(16, 16) GDN_FITS(16, 32) GDN_FITS(16, 64) GDN_FITS(16, 128)
   GDN_FITS(32, 16) GDN_FITS(32, 32) GDN_FITS(32, 64) GDN_FITS(32, 128)
   GDN_FITS(64, 16) GDN_FITS(64, 32) GDN_FITS(64, 64) GDN_FITS(64, 128)
@@ -2120,10 +2127,16 @@ static int device_cus() {
 // Where the 16-column slices fit the compute units at once, one slice per
 // workgroup spreads the chains widest.  Where they would queue, two slices
 // per workgroup share one copy of each chunk's operands and run on separate
-// SIMDs, for about the time per chunk of one.
+// SIMDs, for about the time per chunk of one.  Where even four-slice
+// workgroups fill every compute unit, four slices share each copy: half the
+// operand traffic from L2 into the compute units, which bounds the scan once
+// the chip is full (two stages of the ring instead of three).
 int scan_slices_per_group(bool bf16, int chunk, int dk, int dv, int64_t seq_heads) {
-  if (!bf16 || dv % 32 != 0 || !group_available(chunk, dk)) return 1;
-  return seq_heads * (dv / 16) > device_cus() ? 2 : 1;
+  if (!bf16 || dv % 32 != 0 || !group_available(chunk, dk, 2)) return 1;
+  const int64_t slices = seq_heads * (dv / 16), cus = device_cus();
+  if (slices <= cus) return 1;
+  if (dv % 64 == 0 && group_available(chunk, dk, 4) && slices >= 4 * cus) return 4;
+  return 2;
 }
 
 // GDN_DEBUG_CHECK: one workgroup checks every entry of cu_seqlens.
@@ -2173,7 +2186,7 @@ hipError_t launch_scan(bool bf16, int chunk, int dk, const ScanParams& p,
   return hipGetLastError();
 }
 
-bool two_level_available(bool bf16, int chunk, int dk) { return bf16 && group_available(chunk, dk); }
+bool two_level_available(bool bf16, int chunk, int dk) { return bf16 && group_available(chunk, dk, 2); }
 
 template <int C, int DK>
 static hipError_t launch_two_level_dk(const ScanParams& p, hipStream_t s) {

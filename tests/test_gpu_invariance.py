@@ -36,6 +36,26 @@ def test_packed_equals_separate_calls():
         assert np.array_equal(f[0], fin[i])
 
 
+def test_slices_per_workgroup_do_not_change_results():
+    """A sequence's outputs and final state are bit-equal whether its scan
+    workgroups hold one, two or four 16-column slices: the batch of 140
+    sequences x 8 heads (8960 slices) runs four per workgroup, 12 of them
+    (768 slices) two, and 3 of them (192 slices) one."""
+    w = W.make_workload("packed_255", lengths=("uniform", 140, 1, 200), hk=8, hv=8)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    per_seq = w.v.shape[1] * w.v.shape[2] // 16
+    assert w.n_seqs * per_seq >= 4 * cus and cus < 12 * per_seq < 4 * cus and 3 * per_seq <= cus
+    out, fin, _ = U.run_gpu(w)
+    starts = np.concatenate([[0], np.cumsum(w.lengths)])
+    for pick in (list(range(5, 17)), [0, 77, 139]):
+        s = W.select_sequences(w, pick)
+        o, f, _ = U.run_gpu(s, with_cu=True)
+        so = np.concatenate([[0], np.cumsum(s.lengths)])
+        for j, i in enumerate(pick):
+            assert np.array_equal(o[so[j]:so[j + 1]], out[starts[i]:starts[i + 1]]), f"sequence {i} of {len(pick)}"
+            assert np.array_equal(f[j], fin[i]), f"state {i} of {len(pick)}"
+
+
 def test_empty_sequences_and_init_passthrough():
     w = W.make_workload("long_16k_gqa", lengths=[0, 50, 0, 0, 70, 0], hk=1, hv=3)
     assert w.init_state is not None

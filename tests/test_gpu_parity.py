@@ -61,6 +61,27 @@ def test_reduced_two_slice_groups(name, kw):
     U.check_bf16(out, fin, ro, rf, label=f"two-slice groups {name} {kw}")
 
 
+# Enough (sequence, value head) pairs that four-slice workgroups still fill
+# every compute unit, so the scan runs four slices per workgroup (two
+# stages in its ring); every output is checked.
+GROUPED4 = [
+    ("packed_255", dict(lengths=("uniform", 140, 1, 200), hk=8, hv=8)),
+    ("long_16k_gqa", dict(lengths=[200], hk=16, hv=128)),
+    ("prompt_4k", dict(lengths=[150] * 3, hk=48, hv=48, dk=64, dv=128)),
+]
+
+
+@pytest.mark.parametrize("name,kw", GROUPED4, ids=[f"{n}-{i}" for i, (n, _) in enumerate(GROUPED4)])
+def test_reduced_four_slice_groups(name, kw):
+    w = W.make_workload(name, **kw)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    slices = w.n_seqs * w.v.shape[1] * w.v.shape[2] // 16
+    assert slices >= 4 * cus, "the case must fill the compute units with four-slice workgroups"
+    out, fin, _ = U.run_gpu(w)
+    ro, rf = _ref(w)
+    U.check_bf16(out, fin, ro, rf, label=f"four-slice groups {name} {kw}")
+
+
 @pytest.mark.parametrize("name,kw", REDUCED, ids=[f"{n}-{i}" for i, (n, _) in enumerate(REDUCED)])
 def test_reduced_bf16(name, kw):
     w = W.make_workload(name, **kw)
