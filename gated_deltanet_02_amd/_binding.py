@@ -17,7 +17,7 @@ import torch
 GDN_OK = 0
 # The C ABI these structures and prototypes describe (GDN_ABI_VERSION of
 # include/gdn.h); a library built from other sources is refused at load.
-ABI_VERSION = 8
+ABI_VERSION = 9
 STATUS_NAMES = {0: "GDN_OK", -1: "GDN_ERR_NULL_ARG", -2: "GDN_ERR_DTYPE",
                 -3: "GDN_ERR_SHAPE", -4: "GDN_ERR_LAYOUT",
                 -5: "GDN_ERR_UNSUPPORTED", -6: "GDN_ERR_WORKSPACE",
@@ -122,7 +122,7 @@ def lib():
         L.gdn_graph_cache_clear.argtypes = [ctypes.c_void_p]
         L.gdn_graph_cache_clear.restype = None
         L.gdn_graph_cache_stats.argtypes = [ctypes.c_void_p, P(ctypes.c_int), P(ctypes.c_int64),
-                                            P(ctypes.c_int64), P(ctypes.c_int64)]
+                                            P(ctypes.c_int64), P(ctypes.c_int64), P(ctypes.c_int64)]
         L.gdn_graph_cache_stats.restype = ctypes.c_int
         L.gdn_prefill_graph.argtypes = [ctypes.c_void_p] + [T] * 9 + [
             P(GdnOptions), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
@@ -408,10 +408,12 @@ class GraphCache:
         return out, final_state
 
     def stats(self) -> dict:
-        n, h, m, f = ctypes.c_int(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        n, h, m, u, f = (ctypes.c_int(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(),
+                         ctypes.c_int64())
         _check(self._lib.gdn_graph_cache_stats(self._h, ctypes.byref(n), ctypes.byref(h),
-                                               ctypes.byref(m), ctypes.byref(f)))
-        return {"entries": n.value, "hits": h.value, "misses": m.value, "fallbacks": f.value}
+                                               ctypes.byref(m), ctypes.byref(u), ctypes.byref(f)))
+        return {"entries": n.value, "hits": h.value, "misses": m.value, "updates": u.value,
+                "fallbacks": f.value}
 
     def clear(self):
         self._lib.gdn_graph_cache_clear(self._h)

@@ -1013,11 +1013,18 @@ int gdn_output_gate(const gdn_tensor* x, const gdn_tensor* z, const float* weigh
 
 namespace {
 
+// An entry is found by its shape key (everything but the data pointers,
+// including which optional pointers are NULL) and its pointer key (the data
+// pointers): the launches' grids and kernels depend only on the first.
 struct GraphEntry {
-  std::string key;
+  std::string shape_key, ptr_key;
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
 };
+
+// Pointer variants of one shape kept side by side before a new variant
+// updates the least recently used of them in place.
+constexpr int kVariantsPerShape = 4;
 
 void release(GraphEntry& e) {
   if (e.exec) (void)hipGraphExecDestroy(e.exec);
@@ -1028,13 +1035,17 @@ void release(GraphEntry& e) {
 
 void append(std::string& k, const void* p, size_t n) { k.append((const char*)p, n); }
 
-void append_tensor(std::string& k, const gdn_tensor* t) {
+// A tensor's shape-key part (presence, dtype, shape, strides) and its data
+// pointer in the pointer key.
+void append_tensor(std::string& k, std::string& kp, const gdn_tensor* t) {
   const int32_t none = -1;
   if (!t) {
     append(k, &none, sizeof none);
     return;
   }
-  append(k, &t->data, sizeof t->data);
+  const int32_t null_data = t->data == nullptr;
+  append(k, &null_data, sizeof null_data);
+  append(kp, &t->data, sizeof t->data);
   append(k, &t->dtype, sizeof t->dtype);
   append(k, &t->ndim, sizeof t->ndim);
   append(k, t->shape, sizeof(int64_t) * (size_t)(t->ndim > 0 && t->ndim <= 4 ? t->ndim : 0));
@@ -1047,7 +1058,7 @@ struct gdn_graph_cache {
   std::mutex mu;
   int capacity = 64;
   std::list<GraphEntry> entries;  // most recently used first
-  int64_t hits = 0, misses = 0, fallbacks = 0;
+  int64_t hits = 0, misses = 0, updates = 0, fallbacks = 0;
 };
 
 extern "C" {
@@ -1076,12 +1087,13 @@ void gdn_graph_cache_clear(gdn_graph_cache* cache) {
 }
 
 int gdn_graph_cache_stats(gdn_graph_cache* cache, int* entries, int64_t* hits,
-                          int64_t* misses, int64_t* fallbacks) {
+                          int64_t* misses, int64_t* updates, int64_t* fallbacks) {
   if (!cache) return fail(GDN_ERR_NULL_ARG, "cache is NULL");
   std::lock_guard<std::mutex> lock(cache->mu);
   if (entries) *entries = (int)cache->entries.size();
   if (hits) *hits = cache->hits;
   if (misses) *misses = cache->misses;
+  if (updates) *updates = cache->updates;
   if (fallbacks) *fallbacks = cache->fallbacks;
   return GDN_OK;
 }
@@ -1102,63 +1114,101 @@ int gdn_prefill_graph(gdn_graph_cache* cache, const gdn_tensor* q, const gdn_ten
   g_last_error.clear();
   hipStream_t s = (hipStream_t)stream;
 
-  // The key: every argument the launches depend on.  The kernels read the
+  // The keys: every argument the launches depend on.  The kernels read the
   // sequence lengths from device memory, so a capture stays valid for any
-  // lengths with the same shapes and buffers.
-  std::string key;
+  // lengths with the same shapes and buffers; the buffers themselves enter
+  // the launches only as kernel arguments.
+  std::string key, kp;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
   append(key, &dev, sizeof dev);
   const gdn_tensor* ts[9] = {q, k, v, g, beta, cu_seqlens, init_state, out, final_state};
-  for (const gdn_tensor* t : ts) append_tensor(key, t);
+  for (const gdn_tensor* t : ts) append_tensor(key, kp, t);
   gdn_options o;
   gdn_default_options(&o);
   if (opts) o = *opts;
-  // field by field (the struct's padding carries no value)
+  // field by field (the struct's padding carries no value); pointers by
+  // presence in the shape key and by value in the pointer key
+  auto ptr = [&](const void* p) {
+    const int32_t present = p != nullptr;
+    append(key, &present, sizeof present);
+    append(kp, &p, sizeof p);
+  };
   append(key, &o.chunk, sizeof o.chunk);
   append(key, &o.scale, sizeof o.scale);
   append(key, &o.l2_eps, sizeof o.l2_eps);
   append(key, &o.stages, sizeof o.stages);
   append(key, &o.scan_split, sizeof o.scan_split);
   append(key, &o.flags, sizeof o.flags);
-  append(key, &o.decay_a_log, sizeof o.decay_a_log);
-  append(key, &o.decay_bias, sizeof o.decay_bias);
-  append(key, &o.gate_z, sizeof o.gate_z);
-  append(key, &o.norm_weight, sizeof o.norm_weight);
+  ptr(o.decay_a_log);
+  ptr(o.decay_bias);
+  ptr(o.gate_z);
+  ptr(o.norm_weight);
   append(key, &o.norm_eps, sizeof o.norm_eps);
   append(key, &o.segment_chunks, sizeof o.segment_chunks);
-  append(key, &o.conv_weight, sizeof o.conv_weight);
+  ptr(o.conv_weight);
   append(key, &o.conv_width, sizeof o.conv_width);
-  append(key, &o.conv_state_in, sizeof o.conv_state_in);
-  append(key, &o.conv_state_out, sizeof o.conv_state_out);
-  append(key, &workspace, sizeof workspace);
+  ptr(o.conv_state_in);
+  ptr(o.conv_state_out);
+  ptr(workspace);
   append(key, &workspace_bytes, sizeof workspace_bytes);
 
   std::lock_guard<std::mutex> lock(cache->mu);
+  auto launch_front = [&]() {
+    const hipError_t e = hipGraphLaunch(cache->entries.front().exec, s);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "graph launch: %s", hipGetErrorString(e));
+    return (int)GDN_OK;
+  };
+  int variants = 0;
+  auto oldest = cache->entries.end();
   for (auto it = cache->entries.begin(); it != cache->entries.end(); ++it) {
-    if (it->key == key) {
+    if (it->shape_key != key) continue;
+    if (it->ptr_key == kp) {
       cache->entries.splice(cache->entries.begin(), cache->entries, it);
       ++cache->hits;
-      const hipError_t e = hipGraphLaunch(cache->entries.front().exec, s);
-      if (e != hipSuccess) return fail(GDN_ERR_HIP, "graph launch: %s", hipGetErrorString(e));
-      return GDN_OK;
+      return launch_front();
     }
+    ++variants;
+    oldest = it;
   }
-  ++cache->misses;
-  // Capture on a private stream (the caller's may be the null stream, which
-  // cannot be captured), then launch on the caller's.
-  GraphEntry ent;
-  ent.key = key;
+  // Record the launches on a private stream (the caller's may be the null
+  // stream, which cannot be captured).
+  hipGraph_t graph = nullptr;
   hipStream_t cs = nullptr;
   bool ok = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) == hipSuccess;
   if (ok) ok = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) == hipSuccess;
   if (ok) {
     const int rrc = run(P, q, k, v, g, beta, cu_seqlens, init_state, out, final_state, workspace, cs);
-    const hipError_t ec = hipStreamEndCapture(cs, &ent.graph);
-    ok = rrc == GDN_OK && ec == hipSuccess && ent.graph != nullptr;
+    const hipError_t ec = hipStreamEndCapture(cs, &graph);
+    ok = rrc == GDN_OK && ec == hipSuccess && graph != nullptr;
   }
-  if (ok) ok = hipGraphInstantiate(&ent.exec, ent.graph, nullptr, nullptr, 0) == hipSuccess;
   if (cs) (void)hipStreamDestroy(cs);
+  if (ok && variants >= kVariantsPerShape) {
+    // Same launches on other buffers: update the least recently used
+    // variant's executable graph in place (no instantiation).  Launches of
+    // it already enqueued keep the arguments they were enqueued with.
+    hipGraphNode_t bad = nullptr;
+    hipGraphExecUpdateResult res = hipGraphExecUpdateError;
+    if (hipGraphExecUpdate(oldest->exec, graph, &bad, &res) == hipSuccess &&
+        res == hipGraphExecUpdateSuccess) {
+      (void)hipGraphDestroy(oldest->graph);
+      oldest->graph = graph;
+      oldest->ptr_key = kp;
+      cache->entries.splice(cache->entries.begin(), cache->entries, oldest);
+      ++cache->updates;
+      return launch_front();
+    }
+    (void)hipGetLastError();
+    // refused: the variant is replaced by a new instantiation below
+    release(*oldest);
+    cache->entries.erase(oldest);
+  }
+  ++cache->misses;
+  GraphEntry ent;
+  ent.shape_key = key;
+  ent.ptr_key = kp;
+  ent.graph = graph;
+  if (ok) ok = hipGraphInstantiate(&ent.exec, ent.graph, nullptr, nullptr, 0) == hipSuccess;
   if (!ok) {
     // fall back to the eager launches
     release(ent);
@@ -1167,14 +1217,12 @@ int gdn_prefill_graph(gdn_graph_cache* cache, const gdn_tensor* q, const gdn_ten
     g_last_error.clear();
     return run(P, q, k, v, g, beta, cu_seqlens, init_state, out, final_state, workspace, s);
   }
-  const hipError_t e = hipGraphLaunch(ent.exec, s);
   cache->entries.push_front(ent);
   while ((int)cache->entries.size() > cache->capacity) {
     release(cache->entries.back());
     cache->entries.pop_back();
   }
-  if (e != hipSuccess) return fail(GDN_ERR_HIP, "graph launch: %s", hipGetErrorString(e));
-  return GDN_OK;
+  return launch_front();
 }
 
 }  // extern "C"

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 8
+#define GDN_ABI_VERSION 9
 
 /* Status codes. */
 #define GDN_OK 0
@@ -402,13 +402,20 @@ int gdn_decode(const gdn_tensor* q, const gdn_tensor* k, const gdn_tensor* v,
 
 /*
  * Captured replays.  gdn_prefill_graph behaves as gdn_prefill_ex, but keeps
- * a HIP graph of the launches in `cache`, keyed by every argument (device,
- * tensor descriptors including data pointers, options, workspace pointer and
- * size).  A miss captures the launches on a private stream (stream capture),
- * instantiates the graph and launches it on `stream`; a hit only launches
- * the stored graph, which removes the per-kernel launch cost.  If capture or
- * instantiation fails the call runs the launches eagerly (and counts a
- * fallback).  The sequence lengths are read from cu_seqlens on the device by
+ * a HIP graph of the launches in `cache`.  A graph is found by every
+ * argument the launches depend on: device, tensor descriptors (which
+ * optional tensors and options pointers are NULL, dtypes, shapes, strides),
+ * option values and workspace size (the shape key), and the data, options
+ * and workspace pointers (the pointer key).  A hit (both keys stored) only
+ * launches the stored graph, which removes the per-kernel launch cost.
+ * Otherwise the launches are recorded on a private stream (stream capture):
+ * while fewer than 4 graphs of the same shape key are stored, the recording
+ * is instantiated as a new graph (a miss); from then on the least recently
+ * used graph of that shape key is updated in place to the new pointers
+ * (hipGraphExecUpdate: an update, no instantiation; launches of it already
+ * enqueued keep their arguments), or replaced by a new instantiation if the
+ * update is refused.  If capture or instantiation fails the call runs the
+ * launches eagerly (and counts a fallback).  The sequence lengths are read from cu_seqlens on the device by
  * the kernels themselves, so one capture stays valid for any lengths with
  * the same shapes and buffers (the serving pages key their captures by the
  * length tuple: "Cua-S1 4B 0.2 native text worker"; "Open-Jev-27B-v1.1
@@ -425,7 +432,7 @@ int gdn_graph_cache_create(int capacity, gdn_graph_cache** cache);
 void gdn_graph_cache_destroy(gdn_graph_cache* cache);
 void gdn_graph_cache_clear(gdn_graph_cache* cache);
 int gdn_graph_cache_stats(gdn_graph_cache* cache, int* entries, int64_t* hits,
-                          int64_t* misses, int64_t* fallbacks);
+                          int64_t* misses, int64_t* updates, int64_t* fallbacks);
 int gdn_prefill_graph(gdn_graph_cache* cache, const gdn_tensor* q,
                       const gdn_tensor* k, const gdn_tensor* v,
                       const gdn_tensor* g, const gdn_tensor* beta,

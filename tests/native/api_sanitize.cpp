@@ -193,9 +193,9 @@ int main() {
     expect(gdn_prefill_graph(c, &a.q, &a.k, &a.v, &a.g, &a.b, nullptr, nullptr, &a.out, nullptr, nullptr,
                              (void*)0x1000000, (size_t)1 << 40, nullptr), GDN_ERR_HIP, "graph eager fallback");
     int entries = -1;
-    int64_t hits = -1, misses = -1, fallbacks = -1;
-    expect(gdn_graph_cache_stats(c, &entries, &hits, &misses, &fallbacks), GDN_OK, "cache stats");
-    if (entries != 0 || misses != 1 || fallbacks != 1) {
+    int64_t hits = -1, misses = -1, updates = -1, fallbacks = -1;
+    expect(gdn_graph_cache_stats(c, &entries, &hits, &misses, &updates, &fallbacks), GDN_OK, "cache stats");
+    if (entries != 0 || misses != 1 || updates != 0 || fallbacks != 1) {
       std::printf("FAIL cache counts %d %lld %lld\n", entries, (long long)misses, (long long)fallbacks);
       ++fails;
     }

@@ -47,4 +47,7 @@ hipError_t hipGraphInstantiate(hipGraphExec_t*, hipGraph_t, hipGraphNode_t*, cha
 hipError_t hipGraphLaunch(hipGraphExec_t, hipStream_t) { return hipErrorNoDevice; }
 hipError_t hipGraphExecDestroy(hipGraphExec_t) { return hipErrorNoDevice; }
 hipError_t hipGraphDestroy(hipGraph_t) { return hipErrorNoDevice; }
+hipError_t hipGraphExecUpdate(hipGraphExec_t, hipGraph_t, hipGraphNode_t*, hipGraphExecUpdateResult*) {
+  return hipErrorNoDevice;
+}
 }

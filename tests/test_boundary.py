@@ -439,10 +439,10 @@ def test_graph_cache_host_side(lib):
     assert lib.gdn_graph_cache_create(0, ctypes.byref(cache)) == -3
     assert lib.gdn_graph_cache_create(4, None) == -1
     assert lib.gdn_graph_cache_create(4, ctypes.byref(cache)) == 0
-    n, h, m, f = ctypes.c_int(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    n, h, m, u, f = ctypes.c_int(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
     assert lib.gdn_graph_cache_stats(cache, ctypes.byref(n), ctypes.byref(h), ctypes.byref(m),
-                                     ctypes.byref(f)) == 0
-    assert (n.value, h.value, m.value, f.value) == (0, 0, 0, 0)
+                                     ctypes.byref(u), ctypes.byref(f)) == 0
+    assert (n.value, h.value, m.value, u.value, f.value) == (0, 0, 0, 0, 0)
     a = base()
     r = ctypes.byref
     # a bad argument: missing workspace

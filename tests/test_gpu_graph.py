@@ -99,11 +99,69 @@ def test_graph_cache_evicts_least_recently_used():
     torch.cuda.synchronize()
     st = cache.stats()
     U.say(f"  {st}")
-    assert st == {"entries": 2, "hits": 1, "misses": 4, "fallbacks": 0}
+    assert st == {"entries": 2, "hits": 1, "misses": 4, "updates": 0, "fallbacks": 0}
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
     cache.clear()
     assert cache.stats()["entries"] == 0
+    cache.close()
+
+
+def test_graph_cache_updates_for_fresh_buffers():
+    """Twelve calls of one shape, each on fresh input and output buffers,
+    enqueued with no synchronisation between them: the first four are
+    instantiated, the other eight update the least recently used of them in
+    place (their earlier launches may still be queued).  Every result is bit
+    for bit the eager call's on the same buffers."""
+    kw = dict(lengths=[256], hk=2, hv=2)
+    sets = []
+    for it in range(12):
+        w = W.make_workload("prompt_4k", seed=40 + it, init_std=0.3, **kw)
+        d = W.to_device(w)
+        G.gdn_prefill_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], None, d["init_state"],
+                         d["out"], d["final_state"])
+        sets.append((d, d["out"].clone(), d["final_state"].clone()))
+    torch.cuda.synchronize()
+    ws = G.alloc_workspace(sets[0][0]["q"], sets[0][0]["k"], sets[0][0]["v"])
+    cache = G.GraphCache(capacity=8)
+    for d, _, _ in sets:
+        d["out"].fill_(7.0)
+        d["final_state"].fill_(7.0)
+    torch.cuda.synchronize()
+    for d, _, _ in sets:
+        cache.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], None, d["init_state"], d["out"],
+                      d["final_state"], workspace=ws)
+    torch.cuda.synchronize()
+    st = cache.stats()
+    U.say(f"  {st}")
+    for it, (d, eo, ef) in enumerate(sets):
+        assert torch.equal(d["out"], eo) and torch.equal(d["final_state"], ef), f"call {it}"
+    assert st == {"entries": 4, "hits": 0, "misses": 4, "updates": 8, "fallbacks": 0}
+    cache.close()
+
+
+def test_graph_cache_alternating_buffers_hit():
+    """Two buffer sets used in turn (double buffering) stay two stored
+    graphs: after the first call on each, every call is a hit."""
+    kw = dict(lengths=[200], hk=2, hv=2)
+    sets = []
+    for it in range(2):
+        w = W.make_workload("prompt_4k", seed=60 + it, **kw)
+        d = W.to_device(w)
+        G.gdn_prefill_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], None, None, d["out"], d["final_state"])
+        sets.append((d, d["out"].clone(), d["final_state"].clone()))
+    torch.cuda.synchronize()
+    ws = G.alloc_workspace(sets[0][0]["q"], sets[0][0]["k"], sets[0][0]["v"])
+    cache = G.GraphCache(capacity=8)
+    for it in range(6):
+        d, eo, ef = sets[it % 2]
+        d["out"].fill_(7.0)
+        d["final_state"].fill_(7.0)
+        cache.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], None, None, d["out"],
+                      d["final_state"], workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(d["out"], eo) and torch.equal(d["final_state"], ef), f"call {it}"
+    assert cache.stats() == {"entries": 2, "hits": 4, "misses": 2, "updates": 0, "fallbacks": 0}
     cache.close()
 
 
