@@ -384,9 +384,11 @@ def gdn_decode(q, k, v, g, beta, state, out=None, opts: Optional[GdnOptions] = N
 
 
 class GraphCache:
-    """A gdn_graph_cache: captured replays of gdn_prefill_ex keyed by all of
-    its arguments (see include/gdn.h).  ``prefill`` takes the arguments of
-    gdn_prefill_ex; the workspace is required."""
+    """A gdn_graph_cache: captured replays of gdn_prefill_ex, found by its
+    shapes and options and then by its buffers (new buffers of a stored
+    shape update a stored graph in place; see include/gdn.h).  ``prefill``
+    takes the arguments of gdn_prefill_ex; the workspace is required.
+    ``stats`` counts hits, misses (new graphs), updates and fallbacks."""
 
     def __init__(self, capacity: int = 64):
         self._h = ctypes.c_void_p()
