@@ -68,6 +68,9 @@ GROUPED4 = [
     ("packed_255", dict(lengths=("uniform", 140, 1, 200), hk=8, hv=8)),
     ("long_16k_gqa", dict(lengths=[200], hk=16, hv=128)),
     ("prompt_4k", dict(lengths=[150] * 3, hk=48, hv=48, dk=64, dv=128)),
+    # small heads: the ring's stages are smaller, so it holds four of them
+    ("packed_255", dict(lengths=("uniform", 64, 1, 150), hk=4, hv=4, dk=32, dv=64)),
+    ("packed_255", dict(lengths=("uniform", 40, 1, 150), hk=2, hv=8, dk=16, dv=128)),
 ]
 
 
