@@ -25,7 +25,7 @@ from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 120
+N_CASES = 300
 
 
 @pytest.fixture(scope="module", autouse=True)
