@@ -1778,18 +1778,21 @@ __global__ __launch_bounds__(scan_threads<2>()) void scan_split_kernel(ScanParam
 // Applies the second segment's correction.  Output blocks: per (sequence,
 // head, kFixChunks chunks of the second segment) O^T += H_mid^T (Q' Phi)^T
 // with bf16 operands (the same rounding as the scan's Q' H); each wave keeps
-// H_mid^T's operand units in registers for its (chunk, row tile) jobs.
-// State blocks: per (sequence, head, 16 columns) H_end = Phi_end H_mid + Psi
-// in fp32, one thread per (row, 8 columns) with its row of Phi_end in
-// registers.
+// H_mid^T's operand units in registers and requests the rows of all its
+// (chunk, row tile) jobs before the first product, so the block waits on
+// memory once.  State blocks: per (sequence, head, 16 columns)
+// H_end = Phi_end H_mid + Psi in fp32 MFMA tiles: a wave takes DK / 64 row
+// tiles, with Phi's rows and Psi read straight into operand and accumulator
+// units and H_mid's 16 columns staged once in LDS.
 constexpr int kFixThreads = 256;
-constexpr int kFixChunks = 4;
+constexpr int kFixChunks = 2;
 
 __host__ __device__ constexpr int fix_groups(int l1) { return (l1 + kFixChunks - 1) / kFixChunks; }
 
 template <int C, int DK, int DV>
 __global__ __launch_bounds__(kFixThreads) void scan_fix_kernel(ScanParams p) {
   constexpr int NW = kFixThreads / 64;
+  constexpr int JPW = (kFixChunks * (C / 16) + NW - 1) / NW;  // jobs per wave
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int L1 = p.map.chunks_per_seq - p.split;
@@ -1802,37 +1805,48 @@ __global__ __launch_bounds__(kFixThreads) void scan_fix_kernel(ScanParams p) {
     const int u = (b / (8 * NG)) * 8 + (b % 8), gi = (b / 8) % NG;
     if (u >= n_heads) return;
     const int seq = u / p.hv, h = u % p.hv;
+    // every job's rows first: Q' Phi rows and the outputs they correct
+    typedef typename Raw4<bf16>::type RT;
+    bf16x8 yb[JPW][DK / 32];
+    RT ov[JPW][DV / 16];
+    int n_live[JPW], rows[JPW];
+    bf16* orows[JPW];
+#pragma unroll
+    for (int j = 0; j < JPW; ++j) {
+      const int jb = wave + NW * j;
+      const int i1 = gi * kFixChunks + jb / (C / 16), rt = jb % (C / 16);
+      const bool job = jb < kFixChunks * (C / 16) && i1 < L1;
+      const int cc = seq * p.map.chunks_per_seq + p.split + (job ? i1 : 0);
+      const int tok = seq * p.map.seq_stride + (p.split + (job ? i1 : 0)) * C;
+      n_live[j] = job ? min(C, seq * p.map.seq_stride + p.map.seq_len - tok) : 0;
+      const int r = 16 * rt + (lane & 15);
+      rows[j] = r;
+      const bf16* yrow = (const bf16*)p.sp_y + (((int64_t)cc * p.hv + h) * C + r) * DK + (lane >> 4) * 8;
+#pragma unroll
+      for (int q = 0; q < DK / 32; ++q) yb[j][q] = job ? *(const bf16x8*)(yrow + 32 * q) : bf16x8{};
+      orows[j] = (bf16*)p.out + (int64_t)(tok + r) * p.o_st + (int64_t)h * p.o_sh + (lane >> 4) * 4;
+#pragma unroll
+      for (int ct = 0; ct < DV / 16; ++ct)
+        ov[j][ct] = r < n_live[j] ? load_raw4<bf16>(orows[j] + 16 * ct) : RT{};
+    }
     const bf16* ht = (const bf16*)p.sp_hmid_t + (int64_t)u * DV * DK + (lane & 15) * DK + (lane >> 4) * 8;
     bf16x8 ha[DV / 16][DK / 32];
 #pragma unroll
     for (int ct = 0; ct < DV / 16; ++ct)
 #pragma unroll
       for (int q = 0; q < DK / 32; ++q) ha[ct][q] = *(const bf16x8*)(ht + 16 * ct * DK + 32 * q);
-    for (int jb = wave; jb < kFixChunks * (C / 16); jb += NW) {
-      const int i1 = gi * kFixChunks + jb / (C / 16), rt = jb % (C / 16);
-      if (i1 >= L1) break;
-      const int cc = seq * p.map.chunks_per_seq + p.split + i1;
-      const int tok = seq * p.map.seq_stride + (p.split + i1) * C;
-      const int n = min(C, seq * p.map.seq_stride + p.map.seq_len - tok);
-      const int r = 16 * rt + (lane & 15);
-      const bf16* yrow = (const bf16*)p.sp_y + (((int64_t)cc * p.hv + h) * C + r) * DK + (lane >> 4) * 8;
-      bf16x8 yb[DK / 32];
 #pragma unroll
-      for (int q = 0; q < DK / 32; ++q) yb[q] = *(const bf16x8*)(yrow + 32 * q);
-      bf16* orow = (bf16*)p.out + (int64_t)(tok + r) * p.o_st + (int64_t)h * p.o_sh + (lane >> 4) * 4;
-      // the row's outputs requested together, before the products
-      typename Raw4<bf16>::type ov[DV / 16];
-#pragma unroll
-      for (int ct = 0; ct < DV / 16; ++ct) ov[ct] = r < n ? load_raw4<bf16>(orow + 16 * ct) : uint2{};
+    for (int j = 0; j < JPW; ++j) {
+      if (n_live[j] <= 0) continue;
 #pragma unroll
       for (int ct = 0; ct < DV / 16; ++ct) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int q = 0; q < DK / 32; ++q)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[ct][q], yb[q], acc, 0, 0, 0);
-        if (r < n) {
-          const f32x4 o = raw4_to_f32<bf16>(ov[ct]);
-          store4<bf16>(orow + 16 * ct, o[0] + acc[0], o[1] + acc[1], o[2] + acc[2], o[3] + acc[3]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[ct][q], yb[j][q], acc, 0, 0, 0);
+        if (rows[j] < n_live[j]) {
+          const f32x4 o = raw4_to_f32<bf16>(ov[j][ct]);
+          store4<bf16>(orows[j] + 16 * ct, o[0] + acc[0], o[1] + acc[1], o[2] + acc[2], o[3] + acc[3]);
         }
       }
     }
@@ -1843,35 +1857,37 @@ __global__ __launch_bounds__(kFixThreads) void scan_fix_kernel(ScanParams p) {
   constexpr int NT = DV / 16;
   const int u = b / NT, ct = b % NT;
   if (u >= n_heads) return;
-  __shared__ float sH[DK][16];
+  // H_mid's columns 16 ct .. + 15 as B operand units: for k-tile t, lane
+  // (n, q) holds rows 16 t + 4 q + 0..3 of column n
+  __shared__ f32x4 sB[DK / 16][64];
   const float* hm = p.sp_hmid + (int64_t)u * DK * DV + 16 * ct;
-  for (int idx = tid; idx < DK * 16; idx += kFixThreads) sH[idx / 16][idx % 16] = hm[(int64_t)(idx / 16) * DV + idx % 16];
+  for (int idx = tid; idx < (DK / 16) * 64; idx += kFixThreads) {
+    const int t = idx / 64, l = idx % 64, n = l & 15, q = l >> 4;
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = hm[(int64_t)(16 * t + 4 * q + e) * DV + n];
+    sB[t][l] = v;
+  }
   __syncthreads();
-  const int k = tid / 2, j0 = (tid % 2) * 8;
-  if (k >= DK) return;
-  const float* phr = p.sp_phi + ((int64_t)u * DK + k) * DK;
-  f32x4 a[DK / 4];
+  const int n = lane & 15, q = lane >> 4;
+  for (int rt = wave; rt < DK / 16; rt += NW) {
+    // Psi's tile as the accumulator: lane (n, q) holds rows 16 rt + 4 q + e
+    const float* ps = p.sp_psi + ((int64_t)u * DK + 16 * rt + 4 * q) * DV + 16 * ct + n;
+    f32x4 acc;
 #pragma unroll
-  for (int i = 0; i < DK / 4; ++i) a[i] = *(const f32x4*)(phr + 4 * i);
-  const float* psr = p.sp_psi + ((int64_t)u * DK + k) * DV + 16 * ct + j0;
-  float acc[8];
+    for (int e = 0; e < 4; ++e) acc[e] = ps[(int64_t)e * DV];
+    // Phi's rows 16 rt + n as A operand units: k-tile t, columns 16 t + 4 q + 0..3
+    const float* ph = p.sp_phi + ((int64_t)u * DK + 16 * rt + n) * DK + 4 * q;
+    f32x4 a[DK / 16];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = psr[e];
+    for (int t = 0; t < DK / 16; ++t) a[t] = *(const f32x4*)(ph + 16 * t);
 #pragma unroll
-  for (int i = 0; i < DK / 4; ++i)
+    for (int t = 0; t < DK / 16; ++t) mma16_f32_ab(acc, a[t], sB[t][lane]);
+    settle(acc);
+    float* dst = p.final_state + ((int64_t)u * DK + 16 * rt + 4 * q) * DV + 16 * ct + n;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const f32x4 h0 = *(const f32x4*)&sH[4 * i + ii][j0];
-      const f32x4 h1 = *(const f32x4*)&sH[4 * i + ii][j0 + 4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] = __builtin_fmaf(a[i][ii], h0[e], acc[e]);
-        acc[4 + e] = __builtin_fmaf(a[i][ii], h1[e], acc[4 + e]);
-      }
-    }
-  float* dst = p.final_state + ((int64_t)u * DK + k) * DV + 16 * ct + j0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) dst[e] = acc[e];
+    for (int e = 0; e < 4; ++e) dst[(int64_t)e * DV] = acc[e];
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -226,11 +226,11 @@ typedef struct gdn_options {
  * The state scan's schedule.  Each chunk maps its incoming state affinely
  * (the recurrence above summed over a chunk): H' = M H + B with
  * M = e^{gamma_last} I - K~^T W and B = K~^T U~.
- * GDN_SCAN_TWO_LEVEL splits every sequence (at 5/8 of its chunks) and scans
+ * GDN_SCAN_TWO_LEVEL splits every sequence (at about 17/32 of its chunks) and scans
  * both halves at once: the second from zero, beside the product of its M
  * (d_k more state columns), then adds M-product x (state at the split) to
  * its outputs and final state.  The chain of dependent chunk steps shortens
- * to 5/8 of the chunks; the arithmetic differs from the one-pass scan only
+ * to about 17/32 of the chunks; the arithmetic differs from the one-pass scan only
  * in rounding.  Offered
  * for bf16 inputs without cu_seqlens (uniform sequences), d_k and d_v
  * multiples of 32 and chunks of 32 or 64; GDN_SCAN_TWO_LEVEL elsewhere is

@@ -141,7 +141,7 @@ int main() {
     gdn_default_options(&o);
     o.scan_split = GDN_SCAN_TWO_LEVEL;
     expect(gdn_get_workspace_layout(&a.q, &a.k, &a.v, nullptr, &o, &lay), GDN_OK, "two-level layout");
-    if (lay.split_chunks != 40 || lay.total_bytes <= n) {
+    if (lay.split_chunks != 34 || lay.total_bytes <= n) {
       std::printf("FAIL two-level layout values\n");
       ++fails;
     }

@@ -1,7 +1,7 @@
 """The two-level scan (scan_split = SCAN_TWO_LEVEL) against the float64
 oracle (GPU), beside the one-pass scan on the same inputs.
 
-The two-level scan splits each sequence (at 5/8 of its chunks), scans the
+The two-level scan splits each sequence (at about 17/32 of its chunks), scans the
 second part from zero beside the product of its chunk transitions, and
 corrects the second part's outputs and the final state; the oracle is the
 token recurrence, which knows nothing of segments.  Cases cover an odd
@@ -76,7 +76,7 @@ def test_two_level_uniform_batch_4d():
     v4 = lambda x: x.view(B, L, *x.shape[1:])  # noqa: E731
     lay = G.gdn_get_workspace_layout(v4(d["q"]), v4(d["k"]), v4(d["v"]),
                                      opts=G.options(scan_split=G.SCAN_TWO_LEVEL))
-    assert lay.split_chunks == 3
+    assert lay.split_chunks == 2  # (17 x 4 + 16) // 32
     U.say("  gpu run: uniform batch 3 x 256 as 4-D, two-level")
     G.gdn_prefill_ex(v4(d["q"]), v4(d["k"]), v4(d["v"]), v4(d["g"]), v4(d["beta"]), None,
                      d["init_state"], v4(d["out"]), d["final_state"],
@@ -101,11 +101,11 @@ def test_two_level_without_final_state():
 
 
 def test_prompt_4k_full_two_level():
-    """The 4096-token prompt split at chunk 40."""
+    """The 4096-token prompt split at chunk 34."""
     w = W.make_workload("prompt_4k")
     d = W.to_device(w)
     lay = G.gdn_get_workspace_layout(d["q"], d["k"], d["v"], opts=G.options(scan_split=G.SCAN_TWO_LEVEL))
-    assert lay.split_chunks == 40
+    assert lay.split_chunks == 34  # (17 x 64 + 16) // 32
     ro, rf = oracle.reference_workload(w)
     out2, fin2, _ = U.run_gpu(w, dev=d, scan_split=G.SCAN_TWO_LEVEL)
     U.check_bf16(out2, fin2, ro, rf, label="prompt_4k full, two-level")
